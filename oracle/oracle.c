@@ -1,0 +1,442 @@
+/*
+ * oracle.c -- CPU oracle of the sigmoid top-k routed MoE block.
+ *
+ * TEST INFRASTRUCTURE ONLY. The tests, the smoke check and the benchmark's
+ * CPU baseline call this; the product path never does. It shares no code,
+ * header, table or constant with the HIP library: every step below is
+ * written out again from the pages' statement of the layer.
+ *
+ * What the block computes (one token t with input row x_t):
+ *   router   z[e]  = sum_h x[t,h] * Wr[e,h]                 fp32, see below
+ *            s[e]  = sigmoid(z[e])                          fp32, see below
+ *            key[e]= s[e] + bias[e]                         fp32
+ *   select   ids   = the k experts of largest key           (bias selects only)
+ *   weights  w_j   = s[ids_j] / (sum_j s[ids_j] + eps)      unbiased scores
+ *   experts  SwiGLU: y = W_d (silu(W_g x) * (W_u x)),  W_gu = [W_g; W_u]
+ *            relu^2: y = W_d (relu(W_up x))^2
+ *   combine  out_t = rsf * sum_j w_j y_{t,j} + shared_t     rsf on the sum
+ *            shared_t = W_sd act(W_su x_t), unscaled
+ * Sources: TileGym PR #187 "Weight layout and routing" (gate_up (E,2I,H),
+ * gate rows first; sigmoid scores; bias selects only; divide by sum + 1e-6,
+ * then the routed scaling factor); TensorFold PR #1492 "What" (fp32 router
+ * weights, expert bias, normalised top-4, eps 1e-6) and "Verification" (an
+ * all-NaN router row must not pick one expert twice; float64 reference with
+ * the 4-bit weights dequantised exactly); vllm.cpp PR #684 "The seam
+ * decision" and the W2 commit (relu^2 expert; routed scale multiplies the
+ * finished routed sum before the unscaled shared term is added);
+ * bloomery PR #235 "What" (relu^2 keeps a non-finite input non-finite).
+ *
+ * Precision. Routing is discontinuous in the scores, so the router is not
+ * left to float64: the logits, sigmoid and keys are fp32 in a fixed order
+ * (the pages state the router is fp32; the order and the sigmoid are this
+ * project's reading, spelled out below). Everything after the selection is
+ * float64, with bf16, fp32 and 4-bit inputs converted exactly.
+ *
+ * Build: gcc -O2 -fPIC -shared -fopenmp -ffp-contract=off -fno-fast-math.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ------------------------------------------------------------------ */
+/* inputs                                                              */
+/* ------------------------------------------------------------------ */
+
+/* bf16 -> fp32 is exact: the 16 bits are the top half of the fp32 word. */
+static float bf16_value(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* MLX-style 4-bit affine weight, exactly: element c of row n is
+ * scale[n][c/64] * q + bias[n][c/64], q the nibble at bits 4*(c%8) of word
+ * c/8 (TensorFold PR #1492 "What": MLX 4-bit affine experts; packing is
+ * this project's stated convention). The product of a bf16 scale and a
+ * 4-bit integer and its sum with a bf16 bias are exact in float64. */
+static double affine4_value(const uint32_t *codes_row, const uint16_t *scale_row,
+                            const uint16_t *bias_row, int c, int group)
+{
+    uint32_t q = (codes_row[c / 8] >> (4 * (c % 8))) & 0xFu;
+    return (double)bf16_value(scale_row[c / group]) * (double)q
+         + (double)bf16_value(bias_row[c / group]);
+}
+
+/* ------------------------------------------------------------------ */
+/* router (fp32)                                                       */
+/* ------------------------------------------------------------------ */
+
+/* z = sum over h of x[h] * w[h], accumulated in fp32 from +0, one fused
+ * multiply-add per term, h ascending: acc = fmaf(x[h], w[h], acc). */
+static float router_logit(const uint16_t *x_row, const float *w_row, int H)
+{
+    float acc = 0.0f;
+    for (int h = 0; h < H; ++h)
+        acc = fmaf(bf16_value(x_row[h]), w_row[h], acc);
+    return acc;
+}
+
+/* exp in fp32 for v in [-17, 87] (the sigmoid below never asks for more).
+ * Cody-Waite reduction: n = rint(v * log2 e), r = v - n*ln2 with ln2 split
+ * into a high part carrying trailing zero bits and a low remainder, so that
+ * |r| <= ln2/2 (plus rounding). exp(r) is the Taylor series of e^r through
+ * r^7 (the r^8/8! term is below 6e-9 relative on that interval), summed in
+ * Horner form with fmaf. Finally e^v = 2^n * e^r, an exact scaling. */
+float oracle_exp32(float v)
+{
+    const float log2e = 1.44269504088896340736f;  /* log2(e) rounded to fp32 */
+    const float ln2_hi = 0.693145751953125f;       /* 0x3F317200, 9 low zero bits */
+    const float ln2_lo = 1.42860676533018700e-06f; /* ln 2 - ln2_hi, to fp32 */
+    float n = rintf(v * log2e);
+    float r = fmaf(-n, ln2_hi, v);
+    r = fmaf(-n, ln2_lo, r);
+    float p = 1.0f / 5040.0f;           /* 1/7! */
+    p = fmaf(p, r, 1.0f / 720.0f);      /* 1/6! */
+    p = fmaf(p, r, 1.0f / 120.0f);      /* 1/5! */
+    p = fmaf(p, r, 1.0f / 24.0f);       /* 1/4! */
+    p = fmaf(p, r, 1.0f / 6.0f);        /* 1/3! */
+    p = fmaf(p, r, 0.5f);               /* 1/2! */
+    p = fmaf(p, r, 1.0f);               /* 1/1! */
+    p = fmaf(p, r, 1.0f);               /* 1/0! */
+    return ldexpf(p, (int)n);
+}
+
+/* sigmoid(z) = 1 / (1 + e^-z) in fp32 with a correctly rounded division.
+ * NaN stays NaN; above 17 the quotient is 1 in fp32 anyway, below -87 the
+ * result is taken as 0 so every intermediate stays a normal number. */
+float oracle_sigmoid32(float z)
+{
+    if (z != z)
+        return z;
+    if (z > 17.0f)
+        return 1.0f;
+    if (z < -87.0f)
+        return 0.0f;
+    return 1.0f / (1.0f + oracle_exp32(-z));
+}
+
+/* Elementwise forms of the two functions above, for sweeps. */
+void oracle_exp32_many(const float *v, int n, float *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = oracle_exp32(v[i]);
+}
+
+void oracle_sigmoid32_many(const float *z, int n, float *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = oracle_sigmoid32(z[i]);
+}
+
+/* a ranks before b: any number before NaN; larger key first; equal keys
+ * (+0 and -0 are equal) and NaN against NaN go to the lower index. */
+static int ranks_before(float ka, int a, float kb, int b)
+{
+    int na = (ka != ka), nb = (kb != kb);
+    if (na != nb)
+        return nb;
+    if (!na && ka != kb)
+        return ka > kb;
+    return a < b;
+}
+
+/* ids[0..k-1] = the k best experts by ranks_before, best first. Plain
+ * selection: each pick scans every expert not yet picked, so the picks are
+ * distinct whatever the keys are (an all-NaN row gives 0, 1, ..., k-1). */
+void oracle_topk(const float *keys, int E, int k, int32_t *ids)
+{
+    unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
+    for (int j = 0; j < k; ++j) {
+        int best = -1;
+        for (int e = 0; e < E; ++e) {
+            if (taken[e])
+                continue;
+            if (best < 0 || ranks_before(keys[e], e, keys[best], best))
+                best = e;
+        }
+        taken[best] = 1;
+        ids[j] = best;
+    }
+    free(taken);
+}
+
+/* Route one token: fp32 logits, sigmoid and keys; top-k by key; float64
+ * weights from the unbiased scores. No routed scaling factor here: it
+ * scales the finished routed sum in the combine. */
+static void route_row(const uint16_t *x_row, const float *Wr, const float *bias, int H, int E,
+                      int k, int norm_topk, double eps, float *z, float *s, float *key,
+                      int32_t *ids, double *w)
+{
+    for (int e = 0; e < E; ++e) {
+        z[e] = router_logit(x_row, Wr + (size_t)e * H, H);
+        s[e] = oracle_sigmoid32(z[e]);
+        key[e] = s[e] + (bias ? bias[e] : 0.0f);
+    }
+    oracle_topk(key, E, k, ids);
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j)
+        sum += (double)s[ids[j]];
+    for (int j = 0; j < k; ++j)
+        w[j] = norm_topk ? (double)s[ids[j]] / (sum + eps) : (double)s[ids[j]];
+}
+
+/* Route every token. z, s (each [T,E]) may be NULL. */
+void oracle_route(int T, int H, int E, int k, const uint16_t *x, const float *Wr,
+                  const float *bias, int norm_topk, double eps, float *z_out, float *s_out,
+                  int32_t *ids, double *w, int nthreads)
+{
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        float *z = (float *)malloc(sizeof(float) * (size_t)E * 3);
+        float *s = z + E, *key = z + 2 * E;
+#pragma omp for schedule(static)
+        for (int t = 0; t < T; ++t) {
+            route_row(x + (size_t)t * H, Wr, bias, H, E, k, norm_topk, eps, z, s, key,
+                      ids + (size_t)t * k, w + (size_t)t * k);
+            if (z_out)
+                memcpy(z_out + (size_t)t * E, z, sizeof(float) * E);
+            if (s_out)
+                memcpy(s_out + (size_t)t * E, s, sizeof(float) * E);
+        }
+        free(z);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* plan                                                                */
+/* ------------------------------------------------------------------ */
+
+/* Counting sort of assignments a = t*k + j by expert ids[a], stable in a.
+ * counts[E]; offsets[E+1] with offsets[E] = T*k; sorted[p] = the p-th
+ * assignment in expert-major order; slot_of[a] = its position p. */
+void oracle_plan(int T, int k, int E, const int32_t *ids, int32_t *counts, int32_t *offsets,
+                 int32_t *sorted, int32_t *slot_of)
+{
+    int A = T * k;
+    for (int e = 0; e < E; ++e)
+        counts[e] = 0;
+    for (int a = 0; a < A; ++a)
+        counts[ids[a]] += 1;
+    offsets[0] = 0;
+    for (int e = 0; e < E; ++e)
+        offsets[e + 1] = offsets[e] + counts[e];
+    int32_t *fill = (int32_t *)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+    for (int e = 0; e < E; ++e)
+        fill[e] = offsets[e];
+    for (int a = 0; a < A; ++a) {
+        int p = fill[ids[a]]++;
+        sorted[p] = a;
+        slot_of[a] = p;
+    }
+    free(fill);
+}
+
+/* ------------------------------------------------------------------ */
+/* experts (float64)                                                   */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    int32_t T, H, I, E, k;
+    int32_t act;        /* 0 SwiGLU, 1 relu^2 */
+    int32_t wfmt;       /* 0 bf16, 1 affine-4 */
+    int32_t group;      /* affine-4 group size along the input dimension */
+    int32_t norm_topk;
+    int32_t I_shared;   /* 0: no shared expert */
+    double norm_eps;
+    double rsf;
+    const uint16_t *x;        /* [T,H] bf16 */
+    const float *router_w;    /* [E,H] */
+    const float *bias;        /* [E] or NULL */
+    const void *w_up;         /* bf16 [E,n_up,H] or uint32 codes [E,n_up,H/8] */
+    const uint16_t *w_up_scales, *w_up_biases;     /* [E,n_up,H/group] */
+    const void *w_down;       /* bf16 [E,H,I] or uint32 codes [E,H,I/8] */
+    const uint16_t *w_down_scales, *w_down_biases; /* [E,H,I/group] */
+    const uint16_t *shared_up;   /* bf16 [n_sup,H]: n_sup = 2*I_s (SwiGLU) or I_s */
+    const uint16_t *shared_down; /* bf16 [H,I_s] */
+} oracle_layer;
+
+/* Row n of a weight matrix with K inputs, as float64. */
+static void weight_row(const oracle_layer *L, int is_up, int e, int n, int N, int K, double *row)
+{
+    size_t r = (size_t)e * N + n;
+    if (L->wfmt == 0) {
+        const uint16_t *w = (const uint16_t *)(is_up ? L->w_up : L->w_down) + r * K;
+        for (int c = 0; c < K; ++c)
+            row[c] = (double)bf16_value(w[c]);
+    } else {
+        int G = K / L->group;
+        const uint32_t *codes = (const uint32_t *)(is_up ? L->w_up : L->w_down) + r * (K / 8);
+        const uint16_t *sc = (is_up ? L->w_up_scales : L->w_down_scales) + r * G;
+        const uint16_t *bi = (is_up ? L->w_up_biases : L->w_down_biases) + r * G;
+        for (int c = 0; c < K; ++c)
+            row[c] = affine4_value(codes, sc, bi, c, L->group);
+    }
+}
+
+static double dot(const double *a, const double *b, int n)
+{
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i)
+        acc += a[i] * b[i];
+    return acc;
+}
+
+/* The activation between the two projections, in float64.
+ * SwiGLU: silu(g) * u = g / (1 + e^-g) * u.
+ * relu^2: (u < 0 ? 0 : u)^2, so NaN and +inf pass through, -inf gives 0. */
+static double activate(int act, double g, double u)
+{
+    if (act == 0)
+        return g / (1.0 + exp(-g)) * u;
+    double r = (u < 0.0) ? 0.0 : u;
+    return r * r;
+}
+
+/* The activation, exported for direct checks of its special values. */
+double oracle_activate(int act, double g, double u)
+{
+    return activate(act, g, u);
+}
+
+/* One expert MLP on one input row: y[H] = W_d act(W_up xr). scratch holds
+ * 2*I + max(H, I) doubles. */
+static void expert_mlp(const oracle_layer *L, int e, const double *xr, double *y, double *scratch)
+{
+    int H = L->H, I = L->I;
+    int n_up = (L->act == 0) ? 2 * I : I;
+    double *proj = scratch;            /* [n_up] */
+    double *row = scratch + 2 * I;     /* [max(H, I)] */
+    for (int n = 0; n < n_up; ++n) {
+        weight_row(L, 1, e, n, n_up, H, row);
+        proj[n] = dot(row, xr, H);
+    }
+    for (int i = 0; i < I; ++i)
+        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[I + i]) : activate(1, 0.0, proj[i]);
+    for (int h = 0; h < H; ++h) {
+        weight_row(L, 0, e, h, H, I, row);
+        y[h] = dot(row, proj, I);
+    }
+}
+
+/* The shared expert on one row, unscaled: W_sd act(W_su xr). */
+static void shared_mlp(const oracle_layer *L, const double *xr, double *y, double *scratch)
+{
+    int H = L->H, Is = L->I_shared;
+    int n_up = (L->act == 0) ? 2 * Is : Is;
+    double *proj = scratch;            /* [n_up] */
+    double *row = scratch + 2 * Is;    /* [max(H, Is)] */
+    for (int n = 0; n < n_up; ++n) {
+        const uint16_t *w = L->shared_up + (size_t)n * H;
+        for (int c = 0; c < H; ++c)
+            row[c] = (double)bf16_value(w[c]);
+        proj[n] = dot(row, xr, H);
+    }
+    for (int i = 0; i < Is; ++i)
+        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[Is + i]) : activate(1, 0.0, proj[i]);
+    for (int h = 0; h < H; ++h) {
+        const uint16_t *w = L->shared_down + (size_t)h * Is;
+        for (int c = 0; c < Is; ++c)
+            row[c] = (double)bf16_value(w[c]);
+        y[h] = dot(row, proj, Is);
+    }
+}
+
+/* The whole block for the listed tokens, in float64: out[i,:] is the
+ * block's output row for token tokens[i]. ids / w (each [ntok,k], may be
+ * NULL) receive that token's routing. Tokens are independent, so they are
+ * spread over threads; nothing is reordered inside a token. */
+int oracle_forward_tokens(const oracle_layer *L, const int32_t *tokens, int ntok, double *out,
+                          int32_t *ids_out, double *w_out, int nthreads)
+{
+    int H = L->H, I = L->I, E = L->E, k = L->k;
+    int Is = L->I_shared;
+    int wide = (I > Is ? I : Is);
+    size_t scratch_n = (size_t)2 * wide + (size_t)(H > wide ? H : wide);
+#ifdef _OPENMP
+    if (nthreads > 0)
+        omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    int bad = 0;
+#pragma omp parallel
+    {
+        double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+        double *y = (double *)malloc(sizeof(double) * (size_t)H);
+        double *acc = (double *)malloc(sizeof(double) * (size_t)H);
+        double *scratch = (double *)malloc(sizeof(double) * scratch_n);
+        float *zsk = (float *)malloc(sizeof(float) * (size_t)E * 3);
+        int32_t *ids = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+        double *w = (double *)malloc(sizeof(double) * (size_t)k);
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < ntok; ++i) {
+            int t = tokens[i];
+            if (t < 0 || t >= L->T) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            const uint16_t *x_row = L->x + (size_t)t * H;
+            route_row(x_row, L->router_w, L->bias, H, E, k, L->norm_topk, L->norm_eps, zsk,
+                      zsk + E, zsk + 2 * E, ids, w);
+            for (int h = 0; h < H; ++h)
+                xr[h] = (double)bf16_value(x_row[h]);
+            for (int h = 0; h < H; ++h)
+                acc[h] = 0.0;
+            for (int j = 0; j < k; ++j) {
+                expert_mlp(L, ids[j], xr, y, scratch);
+                for (int h = 0; h < H; ++h)
+                    acc[h] += w[j] * y[h];
+            }
+            double *o = out + (size_t)i * H;
+            for (int h = 0; h < H; ++h)
+                o[h] = L->rsf * acc[h];
+            if (Is > 0) {
+                shared_mlp(L, xr, y, scratch);
+                for (int h = 0; h < H; ++h)
+                    o[h] += y[h];
+            }
+            if (ids_out)
+                memcpy(ids_out + (size_t)i * k, ids, sizeof(int32_t) * k);
+            if (w_out)
+                memcpy(w_out + (size_t)i * k, w, sizeof(double) * k);
+        }
+        free(xr); free(y); free(acc); free(scratch); free(zsk); free(ids); free(w);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Decode rows r0..r0+nr-1 of an affine-4 matrix with K inputs to float64. */
+void oracle_affine4_decode(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                           int rows, int K, int group, double *out)
+{
+    int G = K / group;
+    for (int n = 0; n < rows; ++n)
+        for (int c = 0; c < K; ++c)
+            out[(size_t)n * K + c] = affine4_value(codes + (size_t)n * (K / 8),
+                                                   scales + (size_t)n * G,
+                                                   biases + (size_t)n * G, c, group);
+}
+
+/* Number of threads an OpenMP region here would use. */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,209 @@
+"""ctypes wrapper of ``oracle.c`` (test infrastructure only).
+
+The C source is the oracle: plain loops, fp32 router in a fixed order,
+float64 everywhere after the selection. This file only builds it with gcc
+and marshals NumPy arrays; it holds no step of the block's arithmetic.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "oracle.c")
+DEFAULT_LIB = os.path.join(HERE, "liboracle.so")
+# ORACLE_LIB points the wrapper at another build of oracle.c (the mutation
+# tests load deliberately broken copies this way).
+LIBPATH = os.environ.get("ORACLE_LIB") or DEFAULT_LIB
+CFLAGS = ["-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+          "-std=c11", "-Wall", "-Wextra", "-Werror"]
+
+_lib = None
+
+
+def compile_source(source: str, out: str, werror: bool = True) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    flags = CFLAGS if werror else [f for f in CFLAGS if f != "-Werror"]
+    subprocess.run(["gcc", *flags, source, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (always, unless force is False and it exists)."""
+    if force or not os.path.exists(DEFAULT_LIB) or \
+            os.path.getmtime(DEFAULT_LIB) < os.path.getmtime(SOURCE):
+        compile_source(SOURCE, DEFAULT_LIB)
+    return DEFAULT_LIB
+
+
+class Layer(C.Structure):
+    _fields_ = [
+        ("T", C.c_int32), ("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32), ("k", C.c_int32),
+        ("act", C.c_int32), ("wfmt", C.c_int32), ("group", C.c_int32), ("norm_topk", C.c_int32),
+        ("I_shared", C.c_int32), ("norm_eps", C.c_double), ("rsf", C.c_double),
+        ("x", C.c_void_p), ("router_w", C.c_void_p), ("bias", C.c_void_p),
+        ("w_up", C.c_void_p), ("w_up_scales", C.c_void_p), ("w_up_biases", C.c_void_p),
+        ("w_down", C.c_void_p), ("w_down_scales", C.c_void_p), ("w_down_biases", C.c_void_p),
+        ("shared_up", C.c_void_p), ("shared_down", C.c_void_p),
+    ]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if "ORACLE_LIB" not in os.environ and (
+                not os.path.exists(LIBPATH) or os.path.getmtime(LIBPATH) < os.path.getmtime(SOURCE)):
+            build()
+        L = C.CDLL(LIBPATH)
+        p = C.c_void_p
+        i = C.c_int
+        L.oracle_exp32.restype = C.c_float
+        L.oracle_exp32.argtypes = [C.c_float]
+        L.oracle_sigmoid32.restype = C.c_float
+        L.oracle_sigmoid32.argtypes = [C.c_float]
+        L.oracle_exp32_many.argtypes = [p, i, p]
+        L.oracle_sigmoid32_many.argtypes = [p, i, p]
+        L.oracle_topk.argtypes = [p, i, i, p]
+        L.oracle_route.argtypes = [i, i, i, i, p, p, p, i, C.c_double, p, p, p, p, i]
+        L.oracle_plan.argtypes = [i, i, i, p, p, p, p, p]
+        L.oracle_forward_tokens.argtypes = [C.POINTER(Layer), p, i, p, p, p, i]
+        L.oracle_forward_tokens.restype = C.c_int
+        L.oracle_affine4_decode.argtypes = [p, p, p, i, i, i, p]
+        L.oracle_max_threads.restype = C.c_int
+        L.oracle_activate.restype = C.c_double
+        L.oracle_activate.argtypes = [i, C.c_double, C.c_double]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
+
+
+def exp32(v) -> np.ndarray:
+    v = _c(np.atleast_1d(v), np.float32)
+    out = np.empty_like(v)
+    lib().oracle_exp32_many(_ptr(v), v.size, _ptr(out))
+    return out
+
+
+def sigmoid32(z) -> np.ndarray:
+    z = _c(np.atleast_1d(z), np.float32)
+    out = np.empty_like(z)
+    lib().oracle_sigmoid32_many(_ptr(z), z.size, _ptr(out))
+    return out
+
+
+def activate(act: str, g: float, u: float) -> float:
+    """The expert activation in float64: act "swiglu" -> silu(g)*u, "relu2" -> relu(u)^2."""
+    return lib().oracle_activate(0 if act == "swiglu" else 1, float(g), float(u))
+
+
+def topk(keys, k: int) -> np.ndarray:
+    keys = _c(keys, np.float32)
+    ids = np.empty(k, dtype=np.int32)
+    lib().oracle_topk(_ptr(keys), keys.size, k, _ptr(ids))
+    return ids
+
+
+def route(x, router_w, bias, k: int, norm_topk: bool = True, eps: float = 1e-6,
+          want_scores: bool = False, nthreads: int = 0):
+    """Route every token. Returns ids [T,k] int32 and w [T,k] float64, plus
+    z and s [T,E] fp32 when want_scores."""
+    x = _c(x, np.uint16)
+    router_w = _c(router_w, np.float32)
+    bias = _c(bias, np.float32)
+    T, H = x.shape
+    E = router_w.shape[0]
+    ids = np.empty((T, k), dtype=np.int32)
+    w = np.empty((T, k), dtype=np.float64)
+    z = np.empty((T, E), dtype=np.float32) if want_scores else None
+    s = np.empty((T, E), dtype=np.float32) if want_scores else None
+    lib().oracle_route(T, H, E, k, _ptr(x), _ptr(router_w), _ptr(bias), int(norm_topk), eps,
+                       _ptr(z), _ptr(s), _ptr(ids), _ptr(w), nthreads)
+    if want_scores:
+        return ids, w, z, s
+    return ids, w
+
+
+def plan(ids, E: int):
+    """Counting sort of the assignments by expert. Returns counts [E],
+    offsets [E+1], sorted [A], slot_of [A] (int32)."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    A = T * k
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    srt = np.empty(A, dtype=np.int32)
+    slot = np.empty(A, dtype=np.int32)
+    lib().oracle_plan(T, k, E, _ptr(ids), _ptr(counts), _ptr(offsets), _ptr(srt), _ptr(slot))
+    return counts, offsets, srt, slot
+
+
+def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool = False):
+    """The block's float64 output rows for ``tokens`` ([n, H] float64).
+
+    ``wl`` carries the shapes and flags (a workloads.Workload or anything
+    with the same attributes); ``inp`` the arrays from workloads.generate.
+    """
+    tokens = _c(np.atleast_1d(tokens), np.int32)
+    keep = {}
+
+    def arr(name, dtype):
+        a = inp.get(name)
+        if a is None:
+            return None
+        a = _c(a, dtype)
+        keep[name] = a
+        return a.ctypes.data
+
+    affine = wl.wfmt == "affine4"
+    L = Layer(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
+              act=0 if wl.act == "swiglu" else 1, wfmt=1 if affine else 0,
+              group=wl.group if affine else 0, norm_topk=int(wl.norm_topk),
+              I_shared=wl.I_shared, norm_eps=wl.norm_eps, rsf=wl.rsf,
+              x=arr("x", np.uint16), router_w=arr("router_w", np.float32),
+              bias=arr("bias", np.float32),
+              w_up=arr("w_up", np.uint32 if affine else np.uint16),
+              w_up_scales=arr("w_up_scales", np.uint16), w_up_biases=arr("w_up_biases", np.uint16),
+              w_down=arr("w_down", np.uint32 if affine else np.uint16),
+              w_down_scales=arr("w_down_scales", np.uint16),
+              w_down_biases=arr("w_down_biases", np.uint16),
+              shared_up=arr("shared_up", np.uint16) if wl.I_shared else None,
+              shared_down=arr("shared_down", np.uint16) if wl.I_shared else None)
+    n = tokens.size
+    out = np.empty((n, wl.H), dtype=np.float64)
+    ids = np.empty((n, wl.k), dtype=np.int32)
+    w = np.empty((n, wl.k), dtype=np.float64)
+    rc = lib().oracle_forward_tokens(C.byref(L), _ptr(tokens), n, _ptr(out), _ptr(ids), _ptr(w),
+                                     nthreads)
+    if rc != 0:
+        raise ValueError("token index out of range")
+    if want_routing:
+        return out, ids, w
+    return out
+
+
+def affine4_decode(codes, scales, biases, group: int = 64) -> np.ndarray:
+    """Dequantise affine-4 rows exactly: codes [rows, K/8] uint32, scales and
+    biases [rows, K/group] bf16 bits -> [rows, K] float64."""
+    codes = _c(codes, np.uint32)
+    scales = _c(scales, np.uint16)
+    biases = _c(biases, np.uint16)
+    rows, kw = codes.shape
+    K = kw * 8
+    out = np.empty((rows, K), dtype=np.float64)
+    lib().oracle_affine4_decode(_ptr(codes), _ptr(scales), _ptr(biases), rows, K, group, _ptr(out))
+    return out

@@ -1,0 +1,276 @@
+"""Seeded synthetic workloads for the sigmoid top-k routed MoE block.
+
+This module only draws numbers. It holds no step of the block's arithmetic:
+no router, no sigmoid, no top-k, no expert MLP. Both the HIP path and the
+CPU oracle are fed from here, and nothing here depends on either of them.
+
+Shapes follow the MoE blocks the pages rebuild:
+  * LFM2-8B-A1B: 32 experts, top-4, SwiGLU experts with a fused gate_up
+    weight (E, 2I, H), gate rows first, and down (E, H, I)
+    (TileGym PR #187, "Weight layout and routing").
+  * Nemotron-H: non-gated relu^2 experts (up (E, I, H), down (E, H, I)), a
+    routed scaling factor on the routed sum and an unscaled shared expert
+    (vllm.cpp PR #684, "The seam decision" and the W2 commit message).
+  * MLX 4-bit affine experts, group 64 (TensorFold PR #1492, "What").
+
+Every tensor is drawn in fp32 from NumPy's PCG64 and, where the layer stores
+bf16, rounded to bf16 by round-to-nearest-even. The draws come in a fixed
+order from ``np.random.SeedSequence([0x5EED, seed]).spawn(10)``:
+x, router weight, expert bias, up weight, down weight, shared up, shared
+down, 4-bit codes, 4-bit scales, 4-bit biases. Long draws are taken in
+chunks of 2**24 values from one generator, so the stream is fixed.
+
+Affine-4 packing (our convention, the inputs being synthetic): element c of
+a row lives in 32-bit word c // 8 at bits 4 * (c % 8) (little nibble
+first); the scale and bias of element c are entry c // 64 of the row.
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CHUNK = 1 << 24
+BF16_NAN = 0x7FC0
+BF16_ONE = 0x3F80
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic MoE-block workload.
+
+    act: "swiglu" (gate_up (E, 2I, H), gate rows first) or "relu2"
+    (up (E, I, H)). wfmt: "bf16" or "affine4" (group 64).
+    """
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    act: str = "swiglu"
+    wfmt: str = "bf16"
+    rsf: float = 1.0
+    I_shared: int = 0
+    norm_topk: bool = True
+    norm_eps: float = 1e-6
+    x_std: float = 1.0
+    w_std: float = 0.02
+    router_std: float = 0.02
+    bias_lo: float = -0.05
+    bias_hi: float = 0.05
+    seed: int = 0
+    weight_seed: int | None = None   # draw weights from another seed's stream
+    boost: float = 0.0
+    boosted: tuple = ()
+    nan_rows: tuple = ()
+    zero_tie_row: int | None = None  # x row of zeros + triple bias tie
+    onehot_tie_row: int | None = None  # one-hot x row + two equal logits
+    tie_col: int = 7
+    scale_lo: float = 0.005
+    scale_hi: float = 0.02
+    qbias_lo: float = -0.1
+    qbias_hi: float = 0.1
+    group: int = 64
+
+    @property
+    def A(self) -> int:
+        return self.T * self.k
+
+    @property
+    def n_up(self) -> int:
+        return 2 * self.I if self.act == "swiglu" else self.I
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of this block, in order: a tiny case the oracle runs
+# whole, the LFM2-MoE-shaped prefill chunk, the decode step on the same
+# weights, the Nemotron-H-shaped relu^2 block with a shared expert, and the
+# 4-bit affine experts with four boosted experts.
+TINY = Workload("tiny_t64_e8_k2", T=64, H=128, I=256, E=8, k=2, bias_lo=-0.1, bias_hi=0.1,
+                seed=0, nan_rows=(5, 17), zero_tie_row=30, onehot_tie_row=47)
+PREFILL = Workload("lfm2_prefill_t4096", T=4096, H=2048, I=1792, E=32, k=4, seed=1)
+DECODE = Workload("lfm2_decode_t8", T=8, H=2048, I=1792, E=32, k=4, seed=2, weight_seed=1)
+RELU2 = Workload("nemotron_relu2_t2048", T=2048, H=2688, I=1856, E=128, k=6, act="relu2",
+                 rsf=2.5, I_shared=3712, bias_lo=-0.1, bias_hi=0.1, seed=3)
+AFFINE4 = Workload("affine4_t1024", T=1024, H=2048, I=1792, E=32, k=4, wfmt="affine4", seed=4,
+                   boost=2.0, boosted=(3, 11, 19, 27))
+
+CONFIGS = [TINY, PREFILL, DECODE, RELU2, AFFINE4]
+
+# Mid-sized workloads for parity: small enough that the oracle computes every
+# token in seconds, large enough to span several tiles with ragged tails.
+MID = {
+    "mid_swiglu": Workload("mid_swiglu", T=600, H=512, I=320, E=16, k=4, seed=100),
+    "mid_swiglu_bigseg": Workload("mid_swiglu_bigseg", T=1100, H=256, I=384, E=4, k=2, seed=101),
+    "mid_relu2_shared": Workload("mid_relu2_shared", T=300, H=384, I=192, E=24, k=6, act="relu2",
+                                 rsf=2.5, I_shared=448, bias_lo=-0.1, bias_hi=0.1, seed=102),
+    "mid_affine4": Workload("mid_affine4", T=256, H=512, I=256, E=8, k=2, wfmt="affine4",
+                            seed=103),
+    "mid_affine4_relu2": Workload("mid_affine4_relu2", T=200, H=256, I=320, E=12, k=3,
+                                  act="relu2", wfmt="affine4", rsf=1.5, I_shared=192, seed=104),
+    "mid_nan_ties": Workload("mid_nan_ties", T=333, H=320, I=192, E=16, k=8, bias_lo=-0.1,
+                             bias_hi=0.1, seed=105, nan_rows=(0, 100, 332), zero_tie_row=7,
+                             onehot_tie_row=200, tie_col=3),
+    "mid_e256_k8": Workload("mid_e256_k8", T=96, H=192, I=128, E=256, k=8, seed=106),
+}
+
+
+# --------------------------------------------------------------------------
+# bf16 helpers (storage format only)
+# --------------------------------------------------------------------------
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round to nearest, ties to even); NaN -> 0x7FC0."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32)
+    out = ((u + (((u >> 16) & 1) + np.uint32(0x7FFF))) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        out[nan] = BF16_NAN
+    return out
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# --------------------------------------------------------------------------
+# drawing
+# --------------------------------------------------------------------------
+
+def _normal_bf16(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    for s in range(0, n, CHUNK):
+        m = min(CHUNK, n - s)
+        v = rng.standard_normal(m, dtype=np.float32)
+        v *= np.float32(std)
+        out[s:s + m] = f32_to_bf16_bits(v)
+    return out.reshape(shape)
+
+
+def _normal_f32(rng: np.random.Generator, shape, std: float) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, CHUNK):
+        m = min(CHUNK, n - s)
+        out[s:s + m] = rng.standard_normal(m, dtype=np.float32) * np.float32(std)
+    return out.reshape(shape)
+
+
+def _uniform_f32(rng: np.random.Generator, shape, lo: float, hi: float) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    for s in range(0, n, CHUNK):
+        m = min(CHUNK, n - s)
+        u = rng.random(m, dtype=np.float32)
+        out[s:s + m] = np.float32(lo) + np.float32(hi - lo) * u
+    return out.reshape(shape)
+
+
+def _words(rng: np.random.Generator, shape) -> np.ndarray:
+    """Uniform 32-bit words: each of the 8 nibbles is uniform on 0..15."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint32)
+    for s in range(0, n, CHUNK):
+        m = min(CHUNK, n - s)
+        out[s:s + m] = rng.integers(0, 1 << 32, size=m, dtype=np.uint32)
+    return out.reshape(shape)
+
+
+def _children(seed: int):
+    return [np.random.default_rng(c) for c in np.random.SeedSequence([0x5EED, seed]).spawn(10)]
+
+
+def generate(wl: Workload, need_x: bool = True) -> dict:
+    """Draw every input of ``wl``.
+
+    Returns a dict of C-contiguous NumPy arrays. bf16 tensors are uint16 bit
+    patterns. Keys: x [T,H] bf16, router_w [E,H] f32, bias [E] f32, and
+    for bf16 experts w_up [E,n_up,H], w_down [E,H,I] bf16; for affine-4
+    experts w_up (uint32 codes [E,n_up,H/8]), w_up_scales / w_up_biases
+    (bf16 [E,n_up,H/64]) and the same three for w_down ([E,H,I/8],
+    [E,H,I/64]); shared_up [I_s,H] and shared_down [H,I_s] bf16 when
+    I_shared > 0 (shared_up is [2*I_s,H], gate rows first, for SwiGLU).
+    """
+    E, H, I, T = wl.E, wl.H, wl.I, wl.T
+    xs = _children(wl.seed)
+    ws = _children(wl.weight_seed if wl.weight_seed is not None else wl.seed)
+    (c_x, c_wr, c_b, c_up, c_down, c_su, c_sd, c_codes, c_scales, c_qb) = range(10)
+    out = {}
+    if need_x:
+        out["x"] = _normal_bf16(xs[c_x], (T, H), wl.x_std)
+    out["router_w"] = _normal_f32(ws[c_wr], (E, H), wl.router_std)
+    out["bias"] = _uniform_f32(ws[c_b], (E,), wl.bias_lo, wl.bias_hi)
+    if wl.boost:
+        for e in wl.boosted:
+            out["bias"][e] = np.float32(out["bias"][e] + np.float32(wl.boost))
+    n_up = wl.n_up
+    if wl.wfmt == "bf16":
+        out["w_up"] = _normal_bf16(ws[c_up], (E, n_up, H), wl.w_std)
+        out["w_down"] = _normal_bf16(ws[c_down], (E, H, I), wl.w_std)
+    elif wl.wfmt == "affine4":
+        g = wl.group
+        out["w_up"] = _words(ws[c_codes], (E, n_up, H // 8))
+        out["w_down"] = _words(ws[c_codes], (E, H, I // 8))
+        out["w_up_scales"] = f32_to_bf16_bits(_uniform_f32(ws[c_scales], (E, n_up, H // g),
+                                                           wl.scale_lo, wl.scale_hi))
+        out["w_down_scales"] = f32_to_bf16_bits(_uniform_f32(ws[c_scales], (E, H, I // g),
+                                                             wl.scale_lo, wl.scale_hi))
+        out["w_up_biases"] = f32_to_bf16_bits(_uniform_f32(ws[c_qb], (E, n_up, H // g),
+                                                           wl.qbias_lo, wl.qbias_hi))
+        out["w_down_biases"] = f32_to_bf16_bits(_uniform_f32(ws[c_qb], (E, H, I // g),
+                                                             wl.qbias_lo, wl.qbias_hi))
+    else:
+        raise ValueError(f"unknown weight format {wl.wfmt!r}")
+    if wl.I_shared:
+        n_sup = 2 * wl.I_shared if wl.act == "swiglu" else wl.I_shared
+        out["shared_up"] = _normal_bf16(ws[c_su], (n_sup, H), wl.w_std)
+        out["shared_down"] = _normal_bf16(ws[c_sd], (H, wl.I_shared), wl.w_std)
+    _construct_special_rows(wl, out)
+    return out
+
+
+def _construct_special_rows(wl: Workload, out: dict) -> None:
+    """Rows whose routing is fixed by exact arithmetic, not by rounding.
+
+    * NaN rows: every x entry is a bf16 NaN, so every router logit is NaN.
+    * Zero tie row: x is all zeros, so every logit is +0 and every score
+      the same; the bias of experts 1, 4, 6 is set to 0.125, above every
+      other bias, which makes a three-way tie at the top.
+    * One-hot tie row: x has a single 1.0 at column tie_col, and router
+      weights (2, tie_col) and (5, tie_col) are both 2.0, with bias[5] set
+      to bias[2], so experts 2 and 5 tie above the rest.
+    The edits to the router weight and bias change other rows' routing too;
+    they are part of the workload's definition.
+    """
+    x = out.get("x")
+    if x is not None:
+        for r in wl.nan_rows:
+            x[r, :] = BF16_NAN
+    if wl.zero_tie_row is not None:
+        if x is not None:
+            x[wl.zero_tie_row, :] = 0
+        for e in (1, 4, 6):
+            if e < wl.E:
+                out["bias"][e] = np.float32(0.125)
+    if wl.onehot_tie_row is not None and wl.E > 5:
+        if x is not None:
+            x[wl.onehot_tie_row, :] = 0
+            x[wl.onehot_tie_row, wl.tie_col] = BF16_ONE
+        out["router_w"][2, wl.tie_col] = np.float32(2.0)
+        out["router_w"][5, wl.tie_col] = np.float32(2.0)
+        out["bias"][5] = out["bias"][2]
+
+
+def by_name(name: str) -> Workload:
+    for w in CONFIGS:
+        if w.name == name:
+            return w
+    if name in MID:
+        return MID[name]
+    raise KeyError(name)

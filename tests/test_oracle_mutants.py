@@ -1,0 +1,93 @@
+"""Planted mistakes in the oracle must turn its pins red.
+
+Each mutant is a copy of oracle.c with one plausible mistake (a dropped
+term, a wrong sign or index, a swapped operand, a broken tie rule), built
+with gcc into a temporary directory and loaded in a child pytest through
+ORACLE_LIB. The child runs the pins named for that mutant and must fail.
+Everything here runs on the CPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# name: (text in oracle.c, replacement, pin tests that must catch it); the
+# text and replacement may be tuples for a mistake that spans two sites.
+MUTANTS = {
+    "bias_leaks_into_weights": (
+        "(double)s[ids[j]] / (sum + eps)", "(double)key[ids[j]] / (sum + eps)",
+        ["tests/test_oracle_router.py::test_bias_selects_but_never_weighs"]),
+    "eps_dropped": (
+        "(double)s[ids[j]] / (sum + eps)", "(double)s[ids[j]] / (sum)",
+        ["tests/test_oracle_router.py::test_weights_eps_is_visible_at_tiny_scores"]),
+    "routed_scale_on_shared_term": (
+        "o[h] += y[h];", "o[h] += L->rsf * y[h];",
+        ["tests/test_oracle_experts.py::test_routed_scale_is_linear_and_spares_the_shared_term"]),
+    "relu_not_squared": (
+        "return r * r;", "return r;",
+        ["tests/test_oracle_experts.py::test_activation_special_values"]),
+    "gate_up_swapped": (
+        "activate(0, proj[i], proj[I + i])", "activate(0, proj[I + i], proj[i])",
+        ["tests/test_oracle_experts.py::test_hand_layer_closed_form"]),
+    "silu_sign": (
+        "g / (1.0 + exp(-g)) * u", "g / (1.0 + exp(g)) * u",
+        ["tests/test_oracle_experts.py::test_activation_special_values"]),
+    "ties_to_higher_index": (
+        "    return a < b;\n}", "    return a > b;\n}",
+        ["tests/test_oracle_router.py::test_topk_exhaustive_small_domain"]),
+    "nan_ranks_first": (
+        "        return nb;", "        return na;",
+        ["tests/test_oracle_router.py::test_topk_exhaustive_small_domain"]),
+    "plan_unstable": (
+        "    for (int a = 0; a < A; ++a) {\n        int p = fill[ids[a]]++;",
+        "    for (int a = A - 1; a >= 0; --a) {\n        int p = fill[ids[a]]++;",
+        ["tests/test_oracle_plan.py"]),
+    "sigmoid_sign": (
+        "1.0f / (1.0f + oracle_exp32(-z))", "1.0f / (1.0f + oracle_exp32(z))",
+        ["tests/test_oracle_router.py::test_sigmoid32_closed_form_ln3"]),
+    "logit_order_reversed": (
+        "    for (int h = 0; h < H; ++h)\n        acc = fmaf",
+        "    for (int h = H - 1; h >= 0; --h)\n        acc = fmaf",
+        ["tests/test_oracle_router.py::test_logit_order_is_sequential_fp32_fma"]),
+    "logit_in_double": (
+        ("    float acc = 0.0f;\n    for (int h = 0; h < H; ++h)",
+         "acc = fmaf(bf16_value(x_row[h]), w_row[h], acc);"),
+        ("    double acc = 0.0;\n    for (int h = 0; h < H; ++h)",
+         "acc += (double)bf16_value(x_row[h]) * (double)w_row[h];"),
+        ["tests/test_oracle_router.py::test_logit_order_is_sequential_fp32_fma"]),
+    "router_weight_transposed": (
+        "z[e] = router_logit(x_row, Wr + (size_t)e * H, H);",
+        "z[e] = router_logit(x_row, Wr + (size_t)e, H);",
+        ["tests/test_oracle_router.py::test_logit_zero_row_and_one_hot_row"]),
+    "nibbles_big_endian": (
+        "(codes_row[c / 8] >> (4 * (c % 8)))", "(codes_row[c / 8] >> (4 * (7 - c % 8)))",
+        ["tests/test_oracle_experts.py::test_affine4_decode_hand_cases"]),
+    "affine_group_index": (
+        "bf16_value(scale_row[c / group])", "bf16_value(scale_row[c % group])",
+        ["tests/test_oracle_experts.py::test_affine4_decode_hand_cases"]),
+    "exp_taylor_term_dropped": (
+        "    p = fmaf(p, r, 1.0f / 6.0f);        /* 1/3! */\n", "",
+        ["tests/test_oracle_router.py::test_exp32_sweep_against_libm"]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_killed(name, tmp_path):
+    old, new, pins = MUTANTS[name]
+    src = open(O.SOURCE).read()
+    olds, news = (old, new) if isinstance(old, tuple) else ((old,), (new,))
+    for o, n in zip(olds, news):
+        assert src.count(o) == 1, f"mutation site for {name} not unique"
+        src = src.replace(o, n)
+    mut_src = tmp_path / "oracle_mut.c"
+    mut_src.write_text(src)
+    lib = O.compile_source(str(mut_src), str(tmp_path / "liboracle_mut.so"), werror=False)
+    env = dict(os.environ, ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        *pins], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, f"mutant {name} survived:\n{r.stdout[-2000:]}"

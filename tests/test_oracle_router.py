@@ -1,0 +1,217 @@
+"""Pins of the oracle's router: logits, sigmoid, top-k and weights.
+
+Each check ties the oracle to something other than itself: exact rational
+arithmetic, a closed form, a library routine on a special case, or brute
+force over a small domain. Routing rules: TileGym PR #187 "Weight layout
+and routing" (sigmoid scores, the bias selects only, weights divided by
+their sum + 1e-6); TensorFold PR #1492 "What" and "Verification" (fp32
+router, eps 1e-6, an all-NaN row must not pick one expert twice).
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from sigmoid_top_routing_amd import workloads as W
+
+U32 = 2.0 ** -24
+
+
+def f32ulps(got, ref):
+    """|got - ref| in units of the fp32 spacing at ref."""
+    ref32 = np.abs(ref.astype(np.float32))
+    return np.abs(got.astype(np.float64) - ref) / np.spacing(ref32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- exp / sigmoid
+
+def test_exp32_exact_points():
+    assert oracle.exp32([0.0])[0] == np.float32(1.0)
+    # e^(n ln2) for integer n is 2^n up to the reduction's rounding
+    for n in (-20, -1, 1, 10, 100):
+        v = np.float32(n * math.log(2.0))
+        assert abs(float(oracle.exp32([v])[0]) / math.exp(float(v)) - 1.0) < 2.5e-7
+
+
+def test_exp32_sweep_against_libm():
+    v = np.linspace(-17.0, 87.0, 2_000_001, dtype=np.float32)
+    got = oracle.exp32(v)
+    ref = np.exp(v.astype(np.float64))
+    assert f32ulps(got, ref).max() <= 1.0
+
+
+def test_sigmoid32_special_values():
+    s = oracle.sigmoid32(np.array([0.0, -0.0, np.nan, 17.5, 100.0, np.inf, -87.5, -1e30, -np.inf],
+                                  dtype=np.float32))
+    assert s[0] == np.float32(0.5) and s[1] == np.float32(0.5)
+    assert np.isnan(s[2])
+    assert (s[3:6] == 1.0).all()
+    assert (s[6:9] == 0.0).all()
+
+
+def test_sigmoid32_closed_form_ln3():
+    # sigma(ln 3) = 1 / (1 + 1/3) = 3/4
+    z = np.float32(math.log(3.0))
+    s = float(oracle.sigmoid32([z])[0])
+    exact = 1.0 / (1.0 + math.exp(-float(z)))
+    assert abs(s - 0.75) < 1e-7 and abs(s - exact) <= 2 * np.spacing(np.float32(0.75))
+
+
+def test_sigmoid32_sweep_bound_and_monotone():
+    z = np.linspace(-20.0, 20.0, 4_000_001, dtype=np.float32)
+    s = oracle.sigmoid32(z)
+    ref = 1.0 / (1.0 + np.exp(-z.astype(np.float64)))
+    inside = (z >= -87) & (z <= 17)
+    # three fp32 roundings (e^-z, 1 + e^-z, the quotient) on top of exp32's
+    # ulp: the worst case sits near z = -16.6, where 1 + e^-z crosses 2^24
+    # and its rounding alone is 1 part in 1.7e7.
+    assert f32ulps(s[inside], ref[inside]).max() <= 3.0
+    assert (np.diff(s.astype(np.float64)) >= 0).all()
+    # symmetry sigma(-z) = 1 - sigma(z), to fp32 rounding
+    assert np.abs(s + s[::-1] - 1.0).max() < 3e-7
+
+
+# ---------------------------------------------------------------- logits
+
+def _one_token(x_vals, w_rows, bias=None, k=1):
+    H = len(x_vals)
+    x = W.f32_to_bf16_bits(np.array(x_vals, dtype=np.float32)).reshape(1, H)
+    wr = np.array(w_rows, dtype=np.float32).reshape(-1, H)
+    b = np.zeros(wr.shape[0], np.float32) if bias is None else np.array(bias, np.float32)
+    return oracle.route(x, wr, b, k, want_scores=True)
+
+
+def test_logit_order_is_sequential_fp32_fma():
+    # x = [1, 1, 1, 1], w = [1, 2^24, 1, -2^24]. Exact sum 2; fp32 pairwise
+    # sum 1; fp32 reverse order 2; fp32 ascending fma chain: 1 -> 2^24 + 1
+    # rounds to 2^24 (tie to even) -> again 2^24 -> 0. Only the ascending
+    # fp32 chain gives 0.
+    big = 2.0 ** 24
+    ids, w, z, s = _one_token([1, 1, 1, 1], [[1, big, 1, -big]])
+    assert z[0, 0] == 0.0
+    assert s[0, 0] == 0.5
+
+
+def test_logit_zero_row_and_one_hot_row():
+    rng = np.random.default_rng(1)
+    wr = rng.standard_normal((5, 64)).astype(np.float32)
+    ids, w, z, s = _one_token([0.0] * 64, wr, k=2)
+    assert (z == 0).all() and not np.signbit(z).any()
+    xv = [0.0] * 64
+    xv[17] = -1.5
+    ids, w, z, s = _one_token(xv, wr, k=2)
+    expect = (np.float64(-1.5) * wr[:, 17].astype(np.float64)).astype(np.float32)
+    assert (z[0] == expect).all()
+
+
+def test_logits_within_fp32_error_bound_of_exact_sum():
+    inp = W.generate(W.MID["mid_swiglu"])
+    x = inp["x"]
+    wr = inp["router_w"]
+    ids, w, z, s = oracle.route(x, wr, inp["bias"], 4, want_scores=True)
+    xf = W.bf16_bits_to_f32(x)
+    H = x.shape[1]
+    gamma = H * U32 / (1 - H * U32)
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        t = int(rng.integers(x.shape[0]))
+        e = int(rng.integers(wr.shape[0]))
+        exact = sum(Fraction(float(xf[t, h])) * Fraction(float(wr[e, h])) for h in range(H))
+        mag = float(np.abs(xf[t].astype(np.float64) * wr[e].astype(np.float64)).sum())
+        assert abs(Fraction(float(z[t, e])) - exact) <= Fraction(gamma * mag)
+
+
+# ---------------------------------------------------------------- top-k
+
+def _brute_topk(keys, k):
+    order = sorted(range(len(keys)),
+                   key=lambda e: (math.isnan(keys[e]), 0.0 if math.isnan(keys[e]) else -keys[e], e))
+    return order[:k]
+
+
+def test_topk_exhaustive_small_domain():
+    dom = [float("nan"), -1.0, -0.0, 0.0, 0.5, 1.0]
+    for keys in itertools.product(dom, repeat=4):
+        kk = np.array(keys, dtype=np.float32)
+        for k in range(1, 5):
+            got = list(oracle.topk(kk, k))
+            assert got == _brute_topk(list(keys), k), (keys, k, got)
+            assert len(set(got)) == k
+
+
+def test_topk_all_nan_row_picks_distinct_low_ids():
+    for E, k in ((8, 2), (32, 4), (128, 6), (256, 8)):
+        keys = np.full(E, np.nan, dtype=np.float32)
+        assert list(oracle.topk(keys, k)) == list(range(k))
+
+
+@pytest.mark.parametrize("name", ["tiny_t64_e8_k2", "mid_nan_ties", "mid_e256_k8", "mid_swiglu"])
+def test_route_matches_brute_force_sort_of_keys(name):
+    wl = W.by_name(name)
+    inp = W.generate(wl)
+    ids, w, z, s = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k, want_scores=True)
+    keys = s + inp["bias"][None, :]          # fp32 + fp32, as the router forms its keys
+    for t in range(wl.T):
+        assert list(ids[t]) == _brute_topk([float(v) for v in keys[t]], wl.k), t
+        assert len(set(ids[t])) == wl.k
+
+
+def test_constructed_rows_route_as_built():
+    wl = W.TINY
+    inp = W.generate(wl)
+    ids, w, z, s = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k, want_scores=True)
+    for r in wl.nan_rows:
+        assert np.isnan(z[r]).all() and list(ids[r]) == [0, 1] and np.isnan(w[r]).all()
+    r = wl.zero_tie_row                      # keys 0.5 + 0.125 at experts 1, 4, 6
+    assert (s[r] == 0.5).all() and list(ids[r]) == [1, 4]
+    r = wl.onehot_tie_row                    # z = 2 exactly at experts 2 and 5
+    assert z[r, 2] == 2.0 and z[r, 5] == 2.0 and list(ids[r]) == [2, 5]
+    assert w[r, 0] == w[r, 1]
+
+
+# ---------------------------------------------------------------- weights
+
+def test_weights_closed_form_equal_scores():
+    # zero row: every score is exactly 1/2, so w_j = 0.5 / (0.5 k + 1e-6)
+    for k in (1, 2, 4):
+        ids, w, z, s = _one_token([0.0] * 64, np.zeros((8, 64)), k=k)
+        assert np.allclose(w, 0.5 / (0.5 * k + 1e-6), rtol=1e-15, atol=0)
+
+
+def test_weights_eps_is_visible_at_tiny_scores():
+    # every logit is -16, so every score is sigma32(-16) ~ 1.1e-7 and
+    # w = s / (2 s + 1e-6) ~ 0.092; without eps it would be 0.5, with 1e-20
+    # also 0.5.
+    xv = [0.0] * 64
+    xv[3] = 1.0
+    wr = np.zeros((6, 64), np.float32)
+    wr[:, 3] = -16.0
+    ids, w, z, s = _one_token(xv, wr, k=2)
+    sc = float(oracle.sigmoid32([-16.0])[0])
+    assert abs(sc - 1.0 / (1.0 + math.exp(16.0))) < 1e-13
+    assert np.allclose(w, sc / (2 * sc + 1e-6), rtol=1e-15)
+    assert 0.08 < w[0, 0] < 0.1
+
+
+def test_bias_selects_but_never_weighs():
+    # equal scores 1/2; biases +10 and +5 decide the picks, the weights stay
+    # 0.5 / (1 + 1e-6) each (a leaked bias would give 10.5/16 and 5.5/16)
+    b = np.zeros(8, np.float32)
+    b[3], b[6] = 10.0, 5.0
+    ids, w, z, s = _one_token([0.0] * 64, np.zeros((8, 64)), bias=b, k=2)
+    assert list(ids[0]) == [3, 6]
+    assert np.allclose(w, 0.5 / (1.0 + 1e-6), rtol=1e-15)
+
+
+def test_weights_sum_invariant_and_no_norm_mode():
+    wl = W.MID["mid_swiglu"]
+    inp = W.generate(wl)
+    ids, w, z, s = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k, want_scores=True)
+    S = np.take_along_axis(s, ids, axis=1).astype(np.float64).sum(axis=1)
+    assert np.allclose(w.sum(axis=1), S / (S + 1e-6), rtol=1e-14)
+    ids2, w2 = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k, norm_topk=False)
+    assert (ids2 == ids).all()
+    assert (w2 == np.take_along_axis(s, ids, axis=1).astype(np.float64)).all()
