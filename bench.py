@@ -1,0 +1,219 @@
+"""Benchmark of the sigmoid top-k routed MoE block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+One step is one moe_forward over one batch of synthetic input: router,
+top-k, plan, grouped expert GEMMs with the fused activation, the shared
+expert when the workload has one, and the weighted combine. The default
+workload is the LFM2-MoE-shaped prefill chunk (T=4096, H=2048, I=1792,
+E=32, top-4, bf16 SwiGLU experts). Inputs are resident in HBM before the
+timed region. Prints one JSON line.
+
+Besides the whole-block throughput the line carries:
+  roofline      the dominant kernel (the routed up-projection GEMM) against
+                the bf16 MFMA peak (or HBM for a decode-sized batch), timed
+                with the library's stage events on the call's stream;
+  cpu_baseline  the float64 CPU oracle on a sample of the same tokens;
+  decode        the T=8 decode step on the same weights (HBM-bound), with
+                the 256 MB last-level cache overwritten before every call.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = ("MoE-block tokens/s at 1 MI355X; % bf16 MFMA peak (prefill), % HBM BW (decode)")
+
+
+def flops_of(wl):
+    """Algorithmic MFMA flops of one block call: per assignment 2*n_up*H for
+    the up projection and 2*H*I for the down projection, plus the shared
+    expert on every token."""
+    A = wl.T * wl.k
+    up = 2.0 * A * wl.n_up * wl.H
+    down = 2.0 * A * wl.H * wl.I
+    shared = 0.0
+    if wl.I_shared:
+        n_sup = 2 * wl.I_shared if wl.act == "swiglu" else wl.I_shared
+        shared = 2.0 * wl.T * (n_sup + wl.I_shared) * wl.H
+    return up, down, shared
+
+
+def expert_bytes(wl):
+    """Bytes of one expert's (up, down) weights as stored."""
+    if wl.wfmt == "affine4":
+        up = wl.n_up * wl.H // 2 + 2 * 2 * wl.n_up * (wl.H // 64)
+        down = wl.H * wl.I // 2 + 2 * 2 * wl.H * (wl.I // 64)
+    else:
+        up = 2 * wl.n_up * wl.H
+        down = 2 * wl.H * wl.I
+    return up, down
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        h.update(open(os.path.join(ROOT, "sigmoid_top_routing_amd", "csrc", n), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the kernel source as it is now; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_digest") != source_digest("gemm.hip", "device.hpp"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, budget_s=15.0):
+    import oracle
+    threads = oracle.max_threads()
+    rng = np.random.default_rng(1234)
+    n0 = max(threads, 4)
+    toks = rng.choice(wl.T, size=min(n0, wl.T), replace=False).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.forward_tokens(wl, inp, toks)
+    dt = time.perf_counter() - t0
+    n = int(min(wl.T, max(n0, n0 * budget_s / max(dt, 1e-3))))
+    toks = rng.choice(wl.T, size=n, replace=False).astype(np.int32)
+    t0 = time.perf_counter()
+    oracle.forward_tokens(wl, inp, toks)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of the {wl.T} tokens of {wl.name} (routing and float64 experts "
+                      f"per token), {dt:.1f} s on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lfm2_prefill_t4096")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} asked for)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sigmoid_top_routing_amd import lib
+    from sigmoid_top_routing_amd import workloads as W
+
+    wl = W.by_name(args.workload)
+    inp = W.generate(wl)
+    block = lib.block_from_arrays(wl, inp)
+    x = lib.x_to_device(inp["x"])
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+    block.workspace(block.dims(wl.T), x.device)
+
+    for _ in range(args.warmup):
+        block.forward(x, out=out, ids_out=ids)
+    torch.cuda.synchronize()
+    evs = [lib.StageEvents() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        block.forward(x, out=out, ids_out=ids, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    stages = {k: float(np.mean([e.stage_ms()[k] for e in evs])) for k in lib.STAGES}
+
+    up_f, down_f, sh_f = flops_of(wl)
+    total_f = up_f + down_f + sh_f
+    ids_np = ids.cpu().numpy()
+    D = int(np.unique(ids_np).size)
+    eb_up, eb_down = expert_bytes(wl)
+    A = wl.T * wl.k
+    decode_sized = A <= 64
+    if decode_sized:
+        algo = D * eb_up + wl.T * wl.H * 2 + A * wl.I * 2
+        achieved = algo / (stages["up"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "routed up-projection GEMM", "achieved": achieved,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS}
+    else:
+        achieved = up_f / (stages["up"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "routed up-projection GEMM", "achieved": achieved,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
+    roof["traffic"] = load_traffic("gemm_up", wl.name)
+    roof["avg_launch_us"] = 1e3 * stages["up"]
+
+    result = {
+        "metric": METRIC,
+        "value": wl.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
+                   "act": wl.act, "weights": wl.wfmt, "rsf": wl.rsf, "I_shared": wl.I_shared,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "block": {"tflops": total_f / (ms_per_step * 1e-3) / 1e12,
+                  "frac_bf16_peak": total_f / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "distinct_experts": D, "stages_ms": stages},
+    }
+
+    if not args.no_decode and wl.name == "lfm2_prefill_t4096":
+        result["decode"] = bench_decode(block, W, lib, torch)
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(result))
+
+
+def bench_decode(block, W, lib, torch, steps=20):
+    """T=8 on the prefill weights, the last-level cache overwritten between
+    calls so the expert weights come from HBM."""
+    wl = W.DECODE
+    inp = W.generate(wl, experts=False)
+    x = lib.x_to_device(inp["x"])
+    ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        block.forward(x, out=out, ids_out=ids)
+    times, ups = [], []
+    for _ in range(steps):
+        flush.fill_(1)
+        ev = lib.StageEvents()
+        block.forward(x, out=out, ids_out=ids, events=ev)
+        torch.cuda.synchronize()
+        times.append(ev.total_ms())
+        ups.append(ev.stage_ms())
+    D = int(np.unique(ids.cpu().numpy()).size)
+    eb_up, eb_down = expert_bytes(wl)
+    algo = D * (eb_up + eb_down) + wl.E * wl.H * 4 + 2 * wl.T * wl.H * 2
+    t = float(np.median(times))
+    return {"workload": wl.name, "T": wl.T, "distinct_experts": D, "us_per_step": 1e3 * t,
+            "tokens_per_s": wl.T / (t * 1e-3), "algorithmic_bytes": algo,
+            "GBps": algo / (t * 1e-3) / 1e9, "frac_hbm": algo / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "stages_us": {k: 1e3 * float(np.median([u[k] for u in ups])) for k in lib.STAGES}}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * moe.h -- C ABI of the sigmoid top-k routed mixture-of-experts block on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The block, for a token row x_t (H inputs):
+ *   z[e]  = sum_h x[t,h] Wr[e,h]           fp32, h ascending, one fmaf per term
+ *   s[e]  = 1 / (1 + exp(-z[e]))           fp32 (own exp, correctly rounded division)
+ *   ids   = the k experts of largest s[e] + bias[e]; the bias only selects
+ *   w_j   = s[ids_j] / (sum_j s[ids_j] + norm_eps)   (or s[ids_j] when norm_topk == 0)
+ *   y_j   = W_down[e] act(W_up[e] x_t),  e = ids_j
+ *             SwiGLU: W_up = gate_up (E, 2I, H), gate rows first,
+ *                     act = silu(gate) * up
+ *             relu^2: W_up = up (E, I, H), act = (up < 0 ? 0 : up)^2
+ *   out_t = routed_scale * sum_j w_j y_j + shared_t
+ *   shared_t = W_sd act(W_su x_t), added unscaled (optional)
+ * Sources: TileGym PR #187, "Weight layout and routing" (gate_up layout,
+ * sigmoid routing, bias used only for selection, sum + 1e-6, then the routed
+ * scaling factor); TensorFold PR #1492, "What" and "Verification" (fp32
+ * router weights with expert bias and eps 1e-6; an all-NaN row must not
+ * pick one expert twice); vllm.cpp PR #684, "The seam decision" and its W2
+ * commit (relu^2 expert; the routed scale multiplies the finished routed
+ * sum, the shared output is added untouched; outputs are f32 or bf16 only);
+ * TensorFold issue #548 (one grouped-MoE layer: routing plan plus
+ * per-format experts behind one call, decode rows and prompt rows).
+ *
+ * Conventions for every entry point:
+ *  - Tensors are row-major and live in device memory owned by the caller.
+ *    bf16 tensors are passed as uint16_t bit patterns. Every tensor pointer
+ *    must be 16-byte aligned.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream). The library never allocates, frees or
+ *    synchronises device memory; scratch comes from the caller's workspace.
+ *  - Arguments are checked on the host before anything is enqueued. On an
+ *    error nothing is enqueued, the return value is a negative moe_status
+ *    and moe_last_error() names the argument and what was expected.
+ *  - Results are deterministic: the same inputs give the same bytes, on any
+ *    stream, whatever else runs beside them.
+ *  - Calls are re-entrant; two calls that share a workspace must not overlap.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_E_NULL = -1,        /* a required pointer is NULL */
+    MOE_E_SHAPE = -2,       /* a size is out of range or not a multiple it must be */
+    MOE_E_ALIGN = -3,       /* a tensor pointer is not 16-byte aligned */
+    MOE_E_UNSUPPORTED = -4, /* an option value this build does not implement */
+    MOE_E_WORKSPACE = -5,   /* workspace smaller than moe_workspace_bytes() */
+    MOE_E_HIP = -6          /* the HIP runtime refused a launch */
+} moe_status;
+
+typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
+typedef enum { MOE_W_BF16 = 0, MOE_W_AFFINE4 = 1 } moe_wfmt;
+typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out;
+
+/* Shape and options of one layer call. Limits: T >= 0; 1 <= E <= 256;
+ * 1 <= k <= min(E, 8); H, I and I_shared multiples of 64 (I_shared may be
+ * 0: no shared expert); group == 64 for MOE_W_AFFINE4 (0 otherwise). */
+typedef struct {
+    int32_t T;            /* tokens */
+    int32_t H;            /* hidden size (router and expert input, block output) */
+    int32_t I;            /* expert intermediate size */
+    int32_t E;            /* experts */
+    int32_t k;            /* experts per token */
+    int32_t act;          /* moe_act; the shared expert uses the same activation */
+    int32_t wfmt;         /* moe_wfmt of the routed experts */
+    int32_t group;        /* 4-bit group size along the input dimension (64) */
+    int32_t norm_topk;    /* 1: w = s / (sum s + norm_eps); 0: w = s */
+    float norm_eps;       /* 1e-6 on LFM2-MoE and Nemotron-H */
+    float routed_scale;   /* applied once, to the routed sum only */
+    int32_t I_shared;     /* shared-expert intermediate size, 0 = none */
+    int32_t out_dtype;    /* moe_out */
+} moe_dims;
+
+/* Weights of one layer (device pointers).
+ *  router_w    fp32 [E, H]
+ *  expert_bias fp32 [E] or NULL (selection only, never in the weights)
+ *  w_up        SwiGLU: [E, 2I, H], gate rows 0..I-1 then up rows I..2I-1;
+ *              relu^2: [E, I, H]
+ *  w_down      [E, H, I]
+ *  For MOE_W_BF16 w_up / w_down are bf16 and the *_scales / *_biases are
+ *  unused. For MOE_W_AFFINE4 they are uint32 words of 4-bit codes
+ *  ([E, N, K/8]: element c of a row is bits 4*(c%8) of word c/8), and
+ *  w_*_scales / w_*_biases are bf16 [E, N, K/64]; the weight is
+ *  scale * code + bias (MLX 4-bit affine, group 64; TensorFold PR #1492
+ *  "What").
+ *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
+ *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared]. */
+typedef struct {
+    const float *router_w;
+    const float *expert_bias;
+    const void *w_up;
+    const uint16_t *w_up_scales;
+    const uint16_t *w_up_biases;
+    const void *w_down;
+    const uint16_t *w_down_scales;
+    const uint16_t *w_down_biases;
+    const uint16_t *shared_up;
+    const uint16_t *shared_down;
+} moe_weights;
+
+/* Bytes of workspace moe_forward() and moe_plan() need for these dims. */
+int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
+
+/* Router and top-k (TileGym PR #187 "Weight layout and routing"; TensorFold
+ * PR #1492 "What").
+ *  x        bf16 [T, H]
+ *  ids      int32 [T, k]: the picks, best key first; equal keys go to the
+ *           lower index; a NaN key ranks below every number, so an all-NaN
+ *           row picks 0, 1, ..., k-1 (TensorFold PR #1492 "Verification")
+ *  weights  fp32 [T, k]: unbiased scores, normalised when d->norm_topk;
+ *           routed_scale is not applied here.
+ * Only T, H, E, k, norm_topk and norm_eps of d are read. */
+int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
+              const float *expert_bias, int32_t *ids, float *weights, hipStream_t stream);
+
+/* Expert plan (TensorFold issue #548, the grouped expert plan): histogram,
+ * exclusive scan and a stable permutation of the assignments a = t*k + j
+ * into per-expert segments.
+ *  ids      int32 [T, k]
+ *  counts   int32 [E]
+ *  offsets  int32 [E+1], offsets[E] = number of in-range assignments
+ *  sorted   int32 [T*k]: assignment indices, expert-major, ascending a inside
+ *           an expert; entries past offsets[E] are set to -1
+ *  slot_of  int32 [T*k]: the position of each assignment in sorted, or -1
+ *  fault    int32 [1] or NULL: incremented by the number of ids outside
+ *           [0, E); such assignments are left out of every segment (the
+ *           caller reads it back after the stream completes)
+ * Workspace: moe_workspace_bytes(d). */
+int moe_plan(const moe_dims *d, const int32_t *ids, int32_t *counts, int32_t *offsets,
+             int32_t *sorted, int32_t *slot_of, int32_t *fault, void *workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
+/* The whole block: route, plan, grouped expert GEMMs with the activation
+ * fused into the first, the shared expert, and the weighted combine.
+ *  x    bf16 [T, H]
+ *  out  [T, H], bf16 or fp32 by d->out_dtype: each element is computed in
+ *       fp32 as routed_scale * (fma chain of w_j * y_j, j ascending), plus
+ *       the shared expert's output, and rounded once.
+ *  ids_out, weights_out ([T, k]) and offsets_out ([E+1]) may be NULL; when
+ *  given they receive the routing and the plan offsets of this call.
+ * Workspace: moe_workspace_bytes(d). */
+int moe_forward(const moe_dims *d, const moe_weights *w, const uint16_t *x, void *out,
+                void *workspace, size_t workspace_bytes, hipStream_t stream,
+                int32_t *ids_out, float *weights_out, int32_t *offsets_out);
+
+/* moe_forward, with stage boundaries recorded on the stream for timing:
+ * events[0] before the router, [1] after the router, [2] after the plan,
+ * [3] after the routed up-projection GEMM (gate_up + SwiGLU, or up +
+ * relu^2), [4] after the routed down GEMM, [5] after the shared expert
+ * (same as [4] without one), [6] after the combine. Each entry is a
+ * hipEvent_t created by the caller, or NULL to skip it. */
+#define MOE_PROFILE_EVENTS 7
+int moe_forward_profiled(const moe_dims *d, const moe_weights *w, const uint16_t *x, void *out,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream,
+                         int32_t *ids_out, float *weights_out, int32_t *offsets_out,
+                         hipEvent_t events[MOE_PROFILE_EVENTS]);
+
+/* Text of the last error on this thread ("" after a success). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

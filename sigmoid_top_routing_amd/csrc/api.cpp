@@ -1,0 +1,402 @@
+// api.cpp -- the C ABI declared in include/moe.h: argument checks, the
+// workspace layout and the order of launches.
+//
+// The checks follow the refusal style of the pages' hosts: every size and
+// pointer is checked before anything is enqueued, and the error text names
+// the argument, what it got and what it needed (bloomery PR #235, review of
+// enqueue_pass; vllm.cpp PR #684: a tensor that is not device memory is
+// refused on the host, outputs are f32 or bf16 only).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+int ok() {
+    g_error.clear();
+    return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t ids, w, counts, offsets, sorted, slot, chunk_counts, h, y, hs, ys, total;
+};
+
+Layout layout(const moe_dims &d) {
+    Layout L{};
+    const size_t A = (size_t)d.T * d.k;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += round_up(bytes);
+        return o;
+    };
+    L.ids = take(A * 4);
+    L.w = take(A * 4);
+    L.counts = take((size_t)d.E * 4);
+    L.offsets = take((size_t)(d.E + 1) * 4);
+    L.sorted = take(A * 4);
+    L.slot = take(A * 4);
+    L.chunk_counts = take((size_t)moe::plan_chunks((int)A) * d.E * 4);
+    L.h = take(A * d.I * 2);
+    L.y = take(A * d.H * 4);
+    if (d.I_shared > 0) {
+        L.hs = take((size_t)d.T * d.I_shared * 2);
+        L.ys = take((size_t)d.T * d.H * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+bool aligned(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, code, ...)              \
+    do {                                      \
+        if (!(cond))                          \
+            return fail((code), __VA_ARGS__); \
+    } while (0)
+
+// Shape checks shared by every entry point. `what` names the caller.
+int check_dims(const char *what, const moe_dims *d, bool experts) {
+    REQUIRE(d != nullptr, MOE_E_NULL, "%s: dims is NULL", what);
+    REQUIRE(d->T >= 0 && d->T <= (1 << 24), MOE_E_SHAPE, "%s: T = %d, need 0 <= T <= 2^24", what,
+            d->T);
+    REQUIRE(d->H > 0 && d->H % 64 == 0 && d->H <= 65536, MOE_E_SHAPE,
+            "%s: H = %d, need a positive multiple of 64 up to 65536", what, d->H);
+    REQUIRE(d->E >= 1 && d->E <= 256, MOE_E_SHAPE, "%s: E = %d, need 1 <= E <= 256", what, d->E);
+    REQUIRE(d->k >= 1 && d->k <= 8 && d->k <= d->E, MOE_E_SHAPE,
+            "%s: k = %d, need 1 <= k <= min(E = %d, 8)", what, d->k, d->E);
+    REQUIRE((int64_t)d->T * d->k * d->H < ((int64_t)1 << 31), MOE_E_SHAPE,
+            "%s: T*k*H = %lld, need < 2^31", what, (long long)d->T * d->k * d->H);
+    REQUIRE(d->norm_topk == 0 || d->norm_topk == 1, MOE_E_UNSUPPORTED,
+            "%s: norm_topk = %d, need 0 or 1", what, d->norm_topk);
+    REQUIRE(std::isfinite(d->norm_eps) && d->norm_eps >= 0.0f, MOE_E_SHAPE,
+            "%s: norm_eps = %g, need a finite value >= 0", what, (double)d->norm_eps);
+    if (!experts)
+        return MOE_OK;
+    REQUIRE(d->I > 0 && d->I % 64 == 0 && d->I <= 65536, MOE_E_SHAPE,
+            "%s: I = %d, need a positive multiple of 64 up to 65536", what, d->I);
+    REQUIRE(d->I_shared >= 0 && d->I_shared % 64 == 0 && d->I_shared <= 65536, MOE_E_SHAPE,
+            "%s: I_shared = %d, need 0 or a positive multiple of 64 up to 65536", what,
+            d->I_shared);
+    REQUIRE((int64_t)d->T * d->k * d->I < ((int64_t)1 << 31) &&
+                (int64_t)d->T * d->I_shared < ((int64_t)1 << 31),
+            MOE_E_SHAPE, "%s: T*k*I or T*I_shared reaches 2^31", what);
+    REQUIRE(d->act == MOE_ACT_SWIGLU || d->act == MOE_ACT_RELU2, MOE_E_UNSUPPORTED,
+            "%s: act = %d, need MOE_ACT_SWIGLU (0) or MOE_ACT_RELU2 (1)", what, d->act);
+    REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_AFFINE4, MOE_E_UNSUPPORTED,
+            "%s: wfmt = %d, need MOE_W_BF16 (0) or MOE_W_AFFINE4 (1)", what, d->wfmt);
+    if (d->wfmt == MOE_W_AFFINE4)
+        REQUIRE(d->group == 64, MOE_E_UNSUPPORTED, "%s: group = %d, the 4-bit format needs 64",
+                what, d->group);
+    REQUIRE(d->out_dtype == MOE_OUT_BF16 || d->out_dtype == MOE_OUT_F32, MOE_E_UNSUPPORTED,
+            "%s: out_dtype = %d, need MOE_OUT_BF16 (0) or MOE_OUT_F32 (1)", what, d->out_dtype);
+    REQUIRE(std::isfinite(d->routed_scale), MOE_E_SHAPE, "%s: routed_scale = %g is not finite",
+            what, (double)d->routed_scale);
+    return MOE_OK;
+}
+
+// A required device tensor: not NULL, 16-byte aligned.
+int check_ptr(const char *what, const char *name, const void *p) {
+    REQUIRE(p != nullptr, MOE_E_NULL, "%s: %s is NULL", what, name);
+    REQUIRE(aligned(p), MOE_E_ALIGN, "%s: %s = %p is not 16-byte aligned", what, name, p);
+    return MOE_OK;
+}
+
+int check_opt_ptr(const char *what, const char *name, const void *p) {
+    REQUIRE(p == nullptr || aligned(p), MOE_E_ALIGN, "%s: %s = %p is not 16-byte aligned", what,
+            name, p);
+    return MOE_OK;
+}
+
+// Device memory check, the last check before launching (it is the only one
+// that asks the HIP runtime).
+int check_device(const char *what, const char *name, const void *p) {
+    if (p == nullptr)
+        return MOE_OK;
+    hipPointerAttribute_t attr;
+    const hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_E_SHAPE, "%s: %s = %p is not memory the HIP runtime knows (%s)", what,
+                    name, p, hipGetErrorString(e));
+    }
+    REQUIRE(attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged, MOE_E_SHAPE,
+            "%s: %s = %p is not device memory", what, name, p);
+    return MOE_OK;
+}
+
+#define TRY(expr)                 \
+    do {                          \
+        const int rc_ = (expr);   \
+        if (rc_ != MOE_OK)        \
+            return rc_;           \
+    } while (0)
+
+#define LAUNCH(expr)                                                                       \
+    do {                                                                                   \
+        const hipError_t e_ = (expr);                                                      \
+        if (e_ != hipSuccess)                                                              \
+            return fail(MOE_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e_)); \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int moe_workspace_bytes(const moe_dims *d, size_t *bytes) {
+    const char *what = "moe_workspace_bytes";
+    TRY(check_dims(what, d, true));
+    REQUIRE(bytes != nullptr, MOE_E_NULL, "%s: bytes is NULL", what);
+    *bytes = layout(*d).total;
+    return ok();
+}
+
+int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
+              const float *expert_bias, int32_t *ids, float *weights, hipStream_t stream) {
+    const char *what = "moe_route";
+    TRY(check_dims(what, d, false));
+    if (d->T == 0)
+        return ok();
+    TRY(check_ptr(what, "x", x));
+    TRY(check_ptr(what, "router_w", router_w));
+    TRY(check_opt_ptr(what, "expert_bias", expert_bias));
+    TRY(check_ptr(what, "ids", ids));
+    TRY(check_ptr(what, "weights", weights));
+    for (const auto &pr : {std::make_pair("x", (const void *)x),
+                           std::make_pair("router_w", (const void *)router_w),
+                           std::make_pair("expert_bias", (const void *)expert_bias),
+                           std::make_pair("ids", (const void *)ids),
+                           std::make_pair("weights", (const void *)weights)})
+        TRY(check_device(what, pr.first, pr.second));
+    LAUNCH(moe::launch_route(x, router_w, expert_bias, d->T, d->H, d->E, d->k, d->norm_topk,
+                             d->norm_eps, ids, weights, stream));
+    return ok();
+}
+
+int moe_plan(const moe_dims *d, const int32_t *ids, int32_t *counts, int32_t *offsets,
+             int32_t *sorted, int32_t *slot_of, int32_t *fault, void *workspace,
+             size_t workspace_bytes, hipStream_t stream) {
+    const char *what = "moe_plan";
+    TRY(check_dims(what, d, false));
+    const int A = d->T * d->k;
+    TRY(check_ptr(what, "counts", counts));
+    TRY(check_ptr(what, "offsets", offsets));
+    TRY(check_opt_ptr(what, "fault", fault));
+    if (A > 0) {
+        TRY(check_ptr(what, "ids", ids));
+        TRY(check_ptr(what, "sorted", sorted));
+        TRY(check_ptr(what, "slot_of", slot_of));
+    }
+    // the plan needs only the per-chunk counts of the layout
+    const size_t need = round_up((size_t)moe::plan_chunks(A) * d->E * 4);
+    REQUIRE(workspace_bytes >= need, MOE_E_WORKSPACE, "%s: workspace_bytes = %zu, need >= %zu",
+            what, workspace_bytes, need);
+    if (need > 0)
+        TRY(check_ptr(what, "workspace", workspace));
+    for (const auto &pr : {std::make_pair("ids", (const void *)ids),
+                           std::make_pair("counts", (const void *)counts),
+                           std::make_pair("offsets", (const void *)offsets),
+                           std::make_pair("sorted", (const void *)sorted),
+                           std::make_pair("slot_of", (const void *)slot_of),
+                           std::make_pair("fault", (const void *)fault),
+                           std::make_pair("workspace", (const void *)workspace)})
+        TRY(check_device(what, pr.first, pr.second));
+    LAUNCH(moe::launch_plan(ids, A, d->E, counts, offsets, sorted, slot_of, fault,
+                            (int32_t *)workspace, stream));
+    return ok();
+}
+
+namespace {
+
+int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, const uint16_t *x,
+                 void *out, void *workspace, size_t workspace_bytes, hipStream_t stream,
+                 int32_t *ids_out, float *weights_out, int32_t *offsets_out, hipEvent_t *events) {
+    TRY(check_dims(what, d, true));
+    REQUIRE(w != nullptr, MOE_E_NULL, "%s: weights is NULL", what);
+    TRY(check_ptr(what, "w->router_w", w->router_w));
+    TRY(check_opt_ptr(what, "w->expert_bias", w->expert_bias));
+    TRY(check_ptr(what, "w->w_up", w->w_up));
+    TRY(check_ptr(what, "w->w_down", w->w_down));
+    const bool aff = d->wfmt == MOE_W_AFFINE4;
+    if (aff) {
+        TRY(check_ptr(what, "w->w_up_scales", w->w_up_scales));
+        TRY(check_ptr(what, "w->w_up_biases", w->w_up_biases));
+        TRY(check_ptr(what, "w->w_down_scales", w->w_down_scales));
+        TRY(check_ptr(what, "w->w_down_biases", w->w_down_biases));
+    }
+    if (d->I_shared > 0) {
+        TRY(check_ptr(what, "w->shared_up", w->shared_up));
+        TRY(check_ptr(what, "w->shared_down", w->shared_down));
+    }
+    TRY(check_opt_ptr(what, "ids_out", ids_out));
+    TRY(check_opt_ptr(what, "weights_out", weights_out));
+    TRY(check_opt_ptr(what, "offsets_out", offsets_out));
+    const Layout L = layout(*d);
+    REQUIRE(workspace_bytes >= L.total, MOE_E_WORKSPACE, "%s: workspace_bytes = %zu, need >= %zu",
+            what, workspace_bytes, L.total);
+    if (d->T == 0)
+        return ok();
+    TRY(check_ptr(what, "x", x));
+    TRY(check_ptr(what, "out", out));
+    TRY(check_ptr(what, "workspace", workspace));
+    const void *dev[] = {x, out, workspace, w->router_w, w->expert_bias, w->w_up, w->w_down,
+                         aff ? w->w_up_scales : nullptr, aff ? w->w_up_biases : nullptr,
+                         aff ? w->w_down_scales : nullptr, aff ? w->w_down_biases : nullptr,
+                         d->I_shared ? w->shared_up : nullptr,
+                         d->I_shared ? w->shared_down : nullptr, ids_out, weights_out,
+                         offsets_out};
+    const char *dev_names[] = {"x", "out", "workspace", "w->router_w", "w->expert_bias",
+                               "w->w_up", "w->w_down", "w->w_up_scales", "w->w_up_biases",
+                               "w->w_down_scales", "w->w_down_biases", "w->shared_up",
+                               "w->shared_down", "ids_out", "weights_out", "offsets_out"};
+    for (size_t i = 0; i < sizeof dev / sizeof dev[0]; ++i)
+        TRY(check_device(what, dev_names[i], dev[i]));
+
+    char *ws = (char *)workspace;
+    const int T = d->T, H = d->H, I = d->I, E = d->E, k = d->k, A = T * k;
+    int32_t *ids = ids_out ? ids_out : (int32_t *)(ws + L.ids);
+    float *wts = weights_out ? weights_out : (float *)(ws + L.w);
+    int32_t *counts = (int32_t *)(ws + L.counts);
+    int32_t *offsets = offsets_out ? offsets_out : (int32_t *)(ws + L.offsets);
+    int32_t *sorted = (int32_t *)(ws + L.sorted);
+    int32_t *slot = (int32_t *)(ws + L.slot);
+    uint16_t *h = (uint16_t *)(ws + L.h);
+    float *y = (float *)(ws + L.y);
+
+    auto mark = [&](int i) -> hipError_t {
+        return (events != nullptr && events[i] != nullptr) ? hipEventRecord(events[i], stream)
+                                                           : hipSuccess;
+    };
+    LAUNCH(mark(0));
+    LAUNCH(moe::launch_route(x, w->router_w, w->expert_bias, T, H, E, k, d->norm_topk,
+                             d->norm_eps, ids, wts, stream));
+    LAUNCH(mark(1));
+    LAUNCH(moe::launch_plan(ids, A, E, counts, offsets, sorted, slot, nullptr,
+                            (int32_t *)(ws + L.chunk_counts), stream));
+    LAUNCH(mark(2));
+
+    moe::GemmProblem up{};
+    up.mode = d->act == MOE_ACT_SWIGLU ? moe::kGateUp : moe::kUpRelu2;
+    up.affine4 = aff;
+    up.A = x;
+    up.lda = H;
+    up.gather = sorted;
+    up.gather_div = k;
+    up.offsets = offsets;
+    up.E = E;
+    up.max_rows = A;
+    up.B = w->w_up;
+    up.Bscale = w->w_up_scales;
+    up.Bbias = w->w_up_biases;
+    up.N = d->act == MOE_ACT_SWIGLU ? 2 * I : I;
+    up.K = H;
+    up.I = I;
+    up.C = h;
+    up.ldc = I;
+    LAUNCH(moe::launch_gemm(up, stream));
+    LAUNCH(mark(3));
+
+    moe::GemmProblem down{};
+    down.mode = moe::kDown;
+    down.affine4 = aff;
+    down.A = h;
+    down.lda = I;
+    down.offsets = offsets;
+    down.E = E;
+    down.max_rows = A;
+    down.B = w->w_down;
+    down.Bscale = w->w_down_scales;
+    down.Bbias = w->w_down_biases;
+    down.N = H;
+    down.K = I;
+    down.I = I;
+    down.C = y;
+    down.ldc = H;
+    down.scatter = sorted;
+    LAUNCH(moe::launch_gemm(down, stream));
+    LAUNCH(mark(4));
+
+    const float *shared = nullptr;
+    if (d->I_shared > 0) {
+        const int Is = d->I_shared;
+        uint16_t *hs = (uint16_t *)(ws + L.hs);
+        float *ys = (float *)(ws + L.ys);
+        moe::GemmProblem su{};
+        su.mode = d->act == MOE_ACT_SWIGLU ? moe::kGateUp : moe::kUpRelu2;
+        su.A = x;
+        su.lda = H;
+        su.rows = T;
+        su.E = 1;
+        su.max_rows = T;
+        su.B = w->shared_up;
+        su.N = d->act == MOE_ACT_SWIGLU ? 2 * Is : Is;
+        su.K = H;
+        su.I = Is;
+        su.C = hs;
+        su.ldc = Is;
+        LAUNCH(moe::launch_gemm(su, stream));
+        moe::GemmProblem sd{};
+        sd.mode = moe::kDown;
+        sd.A = hs;
+        sd.lda = Is;
+        sd.rows = T;
+        sd.E = 1;
+        sd.max_rows = T;
+        sd.B = w->shared_down;
+        sd.N = H;
+        sd.K = Is;
+        sd.I = Is;
+        sd.C = ys;
+        sd.ldc = H;
+        LAUNCH(moe::launch_gemm(sd, stream));
+        shared = ys;
+    }
+    LAUNCH(mark(5));
+    LAUNCH(moe::launch_combine(y, wts, shared, T, H, k, d->routed_scale, out,
+                               d->out_dtype == MOE_OUT_F32, stream));
+    LAUNCH(mark(6));
+    return ok();
+}
+
+}  // namespace
+
+int moe_forward(const moe_dims *d, const moe_weights *w, const uint16_t *x, void *out,
+                void *workspace, size_t workspace_bytes, hipStream_t stream, int32_t *ids_out,
+                float *weights_out, int32_t *offsets_out) {
+    return forward_impl("moe_forward", d, w, x, out, workspace, workspace_bytes, stream, ids_out,
+                        weights_out, offsets_out, nullptr);
+}
+
+int moe_forward_profiled(const moe_dims *d, const moe_weights *w, const uint16_t *x, void *out,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream,
+                         int32_t *ids_out, float *weights_out, int32_t *offsets_out,
+                         hipEvent_t events[MOE_PROFILE_EVENTS]) {
+    return forward_impl("moe_forward_profiled", d, w, x, out, workspace, workspace_bytes, stream,
+                        ids_out, weights_out, offsets_out, events);
+}
+
+const char *moe_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

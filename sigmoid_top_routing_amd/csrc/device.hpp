@@ -1,0 +1,97 @@
+// device.hpp -- small device-side helpers shared by the library's kernels.
+//
+// Internal to libmoe; nothing outside sigmoid_top_routing_amd/csrc includes it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round to nearest even; NaN becomes the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// e^v in fp32 for v in [-17, 87]: v = n ln2 + r with n = rint(v log2 e)
+// and a two-part ln2 (the high part has nine zero low bits), then the
+// Taylor polynomial of e^r to degree 7 in Horner form and a scaling by 2^n.
+// Used by the router's sigmoid, whose bits must not depend on a library.
+__device__ __forceinline__ float exp_cw(float v) {
+    const float log2e = 0x1.715476p+0f;
+    const float ln2_hi = 0x1.62e4p-1f;
+    const float ln2_lo = 0x1.7f7d1cp-20f;
+    const float n = __builtin_rintf(v * log2e);
+    float r = __builtin_fmaf(-n, ln2_hi, v);
+    r = __builtin_fmaf(-n, ln2_lo, r);
+    float p = 0x1.a01a02p-13f;                 // 1/5040
+    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f); // 1/720
+    p = __builtin_fmaf(p, r, 0x1.111112p-7f);  // 1/120
+    p = __builtin_fmaf(p, r, 0x1.555556p-5f);  // 1/24
+    p = __builtin_fmaf(p, r, 0x1.555556p-3f);  // 1/6
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    return __builtin_ldexpf(p, (int)n);
+}
+
+// Router score: 1 / (1 + e^-z), division correctly rounded (hipcc's default
+// for fp32 '/'). NaN stays NaN; z > 17 gives 1 (the quotient rounds to 1
+// there anyway); z < -87 gives 0, keeping every intermediate normal.
+__device__ __forceinline__ float sigmoid_score(float z) {
+    if (z != z)
+        return z;
+    if (z > 17.0f)
+        return 1.0f;
+    if (z < -87.0f)
+        return 0.0f;
+    return 1.0f / (1.0f + exp_cw(-z));
+}
+
+// SwiGLU epilogue: silu(g) * u with the hardware exp2 and reciprocal.
+// Not bit-specified; held to the block's output tolerance.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(-g * 0x1.715476p+0f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// relu^2 epilogue: (u < 0 ? 0 : u)^2 in fp32; NaN and +inf pass through.
+__device__ __forceinline__ float relu_sq(float u) {
+    const float r = (u < 0.0f) ? 0.0f : u;
+    return r * r;
+}
+
+// Top-k order key: larger key first, NaN below every number, +0 == -0.
+__device__ __forceinline__ uint32_t order_key(float key) {
+    if (key != key)
+        return 0u;
+    uint32_t u = __float_as_uint(key);
+    if (u == 0x80000000u)
+        u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+    const uint32_t lo = __shfl_xor((int)(uint32_t)v, mask, kWave);
+    const uint32_t hi = __shfl_xor((int)(uint32_t)(v >> 32), mask, kWave);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+}  // namespace moe

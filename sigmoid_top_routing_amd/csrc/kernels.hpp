@@ -1,0 +1,52 @@
+// kernels.hpp -- host-side launchers of the library's kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, int T, int H, int E,
+                        int k, int norm_topk, float eps, int32_t *ids, float *weights,
+                        hipStream_t stream);
+
+// Plan scratch: per-chunk expert counts, plan_chunks(A) x E int32.
+int plan_chunk_size(int A);
+int plan_chunks(int A);
+hipError_t launch_plan(const int32_t *ids, int A, int E, int32_t *counts, int32_t *offsets,
+                       int32_t *sorted, int32_t *slot_of, int32_t *fault, int32_t *chunk_counts,
+                       hipStream_t stream);
+
+// Grouped GEMM over expert segments.
+enum GemmMode { kGateUp = 0, kUpRelu2 = 1, kDown = 2 };
+
+struct GemmProblem {
+    int mode;                 // GemmMode
+    int affine4;              // B is 4-bit affine (codes + bf16 scale / bias, group 64)
+    const uint16_t *A;        // bf16 rows, lda elements apart
+    int lda;
+    const int32_t *gather;    // A row of position p = gather[p] / gather_div (NULL: row p)
+    int gather_div;
+    const int32_t *offsets;   // [E+1] segment bounds (NULL: one segment [0, rows))
+    int rows;                 // rows when offsets == NULL
+    int E;
+    int max_rows;             // bound on offsets[E] (sizes the grid)
+    const void *B;            // [E][N][K] bf16, or uint32 codes [E][N][K/8]
+    const uint16_t *Bscale;   // [E][N][K/64] (affine-4)
+    const uint16_t *Bbias;
+    int N;                    // rows of B per expert
+    int K;
+    int I;                    // kGateUp: gate rows are 0..I-1, up rows I..2I-1
+    void *C;                  // kGateUp / kUpRelu2: bf16 [rows][ldc]; kDown: fp32 [*][ldc]
+    int ldc;
+    const int32_t *scatter;   // kDown: output row of position p = scatter[p] (NULL: row p)
+};
+
+hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
+
+hipError_t launch_combine(const float *y_slot, const float *weights, const float *shared, int T,
+                          int H, int k, float routed_scale, void *out, int out_f32,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -186,7 +186,7 @@ def _children(seed: int):
     return [np.random.default_rng(c) for c in np.random.SeedSequence([0x5EED, seed]).spawn(10)]
 
 
-def generate(wl: Workload, need_x: bool = True) -> dict:
+def generate(wl: Workload, need_x: bool = True, experts: bool = True) -> dict:
     """Draw every input of ``wl``.
 
     Returns a dict of C-contiguous NumPy arrays. bf16 tensors are uint16 bit
@@ -196,6 +196,8 @@ def generate(wl: Workload, need_x: bool = True) -> dict:
     (bf16 [E,n_up,H/64]) and the same three for w_down ([E,H,I/8],
     [E,H,I/64]); shared_up [I_s,H] and shared_down [H,I_s] bf16 when
     I_shared > 0 (shared_up is [2*I_s,H], gate rows first, for SwiGLU).
+    With experts=False only x, router_w and bias are drawn (each tensor has
+    its own stream, so the others are unchanged).
     """
     E, H, I, T = wl.E, wl.H, wl.I, wl.T
     xs = _children(wl.seed)
@@ -210,6 +212,9 @@ def generate(wl: Workload, need_x: bool = True) -> dict:
         for e in wl.boosted:
             out["bias"][e] = np.float32(out["bias"][e] + np.float32(wl.boost))
     n_up = wl.n_up
+    if not experts:
+        _construct_special_rows(wl, out)
+        return out
     if wl.wfmt == "bf16":
         out["w_up"] = _normal_bf16(ws[c_up], (E, n_up, H), wl.w_std)
         out["w_down"] = _normal_bf16(ws[c_down], (E, H, I), wl.w_std)

@@ -1,0 +1,165 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and refuses bad arguments on the host before anything is enqueued
+(no call here reaches a HIP launch)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from sigmoid_top_routing_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*\*?\s*(moe_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = lib.load()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIBPATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def dims(**kw):
+    base = dict(T=16, H=128, I=256, E=8, k=2)
+    base.update(kw)
+    return lib.make_dims(**base)
+
+
+def status_of(fn):
+    try:
+        fn()
+    except lib.MoeError as e:
+        return e.code, str(e)
+    return 0, ""
+
+
+def ws_bytes(d):
+    n = C.c_size_t()
+    rc = lib.load().moe_workspace_bytes(C.byref(d), C.byref(n))
+    return rc, n.value
+
+
+def test_workspace_bytes_grows_with_the_problem():
+    rc, small = ws_bytes(dims())
+    assert rc == 0 and small > 0
+    rc, big = ws_bytes(dims(T=4096, H=2048, I=1792, E=32, k=4))
+    assert rc == 0 and big > 16384 * 2048 * 4
+    rc, shared = ws_bytes(dims(I_shared=128))
+    assert rc == 0 and shared > small
+
+
+@pytest.mark.parametrize("bad,code,word", [
+    (dict(H=100), -2, "H = 100"),
+    (dict(H=0), -2, "H = 0"),
+    (dict(I=96), -2, "I = 96"),
+    (dict(E=0), -2, "E = 0"),
+    (dict(E=300), -2, "E = 300"),
+    (dict(k=3, E=2), -2, "k = 3"),
+    (dict(k=9, E=16), -2, "k = 9"),
+    (dict(T=-1), -2, "T = -1"),
+    (dict(I_shared=100), -2, "I_shared = 100"),
+])
+def test_bad_shapes_are_refused(bad, code, word):
+    rc, _ = ws_bytes(dims(**bad))
+    assert rc == code
+    assert word in lib.load().moe_last_error().decode()
+
+
+def test_unsupported_options_are_refused():
+    d = dims()
+    d.act = 7
+    assert ws_bytes(d)[0] == -4
+    d = dims(wfmt="affine4")
+    d.group = 32
+    assert ws_bytes(d)[0] == -4
+    assert "group = 32" in lib.load().moe_last_error().decode()
+    d = dims()
+    d.out_dtype = 5
+    assert ws_bytes(d)[0] == -4
+
+
+def _fake(addr):
+    return C.c_void_p(addr)
+
+
+def test_forward_refuses_null_misaligned_and_short_workspace():
+    L = lib.load()
+    d = dims()
+    w = lib.Weights()
+    # NULL weights struct
+    rc = L.moe_forward(C.byref(d), None, _fake(0x1000), _fake(0x1000), _fake(0x1000), 1 << 30,
+                       None, None, None, None)
+    assert rc == -1
+    # a missing router weight
+    rc = L.moe_forward(C.byref(d), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       1 << 30, None, None, None, None)
+    assert rc == -1 and "router_w" in L.moe_last_error().decode()
+    # a misaligned expert weight
+    w = lib.Weights(router_w=0x1000, w_up=0x2008, w_down=0x3000)
+    rc = L.moe_forward(C.byref(d), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       1 << 30, None, None, None, None)
+    assert rc == -3 and "w_up" in L.moe_last_error().decode()
+    # a short workspace
+    w = lib.Weights(router_w=0x1000, w_up=0x2000, w_down=0x3000)
+    need = lib.workspace_bytes(d)
+    rc = L.moe_forward(C.byref(d), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       need - 1, None, None, None, None)
+    assert rc == -5 and str(need) in L.moe_last_error().decode()
+    # 4-bit weights without scales
+    da = dims(wfmt="affine4")
+    rc = L.moe_forward(C.byref(da), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       1 << 30, None, None, None, None)
+    assert rc == -1 and "scales" in L.moe_last_error().decode()
+    # a shared expert without its weights
+    ds = dims(I_shared=64)
+    rc = L.moe_forward(C.byref(ds), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       1 << 30, None, None, None, None)
+    assert rc == -1 and "shared_up" in L.moe_last_error().decode()
+
+
+def test_zero_tokens_enqueue_nothing():
+    L = lib.load()
+    d = dims(T=0)
+    w = lib.Weights(router_w=0x1000, w_up=0x2000, w_down=0x3000)
+    rc = L.moe_forward(C.byref(d), C.byref(w), None, None, None, lib.workspace_bytes(d), None,
+                       None, None, None)
+    assert rc == 0 and L.moe_last_error().decode() == ""
+    rc = L.moe_route(C.byref(d), None, None, None, None, None, None)
+    assert rc == 0
+
+
+def test_route_and_plan_refuse_bad_pointers():
+    L = lib.load()
+    d = dims()
+    rc = L.moe_route(C.byref(d), _fake(0x1000), None, None, _fake(0x2000), _fake(0x3000), None)
+    assert rc == -1 and "router_w" in L.moe_last_error().decode()
+    rc = L.moe_route(C.byref(d), _fake(0x1004), _fake(0x1000), None, _fake(0x2000),
+                     _fake(0x3000), None)
+    assert rc == -3 and "x" in L.moe_last_error().decode()
+    rc = L.moe_plan(C.byref(d), _fake(0x1000), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                    _fake(0x1000), None, _fake(0x1000), 0, None)
+    assert rc == -5
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(lib, "_lib", None)
+    monkeypatch.setattr(lib, "LIBPATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        lib.load()
