@@ -40,7 +40,7 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t ids, w, counts, offsets, sorted, slot, chunk_counts, h, y, hs, ys, total;
+    size_t z, ids, w, counts, offsets, sorted, slot, chunk_counts, h, y, hs, ys, total;
 };
 
 Layout layout(const moe_dims &d) {
@@ -52,6 +52,7 @@ Layout layout(const moe_dims &d) {
         off += round_up(bytes);
         return o;
     };
+    L.z = take(moe::route_scratch_bytes(d.T, d.E));
     L.ids = take(A * 4);
     L.w = take(A * 4);
     L.counts = take((size_t)d.E * 4);
@@ -174,7 +175,8 @@ int moe_workspace_bytes(const moe_dims *d, size_t *bytes) {
 }
 
 int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
-              const float *expert_bias, int32_t *ids, float *weights, hipStream_t stream) {
+              const float *expert_bias, int32_t *ids, float *weights, void *workspace,
+              size_t workspace_bytes, hipStream_t stream) {
     const char *what = "moe_route";
     TRY(check_dims(what, d, false));
     if (d->T == 0)
@@ -184,14 +186,21 @@ int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
     TRY(check_opt_ptr(what, "expert_bias", expert_bias));
     TRY(check_ptr(what, "ids", ids));
     TRY(check_ptr(what, "weights", weights));
+    // the router needs only the logits scratch of the layout
+    const size_t need = round_up(moe::route_scratch_bytes(d->T, d->E));
+    REQUIRE(workspace_bytes >= need, MOE_E_WORKSPACE, "%s: workspace_bytes = %zu, need >= %zu",
+            what, workspace_bytes, need);
+    TRY(check_ptr(what, "workspace", workspace));
     for (const auto &pr : {std::make_pair("x", (const void *)x),
                            std::make_pair("router_w", (const void *)router_w),
                            std::make_pair("expert_bias", (const void *)expert_bias),
                            std::make_pair("ids", (const void *)ids),
-                           std::make_pair("weights", (const void *)weights)})
+                           std::make_pair("weights", (const void *)weights),
+                           std::make_pair("workspace", (const void *)workspace)})
         TRY(check_device(what, pr.first, pr.second));
     LAUNCH(moe::launch_route(x, router_w, expert_bias, d->T, d->H, d->E, d->k, d->norm_topk,
-                             d->norm_eps, ids, weights, stream));
+                             d->norm_eps, ids, weights, (float *)workspace, moe::PlanOut{},
+                             nullptr, stream));
     return ok();
 }
 
@@ -290,12 +299,23 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
                                                            : hipSuccess;
     };
     LAUNCH(mark(0));
+    bool plan_done = false;
     LAUNCH(moe::launch_route(x, w->router_w, w->expert_bias, T, H, E, k, d->norm_topk,
-                             d->norm_eps, ids, wts, stream));
+                             d->norm_eps, ids, wts, (float *)(ws + L.z),
+                             moe::PlanOut{counts, offsets, sorted, slot}, &plan_done, stream));
     LAUNCH(mark(1));
-    LAUNCH(moe::launch_plan(ids, A, E, counts, offsets, sorted, slot, nullptr,
-                            (int32_t *)(ws + L.chunk_counts), stream));
+    if (!plan_done)
+        LAUNCH(moe::launch_plan(ids, A, E, counts, offsets, sorted, slot, nullptr,
+                                (int32_t *)(ws + L.chunk_counts), stream));
     LAUNCH(mark(2));
+    // Decode-sized batches (at most two assignments per expert on average)
+    // stream each touched expert's weights once; larger ones take the MFMA
+    // tiles (TensorFold issue #548: decode rows and prompt rows).
+    const bool decode_form = A <= 2 * E;
+    auto run = [&](const moe::GemmProblem &g) {
+        return decode_form && moe::stream_supported(g) ? moe::launch_stream(g, stream)
+                                                       : moe::launch_gemm(g, stream);
+    };
 
     moe::GemmProblem up{};
     up.mode = d->act == MOE_ACT_SWIGLU ? moe::kGateUp : moe::kUpRelu2;
@@ -315,7 +335,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     up.I = I;
     up.C = h;
     up.ldc = I;
-    LAUNCH(moe::launch_gemm(up, stream));
+    LAUNCH(run(up));
     LAUNCH(mark(3));
 
     moe::GemmProblem down{};
@@ -335,7 +355,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     down.C = y;
     down.ldc = H;
     down.scatter = sorted;
-    LAUNCH(moe::launch_gemm(down, stream));
+    LAUNCH(run(down));
     LAUNCH(mark(4));
 
     const float *shared = nullptr;
@@ -356,7 +376,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         su.I = Is;
         su.C = hs;
         su.ldc = Is;
-        LAUNCH(moe::launch_gemm(su, stream));
+        LAUNCH(run(su));
         moe::GemmProblem sd{};
         sd.mode = moe::kDown;
         sd.A = hs;
@@ -370,7 +390,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         sd.I = Is;
         sd.C = ys;
         sd.ldc = H;
-        LAUNCH(moe::launch_gemm(sd, stream));
+        LAUNCH(run(sd));
         shared = ys;
     }
     LAUNCH(mark(5));

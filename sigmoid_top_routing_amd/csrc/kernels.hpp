@@ -7,9 +7,24 @@
 
 namespace moe {
 
+// Plan outputs the router may build itself (all NULL: it does not).
+struct PlanOut {
+    int32_t *counts;    // [E]
+    int32_t *offsets;   // [E+1]
+    int32_t *sorted;    // [T*k]
+    int32_t *slot_of;   // [T*k]
+};
+constexpr int kFusedPlanMaxA = 1024;
+
+// Router + top-k: a logits launch and a top-k launch. z_scratch holds the
+// [T][E] fp32 logits between them (route_scratch_bytes). When `plan` is given
+// and one top-k workgroup covers every token (decode-sized batches), the
+// top-k launch also writes the plan and *plan_done is set; otherwise the
+// caller runs launch_plan.
+size_t route_scratch_bytes(int T, int E);
 hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, int T, int H, int E,
                         int k, int norm_topk, float eps, int32_t *ids, float *weights,
-                        hipStream_t stream);
+                        float *z_scratch, PlanOut plan, bool *plan_done, hipStream_t stream);
 
 // Plan scratch: per-chunk expert counts, plan_chunks(A) x E int32.
 int plan_chunk_size(int A);
@@ -44,6 +59,11 @@ struct GemmProblem {
 };
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
+
+// The same problem in the weight-streaming (decode) form: few A rows per
+// expert, every touched weight row read once, v_dot2 accumulation.
+bool stream_supported(const GemmProblem &p);
+hipError_t launch_stream(const GemmProblem &p, hipStream_t stream);
 
 hipError_t launch_combine(const float *y_slot, const float *weights, const float *shared, int T,
                           int H, int k, float routed_scale, void *out, int out_f32,

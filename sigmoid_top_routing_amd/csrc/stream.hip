@@ -1,0 +1,200 @@
+// stream.hip -- the decode form of the grouped expert GEMMs: each touched
+// expert's weight rows are streamed from HBM once per call, against the few
+// rows of its segment (TensorFold issue #548: decode rows and prompt rows
+// take different kernels over the same weights; TileGym PR #187,
+// "Performance": at batch 1 the block is bound by the weight bytes).
+//
+// Same problem as the MFMA GEMM (GemmProblem, same epilogues, same outputs),
+// different shape of work. A workgroup owns one expert and a run of output
+// units (a gate/up row pair for SwiGLU, else one weight row). Each wave
+// first loads its segment's A rows (up to 4 at a time) into registers:
+// lane l holds elements 512 j + 8 l .. + 7 of every row, for every j. Then
+// for each unit it streams the weight row with fully coalesced 16-byte loads
+// (64 lanes cover 1 KB of a row per instruction, two units in flight), and
+// accumulates with v_dot2_f32_bf16 (two bf16 products per instruction, fp32
+// accumulate). The 64 lane-partial sums of all rows are reduced with a
+// transposing butterfly, which needs far fewer shuffles than reducing each
+// value on its own, and one lane per row applies the epilogue.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;
+constexpr int kTG = 4;         // A rows per pass
+constexpr int kUnroll = 2;     // units in flight per wave
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+__device__ __forceinline__ float dot8(const uint4 &w, const uint4 &x, float c) {
+    c = dot2(w.x, x.x, c);
+    c = dot2(w.y, x.y, c);
+    c = dot2(w.z, x.z, c);
+    c = dot2(w.w, x.w, c);
+    return c;
+}
+
+// v[0..V-1] hold lane partials of V sums. Halve the array log2(V/KEEP)
+// times across lanes (xor 32, 16, ...), then sum the KEEP survivors over the
+// remaining lanes. Afterwards v[0..KEEP-1] of every lane are full sums of
+// the values whose index is given by the lane's bits 5, 4, ... (most
+// significant first) times KEEP.
+template <int V, int KEEP>
+__device__ __forceinline__ void transpose_reduce(float (&v)[V], int lane) {
+    int c = V;
+    int m = 32;
+#pragma unroll
+    for (int step = 0; (V >> step) > KEEP; ++step) {
+        const bool hi = (lane & m) != 0;
+        const int half = c / 2;
+#pragma unroll
+        for (int j = 0; j < V / 2; ++j) {
+            if (j < half) {
+                const float give = hi ? v[j] : v[j + half];
+                const float keep = hi ? v[j + half] : v[j];
+                v[j] = keep + __shfl_xor(give, m, kWave);
+            }
+        }
+        c = half;
+        m >>= 1;
+    }
+    for (; m >= 1; m >>= 1) {
+#pragma unroll
+        for (int j = 0; j < KEEP; ++j)
+            v[j] += __shfl_xor(v[j], m, kWave);
+    }
+}
+
+template <int MODE, int NJ>
+__global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p, int upb) {
+    const int e = p.offsets != nullptr ? (int)blockIdx.x : 0;
+    const int seg0 = p.offsets != nullptr ? p.offsets[e] : 0;
+    const int seg1 = p.offsets != nullptr ? p.offsets[e + 1] : p.rows;
+    if (seg0 >= seg1)
+        return;
+    const int units = MODE == kGateUp ? p.I : p.N;
+    const int u0 = blockIdx.y * upb;
+    const int u1 = min(units, u0 + upb);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int K = p.K;
+    const uint16_t *B = (const uint16_t *)p.B + (size_t)e * p.N * K;
+    constexpr int NR = MODE == kGateUp ? 2 : 1;   // weight rows per unit
+
+    for (int g0 = seg0; g0 < seg1; g0 += kTG) {
+        const int nr = min(kTG, seg1 - g0);
+        uint4 xa[kTG][NJ];
+#pragma unroll
+        for (int r = 0; r < kTG; ++r) {
+            const uint16_t *row = nullptr;
+            if (r < nr) {
+                const int pos = g0 + r;
+                const int arow = p.gather ? p.gather[pos] / p.gather_div : pos;
+                row = p.A + (size_t)arow * p.lda;
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int kk = j * 512 + lane * 8;
+                xa[r][j] = (row != nullptr && kk < K) ? *reinterpret_cast<const uint4 *>(row + kk)
+                                                      : make_uint4(0, 0, 0, 0);
+            }
+        }
+
+        for (int ub = u0 + wave * kUnroll; ub < u1; ub += 4 * kUnroll) {
+            uint4 w[kUnroll][NR][NJ];
+#pragma unroll
+            for (int q = 0; q < kUnroll; ++q) {
+                const int u = ub + q;
+#pragma unroll
+                for (int s = 0; s < NR; ++s) {
+                    const int wrow = s == 0 ? u : p.I + u;
+                    const uint16_t *wp = B + (size_t)wrow * K;
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int kk = j * 512 + lane * 8;
+                        w[q][s][j] = (u < u1 && kk < K) ? *reinterpret_cast<const uint4 *>(wp + kk)
+                                                        : make_uint4(0, 0, 0, 0);
+                    }
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kUnroll; ++q) {
+                const int u = ub + q;
+                // values ordered (row r, weight row s): index r * NR + s
+                float v[kTG * NR];
+#pragma unroll
+                for (int r = 0; r < kTG; ++r)
+#pragma unroll
+                    for (int s = 0; s < NR; ++s) {
+                        float acc = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+                            acc = dot8(w[q][s][j], xa[r][j], acc);
+                        v[r * NR + s] = acc;
+                    }
+                transpose_reduce<kTG * NR, NR>(v, lane);
+                // lane bits 5, 4 name the row r whose sums this lane now holds
+                const int r = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+                if ((lane & 15) == 0 && r < nr && u < u1) {
+                    const int pos = g0 + r;
+                    if (MODE == kGateUp) {
+                        ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
+                            (uint16_t)f32_to_bf16(silu_mul(v[0], v[1]));
+                    } else if (MODE == kUpRelu2) {
+                        ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
+                            (uint16_t)f32_to_bf16(relu_sq(v[0]));
+                    } else {
+                        const int orow = p.scatter ? p.scatter[pos] : pos;
+                        ((float *)p.C)[(size_t)orow * p.ldc + u] = v[0];
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int MODE, int NJ>
+hipError_t launch_nj(const GemmProblem &p, hipStream_t stream) {
+    const int units = MODE == kGateUp ? p.I : p.N;
+    const int upb = 4 * kUnroll * 4;          // 4 waves x 2 units x 4 passes
+    const dim3 grid(p.offsets != nullptr ? p.E : 1, (units + upb - 1) / upb);
+    hipLaunchKernelGGL((k_stream<MODE, NJ>), grid, dim3(kThreads), 0, stream, p, upb);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
+    const int nj = (p.K + 511) / 512;
+    if (nj <= 1)
+        return launch_nj<MODE, 1>(p, stream);
+    if (nj <= 2)
+        return launch_nj<MODE, 2>(p, stream);
+    if (nj <= 4)
+        return launch_nj<MODE, 4>(p, stream);
+    return launch_nj<MODE, 8>(p, stream);
+}
+
+}  // namespace
+
+bool stream_supported(const GemmProblem &p) {
+    return !p.affine4 && p.K <= 4096;
+}
+
+hipError_t launch_stream(const GemmProblem &p, hipStream_t stream) {
+    switch (p.mode) {
+    case kGateUp: return launch_mode<kGateUp>(p, stream);
+    case kUpRelu2: return launch_mode<kUpRelu2>(p, stream);
+    default: return launch_mode<kDown>(p, stream);
+    }
+}
+
+}  // namespace moe

@@ -62,7 +62,7 @@ def load():
         p, i = C.c_void_p, C.c_int
         L.moe_workspace_bytes.argtypes = [C.POINTER(Dims), C.POINTER(C.c_size_t)]
         L.moe_workspace_bytes.restype = i
-        L.moe_route.argtypes = [C.POINTER(Dims), p, p, p, p, p, p]
+        L.moe_route.argtypes = [C.POINTER(Dims), p, p, p, p, p, p, C.c_size_t, p]
         L.moe_route.restype = i
         L.moe_plan.argtypes = [C.POINTER(Dims), p, p, p, p, p, p, p, C.c_size_t, p]
         L.moe_plan.restype = i
@@ -112,8 +112,10 @@ def route(x, router_w, bias, k, norm_topk=True, norm_eps=1e-6, stream=None):
     d = make_dims(T, H, 64, E, k, norm_topk=norm_topk, norm_eps=norm_eps)
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    nbytes = workspace_bytes(d)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
     _check(load().moe_route(C.byref(d), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(ids), _ptr(w),
-                            _stream(stream)))
+                            _ptr(ws), nbytes, _stream(stream)))
     return ids, w
 
 

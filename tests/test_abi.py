@@ -141,18 +141,22 @@ def test_zero_tokens_enqueue_nothing():
     rc = L.moe_forward(C.byref(d), C.byref(w), None, None, None, lib.workspace_bytes(d), None,
                        None, None, None)
     assert rc == 0 and L.moe_last_error().decode() == ""
-    rc = L.moe_route(C.byref(d), None, None, None, None, None, None)
+    rc = L.moe_route(C.byref(d), None, None, None, None, None, None, 0, None)
     assert rc == 0
 
 
 def test_route_and_plan_refuse_bad_pointers():
     L = lib.load()
     d = dims()
-    rc = L.moe_route(C.byref(d), _fake(0x1000), None, None, _fake(0x2000), _fake(0x3000), None)
+    rc = L.moe_route(C.byref(d), _fake(0x1000), None, None, _fake(0x2000), _fake(0x3000),
+                     _fake(0x4000), 1 << 20, None)
     assert rc == -1 and "router_w" in L.moe_last_error().decode()
     rc = L.moe_route(C.byref(d), _fake(0x1004), _fake(0x1000), None, _fake(0x2000),
-                     _fake(0x3000), None)
+                     _fake(0x3000), _fake(0x4000), 1 << 20, None)
     assert rc == -3 and "x" in L.moe_last_error().decode()
+    rc = L.moe_route(C.byref(d), _fake(0x1000), _fake(0x1000), None, _fake(0x2000),
+                     _fake(0x3000), _fake(0x4000), 16, None)
+    assert rc == -5 and "workspace_bytes = 16" in L.moe_last_error().decode()
     rc = L.moe_plan(C.byref(d), _fake(0x1000), _fake(0x1000), _fake(0x1000), _fake(0x1000),
                     _fake(0x1000), None, _fake(0x1000), 0, None)
     assert rc == -5

@@ -205,6 +205,31 @@ def test_forward_full_size_sampled(name):
     assert np.isfinite(out).all()
 
 
+DECODE_CASES = [("tiny_t64_e8_k2", 8), ("tiny_t64_e8_k2", 1), ("mid_swiglu", 8),
+                ("mid_swiglu", 3), ("mid_relu2_shared", 8), ("mid_relu2_shared", 1),
+                ("mid_e256_k8", 64), ("mid_e256_k8", 7), ("mid_nan_ties", 4),
+                ("mid_swiglu_bigseg", 2)]
+
+
+@pytest.mark.parametrize("name,T", DECODE_CASES)
+def test_decode_sized_batches(name, T):
+    # at most two assignments per expert: the router builds the plan in the
+    # same launch and the experts take the weight-streaming form
+    wl, inp = small_inputs(name)
+    wlT = wl.with_(T=T)
+    assert T * wl.k <= 2 * wl.E
+    inpT = dict(inp)
+    inpT["x"] = np.ascontiguousarray(inp["x"][:T])
+    out, ids, w, offs = run_forward(wlT, inpT)
+    ref, ids_ref, w_ref = oracle.forward_tokens(wlT, inpT, np.arange(T), want_routing=True)
+    check_routing(ids, w, ids_ref, w_ref)
+    _, o_ref, _, _ = oracle.plan(ids_ref, wl.E)
+    assert (offs == o_ref).all()
+    out32, _, _, _ = run_forward(wlT, inpT, torch.float32)
+    check_out(out32, ref, tol_for(wl))
+    assert (W.f32_to_bf16_bits(out32) == W.f32_to_bf16_bits(out)).all()
+
+
 # ------------------------------------------------------------------ edges
 
 EDGE = {
