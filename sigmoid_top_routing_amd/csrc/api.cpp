@@ -8,12 +8,13 @@
 // refused on the host, outputs are f32 or bf16 only).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.hpp"
 
 namespace {
@@ -104,6 +105,8 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
     REQUIRE((int64_t)d->T * d->k * d->I < ((int64_t)1 << 31) &&
                 (int64_t)d->T * d->I_shared < ((int64_t)1 << 31),
             MOE_E_SHAPE, "%s: T*k*I or T*I_shared reaches 2^31", what);
+    REQUIRE((int64_t)2 * std::max(d->I, d->I_shared) * d->H < ((int64_t)1 << 31), MOE_E_SHAPE,
+            "%s: 2*max(I, I_shared)*H reaches 2^31 (one expert's weight matrix)", what);
     REQUIRE(d->act == MOE_ACT_SWIGLU || d->act == MOE_ACT_RELU2, MOE_E_UNSUPPORTED,
             "%s: act = %d, need MOE_ACT_SWIGLU (0) or MOE_ACT_RELU2 (1)", what, d->act);
     REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_AFFINE4, MOE_E_UNSUPPORTED,

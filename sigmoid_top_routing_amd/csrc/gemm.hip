@@ -14,22 +14,27 @@
 //                      (bloomery PR #235: relu^2 keeps non-finite inputs)
 //   kDown    y[scatter[p], n] = C[p, n] in fp32, back in assignment order
 //
-// Tiling. A workgroup of 4 waves owns a BM x BN tile of one expert and
+// Which kernel. bf16 weights with K a multiple of 32 and at least 128 go to
+// the persistent direct-to-LDS kernel of grouped_gemm.hip. This file holds
+// the register-staged kernel for the rest: the 4-bit affine weights, whose
+// codes are decoded (scale * q + bias, group 64) to bf16 between the global
+// load and the LDS store, and short or odd K.
+//
+// Tiling. A workgroup of 4 waves owns a BM x 256 tile of one expert and
 // walks K in steps of 64. Per step it stages the A rows (gathered through
 // the plan: row(p) = gather[p] / gather_div, so x is never permuted in
-// memory) and the BN weight rows in LDS, double buffered, with a 16-byte
+// memory) and the 256 weight rows in LDS, double buffered, with a 16-byte
 // XOR swizzle so the MFMA operand reads hit distinct banks. Each wave owns
-// a (BM/2) x (BN/2) quarter and issues v_mfma_f32_32x32x16_bf16 over it.
-// For kGateUp a tile's BN weight rows are BN/2 gate rows and the BN/2 up
-// rows that pair with them, and each wave takes matching gate and up
-// columns, so silu(g) * u is formed in registers without an LDS exchange.
-// The 4-bit affine form decodes its codes (scale * q + bias, group 64) to
-// bf16 on the way into LDS; the MFMA loop is the same.
+// a (BM/2) x 128 quarter and issues v_mfma_f32_32x32x16_bf16 over it.
+// For kGateUp a tile's weight rows are 128 gate rows and the 128 up rows
+// that pair with them, and each wave takes matching gate and up columns, so
+// silu(g) * u is formed in registers without an LDS exchange.
 //
 // Tile order. Workgroups are dispatched to the 8 XCDs round robin, so the
-// block index is remapped to give each XCD a contiguous run of the logical
-// order (n-tile major, m-tile minor): the m-tiles that share a weight tile
-// then run on one XCD and share its L2.
+// block index is remapped to give each XCD an equal contiguous run of the
+// real tiles in m-major, n-minor order: the workgroups resident on an XCD at
+// one time are the n-tiles of one or two m-tiles, which read the same A rows
+// and (an expert's m-tiles being adjacent) the same weight rows from its L2.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -43,30 +48,38 @@ constexpr int kThreads = 256;
 constexpr int kBK = 64;
 constexpr int kXcds = 8;
 
+// 8 chunks of 16 bytes per row of 64 bf16. A ds_read_b128 serves 16 lanes
+// per pass from 64 banks (256 bytes); the fragment reads of 16 consecutive
+// rows then fall in distinct 16-byte bank groups when the chunk is XORed
+// with bits 1-3 of the row (bit 0 already picks the 128-byte half).
 __device__ __forceinline__ int swz(int row, int chunk) {
-    return row * 8 + (chunk ^ (row & 7));
+    return row * 8 + (chunk ^ ((row >> 1) & 7));
 }
 
-// Which expert segment and which BM rows of it this workgroup owns.
-// Returns false when the m-tile index is past the last real tile.
+// Which tile this workgroup owns: the expert, the BM rows of its segment
+// and the n-tile. The real tiles (sum over experts of ceil(rows_e / BM),
+// times n_tiles) are numbered m-major, n-minor, and each XCD takes an equal
+// contiguous share of that numbering: workgroups reach the XCDs round robin
+// (XCD = block % 8) and each XCD starts its workgroups in block order, so the
+// workgroups resident on one XCD at a time are the n-tiles of one or two
+// m-tiles, which share the A rows and the expert's weight rows in that XCD's
+// L2. The grid is sized for the worst case; workgroups past the real tiles
+// return at once. Returns false for those.
 template <int BM>
-__device__ bool locate_tile(const GemmProblem &p, int mt, int *e_out, int *row0, int *row_end) {
-    if (p.offsets == nullptr) {
-        const int tiles = (p.rows + BM - 1) / BM;
-        if (mt >= tiles)
-            return false;
-        *e_out = 0;
-        *row0 = mt * BM;
-        *row_end = p.rows;
-        return true;
-    }
+__device__ bool locate_tile(const GemmProblem &p, int n_tiles, int *e_out, int *row0,
+                            int *row_end, int *nt_out) {
     __shared__ int s_wsum[4];
     __shared__ int s_hit[3];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
     int tiles = 0, lo = 0, hi = 0;
-    if (tid < p.E) {
+    if (p.offsets == nullptr) {
+        if (tid == 0) {
+            hi = p.rows;
+            tiles = (p.rows + BM - 1) / BM;
+        }
+    } else if (tid < p.E) {
         lo = p.offsets[tid];
         hi = p.offsets[tid + 1];
         tiles = (hi - lo + BM - 1) / BM;
@@ -82,45 +95,96 @@ __device__ bool locate_tile(const GemmProblem &p, int mt, int *e_out, int *row0,
     if (tid == 0)
         s_hit[0] = -1;
     __syncthreads();
-    for (int w = 0; w < wave; ++w)
-        incl += s_wsum[w];
+    int total = 0;
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave)
+            incl += s_wsum[w];
+        total += s_wsum[w];
+    }
     const int excl = incl - tiles;
-    if (tid < p.E && mt >= excl && mt < incl) {
+    const int work = total * n_tiles;
+    const int share = (work + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int L = (blockIdx.x % kXcds) * share + slot;
+    if (slot >= share || L >= work)
+        return false;                       // uniform over the workgroup
+    const int mt = L / n_tiles;
+    if (tiles > 0 && mt >= excl && mt < incl) {
         s_hit[0] = tid;
         s_hit[1] = lo + (mt - excl) * BM;
         s_hit[2] = hi;
     }
     __syncthreads();
-    if (s_hit[0] < 0)
-        return false;
     *e_out = s_hit[0];
     *row0 = s_hit[1];
     *row_end = s_hit[2];
+    *nt_out = L % n_tiles;
     return true;
 }
 
-template <int BM, int BN, int MODE, bool AFF>
-__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int mt_max) {
+// worst-case number of m-tiles, then the grid: a whole number of XCD rounds
+// that covers every real tile
+template <int BM>
+int grid_blocks(const GemmProblem &p, int n_tiles) {
+    int mt_max;
+    if (p.offsets == nullptr) {
+        mt_max = (p.rows + BM - 1) / BM;
+    } else {
+        const int nonempty = p.E < p.max_rows ? p.E : p.max_rows;
+        mt_max = (p.max_rows + BM - 1) / BM + nonempty;
+    }
+    const int work = mt_max * n_tiles;
+    return (work + kXcds - 1) / kXcds * kXcds;
+}
+
+// Main loop. A step covers K = 64 in 4 sub-steps of K = 16; a sub-step is
+// TM * TN independent MFMAs, and every memory instruction of the step is
+// placed between two of them so that it issues while the matrix core is
+// busy (scheduling fences keep the written order):
+//   sub-step 0, 1, 2: LDS reads of the next sub-step's fragments (into the
+//                     other half of a register double buffer)
+//   sub-step 2:       also the LDS writes of the staged registers (operands
+//                     of step kt + 1) into the idle LDS buffer
+//   barrier           (the idle buffer is now complete; the current one is
+//                     no longer read)
+//   sub-step 3:       LDS reads of step kt + 1's first fragments, and the
+//                     global loads of step kt + 2 into the staged registers
+// So the global loads have sub-steps 3, 0 and 1 to arrive and the LDS reads
+// a whole sub-step. The loop body has no branches: rows past a segment or
+// past N are clamped to a valid row (their results are never stored) and
+// loads past the last step reload it.
+//
+// Global addresses are a uniform base (the operand, or the expert's weight
+// matrix) plus a 32-bit byte offset per thread; the host limits keep every
+// operand and every expert's matrix under 2^32 bytes.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+__device__ __forceinline__ uint4 load16(const char *base, uint32_t off) {
+    return *reinterpret_cast<const uint4 *>(base + off);
+}
+
+template <int BM, int MODE, bool AFF>
+__global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int n_tiles) {
+    constexpr int BN = 256;
     constexpr int TM = BM / 64;          // 32-row MFMA tiles per wave
     constexpr int TN = BN / 64;          // 32-col MFMA tiles per wave
     constexpr int AR = BM / 32;          // A rows staged per thread per step
     constexpr int BR = BN / 32;          // B rows staged per thread per step (bf16)
     constexpr int BQ = BN / 128;         // B half-rows per thread per step (affine-4)
+    constexpr int BLOADS = AFF ? BQ : BR;
+    constexpr int STAGE = (BM + BN) * 8; // 16-byte slots per LDS buffer
     static_assert(TN % 2 == 0, "gate and up columns come in pairs");
 
-    __shared__ uint4 As[2][BM * 8];
-    __shared__ uint4 Bs[2][BN * 8];
+    __shared__ uint4 smem[2 * STAGE];
     __shared__ int s_out_row[BM];
 
-    // ---- tile
-    const int nblk = gridDim.x;
-    const int bid = blockIdx.x;
-    const int L = (bid % kXcds) * (nblk / kXcds) + bid / kXcds;
-    const int nt = L / mt_max;
-    const int mt = L % mt_max;
-    int e, row0, row_end;
-    if (!locate_tile<BM>(p, mt, &e, &row0, &row_end))
+    int e, row0, row_end, nt;
+    if (!locate_tile<BM>(p, n_tiles, &e, &row0, &row_end, &nt))
         return;
+    e = __builtin_amdgcn_readfirstlane(e);
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    row_end = __builtin_amdgcn_readfirstlane(row_end);
+    nt = __builtin_amdgcn_readfirstlane(nt);
     const int n_out0 = nt * (MODE == kGateUp ? BN / 2 : BN);
 
     const int tid = threadIdx.x;
@@ -136,115 +200,107 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int mt_max)
         }
     }
 
-    // ---- A rows this thread stages
-    const uint16_t *a_ptr[AR];
+    // ---- A rows this thread stages (clamped into the segment)
+    const char *a_base = (const char *)p.A;
+    uint32_t a_off[AR];
 #pragma unroll
     for (int i = 0; i < AR; ++i) {
-        const int r = (tid >> 3) + i * 32;
-        const int pos = row0 + r;
-        if (pos < row_end) {
-            const int arow = p.gather ? p.gather[pos] / p.gather_div : pos;
-            a_ptr[i] = p.A + (size_t)arow * p.lda + chunk * 8;
-        } else {
-            a_ptr[i] = nullptr;
-        }
+        int pos = row0 + (tid >> 3) + i * 32;
+        if (pos >= row_end)
+            pos = row_end - 1;
+        const int arow = p.gather ? p.gather[pos] / p.gather_div : pos;
+        a_off[i] = ((uint32_t)arow * (uint32_t)p.lda + chunk * 8) * 2u;
     }
 
-    // ---- B rows this thread stages
-    auto b_row = [&](int r, bool *ok) -> int {
+    // ---- B rows this thread stages (clamped below N), relative to expert e
+    auto b_row = [&](int r) -> int {
         if (MODE == kGateUp) {
-            const int half = BN / 2;
-            const int n = n_out0 + (r % half);
-            *ok = n < p.I;
-            return r < half ? n : p.I + n;
+            int n = n_out0 + (r % (BN / 2));
+            if (n >= p.I)
+                n = p.I - 1;
+            return r < BN / 2 ? n : p.I + n;
         }
         const int n = n_out0 + r;
-        *ok = n < p.N;
-        return n;
+        return n < p.N ? n : p.N - 1;
     };
-    const uint16_t *b_ptr[AFF ? 1 : BR];
-    const uint32_t *q_ptr[AFF ? BQ : 1];
-    const uint16_t *qs_ptr[AFF ? BQ : 1];
-    const uint16_t *qb_ptr[AFF ? BQ : 1];
+    const size_t e_rows = (size_t)e * p.N;
+    const char *b_base;
+    const char *qs_base = nullptr, *qb_base = nullptr;
+    uint32_t b_off[BLOADS];
+    uint32_t sb_off[AFF ? BQ : 1];
     if (!AFF) {
+        b_base = (const char *)p.B + e_rows * p.K * 2;
 #pragma unroll
-        for (int i = 0; i < BR; ++i) {
-            bool ok;
-            const int wr = b_row((tid >> 3) + i * 32, &ok);
-            b_ptr[i] = ok ? (const uint16_t *)p.B + ((size_t)e * p.N + wr) * p.K + chunk * 8
-                          : nullptr;
-        }
+        for (int i = 0; i < BR; ++i)
+            b_off[i] = ((uint32_t)b_row((tid >> 3) + i * 32) * (uint32_t)p.K + chunk * 8) * 2u;
     } else {
         const int groups = p.K / 64;
+        b_base = (const char *)p.B + e_rows * (p.K / 2);
+        qs_base = (const char *)(p.Bscale + e_rows * groups);
+        qb_base = (const char *)(p.Bbias + e_rows * groups);
 #pragma unroll
         for (int i = 0; i < BQ; ++i) {
             const int q = tid + i * kThreads;
-            bool ok;
-            const int wr = b_row(q >> 1, &ok);
-            const size_t row = (size_t)e * p.N + wr;
-            q_ptr[i] = ok ? (const uint32_t *)p.B + row * (p.K / 8) + (q & 1) * 4 : nullptr;
-            qs_ptr[i] = ok ? p.Bscale + row * groups : nullptr;
-            qb_ptr[i] = ok ? p.Bbias + row * groups : nullptr;
+            const uint32_t row = (uint32_t)b_row(q >> 1);
+            b_off[i] = row * (uint32_t)(p.K / 2) + (q & 1) * 16;
+            sb_off[i] = row * (uint32_t)groups * 2u;
         }
     }
 
     uint4 a_reg[AR];
-    uint4 b_reg[AFF ? BQ : BR];
+    uint4 b_reg[BLOADS];
     uint32_t sb_reg[AFF ? BQ : 1];
 
-    auto load_step = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < AR; ++i)
-            a_reg[i] = a_ptr[i] ? *reinterpret_cast<const uint4 *>(a_ptr[i] + k0)
-                                : make_uint4(0, 0, 0, 0);
-        if (!AFF) {
-#pragma unroll
-            for (int i = 0; i < BR; ++i)
-                b_reg[i] = b_ptr[i] ? *reinterpret_cast<const uint4 *>(b_ptr[i] + k0)
-                                    : make_uint4(0, 0, 0, 0);
+    // staged operand m of a step: A rows first (m < AR), then B rows
+    auto load_one = [&](int k0, int m) {
+        if (m < AR) {
+            a_reg[m] = load16(a_base, a_off[m] + k0 * 2);
+        } else if (!AFF) {
+            b_reg[m - AR] = load16(b_base, b_off[m - AR] + k0 * 2);
         } else {
+            const int i = m - AR;
+            b_reg[i] = load16(b_base, b_off[i] + k0 / 2);
+            const uint32_t g = sb_off[i] + (k0 / 64) * 2;
+            sb_reg[i] = (uint32_t)*(const uint16_t *)(qs_base + g) |
+                        ((uint32_t)*(const uint16_t *)(qb_base + g) << 16);
+        }
+    };
+    auto store_one = [&](uint4 *As, int m) {
+        uint4 *Bs = As + BM * 8;
+        if (m < AR) {
+            As[swz((tid >> 3) + m * 32, chunk)] = a_reg[m];
+        } else if (!AFF) {
+            Bs[swz((tid >> 3) + (m - AR) * 32, chunk)] = b_reg[m - AR];
+        } else {
+            // 32 codes (half a group of 64) -> bf16 of scale * q + bias
+            const int i = m - AR;
+            const int q = tid + i * kThreads;
+            const int r = q >> 1, half = q & 1;
+            const float sc = bf16_to_f32(sb_reg[i] & 0xffffu);
+            const float bi = bf16_to_f32(sb_reg[i] >> 16);
+            const uint32_t words[4] = {b_reg[i].x, b_reg[i].y, b_reg[i].z, b_reg[i].w};
 #pragma unroll
-            for (int i = 0; i < BQ; ++i) {
-                if (q_ptr[i]) {
-                    b_reg[i] = *reinterpret_cast<const uint4 *>(q_ptr[i] + k0 / 8);
-                    sb_reg[i] = (uint32_t)qs_ptr[i][k0 / 64] | ((uint32_t)qb_ptr[i][k0 / 64] << 16);
-                } else {
-                    b_reg[i] = make_uint4(0, 0, 0, 0);
-                    sb_reg[i] = 0;   // scale 0, bias 0: a zero row
+            for (int w = 0; w < 4; ++w) {
+                uint32_t packed[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float lo = __builtin_fmaf(sc, (float)((words[w] >> (8 * c)) & 15u), bi);
+                    const float hi = __builtin_fmaf(sc, (float)((words[w] >> (8 * c + 4)) & 15u), bi);
+                    packed[c] = pack_bf16x2(lo, hi);
                 }
+                Bs[swz(r, half * 4 + w)] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
             }
         }
     };
-
-    auto store_step = [&](int buf) {
+    auto load_step = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < AR; ++i)
-            As[buf][swz((tid >> 3) + i * 32, chunk)] = a_reg[i];
-        if (!AFF) {
+        for (int m = 0; m < AR + BLOADS; ++m)
+            load_one(k0, m);
+    };
+    auto store_step = [&](uint4 *As) {
 #pragma unroll
-            for (int i = 0; i < BR; ++i)
-                Bs[buf][swz((tid >> 3) + i * 32, chunk)] = b_reg[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < BQ; ++i) {
-                const int q = tid + i * kThreads;
-                const int r = q >> 1, half = q & 1;
-                const float sc = bf16_to_f32(sb_reg[i] & 0xffffu);
-                const float bi = bf16_to_f32(sb_reg[i] >> 16);
-                const uint32_t words[4] = {b_reg[i].x, b_reg[i].y, b_reg[i].z, b_reg[i].w};
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t packed[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        const float lo = __builtin_fmaf(sc, (float)((words[w] >> (8 * c)) & 15u), bi);
-                        const float hi = __builtin_fmaf(sc, (float)((words[w] >> (8 * c + 4)) & 15u), bi);
-                        packed[c] = pack_bf16x2(lo, hi);
-                    }
-                    Bs[buf][swz(r, half * 4 + w)] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-                }
-            }
-        }
+        for (int m = 0; m < AR + BLOADS; ++m)
+            store_one(As, m);
     };
 
     f32x16 acc[TM][TN];
@@ -254,90 +310,106 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int mt_max)
         for (int j = 0; j < TN; ++j)
             acc[i][j] = f32x16{};
 
-    // rows of the B tile each of this wave's column tiles reads
-    int b_tile_row[TN];
+    // LDS slot of this lane's fragment piece for each sub-step; the tiles of
+    // a wave sit 32 rows apart, which keeps the swizzle and adds 256 slots
+    const int a_tile_row = wm * (BM / 2);
+    const int b_row0 = MODE == kGateUp ? wn * (BN / 4) : wn * (BN / 2);
+    int b_tile_off[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
         if (MODE == kGateUp)
-            b_tile_row[j] = (j < TN / 2) ? wn * (BN / 4) + j * 32
-                                         : BN / 2 + wn * (BN / 4) + (j - TN / 2) * 32;
+            b_tile_off[j] = (j < TN / 2) ? j * 32 : BN / 2 + (j - TN / 2) * 32;
         else
-            b_tile_row[j] = wn * (BN / 2) + j * 32;
+            b_tile_off[j] = j * 32;
+        b_tile_off[j] *= 8;
     }
-    const int a_tile_row = wm * (BM / 2);
+    int a_slot[kBK / 16], b_slot[kBK / 16];
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int ch = kk * 2 + (lane >> 5);
+        a_slot[kk] = swz(a_tile_row + (lane & 31), ch);
+        b_slot[kk] = BM * 8 + swz(b_row0 + (lane & 31), ch);
+    }
 
     const int KT = p.K / kBK;
+    constexpr int NQ = TM * TN;            // MFMAs per sub-step
+    constexpr int NF = TM + TN;            // fragment reads per sub-step
+    constexpr int NL = AR + BLOADS;        // staged loads (and stores) per step
+    bf16x8 af[2][TM], bfr[2][TN];
+    auto read_frag = [&](const uint4 *S, int slot, int kk, int m) {
+        if (m < TM)
+            af[slot][m] = __builtin_bit_cast(bf16x8, S[a_slot[kk] + m * 256]);
+        else
+            bfr[slot][m - TM] = __builtin_bit_cast(bf16x8, S[b_slot[kk] + b_tile_off[m - TM]]);
+    };
+    auto mfma = [&](int slot, int q) {
+        const int i = q / TN, j = q % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[slot][i], bfr[slot][j], acc[i][j],
+                                                           0, 0, 0);
+    };
+
+    // prologue: step 0 staged and stored, step 1 loads in flight, the first
+    // fragments read
     load_step(0);
-    store_step(0);
+    store_step(smem);
     __syncthreads();
+    load_step((KT > 1 ? 1 : 0) * kBK);
+#pragma unroll
+    for (int m = 0; m < NF; ++m)
+        read_frag(smem, 0, 0, m);
+
     for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT)
-            load_step((kt + 1) * kBK);
+        const uint4 *S = smem + (kt & 1) * STAGE;
+        uint4 *N = smem + ((kt + 1) & 1) * STAGE;
+        const int k2 = (kt + 2 < KT ? kt + 2 : KT - 1) * kBK;
+        fence();
+        // sub-steps 0 and 1
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int ch = kk * 2 + (lane >> 5);
-            bf16x8 af[TM], bfr[TN];
+        for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int r = a_tile_row + i * 32 + (lane & 31);
-                af[i] = __builtin_bit_cast(bf16x8, As[buf][swz(r, ch)]);
+            for (int q = 0; q < NQ; ++q) {
+                mfma(kk & 1, q);
+#pragma unroll
+                for (int m = q * NF / NQ; m < (q + 1) * NF / NQ; ++m)
+                    read_frag(S, (kk + 1) & 1, kk + 1, m);
+                fence();
             }
-#pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const int r = b_tile_row[j] + (lane & 31);
-                bfr[j] = __builtin_bit_cast(bf16x8, Bs[buf][swz(r, ch)]);
-            }
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int j = 0; j < TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j],
-                                                                       0, 0, 0);
         }
-        if (kt + 1 < KT)
-            store_step(buf ^ 1);
+        // sub-step 2: fragments of sub-step 3, then the staged operands of
+        // step kt + 1 into the idle buffer
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            mfma(0, q);
+#pragma unroll
+            for (int m = q * NF / NQ; m < (q + 1) * NF / NQ; ++m)
+                read_frag(S, 1, 3, m);
+#pragma unroll
+            for (int m = q * NL / NQ; m < (q + 1) * NL / NQ; ++m)
+                store_one(N, m);
+            fence();
+        }
         __syncthreads();
+        fence();
+        // sub-step 3: first fragments of step kt + 1, loads of step kt + 2
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            mfma(1, q);
+#pragma unroll
+            for (int m = q * NF / NQ; m < (q + 1) * NF / NQ; ++m)
+                read_frag(N, 0, 0, m);
+#pragma unroll
+            for (int m = q * NL / NQ; m < (q + 1) * NL / NQ; ++m)
+                load_one(k2, m);
+            fence();
+        }
     }
+    __syncthreads();
 
     // ---- epilogue. acc[i][j][r] holds row (8*(r/4) + 4*(lane/32) + r%4) and
     // column (lane % 32) of the 32x32 tile (i, j).
     const int col = lane & 31;
     const int rsub = 4 * (lane >> 5);
-    if (MODE == kGateUp) {
-        uint16_t *h = (uint16_t *)p.C;
-#pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-            const int n = n_out0 + wn * (BN / 4) + j * 32 + col;
-            if (n >= p.I)
-                continue;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int pos = row0 + a_tile_row + i * 32 + 8 * (r >> 2) + rsub + (r & 3);
-                    if (pos < row_end)
-                        h[(size_t)pos * p.ldc + n] =
-                            (uint16_t)f32_to_bf16(silu_mul(acc[i][j][r], acc[i][j + TN / 2][r]));
-                }
-        }
-    } else if (MODE == kUpRelu2) {
-        uint16_t *h = (uint16_t *)p.C;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            const int n = n_out0 + wn * (BN / 2) + j * 32 + col;
-            if (n >= p.N)
-                continue;
-#pragma unroll
-            for (int i = 0; i < TM; ++i)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int pos = row0 + a_tile_row + i * 32 + 8 * (r >> 2) + rsub + (r & 3);
-                    if (pos < row_end)
-                        h[(size_t)pos * p.ldc + n] = (uint16_t)f32_to_bf16(relu_sq(acc[i][j][r]));
-                }
-        }
-    } else {
+    if (MODE == kDown) {
         float *y = (float *)p.C;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -353,30 +425,51 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int mt_max)
                         y[(size_t)orow * p.ldc + n] = acc[i][j][r];
                 }
         }
+        return;
+    }
+    // bf16 h: each wave transposes its (BM/2) x CW block through LDS (the
+    // operand buffers are idle after the last barrier) so the global stores
+    // are whole 16-byte row pieces
+    constexpr int CW = MODE == kGateUp ? BN / 4 : BN / 2;   // output columns per wave
+    constexpr int CT = CW / 32;                              // 32-col tiles per wave
+    uint16_t *hs = (uint16_t *)smem + (size_t)wave * (BM / 2) * CW;
+#pragma unroll
+    for (int j = 0; j < CT; ++j)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = i * 32 + 8 * (r >> 2) + rsub + (r & 3);
+                const float v = MODE == kGateUp ? silu_mul(acc[i][j][r], acc[i][j + TN / 2][r])
+                                                : relu_sq(acc[i][j][r]);
+                hs[row * CW + j * 32 + col] = (uint16_t)f32_to_bf16(v);
+            }
+    __syncthreads();
+    uint16_t *h = (uint16_t *)p.C;
+    const int ncols = MODE == kGateUp ? p.I : p.N;
+    const int wcol0 = n_out0 + wn * CW;
+    constexpr int PIECES = (BM / 2) * CW / 8;                // 16-byte pieces per wave
+#pragma unroll 4
+    for (int q = lane; q < PIECES; q += kWave) {
+        const int row = q / (CW / 8), cc = q % (CW / 8);
+        const int pos = row0 + a_tile_row + row;
+        const int n = wcol0 + cc * 8;
+        if (pos < row_end && n < ncols)
+            *reinterpret_cast<uint4 *>(h + (size_t)pos * p.ldc + n) =
+                *reinterpret_cast<const uint4 *>(hs + row * CW + cc * 8);
     }
 }
 
-template <int BM, int BN, int MODE, bool AFF>
+template <int BM, int MODE, bool AFF>
 hipError_t launch_tile(const GemmProblem &p, hipStream_t stream) {
-    int mt_max;
-    if (p.offsets == nullptr) {
-        mt_max = (p.rows + BM - 1) / BM;
-    } else {
-        const int nonempty = p.E < p.max_rows ? p.E : p.max_rows;
-        mt_max = (p.max_rows + BM - 1) / BM + nonempty;
-    }
     const int n_cols = MODE == kGateUp ? p.I : p.N;
-    const int n_tile = MODE == kGateUp ? BN / 2 : BN;
-    const int nt = (n_cols + n_tile - 1) / n_tile;
-    int blocks = mt_max * nt;
+    const int n_tile = MODE == kGateUp ? 128 : 256;
+    const int n_tiles = (n_cols + n_tile - 1) / n_tile;
+    const int blocks = grid_blocks<BM>(p, n_tiles);
     if (blocks == 0)
         return hipSuccess;
-    // round the grid up to whole XCD rounds; mt_max absorbs the padding
-    while ((mt_max * nt) % kXcds)
-        ++mt_max;
-    blocks = mt_max * nt;
-    hipLaunchKernelGGL((k_gemm<BM, BN, MODE, AFF>), dim3(blocks), dim3(kThreads), 0, stream, p,
-                       mt_max);
+    hipLaunchKernelGGL((k_gemm<BM, MODE, AFF>), dim3(blocks), dim3(kThreads), 0, stream, p,
+                       n_tiles);
     return hipGetLastError();
 }
 
@@ -389,13 +482,15 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
     const int rows = p.offsets != nullptr ? p.max_rows : p.rows;
     const int avg = segs > 0 ? rows / segs : 0;
     if (avg >= 192)
-        return launch_tile<256, 256, MODE, AFF>(p, stream);
-    return launch_tile<128, 256, MODE, AFF>(p, stream);
+        return launch_tile<256, MODE, AFF>(p, stream);
+    return launch_tile<128, MODE, AFF>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
+    if (grouped_supported(p))
+        return launch_grouped(p, stream);
     if (p.affine4) {
         switch (p.mode) {
         case kGateUp: return launch_mode<kGateUp, true>(p, stream);

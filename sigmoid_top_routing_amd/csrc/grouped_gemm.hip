@@ -1,0 +1,621 @@
+// grouped_gemm.hip -- persistent grouped expert GEMM for bf16 weights (gfx950).
+//
+// The same products as the staged kernel in gemm.hip,
+//   C[p, n] = sum_k A[row(p), k] * B[e(p), n, k]   (fp32 accumulate),
+// with the same fused epilogues (silu(g) * u for the gated up projection,
+// relu^2 for the non-gated one, fp32 scatter for the down projection), laid
+// out for the matrix cores and the memory system of one MI355X:
+//
+// * Persistent workgroups. The grid is one workgroup per CU; each walks a
+//   list of tiles (BM token rows of one expert x 256 weight rows), so a
+//   tile's first operand slices are fetched while the previous tile is still
+//   multiplying, and its output stores drain while the next one runs.
+//
+// * Tile order. Workgroups reach the 8 XCDs round robin (XCD = block % 8).
+//   The real tiles (sum over experts of ceil(rows_e / BM), times the n-tiles)
+//   are numbered m-major, n-minor, and each XCD takes an equal contiguous
+//   share; its 32 CUs sweep that share together, so the tiles resident on an
+//   XCD at one time are the n-tiles of one or two m-tiles, which read the
+//   same token rows and (an expert's m-tiles being adjacent) the same weight
+//   rows from that XCD's L2.
+//
+// * Operands go from global memory straight into LDS (global_load_lds, 16
+//   bytes per lane) through a ring of 4 stages of K = 32, requested 3 stages
+//   ahead of the one being multiplied. The request stream runs across tile
+//   boundaries: the last steps of a tile request the first slices of the
+//   next. No VGPRs hold staged data and no LDS writes are issued by the
+//   waves. Rows past a segment or past N are clamped to a valid row; their
+//   results are never stored.
+//
+// * The MFMA v_mfma_f32_32x32x16_bf16 is issued with the weight fragment as
+//   its first operand, so the 32x32 accumulator tile is [weight row][token]:
+//   each lane owns one token and, per group of 4 result registers, 4
+//   consecutive output columns, which the epilogue packs (4 bf16 or 4 fp32)
+//   and stores directly.
+//
+// * A step (K = 32) is two sub-steps of TM x TN independent MFMAs. Every LDS
+//   read and every global request sits between two MFMAs (scheduling fences
+//   keep the written order): sub-step 0 reads the fragments of sub-step 1;
+//   then one barrier makes the next stage visible; sub-step 1 reads the next
+//   step's first fragments and requests the stage 3 steps ahead.
+//
+// Ring hazards. The stage refilled in step g is the one read in step g - 1,
+// whose last fragment reads were consumed by MFMAs before the barrier of
+// step g, and the refill is requested after that barrier. A stage is read
+// only after a barrier preceded by each wave's wait for its own requests of
+// that stage (s_waitcnt vmcnt). The LDS reads and the refill of one step go
+// through separate __restrict__ pointers, so the compiler does not order the
+// reads behind the requests still in flight; the explicit waits do that.
+#include <hip/hip_runtime.h>
+
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBK = 32;          // K per ring stage
+constexpr int kStages = 4;
+constexpr int kAhead = 3;        // stages requested ahead of the one multiplied
+constexpr int kBN = 256;         // weight rows per tile
+constexpr int kXcds = 8;
+constexpr int kMaxE = 256;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format;
+// offsets are range checked against the record count, stride 0).
+constexpr int kBufferWord3 = 0x00020000;
+
+// 16-byte slot of logical chunk c (of 4 per row of 32 bf16) of row r within a
+// stage. A fragment read serves 16 lanes (16 consecutive rows, one chunk) per
+// pass from 64 banks; bits 0-1 of the row pick the 64-byte quarter of the
+// 256-byte bank window and the chunk is XORed with bits 2-3 of the row.
+__device__ __forceinline__ int slot_of(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int BM>
+struct Geo {
+    static constexpr int TM = BM / 64;            // 32-token MFMA tiles per wave
+    static constexpr int TN = kBN / 64;           // 32-weight-row MFMA tiles per wave
+    static constexpr int AI = BM * 4 / kThreads;  // A requests per thread per stage
+    static constexpr int BI = kBN * 4 / kThreads; // B requests per thread per stage
+    static constexpr int PER = AI + BI;
+    static constexpr int STAGE = (BM + kBN) * 4;  // 16-byte slots per stage
+    static constexpr int NQ = TM * TN;            // MFMAs per sub-step
+    static constexpr int NF = TM + TN;            // fragment reads per sub-step
+};
+
+// Where the tiles of one launch are: the prefix of tiles over the segments
+// (a dense problem is one segment) and this workgroup's share of the list.
+struct TileList {
+    const int *pre;      // LDS: first tile index of each segment
+    const int *off;      // LDS: first row of each segment, and the end
+    int nseg, n_tiles, work, share, xcd, cslot, nslots;
+};
+
+// Uniform placement of this workgroup's i-th tile; false past the end.
+template <int BM>
+__device__ __forceinline__ bool place(const TileList &tl, int i, int &e, int &row0, int &row_end,
+                                      int &nt) {
+    const int local = tl.cslot + i * tl.nslots;
+    const int L = tl.xcd * tl.share + local;
+    if (local >= tl.share || L >= tl.work)
+        return false;
+    const int mt = L / tl.n_tiles;
+    // the segment holding m-tile mt: the last e with pre[e] <= mt (empty
+    // segments share their prefix with the next one and are skipped)
+    int lo = 0, hi = tl.nseg - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tl.pre[mid] <= mt)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    e = __builtin_amdgcn_readfirstlane(lo);
+    row0 = __builtin_amdgcn_readfirstlane(tl.off[lo] + (mt - tl.pre[lo]) * BM);
+    row_end = __builtin_amdgcn_readfirstlane(tl.off[lo + 1]);
+    nt = __builtin_amdgcn_readfirstlane(L % tl.n_tiles);
+    return true;
+}
+
+// The A row behind each of this thread's A pieces of a tile, as stored in
+// the plan (a slot, divided by gather_div once it has arrived). Rows past
+// the segment repeat its last row.
+template <int BM>
+__device__ __forceinline__ void gathered_rows(const GemmProblem &p, int row0, int row_end,
+                                              int (&raw)[Geo<BM>::AI]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int i = 0; i < Geo<BM>::AI; ++i) {
+        int pos = row0 + (((wave * Geo<BM>::AI + i) * kWave + lane) >> 2);
+        if (pos >= row_end)
+            pos = row_end - 1;
+        raw[i] = p.gather ? p.gather[pos] : pos;
+    }
+}
+
+template <int BM>
+__device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)[Geo<BM>::AI],
+                                          uint32_t (&off)[Geo<BM>::AI]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+#pragma unroll
+    for (int i = 0; i < Geo<BM>::AI; ++i) {
+        const int s = (wave * Geo<BM>::AI + i) * kWave + lane;
+        const int c = (s & 3) ^ ((s >> 4) & 3);
+        const int arow = p.gather ? raw[i] / p.gather_div : raw[i];
+        off[i] = ((uint32_t)arow * (uint32_t)p.lda + c * 8) * 2u;
+    }
+}
+
+// Request state of the tile whose slices are being fetched.
+template <int BM>
+struct Req {
+    int e, nt;                        // uniform
+    uint32_t a_off[Geo<BM>::AI];      // per thread
+};
+
+// Piece m (A pieces first, then B pieces) of K-slice ks into one stage.
+template <int BM, int MODE>
+__device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmProblem &p,
+                                        const Req<BM> &q, int ks, int m) {
+    using G = Geo<BM>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const uint32_t kb = (uint32_t)ks * (kBK * 2);
+    if (m < G::AI) {
+        __builtin_amdgcn_global_load_lds((const void *)((const char *)p.A + q.a_off[m] + kb),
+                                         (lds_void *)(stage + (wave * G::AI + m) * kWave), 16, 0, 0);
+    } else {
+        const int i = m - G::AI;
+        const int s = (wave * G::BI + i) * kWave + lane;
+        const int r = s >> 2;
+        const int c = (s & 3) ^ ((r >> 2) & 3);
+        int wr;
+        if (MODE == kGateUp) {
+            int n = q.nt * (kBN / 2) + (r & (kBN / 2 - 1));
+            if (n >= p.I)
+                n = p.I - 1;
+            wr = r < kBN / 2 ? n : p.I + n;
+        } else {
+            wr = q.nt * kBN + r;
+            if (wr >= p.N)
+                wr = p.N - 1;
+        }
+        const char *b_base = (const char *)p.B + (size_t)q.e * p.N * p.K * 2;
+        const uint32_t off = ((uint32_t)wr * (uint32_t)p.K + c * 8) * 2u + kb;
+        __builtin_amdgcn_global_load_lds((const void *)(b_base + off),
+                                         (lds_void *)(stage + BM * 4 + (wave * G::BI + i) * kWave),
+                                         16, 0, 0);
+    }
+}
+
+// Fragment registers: slot 0 and 1 of a double buffer over sub-steps.
+template <int BM>
+struct Frags {
+    bf16x8 a[2][Geo<BM>::TM];
+    bf16x8 b[2][Geo<BM>::TN];
+};
+
+// Fragment m (A tiles first, then B tiles) from a stage into a slot.
+template <int BM>
+__device__ __forceinline__ void read_frag(const uint4 *__restrict__ S, Frags<BM> &f, int slot, int m,
+                                          int a_slot, int b_slot, const int *b_toff) {
+    using G = Geo<BM>;
+    if (m < G::TM)
+        f.a[slot][m] = __builtin_bit_cast(bf16x8, S[a_slot + m * 128]);
+    else
+        f.b[slot][m - G::TM] = __builtin_bit_cast(bf16x8, S[b_slot + b_toff[m - G::TM]]);
+}
+
+// One step: multiply stage S (its sub-step 0 fragments are already in slot
+// 0), read the next step's first fragments from Snext, refill Sfill with
+// K-slice ks of the requested tile.
+template <int BM, int MODE>
+__device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uint4 *__restrict__ Snext,
+                                          uint4 *__restrict__ Sfill, const GemmProblem &p,
+                                          const Req<BM> &q, int ks, Frags<BM> &f,
+                                          f32x16 (&acc)[Geo<BM>::TM][Geo<BM>::TN],
+                                          const int (&a_slot)[2], const int (&b_slot)[2],
+                                          const int *b_toff) {
+    using G = Geo<BM>;
+    fence();
+    // sub-step 0: MFMAs on slot 0, fragments of sub-step 1 into slot 1
+#pragma unroll
+    for (int n = 0; n < G::NQ; ++n) {
+        const int i = n / G::TN, j = n % G::TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[0][j], f.a[0][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int m = n * G::NF / G::NQ; m < (n + 1) * G::NF / G::NQ; ++m)
+            read_frag<BM>(S, f, 1, m, a_slot[1], b_slot[1], b_toff);
+        fence();
+    }
+    // the next stage is complete once every wave's own requests for it are:
+    // only the requests of the stage after it may still be in flight
+    wait_vmcnt<G::PER>();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    // sub-step 1: MFMAs on slot 1, the next step's first fragments into
+    // slot 0, and the refill of the stage read in the previous step
+    constexpr int NM = G::NF + G::PER;
+#pragma unroll
+    for (int n = 0; n < G::NQ; ++n) {
+        const int i = n / G::TN, j = n % G::TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[1][j], f.a[1][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int m = n * NM / G::NQ; m < (n + 1) * NM / G::NQ; ++m) {
+            if (m < G::NF)
+                read_frag<BM>(Snext, f, 0, m, a_slot[0], b_slot[0], b_toff);
+            else
+                request<BM, MODE>(Sfill, p, q, ks, m - G::NF);
+        }
+        fence();
+    }
+}
+
+// Prologue: the first kAhead slices of the first tile, then (after the
+// first stage is in) its first fragments.
+template <int BM, int MODE>
+__device__ __forceinline__ void prime(uint4 *__restrict__ s0, uint4 *__restrict__ s1,
+                                      uint4 *__restrict__ s2, const GemmProblem &p, const Req<BM> &q) {
+    using G = Geo<BM>;
+#pragma unroll
+    for (int m = 0; m < G::PER; ++m)
+        request<BM, MODE>(s0, p, q, 0, m);
+#pragma unroll
+    for (int m = 0; m < G::PER; ++m)
+        request<BM, MODE>(s1, p, q, 1, m);
+#pragma unroll
+    for (int m = 0; m < G::PER; ++m)
+        request<BM, MODE>(s2, p, q, 2, m);
+}
+
+template <int BM, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_tiles) {
+    using G = Geo<BM>;
+    constexpr int TM = G::TM, TN = G::TN;
+    __shared__ uint4 ring[kStages * G::STAGE];
+    __shared__ int s_pre[kMaxE + 1];
+    __shared__ int s_off[kMaxE + 1];
+    __shared__ int s_wsum[4];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    // ---- tiles per segment and their prefix
+    const int nseg = p.offsets ? p.E : 1;
+    int tiles = 0;
+    if (tid < nseg) {
+        const int lo = p.offsets ? p.offsets[tid] : 0;
+        const int hi = p.offsets ? p.offsets[tid + 1] : p.rows;
+        s_off[tid] = lo;
+        if (tid == nseg - 1)
+            s_off[nseg] = hi;
+        tiles = (hi - lo + BM - 1) / BM;
+    }
+    int incl = tiles;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(incl, d, kWave);
+        if (lane >= d)
+            incl += o;
+    }
+    if (lane == kWave - 1)
+        s_wsum[wave] = incl;
+    __syncthreads();
+    int total = 0;
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave)
+            incl += s_wsum[w];
+        total += s_wsum[w];
+    }
+    if (tid < nseg)
+        s_pre[tid] = incl - tiles;
+    __syncthreads();
+
+    // ---- this workgroup's tiles: an equal contiguous share per XCD, swept
+    // by that XCD's workgroups in step
+    TileList tl;
+    tl.pre = s_pre;
+    tl.off = s_off;
+    tl.nseg = nseg;
+    tl.n_tiles = n_tiles;
+    tl.work = __builtin_amdgcn_readfirstlane(total) * n_tiles;
+    tl.share = (tl.work + kXcds - 1) / kXcds;
+    tl.xcd = blockIdx.x % kXcds;
+    tl.cslot = blockIdx.x / kXcds;
+    tl.nslots = gridDim.x / kXcds;
+
+    int e, row0, row_end, nt;                // the tile being multiplied
+    if (!place<BM>(tl, 0, e, row0, row_end, nt))
+        return;                              // uniform
+    Req<BM> req;                             // the tile being fetched
+    {
+        int raw[G::AI];
+        gathered_rows<BM>(p, row0, row_end, raw);
+        a_offsets<BM>(p, raw, req.a_off);
+        req.e = e;
+        req.nt = nt;
+    }
+    int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
+    bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
+    int nraw[G::AI];
+    gathered_rows<BM>(p, has_next ? nrow0 : row0, has_next ? nrow_end : row_end, nraw);
+
+    // LDS slots of this lane's fragment pieces for sub-steps 0 and 1; the
+    // tiles of a wave sit 32 rows apart, which keeps the swizzle (+128 slots)
+    const int a_tile_row = wm * (BM / 2);
+    const int b_row0 = MODE == kGateUp ? wn * (kBN / 4) : wn * (kBN / 2);
+    int b_toff[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        if (MODE == kGateUp)
+            b_toff[j] = ((j < TN / 2) ? j * 32 : kBN / 2 + (j - TN / 2) * 32) * 4;
+        else
+            b_toff[j] = j * 32 * 4;
+    }
+    int a_slot[2], b_slot[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const int ch = kk * 2 + (lane >> 5);
+        a_slot[kk] = slot_of(a_tile_row + (lane & 31), ch);
+        b_slot[kk] = BM * 4 + slot_of(b_row0 + (lane & 31), ch);
+    }
+
+    const int KT = p.K / kBK;
+    prime<BM, MODE>(ring, ring + G::STAGE, ring + 2 * G::STAGE, p, req);
+    wait_vmcnt<2 * G::PER>();
+    __builtin_amdgcn_s_barrier();
+    Frags<BM> f;
+#pragma unroll
+    for (int m = 0; m < G::NF; ++m)
+        read_frag<BM>(ring, f, 0, m, a_slot[0], b_slot[0], b_toff);
+
+    // the output as a buffer resource: offsets at or past out_bytes are dropped
+    const uint32_t out_rows = p.offsets ? p.max_rows : p.rows;
+    const uint32_t out_bytes = out_rows * (uint32_t)p.ldc * (MODE == kDown ? 4u : 2u);
+    const __amdgpu_buffer_rsrc_t out_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, (int)out_bytes, kBufferWord3);
+
+    f32x16 acc[TM][TN];
+    int g = 0;                               // steps done by this workgroup
+    for (int ti = 1;; ++ti) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+                acc[i][j] = f32x16{};
+        int orow[TM];                        // output rows of the down projection
+        if (MODE == kDown) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int pos = row0 + a_tile_row + i * 32 + (lane & 31);
+                orow[i] = pos < row_end ? (p.scatter ? p.scatter[pos] : pos) : -1;
+            }
+        }
+        // The last kAhead steps refill with the next tile's first slices;
+        // that tile's A offsets are formed just before (its gathered rows
+        // were requested a tile ago and the waits of the steps so far have
+        // retired those loads). One call site for the step, so all its
+        // requests share one alias scope.
+        for (int kt = 0; kt < KT; ++kt) {
+            uint4 *S = ring + (g & 3) * G::STAGE;
+            uint4 *Sn = ring + ((g + 1) & 3) * G::STAGE;
+            uint4 *Sf = ring + ((g + kAhead) & 3) * G::STAGE;
+            ring_step<BM, MODE>(S, Sn, Sf, p, req, kt + kAhead < KT ? kt + kAhead : kt + kAhead - KT,
+                                f, acc, a_slot, b_slot, b_toff);
+            ++g;
+            if (kt == KT - kAhead - 1) {
+                // a tile past the end re-requests this one (in bounds, never
+                // multiplied)
+                if (has_next) {
+                    // here and not hoisted to the tile start, where the
+                    // gathered rows may not have arrived yet
+#pragma unroll
+                    for (int i = 0; i < G::AI; ++i)
+                        __asm__ volatile("" : "+v"(nraw[i]));
+                    a_offsets<BM>(p, nraw, req.a_off);
+                    req.e = ne;
+                    req.nt = nnt;
+                }
+            }
+        }
+
+        // ---- epilogue. acc[i][j][r]: token (lane % 32) of token tile i,
+        // weight row 8*(r/4) + 4*(lane/32) + r%4 of weight tile j. One
+        // 32x32 tile at a time, with buffer stores whose offset is pushed
+        // past the end of the output for rows past the segment (and columns
+        // past N), which the hardware drops: no branches, so the fences keep
+        // the accumulator reads next to their use.
+        const int nsub = 4 * (lane >> 5);
+        if (MODE == kDown) {
+            const int n0 = nt * kBN + wn * (kBN / 2) + nsub;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const bool col_ok = n0 - nsub + j * 32 < p.N;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const f32x16 &v = acc[i][j];
+                    const uint32_t off = (orow[i] >= 0 && col_ok)
+                                             ? ((uint32_t)orow[i] * (uint32_t)p.ldc + n0 + j * 32) * 4u
+                                             : out_bytes;
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const f32x4 q4 = {v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]};
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, q4), out_rsrc,
+                                                               off + gq * 32, 0, 0);
+                    }
+                    fence();
+                }
+            }
+        } else {
+            // With 256 token rows a lane holds 256 accumulators and has no
+            // VGPRs left to take them all at once, which is what the register
+            // allocator does at the loop exit; the tiles go through LDS one
+            // at a time instead. The stage multiplied last is not refilled
+            // before the next tile's first barrier.
+            constexpr bool kViaLds = BM == 256;
+            lds_u32x4 *park = (lds_u32x4 *)(ring + ((g + kAhead) & 3) * G::STAGE) + wave * 8 * kWave;
+            if (kViaLds)
+                __syncthreads();             // every wave is past its reads of that stage
+            constexpr int JO = MODE == kGateUp ? TN / 2 : TN;     // output column tiles
+            const int ncols = MODE == kGateUp ? p.I : p.N;
+            const int n0 = nt * (MODE == kGateUp ? kBN / 2 : kBN) +
+                           wn * (MODE == kGateUp ? kBN / 4 : kBN / 2) + nsub;
+#pragma unroll
+            for (int j = 0; j < JO; ++j) {
+                const bool col_ok = n0 - nsub + j * 32 < ncols;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    const int pos = row0 + a_tile_row + i * 32 + (lane & 31);
+                    f32x16 gv, uv;
+                    if (kViaLds) {
+                        // through this wave's slice of the stage multiplied
+                        // last, 16 bytes per lane per piece (lane-major)
+                        constexpr int JU = MODE == kGateUp ? TN / 2 : 0;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            park[q * kWave + lane] = __builtin_bit_cast(
+                                u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                             acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
+                            if (MODE == kGateUp)
+                                park[(4 + q) * kWave + lane] = __builtin_bit_cast(
+                                    u32x4, f32x4{acc[i][j + JU][4 * q], acc[i][j + JU][4 * q + 1],
+                                                 acc[i][j + JU][4 * q + 2], acc[i][j + JU][4 * q + 3]});
+                        }
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const f32x4 a4 = __builtin_bit_cast(f32x4, (u32x4)park[q * kWave + lane]);
+                            f32x4 b4 = a4;
+                            if (MODE == kGateUp)
+                                b4 = __builtin_bit_cast(f32x4, (u32x4)park[(4 + q) * kWave + lane]);
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                gv[4 * q + c] = a4[c];
+                                uv[4 * q + c] = b4[c];
+                            }
+                        }
+                    } else {
+                        gv = acc[i][j];
+                        uv = acc[i][MODE == kGateUp ? j + TN / 2 : j];
+                        __asm__ volatile("" : "+v"(gv), "+v"(uv));
+                    }
+                    const uint32_t off = (pos < row_end && col_ok)
+                                             ? ((uint32_t)pos * (uint32_t)p.ldc + n0 + j * 32) * 2u
+                                             : out_bytes;
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        float v[4];
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            v[c] = MODE == kGateUp ? silu_mul(gv[4 * gq + c], uv[4 * gq + c])
+                                                   : relu_sq(gv[4 * gq + c]);
+                        const u32x2 q2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+                        __builtin_amdgcn_raw_buffer_store_b64(q2, out_rsrc, off + gq * 16, 0, 0);
+                    }
+                    fence();
+                }
+            }
+        }
+
+        if (!has_next)
+            break;
+        e = ne;
+        row0 = nrow0;
+        row_end = nrow_end;
+        nt = nnt;
+        has_next = place<BM>(tl, ti + 1, ne, nrow0, nrow_end, nnt);
+        gathered_rows<BM>(p, has_next ? nrow0 : row0, has_next ? nrow_end : row_end, nraw);
+    }
+    // the requests of the last kAhead stages target LDS this workgroup is
+    // about to release
+    wait_vmcnt<0>();
+}
+
+int cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int BM, int MODE>
+hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
+    int mt_max;
+    if (p.offsets == nullptr) {
+        mt_max = (p.rows + BM - 1) / BM;
+    } else {
+        const int nonempty = p.E < p.max_rows ? p.E : p.max_rows;
+        mt_max = (p.max_rows + BM - 1) / BM + nonempty;
+    }
+    const int n_cols = MODE == kGateUp ? p.I : p.N;
+    const int n_tile = MODE == kGateUp ? kBN / 2 : kBN;
+    const int n_tiles = (n_cols + n_tile - 1) / n_tile;
+    const long long work = (long long)mt_max * n_tiles;
+    if (work == 0)
+        return hipSuccess;
+    // one workgroup per CU, a whole number of XCD rounds, no more than the
+    // worst-case tile count needs
+    int blocks = cu_count() / kXcds * kXcds;
+    if (blocks < kXcds)
+        blocks = kXcds;
+    const long long need = (work + kXcds - 1) / kXcds * kXcds;
+    if (need < blocks)
+        blocks = (int)need;
+    hipLaunchKernelGGL((k_grouped<BM, MODE>), dim3(blocks), dim3(kThreads), 0, stream, p, n_tiles);
+    return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
+    int segs = 1;
+    if (p.offsets != nullptr)
+        segs = p.E < p.max_rows ? p.E : p.max_rows;
+    const int rows = p.offsets != nullptr ? p.max_rows : p.rows;
+    const int avg = segs > 0 ? rows / segs : 0;
+    if (avg >= 192)
+        return launch_bm<256, MODE>(p, stream);
+    return launch_bm<128, MODE>(p, stream);
+}
+
+}  // namespace
+
+bool grouped_supported(const GemmProblem &p) {
+    return !p.affine4 && p.K % kBK == 0 && p.K / kBK >= kAhead + 1 &&
+           (p.offsets == nullptr || p.E <= kMaxE);
+}
+
+hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream) {
+    switch (p.mode) {
+    case kGateUp: return launch_mode<kGateUp>(p, stream);
+    case kUpRelu2: return launch_mode<kUpRelu2>(p, stream);
+    default: return launch_mode<kDown>(p, stream);
+    }
+}
+
+}  // namespace moe

@@ -60,6 +60,11 @@ struct GemmProblem {
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
 
+// The persistent direct-to-LDS kernel (bf16 weights, K a multiple of 32 and
+// at least 128); launch_gemm routes the problems it supports there.
+bool grouped_supported(const GemmProblem &p);
+hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream);
+
 // The same problem in the weight-streaming (decode) form: few A rows per
 // expert, every touched weight row read once, v_dot2 accumulation.
 bool stream_supported(const GemmProblem &p);
