@@ -21,7 +21,6 @@ Besides the whole-block throughput the line carries:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -62,23 +61,43 @@ def expert_bytes(wl):
     return up, down
 
 
-def source_digest(*names):
-    h = hashlib.sha256()
-    for n in names:
-        h.update(open(os.path.join(ROOT, "sigmoid_top_routing_amd", "csrc", n), "rb").read())
-    return h.hexdigest()[:16]
-
-
-def load_traffic(kernel, workload):
+def load_traffic(tag, workload, sources):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the kernel source as it is now; else None."""
+    taken on the kernel sources as they are now; else None."""
+    from sigmoid_top_routing_amd import profiling
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(f"{kernel}@{workload}")
-    if not rec or rec.get("source_digest") != source_digest("gemm.hip", "device.hpp"):
+    rec = json.load(open(path)).get(f"{tag}@{workload}")
+    if not rec or rec.get("source_digest") != profiling.source_digest(*sources):
         return None
     return rec.get("bytes_per_launch")
+
+
+# the sources of the kernel the roofline is taken on (bf16 expert GEMMs)
+GEMM_SOURCES = ("grouped_gemm.hip", "device.hpp", "kernels.hpp")
+COPY_BYTES = 256 << 20
+
+
+def profile_run(args):
+    """Untimed calls for a profiler to wrap: `steps` forward calls of the
+    workload, then one device-to-device copy of COPY_BYTES bytes that scales
+    the HBM byte counters."""
+    import torch
+    from sigmoid_top_routing_amd import lib
+    from sigmoid_top_routing_amd import workloads as W
+    wl = W.by_name(args.workload)
+    inp = W.generate(wl)
+    block = lib.block_from_arrays(wl, inp)
+    x = lib.x_to_device(inp["x"])
+    out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
+    for _ in range(args.steps):
+        block.forward(x, out=out)
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profile run: {args.steps} calls of {wl.name}, copy of {COPY_BYTES} bytes", flush=True)
 
 
 def cpu_baseline(wl, inp, budget_s=15.0):
@@ -108,11 +127,16 @@ def main():
     ap.add_argument("--workload", default="lfm2_prefill_t4096")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile-run", action="store_true",
+                    help="untimed calls plus a calibration copy, for rocprofv3 to wrap")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(--gpus {args.gpus} asked for)", file=sys.stderr)
         sys.exit(2)
+    if args.profile_run:
+        profile_run(args)
+        return
 
     import torch
     from sigmoid_top_routing_amd import lib
@@ -162,7 +186,7 @@ def main():
         achieved = up_f / (stages["up"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "routed up-projection GEMM", "achieved": achieved,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
-    roof["traffic"] = load_traffic("gemm_up", wl.name)
+    roof["traffic"] = load_traffic("gemm_up", wl.name, GEMM_SOURCES)
     roof["avg_launch_us"] = 1e3 * stages["up"]
 
     result = {

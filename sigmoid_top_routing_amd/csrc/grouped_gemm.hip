@@ -12,12 +12,12 @@
 //   multiplying, and its output stores drain while the next one runs.
 //
 // * Tile order. Workgroups reach the 8 XCDs round robin (XCD = block % 8).
-//   The real tiles (sum over experts of ceil(rows_e / BM), times the n-tiles)
-//   are numbered m-major, n-minor, and each XCD takes an equal contiguous
-//   share; its 32 CUs sweep that share together, so the tiles resident on an
-//   XCD at one time are the n-tiles of one or two m-tiles, which read the
-//   same token rows and (an expert's m-tiles being adjacent) the same weight
-//   rows from that XCD's L2.
+//   The real tiles are numbered expert by expert, and within an expert
+//   n-tile major, m-tile minor; each XCD takes an equal contiguous share and
+//   its 32 CUs sweep that share together. The tiles resident on an XCD at
+//   one time are then all m-tiles of a run of n-tiles of one or two experts:
+//   the m-tiles of a weight tile read it from HBM once and share it in that
+//   XCD's L2, and the token rows of an m-tile are shared by its n-tiles.
 //
 // * Operands go from global memory straight into LDS (global_load_lds, 16
 //   bytes per lane) through a ring of 4 stages of K = 32, requested 3 stages
@@ -116,21 +116,27 @@ __device__ __forceinline__ bool place(const TileList &tl, int i, int &e, int &ro
     const int L = tl.xcd * tl.share + local;
     if (local >= tl.share || L >= tl.work)
         return false;
-    const int mt = L / tl.n_tiles;
-    // the segment holding m-tile mt: the last e with pre[e] <= mt (empty
-    // segments share their prefix with the next one and are skipped)
+    // segment e owns tiles pre[e] * n_tiles .. pre[e + 1] * n_tiles - 1: the
+    // last e with pre[e] <= L / n_tiles (empty segments share their prefix
+    // with the next one and are skipped)
+    const int mq = L / tl.n_tiles;
     int lo = 0, hi = tl.nseg - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (tl.pre[mid] <= mt)
+        if (tl.pre[mid] <= mq)
             lo = mid;
         else
             hi = mid - 1;
     }
+    // within the segment n-major, m-minor: the m-tiles that share a weight
+    // tile are neighbours in the list, so they run at the same time on one
+    // XCD and the weight rows are read from HBM once
+    const int me = tl.pre[lo + 1] - tl.pre[lo];
+    const int local_t = L - tl.pre[lo] * tl.n_tiles;
     e = __builtin_amdgcn_readfirstlane(lo);
-    row0 = __builtin_amdgcn_readfirstlane(tl.off[lo] + (mt - tl.pre[lo]) * BM);
+    row0 = __builtin_amdgcn_readfirstlane(tl.off[lo] + (local_t % me) * BM);
     row_end = __builtin_amdgcn_readfirstlane(tl.off[lo + 1]);
-    nt = __builtin_amdgcn_readfirstlane(L % tl.n_tiles);
+    nt = __builtin_amdgcn_readfirstlane(local_t / me);
     return true;
 }
 
@@ -329,6 +335,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     }
     if (tid < nseg)
         s_pre[tid] = incl - tiles;
+    if (tid == 0)
+        s_pre[nseg] = total;
     __syncthreads();
 
     // ---- this workgroup's tiles: an equal contiguous share per XCD, swept
