@@ -231,13 +231,25 @@ def bench_decode(block, W, lib, torch, steps=20):
     flush = torch.ones(64 << 20, dtype=torch.int64, device="cuda")
     for _ in range(3):
         block.forward(x, out=out, ids_out=ids)
-    times, ups = [], []
+    # the step alone: one event pair around a plain call (each event recorded
+    # inside the step would add a few microseconds of queue time)
+    times = []
+    for _ in range(steps):
+        flush.sum()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        block.forward(x, out=out, ids_out=ids)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    # the stage breakdown, from calls with the stage events inside
+    ups = []
     for _ in range(steps):
         flush.sum()
         ev = lib.StageEvents()
         block.forward(x, out=out, ids_out=ids, events=ev)
         torch.cuda.synchronize()
-        times.append(ev.total_ms())
         ups.append(ev.stage_ms())
     D = int(np.unique(ids.cpu().numpy()).size)
     eb_up, eb_down = expert_bytes(wl)
@@ -246,7 +258,8 @@ def bench_decode(block, W, lib, torch, steps=20):
     return {"workload": wl.name, "T": wl.T, "distinct_experts": D, "us_per_step": 1e3 * t,
             "tokens_per_s": wl.T / (t * 1e-3), "algorithmic_bytes": algo,
             "GBps": algo / (t * 1e-3) / 1e9, "frac_hbm": algo / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "stages_us": {k: 1e3 * float(np.median([u[k] for u in ups])) for k in lib.STAGES}}
+            "stages_us_with_events": {k: 1e3 * float(np.median([u[k] for u in ups]))
+                                      for k in lib.STAGES}}
 
 
 if __name__ == "__main__":

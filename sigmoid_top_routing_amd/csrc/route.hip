@@ -10,17 +10,10 @@
 //
 // Two launches.
 //
-// k_logits is a small fp32 GEMM, z = x Wr^T, over (token tile x expert
-// tile) workgroups spread across the chip: one CU streams only a few tens of
-// GB/s, so no workgroup may reload the whole router weight for a handful of
-// tokens. A thread owns RT tokens x RE experts (independent fma chains that
-// hide the fma latency); its experts are e0 + et + r*ET so that neighbouring
-// lanes read neighbouring LDS rows. H is walked in chunks: Wr ([expert][h])
-// and x (fp32, [token][h]) for a chunk are staged in LDS with 16-byte row
-// padding, double buffered, and the next chunk's coalesced global loads are
-// issued before the current chunk's fmas. Per four h a thread reads one
-// float4 per token and per expert and issues 4*RT*RE fmas; every chain runs
-// in sequential h order, so z is bit-identical to a plain loop.
+// k_logits computes z = x Wr^T as T*E independent fma chains of length H,
+// each in h order (see the kernel for the layout). The chains are what
+// bound it: at the prefill shapes they fill the chip's fp32 lanes, at a
+// decode step they are latency-bound.
 //
 // k_topk reads z, applies the sigmoid and the bias, and picks the top k of
 // each token with k rounds of a 64-bit (order key, ~index) max over the
@@ -36,143 +29,154 @@ namespace moe {
 namespace {
 
 constexpr int kMaxThreads = 256;
-constexpr int kMaxW = 12;      // float4 router-weight prefetch slots per thread
-constexpr int kMaxX = 8;       // uint4 (8 x bf16) x prefetch slots per thread
-constexpr int kLdsBudget = 100 * 1024;
-constexpr int kRing = 8;       // groups of four h read from LDS ahead of their fmas
 
-template <int RT, int RE>
+// k_logits: one lane per token, C experts per wave (C chains per lane).
+// A workgroup of 4 waves owns 64 tokens and 4*C experts and walks H in
+// chunks of kHC. Per chunk it stages the 64 token rows, converted once to
+// fp32 for the four waves that share them (a lane reads 4 of its own h per
+// 16-byte LDS read; rows are padded by 16 bytes so the 16 lanes of a pass
+// hit distinct banks), and the experts' router rows (every lane of a wave
+// reads the same address: one broadcast per 4 h and expert). The next
+// chunk's global loads are issued before the current chunk's fmas and
+// written to the other LDS buffer after them; within a chunk the LDS reads
+// of the next 16 h are issued before the fmas of the current 16. Every
+// chain runs in h order, so z is bit-identical to a plain loop over h.
+constexpr int kTok = 64;                 // tokens per workgroup (one per lane)
+constexpr int kHC = 256;                 // h per LDS chunk
+constexpr int kXRow = kHC / 4 + 1;       // float4 per staged token row (+ pad)
+constexpr int kWRow = kHC / 4 + 1;       // float4 per staged router row (+ pad)
+constexpr int kXLoads = kTok * (kHC / 8) / kMaxThreads;   // uint4 x loads per thread
+
+template <int C>
 __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restrict__ x,
                                                         const float *__restrict__ Wr, int T,
-                                                        int H, int E, int TT, int ET, int HC,
-                                                        float *__restrict__ z) {
-    extern __shared__ float lds[];
-    const int nthr = kMaxThreads;            // every thread stages, TT * ET compute
-    const int TB = TT * RT;                  // tokens per tile
-    const int EB = ET * RE;                  // experts per tile
-    const int HP = HC + 4;                   // padded LDS row
-    float *const wbuf = lds;                 // [2][EB][HP]
-    float *const xbuf = lds + 2 * EB * HP;   // [2][TB][HP]
+                                                        int H, int E, float *__restrict__ z) {
+    constexpr int EB = 4 * C;                                  // experts per workgroup
+    constexpr int WLOADS = (EB * (kHC / 4) + kMaxThreads - 1) / kMaxThreads;
+    __shared__ float4 xs[2][kTok * kXRow];
+    __shared__ float4 ws[2][EB * kWRow];
 
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.x * TB;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int t0 = blockIdx.x * kTok;
     const int e0 = blockIdx.y * EB;
-    const int tt = tid / ET;
-    const int et = tid % ET;
 
-    float4 wreg[kMaxW];
-    uint4 xreg[kMaxX];
+    uint4 xreg[kXLoads];
+    float4 wreg[WLOADS];
+    // chunk h0 .. h0 + hc - 1 (hc a multiple of 64) into registers
     auto load = [&](int h0, int hc) {
-        const int qw = hc / 4, qx = hc / 8;
-        const int nw = EB * qw, nx = TB * qx;
+        const int q = hc / 8;                                  // uint4 per token row
 #pragma unroll
-        for (int i = 0; i < kMaxW; ++i) {
-            const int idx = tid + i * nthr;
-            if (idx < nw) {
-                const int e = e0 + idx / qw, q = idx % qw;
-                wreg[i] = e < E ? *reinterpret_cast<const float4 *>(Wr + (size_t)e * H + h0 + 4 * q)
-                                : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
+        for (int i = 0; i < kXLoads; ++i) {
+            const int idx = tid + i * kMaxThreads;
+            const int r = idx / (kHC / 8), c = idx % (kHC / 8);
+            const int t = t0 + r;
+            xreg[i] = (t < T && c < q) ? *reinterpret_cast<const uint4 *>(x + (size_t)t * H + h0 + 8 * c)
+                                       : make_uint4(0, 0, 0, 0);
         }
+        const int qw = hc / 4;
 #pragma unroll
-        for (int i = 0; i < kMaxX; ++i) {
-            const int idx = tid + i * nthr;
-            if (idx < nx) {
-                const int t = t0 + idx / qx, q = idx % qx;
-                xreg[i] = t < T ? *reinterpret_cast<const uint4 *>(x + (size_t)t * H + h0 + 8 * q)
-                                : make_uint4(0, 0, 0, 0);
-            }
+        for (int i = 0; i < WLOADS; ++i) {
+            const int idx = tid + i * kMaxThreads;
+            const int r = idx / (kHC / 4), c = idx % (kHC / 4);
+            const int e = e0 + r;
+            wreg[i] = (r < EB && e < E && c < qw)
+                          ? *reinterpret_cast<const float4 *>(Wr + (size_t)e * H + h0 + 4 * c)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
-    auto store = [&](int buf, int hc) {
-        float *ws = wbuf + buf * EB * HP;
-        float *xs = xbuf + buf * TB * HP;
-        const int qw = hc / 4, qx = hc / 8;
-        const int nw = EB * qw, nx = TB * qx;
+    auto store = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < kMaxW; ++i) {
-            const int idx = tid + i * nthr;
-            if (idx < nw)
-                *reinterpret_cast<float4 *>(ws + (idx / qw) * HP + 4 * (idx % qw)) = wreg[i];
+        for (int i = 0; i < kXLoads; ++i) {
+            const int idx = tid + i * kMaxThreads;
+            float4 *row = xs[buf] + (idx / (kHC / 8)) * kXRow + 2 * (idx % (kHC / 8));
+            const uint4 v = xreg[i];
+            row[0] = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
+                                 bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16));
+            row[1] = make_float4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16),
+                                 bf16_to_f32(v.w & 0xffffu), bf16_to_f32(v.w >> 16));
         }
 #pragma unroll
-        for (int i = 0; i < kMaxX; ++i) {
-            const int idx = tid + i * nthr;
-            if (idx < nx) {
-                float *row = xs + (idx / qx) * HP + 8 * (idx % qx);
-                const uint4 v = xreg[i];
-                *reinterpret_cast<float4 *>(row) =
-                    make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
-                                bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16));
-                *reinterpret_cast<float4 *>(row + 4) =
-                    make_float4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16),
-                                bf16_to_f32(v.w & 0xffffu), bf16_to_f32(v.w >> 16));
-            }
+        for (int i = 0; i < WLOADS; ++i) {
+            const int idx = tid + i * kMaxThreads;
+            if (idx / (kHC / 4) < EB)
+                ws[buf][(idx / (kHC / 4)) * kWRow + idx % (kHC / 4)] = wreg[i];
         }
     };
 
-    float acc[RT][RE];
+    float acc[C];
 #pragma unroll
-    for (int i = 0; i < RT; ++i)
+    for (int c = 0; c < C; ++c)
+        acc[c] = 0.0f;
+    // 16 h: x[i] holds h 4i..4i+3 of this lane's token, w[c][i] the same h
+    // of expert c
+    // (the chains alternate instruction by instruction: in-order issue then
+    // never waits on the previous fma of the same chain)
+    auto fma16 = [&](const float4 (&xv)[4], const float4 (&wv)[C][4]) {
 #pragma unroll
-        for (int r = 0; r < RE; ++r)
-            acc[i][r] = 0.0f;
-    const bool computes = tid < TT * ET;
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                acc[c] = __builtin_fmaf(xv[i].x, wv[c][i].x, acc[c]);
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                acc[c] = __builtin_fmaf(xv[i].y, wv[c][i].y, acc[c]);
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                acc[c] = __builtin_fmaf(xv[i].z, wv[c][i].z, acc[c]);
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                acc[c] = __builtin_fmaf(xv[i].w, wv[c][i].w, acc[c]);
+        }
+    };
 
-    int hc = H < HC ? H : HC;
+    int hc = H < kHC ? H : kHC;
     load(0, hc);
     int buf = 0;
-    for (int h0 = 0; h0 < H; h0 += HC) {
-        store(buf, hc);
+    for (int h0 = 0; h0 < H; h0 += kHC) {
+        store(buf);
         __syncthreads();
-        const int hn = h0 + HC;
-        const int hc_next = H - hn < HC ? H - hn : HC;
+        const int hn = h0 + kHC;
+        const int hc_next = H - hn < kHC ? H - hn : kHC;
         if (hn < H)
             load(hn, hc_next);
-        if (computes) {
-            const float *xs = xbuf + buf * TB * HP + (tt * RT) * HP;
-            const float *ws = wbuf + buf * EB * HP + et * HP;
-            // blocks of 4 * kRing h: every LDS read of a block is issued
-            // first, then its fmas (chains in h order), so the read latency
-            // is paid once per block and overlaps the first fmas
-            for (int hh0 = 0; hh0 < hc; hh0 += 4 * kRing) {
-                float4 xv[kRing][RT], wv[kRing][RE];
+        const float4 *xr = xs[buf] + lane * kXRow;
+        const float4 *wr = ws[buf] + (wave * C) * kWRow;
+        float4 xa[4], xb[4];
+        float4 wa[C][4], wb[C][4];
+        auto read16 = [&](int g, float4 (&xv)[4], float4 (&wv)[C][4]) {
 #pragma unroll
-                for (int d = 0; d < kRing; ++d) {
+            for (int i = 0; i < 4; ++i)
+                xv[i] = xr[4 * g + i];
 #pragma unroll
-                    for (int i = 0; i < RT; ++i)
-                        xv[d][i] = *reinterpret_cast<const float4 *>(xs + i * HP + hh0 + 4 * d);
+            for (int c = 0; c < C; ++c)
 #pragma unroll
-                    for (int r = 0; r < RE; ++r)
-                        wv[d][r] = *reinterpret_cast<const float4 *>(ws + r * ET * HP + hh0 + 4 * d);
-                }
-#pragma unroll
-                for (int d = 0; d < kRing; ++d)
-#pragma unroll
-                    for (int i = 0; i < RT; ++i)
-#pragma unroll
-                        for (int r = 0; r < RE; ++r) {
-                            float a = acc[i][r];
-                            a = __builtin_fmaf(xv[d][i].x, wv[d][r].x, a);
-                            a = __builtin_fmaf(xv[d][i].y, wv[d][r].y, a);
-                            a = __builtin_fmaf(xv[d][i].z, wv[d][r].z, a);
-                            a = __builtin_fmaf(xv[d][i].w, wv[d][r].w, a);
-                            acc[i][r] = a;
-                        }
-            }
+                for (int i = 0; i < 4; ++i)
+                    wv[c][i] = wr[c * kWRow + 4 * g + i];
+        };
+        const int groups = hc / 16;          // hc is a multiple of 64: even
+        read16(0, xa, wa);
+        for (int g = 0; g < groups; g += 2) {
+            read16(g + 1, xb, wb);
+            __builtin_amdgcn_sched_barrier(0);
+            fma16(xa, wa);
+            __builtin_amdgcn_sched_barrier(0);
+            read16(g + 2 < groups ? g + 2 : g + 1, xa, wa);   // no branch: no copies
+            __builtin_amdgcn_sched_barrier(0);
+            fma16(xb, wb);
+            __builtin_amdgcn_sched_barrier(0);
         }
         hc = hc_next;
         buf ^= 1;
+        __syncthreads();                    // the buffer refilled next is no longer read
     }
+    const int t = t0 + lane;
 #pragma unroll
-    for (int i = 0; i < RT; ++i) {
-        const int t = t0 + tt * RT + i;
-#pragma unroll
-        for (int r = 0; r < RE; ++r) {
-            const int e = e0 + et + r * ET;
-            if (computes && t < T && e < E)
-                z[(size_t)t * E + e] = acc[i][r];
-        }
+    for (int c = 0; c < C; ++c) {
+        const int e = e0 + wave * C + c;
+        if (t < T && e < E)
+            z[(size_t)t * E + e] = acc[c];
     }
 }
 
@@ -285,62 +289,13 @@ __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ 
     }
 }
 
-template <int RT, int RE>
-void launch_logits(dim3 grid, size_t lds, hipStream_t stream, const uint16_t *x,
-                   const float *Wr, int T, int H, int E, int TT, int ET, int HC, float *z) {
-    static const bool opt_in = [] {
-        (void)hipFuncSetAttribute((const void *)k_logits<RT, RE>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBudget);
-        return true;
-    }();
-    (void)opt_in;
-    hipLaunchKernelGGL((k_logits<RT, RE>), grid, dim3(kMaxThreads), lds, stream, x, Wr, T, H, E,
-                       TT, ET, HC, z);
-}
-
-struct LogitsTiling {
-    int RT, RE, TT, ET, HC;
-    size_t lds;
-    dim3 grid;
-};
-
-// Tile choice. Few tokens: four experts per workgroup and one chain per
-// lane, so the (sequential) chains run side by side on E/4 CUs, each of
-// which stages a whole row range at once. Many tokens: 32 experts per tile
-// and as many tokens as keep about one workgroup per CU, with 2 to 4 chains
-// per lane.
-LogitsTiling choose_tiling(int T, int H, int E) {
-    LogitsTiling c{};
-    const int cus = 256;
-    if (T <= 64) {
-        c.RT = 1;
-        c.RE = 1;
-        c.ET = 4;
-        c.TT = 64;
-        while (c.TT / 2 >= T && c.TT > 1)
-            c.TT /= 2;
-    } else {
-        c.ET = E >= 32 ? 32 : (E >= 16 ? 16 : 8);
-        c.RE = 1;
-        const int etiles = (E + c.ET - 1) / c.ET;
-        const int TT = 256 / c.ET;
-        // tokens per tile so that tiles ~ CUs, 1..4 per thread
-        const int want_tb = (int)(((int64_t)T * etiles + cus - 1) / cus);
-        c.RT = want_tb >= 4 * TT ? 4 : want_tb >= 2 * TT ? 2 : 1;
-        c.TT = TT;
-    }
-    const int TB = c.TT * c.RT, EB = c.ET * c.RE;
-    auto fits = [&](int hc) {
-        return (size_t)2 * sizeof(float) * (EB + TB) * (hc + 4) <= (size_t)kLdsBudget &&
-               EB * hc <= kMaxW * 4 * kMaxThreads && TB * hc <= kMaxX * 8 * kMaxThreads;
-    };
-    // the whole of H in one chunk when it fits (one load round trip)
-    c.HC = 4096;
-    while (c.HC > 8 && !fits(c.HC))
-        c.HC >>= 1;
-    c.lds = (size_t)2 * sizeof(float) * (EB + TB) * (c.HC + 4);
-    c.grid = dim3((T + TB - 1) / TB, (E + EB - 1) / EB);
-    return c;
+// Two chains per lane when that still leaves a few hundred workgroups,
+// else one (decode-sized batches are latency-bound: more workgroups).
+template <int C>
+void launch_logits(hipStream_t stream, const uint16_t *x, const float *Wr, int T, int H, int E,
+                   float *z) {
+    const dim3 grid((T + kTok - 1) / kTok, (E + 4 * C - 1) / (4 * C));
+    hipLaunchKernelGGL(k_logits<C>, grid, dim3(kMaxThreads), 0, stream, x, Wr, T, H, E, z);
 }
 
 }  // namespace
@@ -354,25 +309,13 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
         *plan_done = false;
     if (T == 0)
         return hipSuccess;
-    const LogitsTiling c = choose_tiling(T, H, E);
-    // H is a multiple of 64 and a chunk is a power of two >= 64 (or all of
-    // H), so every chunk is a whole number of ring turns (4 * kRing wide)
-    if (c.HC < 4 * kRing || H % 64 != 0 || c.TT * c.ET > kMaxThreads)
+    if (H % 64 != 0)
         return hipErrorInvalidValue;
-    const int key = c.RT * 10 + c.RE;
-    switch (key) {
-    case 11:
-        launch_logits<1, 1>(c.grid, c.lds, stream, x, Wr, T, H, E, c.TT, c.ET, c.HC, z_scratch);
-        break;
-    case 21:
-        launch_logits<2, 1>(c.grid, c.lds, stream, x, Wr, T, H, E, c.TT, c.ET, c.HC, z_scratch);
-        break;
-    case 41:
-        launch_logits<4, 1>(c.grid, c.lds, stream, x, Wr, T, H, E, c.TT, c.ET, c.HC, z_scratch);
-        break;
-    default:
-        return hipErrorInvalidValue;
-    }
+    const int tblocks = (T + kTok - 1) / kTok;
+    if ((int64_t)tblocks * ((E + 7) / 8) >= 128)
+        launch_logits<2>(stream, x, Wr, T, H, E, z_scratch);
+    else
+        launch_logits<1>(stream, x, Wr, T, H, E, z_scratch);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;
