@@ -14,6 +14,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format;
+// offsets are range checked against the record count, stride 0).
+constexpr int kBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

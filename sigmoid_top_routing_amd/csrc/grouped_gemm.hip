@@ -68,10 +68,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
 
-// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format;
-// offsets are range checked against the record count, stride 0).
-constexpr int kBufferWord3 = 0x00020000;
-
 // 16-byte slot of logical chunk c (of 4 per row of 32 bf16) of row r within a
 // stage. A fragment read serves 16 lanes (16 consecutive rows, one chunk) per
 // pass from 64 banks; bits 0-1 of the row pick the 64-byte quarter of the

@@ -13,7 +13,7 @@
 // k_logits computes z = x Wr^T as T*E independent fma chains of length H,
 // each in h order (see the kernel for the layout). The chains are what
 // bound it: at the prefill shapes they fill the chip's fp32 lanes, at a
-// decode step they are latency-bound.
+// decode step they are latency-bound, and k_logits_few takes that case.
 //
 // k_topk reads z, applies the sigmoid and the bias, and picks the top k of
 // each token with k rounds of a 64-bit (order key, ~index) max over the
@@ -180,6 +180,122 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restri
     }
 }
 
+// k_logits_few: decode-sized batches (T <= 8, H <= 2048). The chains are
+// the whole cost there (H dependent fmas each), so the point is to start
+// them early and never stall them: a workgroup owns 8 experts and every
+// token, requests all of its rows at once (four h-quarters, in order), and
+// moves quarter q to LDS (x converted to fp32) as soon as it has landed;
+// lanes 0..15 of each wave then run the chains of 2 experts x 8 tokens over
+// that quarter, reading 16 h ahead. Rows are padded by 16 bytes, so the 8
+// token rows read together sit in distinct banks.
+constexpr int kFewT = 8;
+constexpr int kFewE = 8;
+constexpr int kFewMaxH = 2048;
+constexpr int kFewRow = kFewMaxH / 4 + 1;          // float4 per staged row (+ pad)
+
+__global__ __launch_bounds__(kMaxThreads) void k_logits_few(const uint16_t *__restrict__ x,
+                                                            const float *__restrict__ Wr, int T,
+                                                            int H, int E, float *__restrict__ z) {
+    __shared__ float4 xs[kFewT * kFewRow];
+    __shared__ float4 ws[kFewE * kFewRow];
+    __shared__ float4 junk[2];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int e0 = blockIdx.x * kFewE;
+    const int hq = H / 4;                           // h per quarter, a multiple of 16
+    const int rs = hq + 1;                          // float4 per staged row
+    // loader: 32 threads per row; row r = tid / 32. Buffer loads return
+    // zeros past the end of x or Wr (and for the offset pushed there when a
+    // piece lies outside the quarter), so every load is issued
+    // unconditionally and the quarters can be waited for one at a time.
+    const int lr = tid / 32, lc = tid % 32;
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, T * H * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Wr, (short)0, E * H * 4, kBufferWord3);
+    const uint32_t kPast = 0x80000000u;
+    uint4 xr[4][2];
+    float4 wr[4][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = lc + 32 * i;              // uint4 of the quarter's row
+            const uint32_t off = q < hq / 8 ? (uint32_t)(lr * H + c * hq + 8 * q) * 2u : kPast;
+            xr[c][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = lc + 32 * i;              // float4 of the quarter's row
+            const uint32_t off =
+                q < hq / 4 ? (uint32_t)((e0 + lr) * H + c * hq + 4 * q) * 4u : kPast;
+            wr[c][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0));
+        }
+    }
+    const int t = lane & 7;
+    const int j = wave * 2 + ((lane >> 3) & 1);
+    const float4 *xrow = xs + t * rs;
+    const float4 *wrow = ws + j * rs;
+    float acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        // pieces outside the quarter go to a junk slot: the stores stay
+        // unconditional and the loads are not moved into a branch
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = lc + 32 * i;
+            const uint4 v = xr[c][i];
+            float4 *d = q < hq / 8 ? xs + lr * rs + (c * hq) / 4 + 2 * q : junk;
+            d[0] = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
+                               bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16));
+            d[1] = make_float4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16),
+                               bf16_to_f32(v.w & 0xffffu), bf16_to_f32(v.w >> 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = lc + 32 * i;
+            float4 *d = q < hq / 4 ? ws + lr * rs + (c * hq) / 4 + q : junk;
+            *d = wr[c][i];
+        }
+        __syncthreads();
+        if (lane < 16) {
+            const int b = (c * hq) / 4, n = hq / 4;     // float4 of this quarter
+            float4 xa[4], wa[4], xb[4], wb[4];
+            auto read = [&](int g, float4 (&xv)[4], float4 (&wv)[4]) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xv[i] = xrow[b + 4 * g + i];
+                    wv[i] = wrow[b + 4 * g + i];
+                }
+            };
+            auto fma16 = [&](const float4 (&xv)[4], const float4 (&wv)[4]) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc = __builtin_fmaf(xv[i].x, wv[i].x, acc);
+                    acc = __builtin_fmaf(xv[i].y, wv[i].y, acc);
+                    acc = __builtin_fmaf(xv[i].z, wv[i].z, acc);
+                    acc = __builtin_fmaf(xv[i].w, wv[i].w, acc);
+                }
+            };
+            const int groups = n / 4;                   // even: hq is a multiple of 32
+            read(0, xa, wa);
+            for (int g = 0; g < groups; g += 2) {
+                read(g + 1, xb, wb);
+                __builtin_amdgcn_sched_barrier(0);
+                fma16(xa, wa);
+                __builtin_amdgcn_sched_barrier(0);
+                read(g + 2 < groups ? g + 2 : g + 1, xa, wa);
+                __builtin_amdgcn_sched_barrier(0);
+                fma16(xb, wb);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    if (lane < 16 && t < T && e0 + j < E)
+        z[(size_t)t * E + e0 + j] = acc;
+}
+
 template <int RE>
 __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ z,
                                                       const float *__restrict__ bias, int T,
@@ -187,8 +303,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ 
                                                       float eps, int32_t *__restrict__ ids,
                                                       float *__restrict__ weights, PlanOut plan) {
     __shared__ int s_ids[kFusedPlanMaxA];
+    __shared__ int s_rank[kFusedPlanMaxA];
     __shared__ int s_cnt[256];
     __shared__ int s_off[256];
+    __shared__ int s_wsum[kMaxThreads / kWave];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int per_block = kMaxThreads / LPT;
@@ -257,35 +375,47 @@ __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ 
 
     // One block holds every token: it also builds the plan (histogram,
     // exclusive scan, stable scatter), saving two launches on decode steps.
+    // Assignment a's place within its expert is the number of earlier
+    // assignments to the same expert, which keeps the scatter stable.
     __syncthreads();
     const int A = T * k;
-    if (tid < E) {
-        int c = 0;
-        for (int a = 0; a < A; ++a)
-            c += s_ids[a] == tid;
-        s_cnt[tid] = c;
+    if (tid < E)
+        s_cnt[tid] = 0;
+    __syncthreads();
+    for (int a = tid; a < A; a += kMaxThreads) {
+        const int v = s_ids[a];
+        int r = 0;
+        for (int b = 0; b < a; ++b)
+            r += s_ids[b] == v;
+        s_rank[a] = r;
+        atomicAdd(&s_cnt[v], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int e = 0; e < E; ++e) {
-            s_off[e] = run;
-            plan.counts[e] = s_cnt[e];
-            plan.offsets[e] = run;
-            run += s_cnt[e];
-        }
-        plan.offsets[E] = run;
+    // exclusive scan of the counts: a wave scan per 64 experts
+    int c = tid < E ? s_cnt[tid] : 0;
+    int incl = c;
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int o = __shfl_up(incl, d, kWave);
+        if (lane >= d)
+            incl += o;
+    }
+    if (lane == kWave - 1)
+        s_wsum[tid / kWave] = incl;
+    __syncthreads();
+    for (int w = 0; w < tid / kWave; ++w)
+        incl += s_wsum[w];
+    if (tid < E) {
+        s_off[tid] = incl - c;
+        plan.counts[tid] = c;
+        plan.offsets[tid] = incl - c;
+        if (tid == E - 1)
+            plan.offsets[E] = incl;
     }
     __syncthreads();
-    if (tid < E) {
-        int pos = s_off[tid];
-        for (int a = 0; a < A; ++a) {
-            if (s_ids[a] == tid) {
-                plan.sorted[pos] = a;
-                plan.slot_of[a] = pos;
-                ++pos;
-            }
-        }
+    for (int a = tid; a < A; a += kMaxThreads) {
+        const int pos = s_off[s_ids[a]] + s_rank[a];
+        plan.sorted[pos] = a;
+        plan.slot_of[a] = pos;
     }
 }
 
@@ -312,7 +442,10 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
     if (H % 64 != 0)
         return hipErrorInvalidValue;
     const int tblocks = (T + kTok - 1) / kTok;
-    if ((int64_t)tblocks * ((E + 7) / 8) >= 128)
+    if (T <= kFewT && H <= kFewMaxH && H % 128 == 0)
+        hipLaunchKernelGGL(k_logits_few, dim3((E + kFewE - 1) / kFewE), dim3(kMaxThreads), 0,
+                           stream, x, Wr, T, H, E, z_scratch);
+    else if ((int64_t)tblocks * ((E + 7) / 8) >= 128)
         launch_logits<2>(stream, x, Wr, T, H, E, z_scratch);
     else
         launch_logits<1>(stream, x, Wr, T, H, E, z_scratch);

@@ -5,16 +5,22 @@
 // "Performance": at batch 1 the block is bound by the weight bytes).
 //
 // Same problem as the MFMA GEMM (GemmProblem, same epilogues, same outputs),
-// different shape of work. A workgroup owns one expert and a run of output
-// units (a gate/up row pair for SwiGLU, else one weight row). Each wave
-// first loads its segment's A rows (up to 4 at a time) into registers:
-// lane l holds elements 512 j + 8 l .. + 7 of every row, for every j. Then
-// for each unit it streams the weight row with fully coalesced 16-byte loads
-// (64 lanes cover 1 KB of a row per instruction, two units in flight), and
-// accumulates with v_dot2_f32_bf16 (two bf16 products per instruction, fp32
-// accumulate). The 64 lane-partial sums of all rows are reduced with a
-// transposing butterfly, which needs far fewer shuffles than reducing each
-// value on its own, and one lane per row applies the epilogue.
+// different shape of work, laid out for HBM throughput. A plain read of cold
+// rows reaches about 6 TB/s on this part when each wave reads a few rows and
+// the waves in flight cover one contiguous stretch of memory; it falls
+// towards 4.5 TB/s when each wave walks dozens of rows, and further when the
+// reads in flight are spread over many experts whose weights sit a multiple
+// of 2 MB apart. So a wave here owns a single output unit (a gate/up row
+// pair for SwiGLU, else one weight row), a workgroup owns 8 consecutive
+// units of one expert, and consecutive workgroups take consecutive units of
+// the same expert. Each wave requests its weight rows first, with fully
+// coalesced 16-byte loads (64 lanes cover 1 KB of a row per instruction),
+// while the workgroup stages the segment's token rows, up to 4 at a time,
+// in LDS. Lane l takes elements 512 j + 8 l .. + 7 of every row, for every
+// j, and accumulates with v_dot2_f32_bf16 (two bf16 products per
+// instruction, fp32 accumulate). The 64 lane-partial sums of all rows are
+// reduced with a transposing butterfly, which needs far fewer shuffles than
+// reducing each value on its own, and one lane per row applies the epilogue.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -26,9 +32,14 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
-constexpr int kTG = 4;         // A rows per pass
-constexpr int kUnroll = 2;     // units in flight per wave
+constexpr int kThreads = 512;
+constexpr int kTG = 4;         // token rows per group
+
+// output units per wave: one (many short-lived waves stream fastest)
+template <int NJ>
+constexpr int units_per_wave() { return 1; }
+template <int NJ>
+constexpr int units_per_block() { return kThreads / kWave * units_per_wave<NJ>(); }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -75,87 +86,103 @@ __device__ __forceinline__ void transpose_reduce(float (&v)[V], int lane) {
 }
 
 template <int MODE, int NJ>
-__global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p, int upb) {
-    const int e = p.offsets != nullptr ? (int)blockIdx.x : 0;
+__global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
+    constexpr int NR = MODE == kGateUp ? 2 : 1;   // weight rows per unit
+    constexpr int UW = units_per_wave<NJ>();
+    __shared__ uint4 xs[kTG][NJ * kWave];          // token rows, bf16
+    const int lane = threadIdx.x & (kWave - 1);
+    // blockIdx.y names the expert among those with rows (in expert order),
+    // so the workgroups in flight stream neighbouring rows of one or two
+    // experts and none is spent on an empty one
+    int e = 0;
+    if (p.offsets != nullptr) {
+        e = -1;
+        int want = blockIdx.y;
+        for (int base = 0; base < p.E && e < 0; base += kWave) {
+            const int x = base + lane;
+            const bool busy = x < p.E && p.offsets[x + 1] > p.offsets[x];
+            const uint64_t m = __ballot(busy);
+            const int below = __popcll(m & ((1ull << lane) - 1ull));
+            const uint64_t hit = __ballot(busy && below == want);
+            if (hit != 0)
+                e = base + __ffsll((unsigned long long)hit) - 1;
+            want -= __popcll(m);
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
+        if (e < 0)
+            return;                                // uniform
+    }
     const int seg0 = p.offsets != nullptr ? p.offsets[e] : 0;
     const int seg1 = p.offsets != nullptr ? p.offsets[e + 1] : p.rows;
     if (seg0 >= seg1)
-        return;
+        return;                                    // uniform
     const int units = MODE == kGateUp ? p.I : p.N;
-    const int u0 = blockIdx.y * upb;
-    const int u1 = min(units, u0 + upb);
-    const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int K = p.K;
     const uint16_t *B = (const uint16_t *)p.B + (size_t)e * p.N * K;
-    constexpr int NR = MODE == kGateUp ? 2 : 1;   // weight rows per unit
+    const int ub = blockIdx.x * units_per_block<NJ>() + wave * UW;
 
-    for (int g0 = seg0; g0 < seg1; g0 += kTG) {
-        const int nr = min(kTG, seg1 - g0);
-        uint4 xa[kTG][NJ];
+    // this wave's weight rows, requested before anything else
+    uint4 w[UW][NR][NJ];
 #pragma unroll
-        for (int r = 0; r < kTG; ++r) {
-            const uint16_t *row = nullptr;
-            if (r < nr) {
-                const int pos = g0 + r;
-                const int arow = p.gather ? p.gather[pos] / p.gather_div : pos;
-                row = p.A + (size_t)arow * p.lda;
-            }
+    for (int i = 0; i < UW; ++i) {
+        const int u = ub + i;
+#pragma unroll
+        for (int s = 0; s < NR; ++s) {
+            const uint16_t *wp = B + (size_t)(s == 0 ? u : p.I + u) * K;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int kk = j * 512 + lane * 8;
-                xa[r][j] = (row != nullptr && kk < K) ? *reinterpret_cast<const uint4 *>(row + kk)
-                                                      : make_uint4(0, 0, 0, 0);
+                w[i][s][j] = (u < units && kk < K) ? *reinterpret_cast<const uint4 *>(wp + kk)
+                                                   : make_uint4(0, 0, 0, 0);
             }
         }
+    }
 
-        for (int ub = u0 + wave * kUnroll; ub < u1; ub += 4 * kUnroll) {
-            uint4 w[kUnroll][NR][NJ];
+    for (int g0 = seg0; g0 < seg1; g0 += kTG) {
+        const int nr = min(kTG, seg1 - g0);
+        if (g0 != seg0)
+            __syncthreads();                       // the previous group is read
+        for (int idx = threadIdx.x; idx < kTG * NJ * kWave; idx += kThreads) {
+            const int r = idx / (NJ * kWave), c = idx % (NJ * kWave);
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (r < nr && c * 8 < K) {
+                const int pos = g0 + r;
+                const int arow = p.gather ? p.gather[pos] / p.gather_div : pos;
+                v = *reinterpret_cast<const uint4 *>(p.A + (size_t)arow * p.lda + c * 8);
+            }
+            xs[r][c] = v;
+        }
+        __syncthreads();
 #pragma unroll
-            for (int q = 0; q < kUnroll; ++q) {
-                const int u = ub + q;
+        for (int i = 0; i < UW; ++i) {
+            const int u = ub + i;
+            // values ordered (row r, weight row s): index r * NR + s
+            float v[kTG * NR];
+#pragma unroll
+            for (int r = 0; r < kTG; ++r)
 #pragma unroll
                 for (int s = 0; s < NR; ++s) {
-                    const int wrow = s == 0 ? u : p.I + u;
-                    const uint16_t *wp = B + (size_t)wrow * K;
+                    float acc = 0.0f;
 #pragma unroll
-                    for (int j = 0; j < NJ; ++j) {
-                        const int kk = j * 512 + lane * 8;
-                        w[q][s][j] = (u < u1 && kk < K) ? *reinterpret_cast<const uint4 *>(wp + kk)
-                                                        : make_uint4(0, 0, 0, 0);
-                    }
+                    for (int j = 0; j < NJ; ++j)
+                        acc = dot8(w[i][s][j], xs[r][j * kWave + lane], acc);
+                    v[r * NR + s] = acc;
                 }
-            }
-#pragma unroll
-            for (int q = 0; q < kUnroll; ++q) {
-                const int u = ub + q;
-                // values ordered (row r, weight row s): index r * NR + s
-                float v[kTG * NR];
-#pragma unroll
-                for (int r = 0; r < kTG; ++r)
-#pragma unroll
-                    for (int s = 0; s < NR; ++s) {
-                        float acc = 0.0f;
-#pragma unroll
-                        for (int j = 0; j < NJ; ++j)
-                            acc = dot8(w[q][s][j], xa[r][j], acc);
-                        v[r * NR + s] = acc;
-                    }
-                transpose_reduce<kTG * NR, NR>(v, lane);
-                // lane bits 5, 4 name the row r whose sums this lane now holds
-                const int r = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
-                if ((lane & 15) == 0 && r < nr && u < u1) {
-                    const int pos = g0 + r;
-                    if (MODE == kGateUp) {
-                        ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
-                            (uint16_t)f32_to_bf16(silu_mul(v[0], v[1]));
-                    } else if (MODE == kUpRelu2) {
-                        ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
-                            (uint16_t)f32_to_bf16(relu_sq(v[0]));
-                    } else {
-                        const int orow = p.scatter ? p.scatter[pos] : pos;
-                        ((float *)p.C)[(size_t)orow * p.ldc + u] = v[0];
-                    }
+            transpose_reduce<kTG * NR, NR>(v, lane);
+            // lane bits 5, 4 name the row r whose sums this lane now holds
+            const int r = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+            if ((lane & 15) == 0 && r < nr && u < units) {
+                const int pos = g0 + r;
+                if (MODE == kGateUp) {
+                    ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
+                        (uint16_t)f32_to_bf16(silu_mul(v[0], v[1]));
+                } else if (MODE == kUpRelu2) {
+                    ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
+                        (uint16_t)f32_to_bf16(relu_sq(v[0]));
+                } else {
+                    const int orow = p.scatter ? p.scatter[pos] : pos;
+                    ((float *)p.C)[(size_t)orow * p.ldc + u] = v[0];
                 }
             }
         }
@@ -165,9 +192,9 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p, int upb) {
 template <int MODE, int NJ>
 hipError_t launch_nj(const GemmProblem &p, hipStream_t stream) {
     const int units = MODE == kGateUp ? p.I : p.N;
-    const int upb = 4 * kUnroll * 4;          // 4 waves x 2 units x 4 passes
-    const dim3 grid(p.offsets != nullptr ? p.E : 1, (units + upb - 1) / upb);
-    hipLaunchKernelGGL((k_stream<MODE, NJ>), grid, dim3(kThreads), 0, stream, p, upb);
+    const int upb = units_per_block<NJ>();
+    const dim3 grid((units + upb - 1) / upb, p.offsets != nullptr ? p.E : 1);
+    hipLaunchKernelGGL((k_stream<MODE, NJ>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
