@@ -24,8 +24,9 @@
 //   ahead of the one being multiplied. The request stream runs across tile
 //   boundaries: the last steps of a tile request the first slices of the
 //   next. No VGPRs hold staged data and no LDS writes are issued by the
-//   waves. Rows past a segment or past N are clamped to a valid row; their
-//   results are never stored.
+//   waves. Token rows past a segment (padding of its last tile) are read
+//   as zeros by range-checked loads, which costs no memory traffic; weight
+//   rows past N are clamped to a valid row. Neither result is stored.
 //
 // * The MFMA v_mfma_f32_32x32x16_bf16 is issued with the weight fragment as
 //   its first operand, so the 32x32 accumulator tile is [weight row][token]:
@@ -62,6 +63,7 @@ constexpr int kAhead = 3;        // stages requested ahead of the one multiplied
 constexpr int kBN = 256;         // weight rows per tile
 constexpr int kXcds = 8;
 constexpr int kMaxE = 256;
+constexpr uint32_t kPastA = 0x80000000u;   // an A offset past every A matrix: reads zeros
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -137,25 +139,29 @@ __device__ __forceinline__ bool place(const TileList &tl, int i, int &e, int &ro
 }
 
 // The A row behind each of this thread's A pieces of a tile, as stored in
-// the plan (a slot, divided by gather_div once it has arrived). Rows past
-// the segment repeat its last row.
+// the plan (a slot, divided by gather_div once it has arrived). Returns a
+// mask of the pieces that lie on rows of the segment; the others (rows past
+// its end, which only pad the tile) are read as zeros.
 template <int BM>
-__device__ __forceinline__ void gathered_rows(const GemmProblem &p, int row0, int row_end,
-                                              int (&raw)[Geo<BM>::AI]) {
+__device__ __forceinline__ int gathered_rows(const GemmProblem &p, int row0, int row_end,
+                                             int (&raw)[Geo<BM>::AI]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
+    int valid = 0;
 #pragma unroll
     for (int i = 0; i < Geo<BM>::AI; ++i) {
         int pos = row0 + (((wave * Geo<BM>::AI + i) * kWave + lane) >> 2);
+        valid |= (pos < row_end ? 1 : 0) << i;
         if (pos >= row_end)
             pos = row_end - 1;
         raw[i] = p.gather ? p.gather[pos] : pos;
     }
+    return valid;
 }
 
 template <int BM>
 __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)[Geo<BM>::AI],
-                                          uint32_t (&off)[Geo<BM>::AI]) {
+                                          int valid, uint32_t (&off)[Geo<BM>::AI]) {
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
 #pragma unroll
@@ -163,8 +169,16 @@ __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)
         const int s = (wave * Geo<BM>::AI + i) * kWave + lane;
         const int c = (s & 3) ^ ((s >> 4) & 3);
         const int arow = p.gather ? raw[i] / p.gather_div : raw[i];
-        off[i] = ((uint32_t)arow * (uint32_t)p.lda + c * 8) * 2u;
+        off[i] = (valid >> i) & 1 ? ((uint32_t)arow * (uint32_t)p.lda + c * 8) * 2u : kPastA;
     }
+}
+
+// 16 bytes per lane from `base` + off into LDS at dst + 16 lane, range
+// checked: offsets at or past 2^31 read zeros.
+__device__ __forceinline__ void buffer_to_lds16(const void *base, uint4 *dst, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, 0);
 }
 
 // Request state of the tile whose slices are being fetched.
@@ -183,8 +197,9 @@ __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmPro
     const int wave = threadIdx.x / kWave;
     const uint32_t kb = (uint32_t)ks * (kBK * 2);
     if (m < G::AI) {
-        __builtin_amdgcn_global_load_lds((const void *)((const char *)p.A + q.a_off[m] + kb),
-                                         (lds_void *)(stage + (wave * G::AI + m) * kWave), 16, 0, 0);
+        // a range-checked load: pieces of padding rows (offset kPastA) read
+        // as zeros
+        buffer_to_lds16(p.A, stage + (wave * G::AI + m) * kWave, q.a_off[m] + kb);
     } else {
         const int i = m - G::AI;
         const int s = (wave * G::BI + i) * kWave + lane;
@@ -216,15 +231,21 @@ struct Frags {
     bf16x8 b[2][Geo<BM>::TN];
 };
 
-// Fragment m (A tiles first, then B tiles) from a stage into a slot.
+// Fragment m from a stage into a slot, in the order the MFMAs of a sub-step
+// first use them (they run weight tile j fastest): A tile 0, B tiles 0 ..
+// TN - 1, then A tiles 1 .. TM - 1. The reads of a sub-step are spread over
+// its MFMAs, so the ones needed first by the next sub-step are in flight
+// longest.
 template <int BM>
 __device__ __forceinline__ void read_frag(const uint4 *__restrict__ S, Frags<BM> &f, int slot, int m,
                                           int a_slot, int b_slot, const int *b_toff) {
     using G = Geo<BM>;
-    if (m < G::TM)
-        f.a[slot][m] = __builtin_bit_cast(bf16x8, S[a_slot + m * 128]);
+    if (m == 0)
+        f.a[slot][0] = __builtin_bit_cast(bf16x8, S[a_slot]);
+    else if (m <= G::TN)
+        f.b[slot][m - 1] = __builtin_bit_cast(bf16x8, S[b_slot + b_toff[m - 1]]);
     else
-        f.b[slot][m - G::TM] = __builtin_bit_cast(bf16x8, S[b_slot + b_toff[m - G::TM]]);
+        f.a[slot][m - G::TN] = __builtin_bit_cast(bf16x8, S[a_slot + (m - G::TN) * 128]);
 }
 
 // One step: multiply stage S (its sub-step 0 fragments are already in slot
@@ -244,9 +265,10 @@ __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uin
     for (int n = 0; n < G::NQ; ++n) {
         const int i = n / G::TN, j = n % G::TN;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[0][j], f.a[0][i], acc[i][j], 0, 0, 0);
-#pragma unroll
-        for (int m = n * G::NF / G::NQ; m < (n + 1) * G::NF / G::NQ; ++m)
-            read_frag<BM>(S, f, 1, m, a_slot[1], b_slot[1], b_toff);
+        // one read per MFMA from the first: all have landed by the
+        // barrier, where the next sub-step starts
+        if (n < G::NF)
+            read_frag<BM>(S, f, 1, n, a_slot[1], b_slot[1], b_toff);
         fence();
     }
     // the next stage is complete once every wave's own requests for it are:
@@ -354,15 +376,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     Req<BM> req;                             // the tile being fetched
     {
         int raw[G::AI];
-        gathered_rows<BM>(p, row0, row_end, raw);
-        a_offsets<BM>(p, raw, req.a_off);
+        const int valid = gathered_rows<BM>(p, row0, row_end, raw);
+        a_offsets<BM>(p, raw, valid, req.a_off);
         req.e = e;
         req.nt = nt;
     }
     int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
     bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
     int nraw[G::AI];
-    gathered_rows<BM>(p, has_next ? nrow0 : row0, has_next ? nrow_end : row_end, nraw);
+    int nvalid = gathered_rows<BM>(p, has_next ? nrow0 : row0, has_next ? nrow_end : row_end, nraw);
 
     // LDS slots of this lane's fragment pieces for sub-steps 0 and 1; the
     // tiles of a wave sit 32 rows apart, which keeps the swizzle (+128 slots)
@@ -436,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
                     for (int i = 0; i < G::AI; ++i)
                         __asm__ volatile("" : "+v"(nraw[i]));
-                    a_offsets<BM>(p, nraw, req.a_off);
+                    a_offsets<BM>(p, nraw, nvalid, req.a_off);
                     req.e = ne;
                     req.nt = nnt;
                 }
@@ -547,7 +569,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         row_end = nrow_end;
         nt = nnt;
         has_next = place<BM>(tl, ti + 1, ne, nrow0, nrow_end, nnt);
-        gathered_rows<BM>(p, has_next ? nrow0 : row0, has_next ? nrow_end : row_end, nraw);
+        nvalid = gathered_rows<BM>(p, has_next ? nrow0 : row0, has_next ? nrow_end : row_end, nraw);
     }
     // the requests of the last kAhead stages target LDS this workgroup is
     // about to release
@@ -610,8 +632,10 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 }  // namespace
 
 bool grouped_supported(const GemmProblem &p) {
+    // every A offset (rows of A times lda, in bytes) stays below kPastA
+    const long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
     return !p.affine4 && p.K % kBK == 0 && p.K / kBK >= kAhead + 1 &&
-           (p.offsets == nullptr || p.E <= kMaxE);
+           (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA;
 }
 
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream) {
