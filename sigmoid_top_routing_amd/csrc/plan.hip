@@ -66,6 +66,8 @@ __global__ __launch_bounds__(kThreads) void k_plan_scatter(
     // totals, earlier-chunk counts and the exclusive scan over experts
     int total = 0, before = 0;
     if (tid < E) {
+        // the loads of a batch are independent: one wait per 16 chunks
+#pragma unroll 16
         for (int b = 0; b < nchunks; ++b) {
             const int c = chunk_counts[(size_t)b * E + tid];
             total += c;
