@@ -173,8 +173,8 @@ __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)
     }
 }
 
-// 16 bytes per lane from `base` + off into LDS at dst + 16 lane, range
-// checked: offsets at or past 2^31 read zeros.
+// 16 bytes per lane from `base` + off into LDS at dst + 16 lane, through a
+// raw buffer resource: offsets at or past 2^31 read zeros.
 __device__ __forceinline__ void buffer_to_lds16(const void *base, uint4 *dst, uint32_t off) {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, kBufferWord3);
@@ -184,43 +184,53 @@ __device__ __forceinline__ void buffer_to_lds16(const void *base, uint4 *dst, ui
 // Request state of the tile whose slices are being fetched.
 template <int BM>
 struct Req {
-    int e, nt;                        // uniform
-    uint32_t a_off[Geo<BM>::AI];      // per thread
+    const char *b_base;               // uniform: the expert's weight rows
+    uint32_t a_off[Geo<BM>::AI];      // per thread, bytes at K-slice 0
+    uint32_t b_off[Geo<BM>::BI];
 };
+
+// The weight side of a tile's requests: the expert's base and, per B piece
+// of this thread, the byte offset of its row and chunk at K-slice 0 (rows
+// past N are clamped to a valid row).
+template <int BM, int MODE>
+__device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, Req<BM> &q) {
+    using G = Geo<BM>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    q.b_base = (const char *)p.B + (size_t)e * p.N * p.K * 2;
+#pragma unroll
+    for (int i = 0; i < G::BI; ++i) {
+        const int s = (wave * G::BI + i) * kWave + lane;
+        const int r = s >> 2;
+        const int c = (s & 3) ^ ((r >> 2) & 3);
+        int wr;
+        if (MODE == kGateUp) {
+            int n = nt * (kBN / 2) + (r & (kBN / 2 - 1));
+            if (n >= p.I)
+                n = p.I - 1;
+            wr = r < kBN / 2 ? n : p.I + n;
+        } else {
+            wr = nt * kBN + r;
+            if (wr >= p.N)
+                wr = p.N - 1;
+        }
+        q.b_off[i] = ((uint32_t)wr * (uint32_t)p.K + c * 8) * 2u;
+    }
+}
 
 // Piece m (A pieces first, then B pieces) of K-slice ks into one stage.
 template <int BM, int MODE>
 __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmProblem &p,
                                         const Req<BM> &q, int ks, int m) {
     using G = Geo<BM>;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t kb = (uint32_t)ks * (kBK * 2);
     if (m < G::AI) {
-        // a range-checked load: pieces of padding rows (offset kPastA) read
-        // as zeros
+        // pieces of padding rows (offset kPastA) read as zeros
         buffer_to_lds16(p.A, stage + (wave * G::AI + m) * kWave, q.a_off[m] + kb);
     } else {
         const int i = m - G::AI;
-        const int s = (wave * G::BI + i) * kWave + lane;
-        const int r = s >> 2;
-        const int c = (s & 3) ^ ((r >> 2) & 3);
-        int wr;
-        if (MODE == kGateUp) {
-            int n = q.nt * (kBN / 2) + (r & (kBN / 2 - 1));
-            if (n >= p.I)
-                n = p.I - 1;
-            wr = r < kBN / 2 ? n : p.I + n;
-        } else {
-            wr = q.nt * kBN + r;
-            if (wr >= p.N)
-                wr = p.N - 1;
-        }
-        const char *b_base = (const char *)p.B + (size_t)q.e * p.N * p.K * 2;
-        const uint32_t off = ((uint32_t)wr * (uint32_t)p.K + c * 8) * 2u + kb;
-        __builtin_amdgcn_global_load_lds((const void *)(b_base + off),
-                                         (lds_void *)(stage + BM * 4 + (wave * G::BI + i) * kWave),
-                                         16, 0, 0);
+        buffer_to_lds16(q.b_base, stage + BM * 4 + (wave * G::BI + i) * kWave, q.b_off[i] + kb);
     }
 }
 
@@ -378,8 +388,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         int raw[G::AI];
         const int valid = gathered_rows<BM>(p, row0, row_end, raw);
         a_offsets<BM>(p, raw, valid, req.a_off);
-        req.e = e;
-        req.nt = nt;
+        b_offsets<BM, MODE>(p, e, nt, req);
     }
     int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
     bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
@@ -459,8 +468,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                     for (int i = 0; i < G::AI; ++i)
                         __asm__ volatile("" : "+v"(nraw[i]));
                     a_offsets<BM>(p, nraw, nvalid, req.a_off);
-                    req.e = ne;
-                    req.nt = nnt;
+                    b_offsets<BM, MODE>(p, ne, nnt, req);
                 }
             }
         }
@@ -633,9 +641,11 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 
 bool grouped_supported(const GemmProblem &p) {
     // every A offset (rows of A times lda, in bytes) stays below kPastA
+    // and every weight offset within one expert, stay below kPastA
     const long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
     return !p.affine4 && p.K % kBK == 0 && p.K / kBK >= kAhead + 1 &&
-           (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA;
+           (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA &&
+           (long long)p.N * p.K * 2 < (long long)kPastA;
 }
 
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream) {
