@@ -19,14 +19,16 @@
 //   the m-tiles of a weight tile read it from HBM once and share it in that
 //   XCD's L2, and the token rows of an m-tile are shared by its n-tiles.
 //
-// * Operands go from global memory straight into LDS (global_load_lds, 16
-//   bytes per lane) through a ring of 4 stages of K = 32, requested 3 stages
-//   ahead of the one being multiplied. The request stream runs across tile
-//   boundaries: the last steps of a tile request the first slices of the
-//   next. No VGPRs hold staged data and no LDS writes are issued by the
-//   waves. Token rows past a segment (padding of its last tile) are read
-//   as zeros by range-checked loads, which costs no memory traffic; weight
-//   rows past N are clamped to a valid row. Neither result is stored.
+// * Operands go from global memory straight into LDS (buffer loads with the
+//   LDS bit, 16 bytes per lane) through a ring of 4 stages of K = 32,
+//   requested 3 stages ahead of the one being multiplied. The request stream
+//   runs across tile boundaries: the last steps of a tile request the first
+//   slices of the next. No VGPRs hold staged data and no LDS writes are
+//   issued by the waves. Each request's byte offset at K-slice 0 is formed
+//   once per tile, so a step only adds the slice offset. Token rows past a
+//   segment (padding of its last tile) are read as zeros by the range check,
+//   which costs no memory traffic; weight rows past N are clamped to a valid
+//   row. Neither result is stored.
 //
 // * The MFMA v_mfma_f32_32x32x16_bf16 is issued with the weight fragment as
 //   its first operand, so the 32x32 accumulator tile is [weight row][token]:

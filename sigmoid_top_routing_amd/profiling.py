@@ -13,7 +13,8 @@ counter is divided by what the same counter reads, per byte, for the largest
 plain device-to-device copy in the same run (a copy of --copy-bytes bytes
 reads and writes exactly that many bytes), and the result is stored under
 "<kernel tag>@<workload>" in profiles/traffic.json together with a digest of
-the kernel sources it was taken on.
+the code of the kernel sources it was taken on (comments and spacing are not
+part of the digest).
 """
 from __future__ import annotations
 
@@ -36,11 +37,19 @@ def short_name(name: str) -> str:
     return re.sub(r"\(.*\)$", "", name)[:90]
 
 
+def code_text(source: str) -> str:
+    """The source without comments and with whitespace collapsed: what the
+    compiler sees, so a comment edit keeps a record valid."""
+    source = re.sub(r"/\*.*?\*/", " ", source, flags=re.S)
+    source = re.sub(r"//[^\n]*", " ", source)
+    return " ".join(source.split())
+
+
 def source_digest(*names: str) -> str:
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(HERE, "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(HERE, "csrc", n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
