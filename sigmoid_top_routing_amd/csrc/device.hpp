@@ -18,6 +18,24 @@ constexpr int kWave = 64;
 // offsets are range checked against the record count, stride 0).
 constexpr int kBufferWord3 = 0x00020000;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from `base` + off into LDS at dst + 16 lane, through a
+// raw buffer resource: offsets at or past 2^31 read zeros.
+__device__ __forceinline__ void buffer_to_lds16(const void *base, uint4 *dst, uint32_t off) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, kBufferWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }

@@ -67,7 +67,6 @@ constexpr int kXcds = 8;
 constexpr int kMaxE = 256;
 constexpr uint32_t kPastA = 0x80000000u;   // an A offset past every A matrix: reads zeros
 
-typedef __attribute__((address_space(3))) void lds_void;
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
@@ -79,14 +78,6 @@ typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
 __device__ __forceinline__ int slot_of(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
-
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding: vmcnt bits
-// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt field");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <int BM>
 struct Geo {
@@ -173,14 +164,6 @@ __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)
         const int arow = p.gather ? raw[i] / p.gather_div : raw[i];
         off[i] = (valid >> i) & 1 ? ((uint32_t)arow * (uint32_t)p.lda + c * 8) * 2u : kPastA;
     }
-}
-
-// 16 bytes per lane from `base` + off into LDS at dst + 16 lane, through a
-// raw buffer resource: offsets at or past 2^31 read zeros.
-__device__ __forceinline__ void buffer_to_lds16(const void *base, uint4 *dst, uint32_t off) {
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, kBufferWord3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, 0);
 }
 
 // Request state of the tile whose slices are being fetched.

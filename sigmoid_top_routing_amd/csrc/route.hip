@@ -180,6 +180,142 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restri
     }
 }
 
+// k_logits_ring: the same lanes and chains as k_logits<2> (a lane per token,
+// two experts per wave: 64 tokens and 8 experts per workgroup), for H a
+// multiple of 128. The operands come in by range-checked buffer loads
+// straight into a ring of 4 LDS stages of 128 h (x as bf16, the router rows
+// as fp32), requested three stages ahead, so the chains do not wait on
+// memory once the ring is full; no registers hold staged data. A token row's
+// 16-byte pieces (8 h) sit at piece c ^ (t % 16) of its LDS row, so the 16
+// lanes of a 16-byte read hit distinct banks; the router rows are read by
+// every lane at once (broadcast). Every chain still runs in h order.
+constexpr int kRingH = 128;
+constexpr int kRingStages = 4;
+constexpr int kRingX = kTok * (kRingH / 8);             // 16-byte x pieces per stage
+constexpr int kRingW = 8 * (kRingH / 4);                // 16-byte router pieces per stage
+constexpr int kRingStage = kRingX + kRingW;             // 20 KB
+constexpr int kRingPer = kRingStage / kMaxThreads;      // requests per thread per stage
+constexpr uint32_t kRingPast = 0x80000000u;             // an offset that reads zeros
+
+// One stage: the chains over stage S (128 h); the refill of stage F with h
+// block sf (none when sf < 0). One call site, so the LDS reads of S and the
+// loads into F share one alias scope and the compiler does not order the
+// reads behind loads still in flight; the caller's waits do that.
+__device__ __forceinline__ void ring_stage(const uint4 *__restrict__ S, uint4 *__restrict__ F,
+                                           const uint16_t *x, const float *Wr,
+                                           const uint32_t (&xoff)[kRingPer - 1], uint32_t woff,
+                                           int sf, float &acc0, float &acc1) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    if (sf >= 0) {
+#pragma unroll
+        for (int q = 0; q < kRingPer - 1; ++q)
+            buffer_to_lds16(x, F + (q * 4 + wave) * kWave, xoff[q] + sf * (kRingH * 2));
+        buffer_to_lds16(Wr, F + kRingX + wave * kWave, woff + sf * (kRingH * 4));
+    }
+    const int t = lane;
+    const uint4 *xrow = S + t * (kRingH / 8);
+    const float4 *wa = reinterpret_cast<const float4 *>(S + kRingX) + (2 * wave) * (kRingH / 4);
+    const float4 *wb = wa + kRingH / 4;
+    // 8 h per group: one 16-byte x piece, two float4 of each router row
+    auto read = [&](int g, uint4 &xv, float4 (&av)[2], float4 (&bv)[2]) {
+        xv = xrow[g ^ (t & 15)];
+        av[0] = wa[2 * g];
+        av[1] = wa[2 * g + 1];
+        bv[0] = wb[2 * g];
+        bv[1] = wb[2 * g + 1];
+    };
+    auto fma8 = [&](const uint4 &xv, const float4 (&av)[2], const float4 (&bv)[2]) {
+        const float xs[8] = {bf16_to_f32(xv.x & 0xffffu), bf16_to_f32(xv.x >> 16),
+                             bf16_to_f32(xv.y & 0xffffu), bf16_to_f32(xv.y >> 16),
+                             bf16_to_f32(xv.z & 0xffffu), bf16_to_f32(xv.z >> 16),
+                             bf16_to_f32(xv.w & 0xffffu), bf16_to_f32(xv.w >> 16)};
+        const float as[8] = {av[0].x, av[0].y, av[0].z, av[0].w, av[1].x, av[1].y, av[1].z, av[1].w};
+        const float bs[8] = {bv[0].x, bv[0].y, bv[0].z, bv[0].w, bv[1].x, bv[1].y, bv[1].z, bv[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc0 = __builtin_fmaf(xs[i], as[i], acc0);
+            acc1 = __builtin_fmaf(xs[i], bs[i], acc1);
+        }
+    };
+    uint4 xa, xb;
+    float4 aa[2], ba[2], ab[2], bb[2];
+    constexpr int G = kRingH / 8;                           // 16 groups, even
+    read(0, xa, aa, ba);
+#pragma unroll
+    for (int g = 0; g < G; g += 2) {
+        read(g + 1, xb, ab, bb);
+        __builtin_amdgcn_sched_barrier(0);
+        fma8(xa, aa, ba);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g + 2 < G)
+            read(g + 2, xa, aa, ba);
+        __builtin_amdgcn_sched_barrier(0);
+        fma8(xb, ab, bb);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__global__ __launch_bounds__(kMaxThreads) void k_logits_ring(const uint16_t *__restrict__ x,
+                                                             const float *__restrict__ Wr, int T,
+                                                             int H, int E, float *__restrict__ z) {
+    __shared__ uint4 ring[kRingStages * kRingStage];    // 80 KB
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int t0 = blockIdx.x * kTok;
+    const int e0 = blockIdx.y * 8;
+    const int S = H / kRingH;
+    // byte offsets of this thread's pieces in h block 0; rows past T or E
+    // read zeros
+    uint32_t xoff[kRingPer - 1];
+#pragma unroll
+    for (int q = 0; q < kRingPer - 1; ++q) {
+        const int pos = (q * 4 + wave) * kWave + lane;     // LDS piece
+        const int r = pos / (kRingH / 8), c = (pos % (kRingH / 8)) ^ (r & 15);
+        xoff[q] = t0 + r < T ? ((uint32_t)(t0 + r) * (uint32_t)H + 8u * c) * 2u : kRingPast;
+    }
+    uint32_t woff;
+    {
+        const int pos = wave * kWave + lane;
+        const int j = pos / (kRingH / 4), c = pos % (kRingH / 4);
+        woff = e0 + j < E ? ((uint32_t)(e0 + j) * (uint32_t)H + 4u * c) * 4u : kRingPast;
+    }
+    // the first three stages
+#pragma unroll
+    for (int s = 0; s < kRingStages - 1; ++s) {
+        if (s < S) {
+            uint4 *F = ring + s * kRingStage;
+#pragma unroll
+            for (int q = 0; q < kRingPer - 1; ++q)
+                buffer_to_lds16(x, F + (q * 4 + wave) * kWave, xoff[q] + s * (kRingH * 2));
+            buffer_to_lds16(Wr, F + kRingX + wave * kWave, woff + s * (kRingH * 4));
+        }
+    }
+    float acc0 = 0.0f, acc1 = 0.0f;
+    for (int s = 0; s < S; ++s) {
+        // stage s is in once at most the requests of the two stages after
+        // it are still in flight (fewer near the end)
+        if (s + 2 < S)
+            wait_vmcnt<2 * kRingPer>();
+        else if (s + 1 < S)
+            wait_vmcnt<kRingPer>();
+        else
+            wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();       // every wave's pieces are in; stage s - 1 is read
+        ring_stage(ring + (s & 3) * kRingStage, ring + ((s + 3) & 3) * kRingStage, x, Wr, xoff,
+                   woff, s + 3 < S ? s + 3 : -1, acc0, acc1);
+    }
+    const int t = t0 + lane;
+    const int e = e0 + 2 * wave;
+    if (t < T) {
+        if (e < E)
+            z[(size_t)t * E + e] = acc0;
+        if (e + 1 < E)
+            z[(size_t)t * E + e + 1] = acc1;
+    }
+}
+
 // k_logits_few: decode-sized batches (T <= 8, H <= 2048). The chains are
 // the whole cost there (H dependent fmas each), so the point is to start
 // them early and never stall them: a workgroup owns 8 experts and every
@@ -445,6 +581,9 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
     if (T <= kFewT && H <= kFewMaxH && H % 128 == 0)
         hipLaunchKernelGGL(k_logits_few, dim3((E + kFewE - 1) / kFewE), dim3(kMaxThreads), 0,
                            stream, x, Wr, T, H, E, z_scratch);
+    else if ((int64_t)tblocks * ((E + 7) / 8) >= 128 && H % kRingH == 0)
+        hipLaunchKernelGGL(k_logits_ring, dim3(tblocks, (E + 7) / 8), dim3(kMaxThreads), 0, stream,
+                           x, Wr, T, H, E, z_scratch);
     else if ((int64_t)tblocks * ((E + 7) / 8) >= 128)
         launch_logits<2>(stream, x, Wr, T, H, E, z_scratch);
     else
