@@ -8,7 +8,7 @@
 //   ids[t,:] = k experts by key, best first; ties to the lower index; NaN last
 //   w[t,j]   = s[t,ids_j] / (sum_j s[t,ids_j] + eps)
 //
-// Two launches.
+// Two launches, or one for decode-sized batches (k_route_decode).
 //
 // k_logits computes z = x Wr^T as T*E independent fma chains of length H,
 // each in h order (see the kernel for the layout). The chains are what
@@ -432,17 +432,22 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits_few(const uint16_t *__re
         z[(size_t)t * E + e0 + j] = acc;
 }
 
+// LDS ints the fused plan of topk_block works in.
+constexpr int kTopkLds = 2 * kFusedPlanMaxA + 2 * 256 + kMaxThreads / kWave;
+
+// The top-k, the weights and (plan.counts given) the fused plan of the
+// tokens of this workgroup, from z (global memory or LDS), with kTopkLds
+// ints of LDS at lds. Every thread of the workgroup calls it.
 template <int RE>
-__global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ z,
-                                                      const float *__restrict__ bias, int T,
-                                                      int E, int k, int LPT, int norm_topk,
-                                                      float eps, int32_t *__restrict__ ids,
-                                                      float *__restrict__ weights, PlanOut plan) {
-    __shared__ int s_ids[kFusedPlanMaxA];
-    __shared__ int s_rank[kFusedPlanMaxA];
-    __shared__ int s_cnt[256];
-    __shared__ int s_off[256];
-    __shared__ int s_wsum[kMaxThreads / kWave];
+__device__ __forceinline__ void topk_block(const float *z, const float *__restrict__ bias, int T,
+                                           int E, int k, int LPT, int norm_topk, float eps,
+                                           int32_t *__restrict__ ids, float *__restrict__ weights,
+                                           PlanOut plan, int *lds) {
+    int *s_ids = lds;
+    int *s_rank = s_ids + kFusedPlanMaxA;
+    int *s_cnt = s_rank + kFusedPlanMaxA;
+    int *s_off = s_cnt + 256;
+    int *s_wsum = s_off + 256;
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int per_block = kMaxThreads / LPT;
@@ -521,6 +526,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ 
     for (int a = tid; a < A; a += kMaxThreads) {
         const int v = s_ids[a];
         int r = 0;
+#pragma unroll 8
         for (int b = 0; b < a; ++b)
             r += s_ids[b] == v;
         s_rank[a] = r;
@@ -555,6 +561,160 @@ __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ 
     }
 }
 
+template <int RE>
+__global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ z,
+                                                      const float *__restrict__ bias, int T,
+                                                      int E, int k, int LPT, int norm_topk,
+                                                      float eps, int32_t *__restrict__ ids,
+                                                      float *__restrict__ weights, PlanOut plan) {
+    __shared__ int lds[kTopkLds];
+    topk_block<RE>(z, bias, T, E, k, LPT, norm_topk, eps, ids, weights, plan, lds);
+}
+
+// k_route_decode: the whole router of a decode-sized batch (T <= 8,
+// E <= 32, H a multiple of 128, H <= 2048) in one workgroup: the logits,
+// then the top-k, the weights and the plan, with z kept in LDS. Lane l of
+// wave w runs the chain of token l % 8 and expert 8 w + l / 8 (one chain per
+// lane: the chain latency, H dependent fmas, is the floor of this step, so
+// the loop carries nothing but the fmas and their LDS reads). The token
+// rows are converted to fp32 into LDS once, at the start (rows padded by 16
+// bytes: the 8 rows a read touches fall in distinct banks); the router rows
+// stream through a ring of 5 LDS stages of 128 h, requested four stages
+// ahead by range-checked buffer loads, pieces at swizzled slots (router row
+// e: piece c ^ 2 (e % 8)).
+constexpr int kDecT = 8;
+constexpr int kDecE = 32;
+constexpr int kDecMaxH = 2048;
+constexpr int kDecXRow = kDecMaxH / 4 + 1;              // float4 per token row (+ pad)
+constexpr int kDecX = kDecT * kDecXRow;                 // 65.6 KB
+constexpr int kDecW = kDecE * (kRingH / 4);             // 1024 router pieces per stage (16 KB)
+constexpr int kDecStages = 5;
+constexpr int kDecAhead = kDecStages - 1;
+
+// One stage: the chain over W's 128 h (x from X at float4 column c0), and the
+// refill of stage F with h block sf. One call site, so the LDS reads and the
+// loads into F share one alias scope.
+__device__ __forceinline__ void dec_stage(const float4 *__restrict__ X,
+                                          const uint4 *__restrict__ W, uint4 *__restrict__ F,
+                                          const float *Wr, const uint32_t (&woff)[4], int sf,
+                                          int c0, bool compute, float &acc) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        buffer_to_lds16(Wr, F + (q * 4 + wave) * kWave, woff[q] + sf * (kRingH * 4));
+    if (!compute)
+        return;
+    const int t = lane & 7;
+    const int e = wave * 8 + (lane >> 3);
+    const float4 *xrow = X + t * kDecXRow + c0;
+    const float4 *wrow = reinterpret_cast<const float4 *>(W) + e * (kRingH / 4);
+    const int wsw = 2 * (e & 7);
+    auto fma4 = [&](const float4 &xv, const float4 &wv) {
+        acc = __builtin_fmaf(xv.x, wv.x, acc);
+        acc = __builtin_fmaf(xv.y, wv.y, acc);
+        acc = __builtin_fmaf(xv.z, wv.z, acc);
+        acc = __builtin_fmaf(xv.w, wv.w, acc);
+    };
+    // 4 h per group; the reads run two groups ahead of the fmas
+    constexpr int G = kRingH / 4;                           // 32 groups
+    float4 xv[3], wv[3];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        xv[g] = xrow[g];
+        wv[g] = wrow[g ^ wsw];
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if (g + 2 < G) {
+            xv[(g + 2) % 3] = xrow[g + 2];
+            wv[(g + 2) % 3] = wrow[(g + 2) ^ wsw];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        fma4(xv[g % 3], wv[g % 3]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+__global__ __launch_bounds__(kMaxThreads) void k_route_decode(
+    const uint16_t *__restrict__ x, const float *__restrict__ Wr, const float *__restrict__ bias,
+    int T, int H, int E, int k, int LPT, int norm_topk, float eps, int32_t *__restrict__ ids,
+    float *__restrict__ weights, PlanOut plan) {
+    // one LDS object: the fp32 token rows, then the ring; reused after the
+    // logits for z and the top-k's work space (a second LDS object would make
+    // the compiler wait for every load into the ring before any read of it)
+    __shared__ uint4 lds[kDecX + kDecStages * kDecW];   // 146 KB
+    float4 *X = reinterpret_cast<float4 *>(lds);
+    uint4 *ring = lds + kDecX;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int S = H / kRingH;
+    // the token rows: 8 pieces of 8 bf16 per thread, in registers first,
+    // by range-checked loads issued together (pieces past T or H read zeros)
+    constexpr int kXPieces = kDecT * (kDecMaxH / 8) / kMaxThreads;
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, 0x7fffffff, kBufferWord3);
+    uint4 xr[kXPieces];
+#pragma unroll
+    for (int i = 0; i < kXPieces; ++i) {
+        const int pos = i * kMaxThreads + tid;
+        const int r = pos / (kDecMaxH / 8), c = pos % (kDecMaxH / 8);
+        const uint32_t off = (r < T && 8 * c < H) ? ((uint32_t)r * (uint32_t)H + 8u * c) * 2u : kRingPast;
+        xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
+    }
+    // byte offsets of this thread's router pieces in h block 0; rows past E
+    // read zeros
+    uint32_t woff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int pos = (q * 4 + wave) * kWave + lane;
+        const int j = pos / (kRingH / 4), c = (pos % (kRingH / 4)) ^ (2 * (j & 7));
+        woff[q] = j < E ? ((uint32_t)j * (uint32_t)H + 4u * c) * 4u : kRingPast;
+    }
+    float acc = 0.0f;
+    // Iterations -4 .. -1 only request h blocks 0 .. 3; every request comes
+    // from the one call site below, in one alias scope. 4 requests per
+    // iteration and wave (past the end the last h block again, into the
+    // slot read in the previous iteration): stage s is in once at most the
+    // 12 requests after it are in flight.
+    for (int s = -kDecAhead; s < S; ++s) {
+        wait_vmcnt<4 * (kDecAhead - 1)>();
+        __builtin_amdgcn_s_barrier();       // also: the token rows are in LDS
+        const int sc = s < 0 ? 0 : s;
+        dec_stage(X, ring + (sc % kDecStages) * kDecW, ring + ((s + kDecAhead) % kDecStages) * kDecW,
+                  Wr, woff, s + kDecAhead < S ? s + kDecAhead : S - 1, sc * (kRingH / 4), s >= 0,
+                  acc);
+        if (s == -1) {
+            // the token rows to fp32, once the first router blocks are on
+            // their way (visible after the next barrier)
+#pragma unroll
+            for (int i = 0; i < kXPieces; ++i) {
+                const int pos = i * kMaxThreads + tid;
+                const int r = pos / (kDecMaxH / 8), c = pos % (kDecMaxH / 8);
+                const uint4 v = xr[i];
+                float4 *d = X + r * kDecXRow + 2 * c;
+                d[0] = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
+                                   bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16));
+                d[1] = make_float4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16),
+                                   bf16_to_f32(v.w & 0xffffu), bf16_to_f32(v.w >> 16));
+            }
+        }
+    }
+    wait_vmcnt<0>();                        // the last requests land before the LDS is reused
+    __syncthreads();                        // and every wave is past its reads
+    float *zs = reinterpret_cast<float *>(lds);
+    {
+        const int t = lane & 7;
+        const int e = wave * 8 + (lane >> 3);
+        if (t < T && e < E)
+            zs[t * E + e] = acc;
+    }
+    __syncthreads();
+    topk_block<1>(zs, bias, T, E, k, LPT, norm_topk, eps, ids, weights, plan,
+                  reinterpret_cast<int *>(lds) + kDecT * kDecE);
+}
+
 // Two chains per lane when that still leaves a few hundred workgroups,
 // else one (decode-sized batches are latency-bound: more workgroups).
 template <int C>
@@ -577,6 +737,21 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
         return hipSuccess;
     if (H % 64 != 0)
         return hipErrorInvalidValue;
+    if (T <= kDecT && E <= kDecE && H % kRingH == 0 && H <= kDecMaxH) {
+        // one workgroup: logits, top-k, weights and (when it fits) the plan
+        int LPT = 2;
+        while (LPT < E)
+            LPT <<= 1;
+        const bool fuse = plan.counts != nullptr && T * k <= kFusedPlanMaxA;
+        if (!fuse)
+            plan = PlanOut{};
+        hipLaunchKernelGGL(k_route_decode, dim3(1), dim3(kMaxThreads), 0, stream, x, Wr, bias, T, H,
+                           E, k, LPT, norm_topk, eps, ids, weights, plan);
+        const hipError_t err = hipGetLastError();
+        if (err == hipSuccess && plan_done != nullptr)
+            *plan_done = fuse;
+        return err;
+    }
     const int tblocks = (T + kTok - 1) / kTok;
     if (T <= kFewT && H <= kFewMaxH && H % 128 == 0)
         hipLaunchKernelGGL(k_logits_few, dim3((E + kFewE - 1) / kFewE), dim3(kMaxThreads), 0,

@@ -31,6 +31,13 @@ namespace moe {
 namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// A weight piece: read once per call, so the load is marked non-temporal
+// (streamed past the caches rather than kept in them).
+__device__ __forceinline__ uint4 stream_load(const uint16_t *p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p)));
+}
 
 constexpr int kThreads = 512;
 constexpr int kTG = 4;         // token rows per group
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
                 const int kk = j * 512 + lane * 8;
-                w[i][s][j] = (u < units && kk < K) ? *reinterpret_cast<const uint4 *>(wp + kk)
+                w[i][s][j] = (u < units && kk < K) ? stream_load(wp + kk)
                                                    : make_uint4(0, 0, 0, 0);
             }
         }
