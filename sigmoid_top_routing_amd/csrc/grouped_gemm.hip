@@ -60,8 +60,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBK = 32;          // K per ring stage
-constexpr int kStages = 4;
-constexpr int kAhead = 3;        // stages requested ahead of the one multiplied
+// Ring depth: NS stages, NS - 1 requested ahead of the one multiplied. Four
+// for 256-row tiles (32 KB stages); six for 128-row tiles (24 KB stages),
+// which carry half the MFMAs per weight byte and stream weights from HBM
+// when segments are short, so they need more bytes in flight.
+constexpr int kStagesSmall = 4;
+constexpr int kStagesDeep = 6;
 constexpr int kBN = 256;         // weight rows per tile
 constexpr int kXcds = 8;
 constexpr int kMaxE = 256;
@@ -246,7 +250,7 @@ __device__ __forceinline__ void read_frag(const uint4 *__restrict__ S, Frags<BM>
 // One step: multiply stage S (its sub-step 0 fragments are already in slot
 // 0), read the next step's first fragments from Snext, refill Sfill with
 // K-slice ks of the requested tile.
-template <int BM, int MODE>
+template <int BM, int MODE, int NS>
 __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uint4 *__restrict__ Snext,
                                           uint4 *__restrict__ Sfill, const GemmProblem &p,
                                           const Req<BM> &q, int ks, Frags<BM> &f,
@@ -267,8 +271,8 @@ __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uin
         fence();
     }
     // the next stage is complete once every wave's own requests for it are:
-    // only the requests of the stage after it may still be in flight
-    wait_vmcnt<G::PER>();
+    // only the requests of the NS - 3 stages after it may still be in flight
+    wait_vmcnt<(NS - 3) * G::PER>();
     __builtin_amdgcn_s_barrier();
     fence();
     // sub-step 1: MFMAs on slot 1, the next step's first fragments into
@@ -289,28 +293,25 @@ __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uin
     }
 }
 
-// Prologue: the first kAhead slices of the first tile, then (after the
-// first stage is in) its first fragments.
-template <int BM, int MODE>
-__device__ __forceinline__ void prime(uint4 *__restrict__ s0, uint4 *__restrict__ s1,
-                                      uint4 *__restrict__ s2, const GemmProblem &p, const Req<BM> &q) {
+// Prologue: the first NS - 1 slices of the first tile into stages 0 ..
+// NS - 2.
+template <int BM, int MODE, int NS>
+__device__ __forceinline__ void prime(uint4 *__restrict__ ring, const GemmProblem &p,
+                                      const Req<BM> &q) {
     using G = Geo<BM>;
 #pragma unroll
-    for (int m = 0; m < G::PER; ++m)
-        request<BM, MODE>(s0, p, q, 0, m);
+    for (int st = 0; st < NS - 1; ++st)
 #pragma unroll
-    for (int m = 0; m < G::PER; ++m)
-        request<BM, MODE>(s1, p, q, 1, m);
-#pragma unroll
-    for (int m = 0; m < G::PER; ++m)
-        request<BM, MODE>(s2, p, q, 2, m);
+        for (int m = 0; m < G::PER; ++m)
+            request<BM, MODE>(ring + st * G::STAGE, p, q, st, m);
 }
 
-template <int BM, int MODE>
+template <int BM, int MODE, int NS>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_tiles) {
     using G = Geo<BM>;
     constexpr int TM = G::TM, TN = G::TN;
-    __shared__ uint4 ring[kStages * G::STAGE];
+    constexpr int kAhead = NS - 1;           // stages requested ahead of the one multiplied
+    __shared__ uint4 ring[NS * G::STAGE];
     __shared__ int s_pre[kMaxE + 1];
     __shared__ int s_off[kMaxE + 1];
     __shared__ int s_wsum[4];
@@ -401,8 +402,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     }
 
     const int KT = p.K / kBK;
-    prime<BM, MODE>(ring, ring + G::STAGE, ring + 2 * G::STAGE, p, req);
-    wait_vmcnt<2 * G::PER>();
+    prime<BM, MODE, NS>(ring, p, req);
+    wait_vmcnt<(NS - 2) * G::PER>();
     __builtin_amdgcn_s_barrier();
     Frags<BM> f;
 #pragma unroll
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, (int)out_bytes, kBufferWord3);
 
     f32x16 acc[TM][TN];
-    int g = 0;                               // steps done by this workgroup
+    int sl = 0;                              // ring slot of the next step (steps done % NS)
     for (int ti = 1;; ++ti) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -437,12 +438,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         // retired those loads). One call site for the step, so all its
         // requests share one alias scope.
         for (int kt = 0; kt < KT; ++kt) {
-            uint4 *S = ring + (g & 3) * G::STAGE;
-            uint4 *Sn = ring + ((g + 1) & 3) * G::STAGE;
-            uint4 *Sf = ring + ((g + kAhead) & 3) * G::STAGE;
-            ring_step<BM, MODE>(S, Sn, Sf, p, req, kt + kAhead < KT ? kt + kAhead : kt + kAhead - KT,
+            // ring slots: g % NS multiplied, the next one read ahead, the
+            // one before (multiplied last step) refilled
+            const int sn = sl + 1 == NS ? 0 : sl + 1;
+            const int sf = sl == 0 ? NS - 1 : sl - 1;
+            uint4 *S = ring + sl * G::STAGE;
+            uint4 *Sn = ring + sn * G::STAGE;
+            uint4 *Sf = ring + sf * G::STAGE;
+            sl = sn;
+            ring_step<BM, MODE, NS>(S, Sn, Sf, p, req, kt + kAhead < KT ? kt + kAhead : kt + kAhead - KT,
                                 f, acc, a_slot, b_slot, b_toff);
-            ++g;
             if (kt == KT - kAhead - 1) {
                 // a tile past the end re-requests this one (in bounds, never
                 // multiplied)
@@ -492,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
             // at a time instead. The stage multiplied last is not refilled
             // before the next tile's first barrier.
             constexpr bool kViaLds = BM == 256;
-            lds_u32x4 *park = (lds_u32x4 *)(ring + ((g + kAhead) & 3) * G::STAGE) + wave * 8 * kWave;
+            lds_u32x4 *park = (lds_u32x4 *)(ring + (sl == 0 ? NS - 1 : sl - 1) * G::STAGE) + wave * 8 * kWave;
             if (kViaLds)
                 __syncthreads();             // every wave is past its reads of that stage
             constexpr int JO = MODE == kGateUp ? TN / 2 : TN;     // output column tiles
@@ -583,8 +588,9 @@ int cu_count() {
     return cached[dev];
 }
 
+// Tiles of the worst case (every segment ragged) for BM-row tiles.
 template <int BM, int MODE>
-hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
+long long tiles_bound(const GemmProblem &p, int &n_tiles) {
     int mt_max;
     if (p.offsets == nullptr) {
         mt_max = (p.rows + BM - 1) / BM;
@@ -594,8 +600,14 @@ hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
     }
     const int n_cols = MODE == kGateUp ? p.I : p.N;
     const int n_tile = MODE == kGateUp ? kBN / 2 : kBN;
-    const int n_tiles = (n_cols + n_tile - 1) / n_tile;
-    const long long work = (long long)mt_max * n_tiles;
+    n_tiles = (n_cols + n_tile - 1) / n_tile;
+    return (long long)mt_max * n_tiles;
+}
+
+template <int BM, int MODE>
+hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
+    int n_tiles = 0;
+    const long long work = tiles_bound<BM, MODE>(p, n_tiles);
     if (work == 0)
         return hipSuccess;
     // one workgroup per CU, a whole number of XCD rounds, no more than the
@@ -606,7 +618,16 @@ hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
     const long long need = (work + kXcds - 1) / kXcds * kXcds;
     if (need < blocks)
         blocks = (int)need;
-    hipLaunchKernelGGL((k_grouped<BM, MODE>), dim3(blocks), dim3(kThreads), 0, stream, p, n_tiles);
+    // the deep ring for 128-row tiles where K has the slices to fill it
+    if constexpr (BM == 128) {
+        if (p.K / kBK >= kStagesDeep) {
+            hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesDeep>), dim3(blocks), dim3(kThreads), 0,
+                               stream, p, n_tiles);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesSmall>), dim3(blocks), dim3(kThreads), 0, stream,
+                       p, n_tiles);
     return hipGetLastError();
 }
 
@@ -617,7 +638,10 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
         segs = p.E < p.max_rows ? p.E : p.max_rows;
     const int rows = p.offsets != nullptr ? p.max_rows : p.rows;
     const int avg = segs > 0 ? rows / segs : 0;
-    if (avg >= 192)
+    // 256-row tiles for long segments, unless a dense problem then has fewer
+    // tiles than CUs (128-row tiles put twice as many CUs to work)
+    int n_tiles = 0;
+    if (avg >= 192 && (p.offsets != nullptr || tiles_bound<256, MODE>(p, n_tiles) >= cu_count()))
         return launch_bm<256, MODE>(p, stream);
     return launch_bm<128, MODE>(p, stream);
 }
@@ -628,7 +652,7 @@ bool grouped_supported(const GemmProblem &p) {
     // every A offset (rows of A times lda, in bytes) stays below kPastA
     // and every weight offset within one expert, stay below kPastA
     const long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
-    return !p.affine4 && p.K % kBK == 0 && p.K / kBK >= kAhead + 1 &&
+    return !p.affine4 && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
            (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA &&
            (long long)p.N * p.K * 2 < (long long)kPastA;
 }
