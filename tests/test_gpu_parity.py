@@ -92,6 +92,46 @@ def test_route_matches_oracle(name):
     check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref)
 
 
+# Batches of at most 8 tokens take the one-workgroup router (E <= 32, H a
+# multiple of 128, H <= 2048: one fma chain per lane, a 5-stage ring over
+# H, fewer h blocks than ring stages at H = 128 and 256), past those limits
+# the 8-experts-per-workgroup decode logits (E > 32) or the tiled logits
+# (H > 2048); every shape here is one of those paths at an edge.
+ROUTE_DECODE = {
+    "t1_h2048_e32_k4": dict(T=1, H=2048, E=32, k=4),
+    "t5_h2048_e32_k4": dict(T=5, H=2048, E=32, k=4),
+    "t8_h128_e32_k8": dict(T=8, H=128, E=32, k=8),
+    "t8_h256_e7_k3": dict(T=8, H=256, E=7, k=3),
+    "t3_h384_e20_k2": dict(T=3, H=384, E=20, k=2),
+    "t2_h640_e32_k1": dict(T=2, H=640, E=32, k=1),
+    "t8_h1024_e32_nan_ties": dict(T=8, H=1024, E=32, k=4, nan_rows=(2,), zero_tie_row=5,
+                                  onehot_tie_row=6),
+    "t8_h2048_e33_k4": dict(T=8, H=2048, E=33, k=4),
+    "t6_h256_e64_k4": dict(T=6, H=256, E=64, k=4),
+    "t7_h2176_e32_k4": dict(T=7, H=2176, E=32, k=4),
+}
+
+
+@pytest.mark.parametrize("case", sorted(ROUTE_DECODE))
+def test_route_decode_sized(case):
+    wl = W.Workload("route_" + case, I=64, seed=300 + sorted(ROUTE_DECODE).index(case),
+                    **ROUTE_DECODE[case])
+    inp = W.generate(wl, experts=False)
+    x = lib.x_to_device(inp["x"])
+    wr = torch.from_numpy(inp["router_w"]).to(DEV)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    ids, w = lib.route(x, wr, b, wl.k, wl.norm_topk, wl.norm_eps)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k, wl.norm_topk,
+                                  wl.norm_eps)
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref)
+    # and the plan of those ids
+    counts, offsets, srt, slot = lib.plan(ids, wl.E)
+    torch.cuda.synchronize()
+    c_ref, o_ref, s_ref, sl_ref = oracle.plan(ids_ref, wl.E)
+    assert (offsets.cpu().numpy() == o_ref).all() and (srt.cpu().numpy() == s_ref).all()
+
+
 def test_route_without_bias_and_without_norm():
     wl, inp = small_inputs("mid_swiglu")
     x = lib.x_to_device(inp["x"])
