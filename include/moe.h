@@ -120,7 +120,8 @@ int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
  *           row picks 0, 1, ..., k-1 (TensorFold PR #1492 "Verification")
  *  weights  fp32 [T, k]: unbiased scores, normalised when d->norm_topk;
  *           routed_scale is not applied here.
- * Workspace: moe_workspace_bytes(d) (the router uses T*E*4 bytes of it).
+ * Workspace: moe_workspace_bytes(d) (the router uses T*E*4 bytes of it, or
+ * T*E*(H/64)*4 when T <= 8 and E <= 32: the partial logits of every slice).
  * Only T, H, E, k, norm_topk and norm_eps of d are read. */
 int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
               const float *expert_bias, int32_t *ids, float *weights, void *workspace,

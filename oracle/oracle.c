@@ -28,8 +28,9 @@
  *
  * Precision. Routing is discontinuous in the scores, so the router is not
  * left to float64: the logits, sigmoid and keys are fp32 in a fixed order
- * (the pages state the router is fp32; the order and the sigmoid are this
- * project's reading, spelled out below). Everything after the selection is
+ * (the pages state the router is fp32 and that its K slices are added by
+ * the top-k; the slice width and the sigmoid are this project's reading,
+ * spelled out below). Everything after the selection is
  * float64, with bf16, fp32 and 4-bit inputs converted exactly.
  *
  * Build: gcc -O2 -fPIC -shared -fopenmp -ffp-contract=off -fno-fast-math.
@@ -73,14 +74,28 @@ static double affine4_value(const uint32_t *codes_row, const uint16_t *scale_row
 /* router (fp32)                                                       */
 /* ------------------------------------------------------------------ */
 
-/* z = sum over h of x[h] * w[h], accumulated in fp32 from +0, one fused
- * multiply-add per term, h ascending: acc = fmaf(x[h], w[h], acc). */
+/* z = sum over h of x[h] * w[h] in fp32, as K slices whose bounds depend on
+ * H alone (TensorFold issue #548: the Nemotron score top-k adds the router's
+ * K slices itself, and a kernel's K slices come from the weight's shape, so
+ * a row's bits do not depend on how many rows share a launch). The slice
+ * width is not stated; it is taken as 64 h here. Slice s covers h = 64 s ..
+ * 64 s + 63 (the last one may be shorter): its partial starts at +0 and
+ * takes one fused multiply-add per h, ascending, p = fmaf(x[h], w[h], p).
+ * The partials are then added in ascending slice order, from +0:
+ * z = (((+0 + p_0) + p_1) + ...). */
+#define ROUTER_SLICE 64
+
 static float router_logit(const uint16_t *x_row, const float *w_row, int H)
 {
-    float acc = 0.0f;
-    for (int h = 0; h < H; ++h)
-        acc = fmaf(bf16_value(x_row[h]), w_row[h], acc);
-    return acc;
+    float z = 0.0f;
+    for (int h0 = 0; h0 < H; h0 += ROUTER_SLICE) {
+        int h1 = h0 + ROUTER_SLICE < H ? h0 + ROUTER_SLICE : H;
+        float p = 0.0f;
+        for (int h = h0; h < h1; ++h)
+            p = fmaf(bf16_value(x_row[h]), w_row[h], p);
+        z = z + p;
+    }
+    return z;
 }
 
 /* exp in fp32 for v in [-17, 87] (the sigmoid below never asks for more).

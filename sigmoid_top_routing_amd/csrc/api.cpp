@@ -53,7 +53,7 @@ Layout layout(const moe_dims &d) {
         off += round_up(bytes);
         return o;
     };
-    L.z = take(moe::route_scratch_bytes(d.T, d.E));
+    L.z = take(moe::route_scratch_bytes(d.T, d.H, d.E));
     L.ids = take(A * 4);
     L.w = take(A * 4);
     L.counts = take((size_t)d.E * 4);
@@ -190,7 +190,7 @@ int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
     TRY(check_ptr(what, "ids", ids));
     TRY(check_ptr(what, "weights", weights));
     // the router needs only the logits scratch of the layout
-    const size_t need = round_up(moe::route_scratch_bytes(d->T, d->E));
+    const size_t need = round_up(moe::route_scratch_bytes(d->T, d->H, d->E));
     REQUIRE(workspace_bytes >= need, MOE_E_WORKSPACE, "%s: workspace_bytes = %zu, need >= %zu",
             what, workspace_bytes, need);
     TRY(check_ptr(what, "workspace", workspace));

@@ -17,11 +17,12 @@ struct PlanOut {
 constexpr int kFusedPlanMaxA = 1024;
 
 // Router + top-k: a logits launch and a top-k launch. z_scratch holds the
-// [T][E] fp32 logits between them (route_scratch_bytes). When `plan` is given
-// and one top-k workgroup covers every token (decode-sized batches), the
-// top-k launch also writes the plan and *plan_done is set; otherwise the
-// caller runs launch_plan.
-size_t route_scratch_bytes(int T, int E);
+// [T][E] fp32 logits between them, or for batches of at most 8 tokens and
+// 32 experts the [H/64][T][E] partial logits of the slices
+// (route_scratch_bytes). When `plan` is given and one top-k workgroup covers
+// every token (decode-sized batches), the top-k launch also writes the plan
+// and *plan_done is set; otherwise the caller runs launch_plan.
+size_t route_scratch_bytes(int T, int H, int E);
 hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, int T, int H, int E,
                         int k, int norm_topk, float eps, int32_t *ids, float *weights,
                         float *z_scratch, PlanOut plan, bool *plan_done, hipStream_t stream);

@@ -2,18 +2,25 @@
 //
 // What is computed (TileGym PR #187, "Weight layout and routing"; TensorFold
 // PR #1492, "What" and "Verification"):
-//   z[t,e]   = sum_h x[t,h] * Wr[e,h], fp32, one fma per term, h ascending
+//   p[t,e,j] = sum of x[t,h] * Wr[e,h] over slice j (h = 64 j .. 64 j + 63),
+//              fp32, from +0, one fma per term, h ascending
+//   z[t,e]   = p[t,e,0] + p[t,e,1] + ..., fp32, from +0, j ascending
+//              (TensorFold issue #548: the router's K slices, fixed by H
+//              alone, are added by the top-k; the width is not given, 64 is
+//              this library's)
 //   s[t,e]   = 1 / (1 + e^-z)           (own exp, correctly rounded division)
 //   key[t,e] = s[t,e] + bias[e]          (the bias only selects)
 //   ids[t,:] = k experts by key, best first; ties to the lower index; NaN last
 //   w[t,j]   = s[t,ids_j] / (sum_j s[t,ids_j] + eps)
 //
-// Two launches, or one for decode-sized batches (k_route_decode).
+// Two launches: the logits, then the top-k (which for decode-sized batches
+// also adds the slices, k_route_fold).
 //
-// k_logits computes z = x Wr^T as T*E independent fma chains of length H,
-// each in h order (see the kernel for the layout). The chains are what
-// bound it: at the prefill shapes they fill the chip's fp32 lanes, at a
-// decode step they are latency-bound, and k_logits_few takes that case.
+// k_logits computes z = x Wr^T as T*E*(H/64) independent fma chains of
+// length 64, each in h order, and adds each (t, e)'s slices in order (see the
+// kernel for the layout). The chains are what bound it: at the prefill
+// shapes they fill the chip's fp32 lanes, at a decode step they are
+// latency-bound, and k_logits_few takes that case.
 //
 // k_topk reads z, applies the sigmoid and the bias, and picks the top k of
 // each token with k rounds of a 64-bit (order key, ~index) max over the
@@ -39,8 +46,8 @@ constexpr int kMaxThreads = 256;
 // reads the same address: one broadcast per 4 h and expert). The next
 // chunk's global loads are issued before the current chunk's fmas and
 // written to the other LDS buffer after them; within a chunk the LDS reads
-// of the next 16 h are issued before the fmas of the current 16. Every
-// chain runs in h order, so z is bit-identical to a plain loop over h.
+// of the next 16 h are issued before the fmas of the current 16. Each slice
+// of 64 h is one chain in h order, added to z when it ends.
 constexpr int kTok = 64;                 // tokens per workgroup (one per lane)
 constexpr int kHC = 256;                 // h per LDS chunk
 constexpr int kXRow = kHC / 4 + 1;       // float4 per staged token row (+ pad)
@@ -105,10 +112,20 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restri
         }
     };
 
-    float acc[C];
+    float acc[C], zc[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c)
+    for (int c = 0; c < C; ++c) {
         acc[c] = 0.0f;
+        zc[c] = 0.0f;
+    }
+    // the slice just finished goes into z, and the next one starts at +0
+    auto fold = [&]() {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            zc[c] = zc[c] + acc[c];
+            acc[c] = 0.0f;
+        }
+    };
     // 16 h: x[i] holds h 4i..4i+3 of this lane's token, w[c][i] the same h
     // of expert c
     // (the chains alternate instruction by instruction: in-order issue then
@@ -155,7 +172,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restri
                 for (int i = 0; i < 4; ++i)
                     wv[c][i] = wr[c * kWRow + 4 * g + i];
         };
-        const int groups = hc / 16;          // hc is a multiple of 64: even
+        const int groups = hc / 16;          // hc is a multiple of 64: 4 groups a slice
         read16(0, xa, wa);
         for (int g = 0; g < groups; g += 2) {
             read16(g + 1, xb, wb);
@@ -165,6 +182,8 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restri
             read16(g + 2 < groups ? g + 2 : g + 1, xa, wa);   // no branch: no copies
             __builtin_amdgcn_sched_barrier(0);
             fma16(xb, wb);
+            if ((g & 3) == 2)
+                fold();
             __builtin_amdgcn_sched_barrier(0);
         }
         hc = hc_next;
@@ -176,11 +195,11 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restri
     for (int c = 0; c < C; ++c) {
         const int e = e0 + wave * C + c;
         if (t < T && e < E)
-            z[(size_t)t * E + e] = acc[c];
+            z[(size_t)t * E + e] = zc[c];
     }
 }
 
-// k_logits_ring: the same lanes and chains as k_logits<2> (a lane per token,
+// k_logits_ring: the same lanes as k_logits<2> (a lane per token,
 // two experts per wave: 64 tokens and 8 experts per workgroup), for H a
 // multiple of 128. The operands come in by range-checked buffer loads
 // straight into a ring of 4 LDS stages of 128 h (x as bf16, the router rows
@@ -188,7 +207,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restri
 // memory once the ring is full; no registers hold staged data. A token row's
 // 16-byte pieces (8 h) sit at piece c ^ (t % 16) of its LDS row, so the 16
 // lanes of a 16-byte read hit distinct banks; the router rows are read by
-// every lane at once (broadcast). Every chain still runs in h order.
+// every lane at once (broadcast). A stage holds two slices.
 constexpr int kRingH = 128;
 constexpr int kRingStages = 4;
 constexpr int kRingX = kTok * (kRingH / 8);             // 16-byte x pieces per stage
@@ -217,30 +236,53 @@ __device__ __forceinline__ void ring_stage(const uint4 *__restrict__ S, uint4 *_
     const uint4 *xrow = S + t * (kRingH / 8);
     const float4 *wa = reinterpret_cast<const float4 *>(S + kRingX) + (2 * wave) * (kRingH / 4);
     const float4 *wb = wa + kRingH / 4;
-    // 8 h per group: one 16-byte x piece, two float4 of each router row
-    auto read = [&](int g, uint4 &xv, float4 (&av)[2], float4 (&bv)[2]) {
-        xv = xrow[g ^ (t & 15)];
-        av[0] = wa[2 * g];
-        av[1] = wa[2 * g + 1];
-        bv[0] = wb[2 * g];
-        bv[1] = wb[2 * g + 1];
-    };
-    auto fma8 = [&](const uint4 &xv, const float4 (&av)[2], const float4 (&bv)[2]) {
-        const float xs[8] = {bf16_to_f32(xv.x & 0xffffu), bf16_to_f32(xv.x >> 16),
-                             bf16_to_f32(xv.y & 0xffffu), bf16_to_f32(xv.y >> 16),
-                             bf16_to_f32(xv.z & 0xffffu), bf16_to_f32(xv.z >> 16),
-                             bf16_to_f32(xv.w & 0xffffu), bf16_to_f32(xv.w >> 16)};
-        const float as[8] = {av[0].x, av[0].y, av[0].z, av[0].w, av[1].x, av[1].y, av[1].z, av[1].w};
-        const float bs[8] = {bv[0].x, bv[0].y, bv[0].z, bv[0].w, bv[1].x, bv[1].y, bv[1].z, bv[1].w};
+    // The stage's two slices (h 0..63 and 64..127) run side by side: four
+    // chains per lane (2 experts x 2 slices). 8 h per group and slice: one
+    // 16-byte x piece, two float4 of each router row.
+    auto read = [&](int g, uint4 (&xv)[2], float4 (&av)[2][2], float4 (&bv)[2][2]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            acc0 = __builtin_fmaf(xs[i], as[i], acc0);
-            acc1 = __builtin_fmaf(xs[i], bs[i], acc1);
+        for (int j = 0; j < 2; ++j) {
+            const int q = g + 8 * j;
+            xv[j] = xrow[q ^ (t & 15)];
+            av[j][0] = wa[2 * q];
+            av[j][1] = wa[2 * q + 1];
+            bv[j][0] = wb[2 * q];
+            bv[j][1] = wb[2 * q + 1];
         }
     };
-    uint4 xa, xb;
-    float4 aa[2], ba[2], ab[2], bb[2];
-    constexpr int G = kRingH / 8;                           // 16 groups, even
+    float pa[2] = {0.0f, 0.0f}, pb[2] = {0.0f, 0.0f};
+    auto fma8 = [&](const uint4 (&xv)[2], const float4 (&av)[2][2], const float4 (&bv)[2][2]) {
+        float xs[2][8], as[2][8], bs[2][8];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint4 v = xv[j];
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xs[j][2 * i] = bf16_to_f32(u[i] & 0xffffu);
+                xs[j][2 * i + 1] = bf16_to_f32(u[i] >> 16);
+            }
+            const float4 a0 = av[j][0], a1 = av[j][1], b0 = bv[j][0], b1 = bv[j][1];
+            const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+            const float bl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                as[j][i] = al[i];
+                bs[j][i] = bl[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                pa[j] = __builtin_fmaf(xs[j][i], as[j][i], pa[j]);
+                pb[j] = __builtin_fmaf(xs[j][i], bs[j][i], pb[j]);
+            }
+        }
+    };
+    uint4 xa[2], xb[2];
+    float4 aa[2][2], ba[2][2], ab[2][2], bb[2][2];
+    constexpr int G = kRingH / 16;                          // 8 groups per slice, even
     read(0, xa, aa, ba);
 #pragma unroll
     for (int g = 0; g < G; g += 2) {
@@ -248,12 +290,15 @@ __device__ __forceinline__ void ring_stage(const uint4 *__restrict__ S, uint4 *_
         __builtin_amdgcn_sched_barrier(0);
         fma8(xa, aa, ba);
         __builtin_amdgcn_sched_barrier(0);
-        if (g + 2 < G)
-            read(g + 2, xa, aa, ba);
+        read(g + 2 < G ? g + 2 : G - 1, xa, aa, ba);       // no branch: no copies
         __builtin_amdgcn_sched_barrier(0);
         fma8(xb, ab, bb);
         __builtin_amdgcn_sched_barrier(0);
     }
+    acc0 = acc0 + pa[0];
+    acc0 = acc0 + pa[1];
+    acc1 = acc1 + pb[0];
+    acc1 = acc1 + pb[1];
 }
 
 __global__ __launch_bounds__(kMaxThreads) void k_logits_ring(const uint16_t *__restrict__ x,
@@ -317,7 +362,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits_ring(const uint16_t *__r
 }
 
 // k_logits_few: decode-sized batches (T <= 8, H <= 2048). The chains are
-// the whole cost there (H dependent fmas each), so the point is to start
+// the whole cost there (H dependent fmas each, 64 at a time), so the point is to start
 // them early and never stall them: a workgroup owns 8 experts and every
 // token, requests all of its rows at once (four h-quarters, in order), and
 // moves quarter q to LDS (x converted to fp32) as soon as it has landed;
@@ -373,7 +418,7 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits_few(const uint16_t *__re
     const int j = wave * 2 + ((lane >> 3) & 1);
     const float4 *xrow = xs + t * rs;
     const float4 *wrow = ws + j * rs;
-    float acc = 0.0f;
+    float acc = 0.0f, zc = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         // pieces outside the quarter go to a junk slot: the stores stay
@@ -414,22 +459,31 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits_few(const uint16_t *__re
                     acc = __builtin_fmaf(xv[i].w, wv[i].w, acc);
                 }
             };
+            // a slice (64 h) ends after a group when the group's end is a
+            // multiple of 64: its chain goes into z, the next starts at +0
+            auto fold = [&](int g) {
+                const bool end = ((c * hq + 16 * (g + 1)) & 63) == 0;
+                zc = end ? zc + acc : zc;
+                acc = end ? 0.0f : acc;
+            };
             const int groups = n / 4;                   // even: hq is a multiple of 32
             read(0, xa, wa);
             for (int g = 0; g < groups; g += 2) {
                 read(g + 1, xb, wb);
                 __builtin_amdgcn_sched_barrier(0);
                 fma16(xa, wa);
+                fold(g);
                 __builtin_amdgcn_sched_barrier(0);
                 read(g + 2 < groups ? g + 2 : g + 1, xa, wa);
                 __builtin_amdgcn_sched_barrier(0);
                 fma16(xb, wb);
+                fold(g + 1);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
     if (lane < 16 && t < T && e0 + j < E)
-        z[(size_t)t * E + e0 + j] = acc;
+        z[(size_t)t * E + e0 + j] = zc;
 }
 
 // LDS ints the fused plan of topk_block works in.
@@ -437,8 +491,9 @@ constexpr int kTopkLds = 2 * kFusedPlanMaxA + 2 * 256 + kMaxThreads / kWave;
 
 // The top-k, the weights and (plan.counts given) the fused plan of the
 // tokens of this workgroup, from z (global memory or LDS), with kTopkLds
-// ints of LDS at lds. Every thread of the workgroup calls it.
-template <int RE>
+// ints of LDS at lds. Every thread of the workgroup calls it. RE experts
+// per lane; with one, LPT <= MAXL.
+template <int RE, int MAXL = 64>
 __device__ __forceinline__ void topk_block(const float *z, const float *__restrict__ bias, int T,
                                            int E, int k, int LPT, int norm_topk, float eps,
                                            int32_t *__restrict__ ids, float *__restrict__ weights,
@@ -465,49 +520,87 @@ __device__ __forceinline__ void topk_block(const float *z, const float *__restri
         const float key = s[r] + (bias != nullptr && real ? bias[e] : 0.0f);
         cand[r] = real ? (((uint64_t)order_key(key) << 32) | (uint32_t)(0xffffu - e)) : 0ull;
     }
-    int pick_e[8];
-    float pick_s[8];
+    if constexpr (RE == 1) {
+        // One expert per lane: each lane ranks its candidate among its
+        // token's (every lane of the token reads the token's LPT candidates
+        // from LDS; the count of larger ones is the rank), and the lane of
+        // rank j < k is pick j. No cross-lane shuffles on the way. The
+        // candidates use the LDS of the plan's counts and offsets, the picked
+        // scores that of its ranks: both are written again only after the
+        // plan's first barrier.
+        uint64_t *c64 = reinterpret_cast<uint64_t *>(s_cnt);
+        float *pick_s = reinterpret_cast<float *>(s_rank);
+        c64[tid] = cand[0];
+        __syncthreads();
+        const uint64_t *row = c64 + tb * LPT;
+        int rank = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        pick_e[j] = 0;
-        pick_s[j] = 0.0f;
-        if (j < k) {
-            uint64_t best = 0;
-#pragma unroll
-            for (int r = 0; r < RE; ++r)
-                best = cand[r] > best ? cand[r] : best;
-            for (int m = 1; m < LPT; m <<= 1) {
-                const uint64_t o = shfl_xor_u64(best, m);
-                best = o > best ? o : best;
-            }
-            const int e_win = 0xffff - (int)(best & 0xffffu);
-            // the owning lane supplies the unbiased score and retires the pick
-            float mine = 0.0f;
-#pragma unroll
-            for (int r = 0; r < RE; ++r) {
-                if (eg + r * LPT == e_win) {
-                    mine = s[r];
-                    cand[r] = 0ull;
-                }
-            }
-            pick_e[j] = e_win;
-            pick_s[j] = __shfl(mine, (lane & ~(LPT - 1)) + e_win % LPT, kWave);
+        for (int i = 0; i < MAXL; i += 2) {
+            // past LPT: a valid entry again, not counted (no branch)
+            const ulonglong2 v = *reinterpret_cast<const ulonglong2 *>(row + (i & (LPT - 1)));
+            rank += i < LPT ? (v.x > cand[0]) + (v.y > cand[0]) : 0;
         }
-    }
-    if (eg == 0 && t < T) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            if (j < k)
-                sum += pick_s[j];
-        const float denom = sum + eps;
+        const int e = eg;
+        const bool pick = t < T && e < E && rank < k;
+        if (pick) {
+            ids[(size_t)t * k + rank] = e;
+            pick_s[tb * k + rank] = s[0];
+            if (plan.counts != nullptr)
+                s_ids[tb * k + rank] = e;
+        }
+        __syncthreads();
+        if (pick) {
+            float sum = 0.0f;
+            for (int j = 0; j < k; ++j)
+                sum += pick_s[tb * k + j];
+            const float denom = sum + eps;
+            weights[(size_t)t * k + rank] = norm_topk ? s[0] / denom : s[0];
+        }
+    } else {
+        int pick_e[8];
+        float pick_s[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+            pick_e[j] = 0;
+            pick_s[j] = 0.0f;
             if (j < k) {
-                ids[(size_t)t * k + j] = pick_e[j];
-                weights[(size_t)t * k + j] = norm_topk ? pick_s[j] / denom : pick_s[j];
-                if (plan.counts != nullptr)
-                    s_ids[tb * k + j] = pick_e[j];
+                uint64_t best = 0;
+#pragma unroll
+                for (int r = 0; r < RE; ++r)
+                    best = cand[r] > best ? cand[r] : best;
+                for (int m = 1; m < LPT; m <<= 1) {
+                    const uint64_t o = shfl_xor_u64(best, m);
+                    best = o > best ? o : best;
+                }
+                const int e_win = 0xffff - (int)(best & 0xffffu);
+                // the owning lane supplies the unbiased score and retires the pick
+                float mine = 0.0f;
+#pragma unroll
+                for (int r = 0; r < RE; ++r) {
+                    if (eg + r * LPT == e_win) {
+                        mine = s[r];
+                        cand[r] = 0ull;
+                    }
+                }
+                pick_e[j] = e_win;
+                pick_s[j] = __shfl(mine, (lane & ~(LPT - 1)) + e_win % LPT, kWave);
+            }
+        }
+        if (eg == 0 && t < T) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < k)
+                    sum += pick_s[j];
+            const float denom = sum + eps;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < k) {
+                    ids[(size_t)t * k + j] = pick_e[j];
+                    weights[(size_t)t * k + j] = norm_topk ? pick_s[j] / denom : pick_s[j];
+                    if (plan.counts != nullptr)
+                        s_ids[tb * k + j] = pick_e[j];
+                }
             }
         }
     }
@@ -571,148 +664,145 @@ __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ 
     topk_block<RE>(z, bias, T, E, k, LPT, norm_topk, eps, ids, weights, plan, lds);
 }
 
-// k_route_decode: the whole router of a decode-sized batch (T <= 8,
-// E <= 32, H a multiple of 128, H <= 2048) in one workgroup: the logits,
-// then the top-k, the weights and the plan, with z kept in LDS. Lane l of
-// wave w runs the chain of token l % 8 and expert 8 w + l / 8 (one chain per
-// lane: the chain latency, H dependent fmas, is the floor of this step, so
-// the loop carries nothing but the fmas and their LDS reads). The token
-// rows are converted to fp32 into LDS once, at the start (rows padded by 16
-// bytes: the 8 rows a read touches fall in distinct banks); the router rows
-// stream through a ring of 5 LDS stages of 128 h, requested four stages
-// ahead by range-checked buffer loads, pieces at swizzled slots (router row
-// e: piece c ^ 2 (e % 8)).
+// The router of a decode-sized batch (T <= 8, E <= 32) in two launches.
+// There are only T*E <= 256 logits, so one workgroup cannot keep many chains
+// in flight, and every operand it reads from LDS feeds a single fma. The
+// slices make the work split across the chip instead: k_logits_part gives
+// each workgroup kPartSlices slices of every (t, e), loaded straight into
+// registers (no LDS: lane l of wave w takes token l % 8 and expert
+// 8 w + l / 8, and reads its own 256 bytes of router row and 128 bytes of
+// token row per slice), and writes the partials p[j][t][e]. Then
+// k_route_fold, one workgroup, adds each (t, e)'s partials in slice order
+// into z (in LDS) and runs the top-k, the weights and the plan on it.
 constexpr int kDecT = 8;
 constexpr int kDecE = 32;
-constexpr int kDecMaxH = 2048;
-constexpr int kDecXRow = kDecMaxH / 4 + 1;              // float4 per token row (+ pad)
-constexpr int kDecX = kDecT * kDecXRow;                 // 65.6 KB
-constexpr int kDecW = kDecE * (kRingH / 4);             // 1024 router pieces per stage (16 KB)
-constexpr int kDecStages = 5;
-constexpr int kDecAhead = kDecStages - 1;
+constexpr uint32_t kDecPast = 0x80000000u;             // an offset that reads zeros
 
-// One stage: the chain over W's 128 h (x from X at float4 column c0), and the
-// refill of stage F with h block sf. One call site, so the LDS reads and the
-// loads into F share one alias scope.
-__device__ __forceinline__ void dec_stage(const float4 *__restrict__ X,
-                                          const uint4 *__restrict__ W, uint4 *__restrict__ F,
-                                          const float *Wr, const uint32_t (&woff)[4], int sf,
-                                          int c0, bool compute, float &acc) {
+// (one workgroup per CU: the registers go to the loads in flight). SP
+// slices per workgroup.
+template <int SP>
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+k_logits_part(const uint16_t *__restrict__ x,
+                                                             const float *__restrict__ Wr, int T,
+                                                             int H, int E,
+                                                             float *__restrict__ part) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-        buffer_to_lds16(Wr, F + (q * 4 + wave) * kWave, woff[q] + sf * (kRingH * 4));
-    if (!compute)
-        return;
+    const int wave = threadIdx.x / kWave;
     const int t = lane & 7;
     const int e = wave * 8 + (lane >> 3);
-    const float4 *xrow = X + t * kDecXRow + c0;
-    const float4 *wrow = reinterpret_cast<const float4 *>(W) + e * (kRingH / 4);
-    const int wsw = 2 * (e & 7);
-    auto fma4 = [&](const float4 &xv, const float4 &wv) {
-        acc = __builtin_fmaf(xv.x, wv.x, acc);
-        acc = __builtin_fmaf(xv.y, wv.y, acc);
-        acc = __builtin_fmaf(xv.z, wv.z, acc);
-        acc = __builtin_fmaf(xv.w, wv.w, acc);
-    };
-    // 4 h per group; the reads run two groups ahead of the fmas
-    constexpr int G = kRingH / 4;                           // 32 groups
-    float4 xv[3], wv[3];
+    const int S = H / 64;
+    const int j0 = SP * blockIdx.x;
+    const __amdgpu_buffer_rsrc_t xrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, 0x7fffffff, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t wrsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)Wr, (short)0, 0x7fffffff, kBufferWord3);
+    // every load issued at once; rows past T or E and a slice past the end
+    // read zeros
+    uint4 xv[SP][8];
+    float4 wv[SP][16];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        xv[g] = xrow[g];
-        wv[g] = wrow[g ^ wsw];
-    }
+    for (int j = 0; j < SP; ++j) {
+        const int h0 = (j0 + j) * 64;
+        const bool in = j0 + j < S;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        if (g + 2 < G) {
-            xv[(g + 2) % 3] = xrow[g + 2];
-            wv[(g + 2) % 3] = wrow[(g + 2) ^ wsw];
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t off =
+                (in && t < T) ? ((uint32_t)t * (uint32_t)H + (uint32_t)(h0 + 8 * i)) * 2u : kDecPast;
+            xv[j][i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
         }
-        __builtin_amdgcn_sched_barrier(0);
-        fma4(xv[g % 3], wv[g % 3]);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t off =
+                (in && e < E) ? ((uint32_t)e * (uint32_t)H + (uint32_t)(h0 + 4 * i)) * 4u : kDecPast;
+            wv[j][i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, off, 0, 0));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);                  // every request before any wait
+    // the slices' chains side by side, h ascending in each
+    float p[SP];
+#pragma unroll
+    for (int j = 0; j < SP; ++j)
+        p[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float xs[SP][8], ws[SP][8];
+#pragma unroll
+        for (int j = 0; j < SP; ++j) {
+            const uint4 v = xv[j][i];
+            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                xs[j][2 * q] = bf16_to_f32(u[q] & 0xffffu);
+                xs[j][2 * q + 1] = bf16_to_f32(u[q] >> 16);
+            }
+            const float4 a = wv[j][2 * i], b = wv[j][2 * i + 1];
+            const float w8[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                ws[j][q] = w8[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+#pragma unroll
+            for (int j = 0; j < SP; ++j)
+                p[j] = __builtin_fmaf(xs[j][q], ws[j][q], p[j]);
+        }
+    }
+    if (t < T && e < E) {
+#pragma unroll
+        for (int j = 0; j < SP; ++j)
+            if (j0 + j < S)
+                part[((size_t)(j0 + j) * T + t) * E + e] = p[j];
     }
 }
 
-__global__ __launch_bounds__(kMaxThreads) void k_route_decode(
-    const uint16_t *__restrict__ x, const float *__restrict__ Wr, const float *__restrict__ bias,
-    int T, int H, int E, int k, int LPT, int norm_topk, float eps, int32_t *__restrict__ ids,
-    float *__restrict__ weights, PlanOut plan) {
-    // one LDS object: the fp32 token rows, then the ring; reused after the
-    // logits for z and the top-k's work space (a second LDS object would make
-    // the compiler wait for every load into the ring before any read of it)
-    __shared__ uint4 lds[kDecX + kDecStages * kDecW];   // 146 KB
-    float4 *X = reinterpret_cast<float4 *>(lds);
-    uint4 *ring = lds + kDecX;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int S = H / kRingH;
-    // the token rows: 8 pieces of 8 bf16 per thread, in registers first,
-    // by range-checked loads issued together (pieces past T or H read zeros)
-    constexpr int kXPieces = kDecT * (kDecMaxH / 8) / kMaxThreads;
-    const __amdgpu_buffer_rsrc_t xrsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)x, (short)0, 0x7fffffff, kBufferWord3);
-    uint4 xr[kXPieces];
-#pragma unroll
-    for (int i = 0; i < kXPieces; ++i) {
-        const int pos = i * kMaxThreads + tid;
-        const int r = pos / (kDecMaxH / 8), c = pos % (kDecMaxH / 8);
-        const uint32_t off = (r < T && 8 * c < H) ? ((uint32_t)r * (uint32_t)H + 8u * c) * 2u : kRingPast;
-        xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrsrc, off, 0, 0));
-    }
-    // byte offsets of this thread's router pieces in h block 0; rows past E
-    // read zeros
-    uint32_t woff[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int pos = (q * 4 + wave) * kWave + lane;
-        const int j = pos / (kRingH / 4), c = (pos % (kRingH / 4)) ^ (2 * (j & 7));
-        woff[q] = j < E ? ((uint32_t)j * (uint32_t)H + 4u * c) * 4u : kRingPast;
-    }
-    float acc = 0.0f;
-    // Iterations -4 .. -1 only request h blocks 0 .. 3; every request comes
-    // from the one call site below, in one alias scope. 4 requests per
-    // iteration and wave (past the end the last h block again, into the
-    // slot read in the previous iteration): stage s is in once at most the
-    // 12 requests after it are in flight.
-    for (int s = -kDecAhead; s < S; ++s) {
-        wait_vmcnt<4 * (kDecAhead - 1)>();
-        __builtin_amdgcn_s_barrier();       // also: the token rows are in LDS
-        const int sc = s < 0 ? 0 : s;
-        dec_stage(X, ring + (sc % kDecStages) * kDecW, ring + ((s + kDecAhead) % kDecStages) * kDecW,
-                  Wr, woff, s + kDecAhead < S ? s + kDecAhead : S - 1, sc * (kRingH / 4), s >= 0,
-                  acc);
-        if (s == -1) {
-            // the token rows to fp32, once the first router blocks are on
-            // their way (visible after the next barrier)
-#pragma unroll
-            for (int i = 0; i < kXPieces; ++i) {
-                const int pos = i * kMaxThreads + tid;
-                const int r = pos / (kDecMaxH / 8), c = pos % (kDecMaxH / 8);
-                const uint4 v = xr[i];
-                float4 *d = X + r * kDecXRow + 2 * c;
-                d[0] = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
-                                   bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16));
-                d[1] = make_float4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16),
-                                   bf16_to_f32(v.w & 0xffffu), bf16_to_f32(v.w >> 16));
-            }
-        }
-    }
-    wait_vmcnt<0>();                        // the last requests land before the LDS is reused
-    __syncthreads();                        // and every wave is past its reads
+constexpr int kPartSlices = 1;                          // slices per k_logits_part workgroup
+
+constexpr int kFoldBatch = 32;                          // partial loads in flight per lane
+
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
+k_route_fold(
+    const float *__restrict__ part, const float *__restrict__ bias, int T, int H, int E, int k,
+    int LPT, int norm_topk, float eps, int32_t *__restrict__ ids, float *__restrict__ weights,
+    PlanOut plan) {
+    __shared__ int lds[kDecT * kDecE + kDecE + kTopkLds];
     float *zs = reinterpret_cast<float *>(lds);
-    {
-        const int t = lane & 7;
-        const int e = wave * 8 + (lane >> 3);
-        if (t < T && e < E)
-            zs[t * E + e] = acc;
+    float *bs = zs + kDecT * kDecE;                     // the bias, read with the partials
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int t = lane & 7;
+    const int e = wave * 8 + (lane >> 3);
+    const int S = H / 64;
+    const bool real = t < T && e < E;
+    const __amdgpu_buffer_rsrc_t prsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)part, (short)0, 0x7fffffff, kBufferWord3);
+    const uint32_t base = real ? (uint32_t)(t * E + e) * 4u : kDecPast;
+    const uint32_t stride = (uint32_t)(T * E) * 4u;
+    const int tid = threadIdx.x;
+    float b = 0.0f;
+    if (bias != nullptr && tid < E)
+        b = bias[tid];
+    // z = ((+0 + p_0) + p_1) + ...: a batch of loads, then its adds in order
+    float z = 0.0f;
+    for (int j0 = 0; j0 < S; j0 += kFoldBatch) {
+        float v[kFoldBatch];
+#pragma unroll
+        for (int i = 0; i < kFoldBatch; ++i) {
+            const uint32_t off = j0 + i < S && real ? base + (uint32_t)(j0 + i) * stride : kDecPast;
+            v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prsrc, off, 0, 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kFoldBatch; ++i)
+            z = j0 + i < S ? z + v[i] : z;
     }
+    if (real)
+        zs[t * E + e] = z;
+    if (tid < E)
+        bs[tid] = b;
     __syncthreads();
-    topk_block<1>(zs, bias, T, E, k, LPT, norm_topk, eps, ids, weights, plan,
-                  reinterpret_cast<int *>(lds) + kDecT * kDecE);
+    topk_block<1, kDecE>(zs, bias != nullptr ? bs : nullptr, T, E, k, LPT, norm_topk, eps, ids,
+                         weights, plan, lds + kDecT * kDecE + kDecE);
 }
 
 // Two chains per lane when that still leaves a few hundred workgroups,
@@ -726,7 +816,14 @@ void launch_logits(hipStream_t stream, const uint16_t *x, const float *Wr, int T
 
 }  // namespace
 
-size_t route_scratch_bytes(int T, int E) { return (size_t)T * E * sizeof(float); }
+// Batches of at most 8 tokens and 32 experts take the two-launch decode
+// router, whose scratch holds every slice's partial logits.
+bool decode_router(int T, int E) { return T <= kDecT && E <= kDecE; }
+
+size_t route_scratch_bytes(int T, int H, int E) {
+    const size_t slices = decode_router(T, E) ? (size_t)(H / 64) : 1;
+    return slices * T * E * sizeof(float);
+}
 
 hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, int T, int H, int E,
                         int k, int norm_topk, float eps, int32_t *ids, float *weights,
@@ -737,17 +834,24 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
         return hipSuccess;
     if (H % 64 != 0)
         return hipErrorInvalidValue;
-    if (T <= kDecT && E <= kDecE && H % kRingH == 0 && H <= kDecMaxH) {
-        // one workgroup: logits, top-k, weights and (when it fits) the plan
+    if (decode_router(T, E)) {
+        // partial logits over the chip, then one workgroup: fold, top-k,
+        // weights and (when it fits) the plan
+        const int S = H / 64;
+        hipLaunchKernelGGL(k_logits_part<kPartSlices>, dim3((S + kPartSlices - 1) / kPartSlices),
+                           dim3(kMaxThreads), 0, stream, x, Wr, T, H, E, z_scratch);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
         int LPT = 2;
         while (LPT < E)
             LPT <<= 1;
         const bool fuse = plan.counts != nullptr && T * k <= kFusedPlanMaxA;
         if (!fuse)
             plan = PlanOut{};
-        hipLaunchKernelGGL(k_route_decode, dim3(1), dim3(kMaxThreads), 0, stream, x, Wr, bias, T, H,
-                           E, k, LPT, norm_topk, eps, ids, weights, plan);
-        const hipError_t err = hipGetLastError();
+        hipLaunchKernelGGL(k_route_fold, dim3(1), dim3(kMaxThreads), 0, stream, z_scratch, bias, T,
+                           H, E, k, LPT, norm_topk, eps, ids, weights, plan);
+        err = hipGetLastError();
         if (err == hipSuccess && plan_done != nullptr)
             *plan_done = fuse;
         return err;

@@ -272,6 +272,41 @@ def _construct_special_rows(wl: Workload, out: dict) -> None:
         out["bias"][5] = out["bias"][2]
 
 
+def slice_order_inputs(T: int, H: int, E: int) -> dict:
+    """Router inputs whose top experts depend on how the logit is summed.
+
+    x[t, h] = 2^(t % 3) for every h (a power of two: every product and sum
+    below scales exactly), bias 0. Expert e's router row is zero except for
+    one pattern, chosen by e % 4 and placed at slice m_e (slices of 64 h;
+    m_e spread over H / 64 - 4 positions), with b = 2^24:
+      0: w[64m + 63] = b, w[64m + 64] = 1, w[64m + 65] = -b   (across a slice end)
+      1: w[64m + 31] = b, w[64m + 32] = 1, w[64m + 33] = -b   (inside one slice)
+      2: w[64m] = b, w[64(m+1)] = 1, w[64(m+2)] = 1, w[64(m+3)] = -b
+      3: w[5] = 0.5
+    Needs H >= 256 and H % 64 == 0. Returns x (bf16 bits), router_w, bias and
+    the pattern of each expert."""
+    assert H >= 256 and H % 64 == 0
+    b = np.float32(2.0 ** 24)
+    wr = np.zeros((E, H), np.float32)
+    n = H // 64 - 4
+    pattern = np.arange(E) % 4
+    for e in range(E):
+        m = (e * 7 + 3) % (n + 1)
+        p = pattern[e]
+        if p == 0:
+            wr[e, 64 * m + 63], wr[e, 64 * m + 64], wr[e, 64 * m + 65] = b, 1, -b
+        elif p == 1:
+            wr[e, 64 * m + 31], wr[e, 64 * m + 32], wr[e, 64 * m + 33] = b, 1, -b
+        elif p == 2:
+            wr[e, 64 * m], wr[e, 64 * (m + 1)], wr[e, 64 * (m + 2)], wr[e, 64 * (m + 3)] = b, 1, 1, -b
+        else:
+            wr[e, 5] = 0.5
+    x = np.empty((T, H), np.uint16)
+    for t in range(T):
+        x[t, :] = f32_to_bf16_bits(np.full(1, 2.0 ** (t % 3), np.float32))[0]
+    return {"x": x, "router_w": wr, "bias": np.zeros(E, np.float32), "pattern": pattern}
+
+
 def by_name(name: str) -> Workload:
     for w in CONFIGS:
         if w.name == name:

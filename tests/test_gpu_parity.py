@@ -112,6 +112,40 @@ ROUTE_DECODE = {
 }
 
 
+# Router rows whose top experts change with the logit's summation order
+# (slices of 64 h, each an ascending fma chain, added in ascending order):
+# a wrong slice width, one chain over all h, or the slices added in another
+# order moves some expert's logit by 1 or 2 and changes the picks. One shape
+# per router path: the one-workgroup decode router, the 8-experts decode
+# logits, the LDS-ring logits and the register-staged logits (C = 1 and 2).
+SLICE_ORDER = {
+    "decode_t8_h2048_e32": (8, 2048, 32),
+    "decode_t1_h256_e32": (1, 256, 32),
+    "few_t8_h2048_e64": (8, 2048, 64),
+    "ring_t4096_h2048_e32": (4096, 2048, 32),
+    "logits1_t100_h2048_e32": (100, 2048, 32),
+    "logits1_t8_h2176_e32": (8, 2176, 32),
+    "logits2_t3000_h576_e32": (3000, 576, 32),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SLICE_ORDER))
+def test_route_slice_order(case):
+    T, H, E = SLICE_ORDER[case]
+    k = 8
+    inp = W.slice_order_inputs(T, H, E)
+    x = lib.x_to_device(inp["x"])
+    wr = torch.from_numpy(inp["router_w"]).to(DEV)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    ids, w = lib.route(x, wr, b, k, 1, 1e-6)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route(inp["x"], inp["router_w"], inp["bias"], k, 1, 1e-6)
+    # the picks the pins fix by hand: the experts of pattern 0 (logit 1) first
+    first = np.nonzero(inp["pattern"] == 0)[0][:k]
+    assert (ids_ref[:, :first.size] == first).all()
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref)
+
+
 @pytest.mark.parametrize("case", sorted(ROUTE_DECODE))
 def test_route_decode_sized(case):
     wl = W.Workload("route_" + case, I=64, seed=300 + sorted(ROUTE_DECODE).index(case),
@@ -268,6 +302,26 @@ def test_decode_sized_batches(name, T):
     out32, _, _, _ = run_forward(wlT, inpT, torch.float32)
     check_out(out32, ref, tol_for(wl))
     assert (W.f32_to_bf16_bits(out32) == W.f32_to_bf16_bits(out)).all()
+
+
+def test_decode_sized_calls_reuse_one_workspace():
+    # Decode-sized calls of 6, 3 and 6 tokens on one workspace (poisoned
+    # before the first): nothing a call needs may be left over from the one
+    # before. relu^2 experts, routed scale 2.5, fp32 and bf16 outputs.
+    wl = W.Workload("fused_combine", T=6, H=384, I=192, E=16, k=2, seed=210, act="relu2",
+                    rsf=2.5)
+    inp = W.generate(wl)
+    block = lib.block_from_arrays(wl, inp)
+    ws = poisoned((lib.workspace_bytes(block.dims(6, torch.float32)),), torch.uint8)
+    for T, dt in ((6, torch.float32), (3, torch.bfloat16), (6, torch.bfloat16)):
+        wlT = wl.with_(T=T)
+        inpT = dict(inp)
+        inpT["x"] = np.ascontiguousarray(inp["x"][:T])
+        out = poisoned((T, wl.H), dt)
+        block.forward(lib.x_to_device(inpT["x"]), out_dtype=dt, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.forward_tokens(wlT, inpT, np.arange(T))
+        check_out(to_np(out), ref, tol_for(wl))
 
 
 # ------------------------------------------------------------------ edges

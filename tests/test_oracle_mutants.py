@@ -51,15 +51,28 @@ MUTANTS = {
         "1.0f / (1.0f + oracle_exp32(-z))", "1.0f / (1.0f + oracle_exp32(z))",
         ["tests/test_oracle_router.py::test_sigmoid32_closed_form_ln3"]),
     "logit_order_reversed": (
-        "    for (int h = 0; h < H; ++h)\n        acc = fmaf",
-        "    for (int h = H - 1; h >= 0; --h)\n        acc = fmaf",
+        "        for (int h = h0; h < h1; ++h)\n            p = fmaf",
+        "        for (int h = h1 - 1; h >= h0; --h)\n            p = fmaf",
         ["tests/test_oracle_router.py::test_logit_order_is_sequential_fp32_fma"]),
     "logit_in_double": (
-        ("    float acc = 0.0f;\n    for (int h = 0; h < H; ++h)",
-         "acc = fmaf(bf16_value(x_row[h]), w_row[h], acc);"),
-        ("    double acc = 0.0;\n    for (int h = 0; h < H; ++h)",
-         "acc += (double)bf16_value(x_row[h]) * (double)w_row[h];"),
+        ("        float p = 0.0f;\n        for (int h = h0; h < h1; ++h)",
+         "p = fmaf(bf16_value(x_row[h]), w_row[h], p);"),
+        ("        double p = 0.0;\n        for (int h = h0; h < h1; ++h)",
+         "p += (double)bf16_value(x_row[h]) * (double)w_row[h];"),
         ["tests/test_oracle_router.py::test_logit_order_is_sequential_fp32_fma"]),
+    "logit_slice_width_32": (
+        "#define ROUTER_SLICE 64", "#define ROUTER_SLICE 32",
+        ["tests/test_oracle_router.py::test_logit_slices_and_their_sum_order"]),
+    "logit_slice_width_128": (
+        "#define ROUTER_SLICE 64", "#define ROUTER_SLICE 128",
+        ["tests/test_oracle_router.py::test_logit_slices_and_their_sum_order"]),
+    "logit_one_chain": (
+        "        float p = 0.0f;\n", "        float p = z;\n        z = 0.0f;\n",
+        ["tests/test_oracle_router.py::test_logit_slices_and_their_sum_order"]),
+    "logit_slices_summed_backwards": (
+        "for (int h0 = 0; h0 < H; h0 += ROUTER_SLICE) {",
+        "for (int h0 = (H - 1) / ROUTER_SLICE * ROUTER_SLICE; h0 >= 0; h0 -= ROUTER_SLICE) {",
+        ["tests/test_oracle_router.py::test_logit_slices_and_their_sum_order"]),
     "router_weight_transposed": (
         "z[e] = router_logit(x_row, Wr + (size_t)e * H, H);",
         "z[e] = router_logit(x_row, Wr + (size_t)e, H);",

@@ -85,14 +85,56 @@ def _one_token(x_vals, w_rows, bias=None, k=1):
 
 
 def test_logit_order_is_sequential_fp32_fma():
-    # x = [1, 1, 1, 1], w = [1, 2^24, 1, -2^24]. Exact sum 2; fp32 pairwise
-    # sum 1; fp32 reverse order 2; fp32 ascending fma chain: 1 -> 2^24 + 1
-    # rounds to 2^24 (tie to even) -> again 2^24 -> 0. Only the ascending
-    # fp32 chain gives 0.
+    # Within one slice (H = 4 < 64): x = [1, 1, 1, 1], w = [1, 2^24, 1,
+    # -2^24]. Exact sum 2; fp32 pairwise sum 1; fp32 reverse order 2; fp32
+    # ascending fma chain: 1 -> 2^24 + 1 rounds to 2^24 (tie to even) ->
+    # again 2^24 -> 0. Only the ascending fp32 chain gives 0.
     big = 2.0 ** 24
     ids, w, z, s = _one_token([1, 1, 1, 1], [[1, big, 1, -big]])
     assert z[0, 0] == 0.0
     assert s[0, 0] == 0.5
+
+
+def test_logit_slices_and_their_sum_order():
+    # TensorFold issue #548: the router's K slices are summed by the top-k,
+    # slice bounds from H alone. Reading: slices of 64 h, each an ascending
+    # fp32 fma chain from +0, partials added in ascending slice order. x = 1,
+    # H = 256; each router row isolates one part of that reading (2^24 + 1
+    # rounds back to 2^24, so the cancellations below depend on the grouping).
+    big = 2.0 ** 24
+    rows = np.zeros((3, 256), np.float64)
+    # row 0: w[31] = 2^24, w[32] = 1, w[33] = -2^24 in one 64-slice: the
+    # chain cancels to 0 (slices of 32 would give 2^24 + (1 - 2^24) = 1)
+    rows[0, 31], rows[0, 32], rows[0, 33] = big, 1.0, -big
+    # row 1: w[63] = 2^24 | w[64] = 1, w[65] = -2^24 across the boundary:
+    # 2^24 + (1 - 2^24) = 1 (one chain over 128 h, or over all H, gives 0)
+    rows[1, 63], rows[1, 64], rows[1, 65] = big, 1.0, -big
+    # row 2: slice partials 2^24, 1, 1, -2^24: ascending sum 0; descending
+    # sum 2; pairwise (2^24 + 1) + (1 - 2^24) = 1
+    rows[2, 0], rows[2, 64], rows[2, 128], rows[2, 192] = big, 1.0, 1.0, -big
+    ids, w, z, s = _one_token([1.0] * 256, rows, k=2)
+    assert z[0].tolist() == [0.0, 1.0, 0.0]
+
+
+def slice_order_expected(inp, k):
+    """Logits and top-k of slice_order_inputs, worked out by hand: pattern 0
+    sums to 1 (2^24 + (1 - 2^24)), patterns 1 and 2 to 0 (2^24 + 1 rounds
+    to 2^24), pattern 3 to 0.5; all scaled by the token's power of two."""
+    T = inp["x"].shape[0]
+    per_pattern = np.array([1.0, 0.0, 0.0, 0.5])
+    z = np.stack([per_pattern[inp["pattern"]] * 2.0 ** (t % 3) for t in range(T)])
+    E = z.shape[1]
+    ids = np.array([sorted(range(E), key=lambda e: (-z[t, e], e))[:k] for t in range(T)])
+    return z.astype(np.float32), ids
+
+
+@pytest.mark.parametrize("H", [256, 576, 2048])
+def test_logit_slices_on_constructed_rows(H):
+    inp = W.slice_order_inputs(6, H, 32)
+    ids, w, z, s = oracle.route(inp["x"], inp["router_w"], inp["bias"], 8, want_scores=True)
+    z_hand, ids_hand = slice_order_expected(inp, 8)
+    assert (z == z_hand).all()
+    assert (ids == ids_hand).all()
 
 
 def test_logit_zero_row_and_one_hot_row():
