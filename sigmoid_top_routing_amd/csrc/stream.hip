@@ -101,26 +101,34 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
     // blockIdx.y names the expert among those with rows (in expert order),
     // so the workgroups in flight stream neighbouring rows of one or two
     // experts and none is spent on an empty one
-    int e = 0;
+    // (the segment's bounds come from the lane that tested the expert, so
+    // the weight requests wait for one round of loads, not three)
+    int e = 0, seg0 = 0, seg1 = p.rows;
     if (p.offsets != nullptr) {
         e = -1;
         int want = blockIdx.y;
         for (int base = 0; base < p.E && e < 0; base += kWave) {
             const int x = base + lane;
-            const bool busy = x < p.E && p.offsets[x + 1] > p.offsets[x];
+            const int lo = x < p.E ? p.offsets[x] : 0;
+            const int hi = x < p.E ? p.offsets[x + 1] : 0;
+            const bool busy = hi > lo;
             const uint64_t m = __ballot(busy);
             const int below = __popcll(m & ((1ull << lane) - 1ull));
             const uint64_t hit = __ballot(busy && below == want);
-            if (hit != 0)
-                e = base + __ffsll((unsigned long long)hit) - 1;
+            if (hit != 0) {
+                const int src = __ffsll((unsigned long long)hit) - 1;
+                e = base + src;
+                seg0 = __shfl(lo, src, kWave);
+                seg1 = __shfl(hi, src, kWave);
+            }
             want -= __popcll(m);
         }
         e = __builtin_amdgcn_readfirstlane(e);
         if (e < 0)
             return;                                // uniform
+        seg0 = __builtin_amdgcn_readfirstlane(seg0);
+        seg1 = __builtin_amdgcn_readfirstlane(seg1);
     }
-    const int seg0 = p.offsets != nullptr ? p.offsets[e] : 0;
-    const int seg1 = p.offsets != nullptr ? p.offsets[e + 1] : p.rows;
     if (seg0 >= seg1)
         return;                                    // uniform
     const int units = MODE == kGateUp ? p.I : p.N;
