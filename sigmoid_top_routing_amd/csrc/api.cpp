@@ -355,9 +355,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     down.N = H;
     down.K = I;
     down.I = I;
-    down.C = y;
+    down.C = y;                        // rows in segment order: the combine gathers them
     down.ldc = H;
-    down.scatter = sorted;
     LAUNCH(run(down));
     LAUNCH(mark(4));
 
@@ -397,7 +396,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         shared = ys;
     }
     LAUNCH(mark(5));
-    LAUNCH(moe::launch_combine(y, wts, shared, T, H, k, d->routed_scale, out,
+    LAUNCH(moe::launch_combine(y, slot, wts, shared, T, H, k, d->routed_scale, out,
                                d->out_dtype == MOE_OUT_F32, stream));
     LAUNCH(mark(6));
     return ok();

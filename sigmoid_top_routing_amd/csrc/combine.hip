@@ -1,6 +1,6 @@
 // combine.hip -- weighted combine back to token order plus the shared expert.
 //
-//   acc = 0; acc = fma(w[t,j], y[t*k+j, h], acc) for j = 0..k-1 (ascending)
+//   acc = 0; acc = fma(w[t,j], y[slot_of[t*k+j], h], acc) for j = 0..k-1 (ascending)
 //   acc = acc * routed_scale          (the routed sum is scaled once, here)
 //   acc = acc + shared[t, h]          (the shared expert is added unscaled)
 //   out[t, h] = round(acc)            (bf16 nearest-even, or fp32 as is)
@@ -10,8 +10,11 @@
 // ("Weight layout and routing"): the routed scaling factor comes after the
 // normalised weights.
 //
-// Each thread produces 8 consecutive outputs of one token: k 32-byte reads
-// of y and one 16-byte (bf16) or 32-byte (fp32) store, all coalesced.
+// y holds the down projection's rows in segment order (assignment a at row
+// slot_of[a], the plan's position), so the expert kernels write whole rows
+// where their tiles are and the combine gathers a token's k rows. Each
+// thread produces 8 consecutive outputs of one token: k 32-byte reads of y
+// and one 16-byte (bf16) or 32-byte (fp32) store, all coalesced.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -24,6 +27,7 @@ namespace {
 constexpr int kThreads = 256;
 
 __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ y,
+                                                      const int32_t *__restrict__ slot,
                                                       const float *__restrict__ w,
                                                       const float *__restrict__ shared, int T,
                                                       int H, int k, float rsf, void *out,
@@ -40,7 +44,8 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ 
         acc[c] = 0.0f;
     for (int j = 0; j < k; ++j) {
         const float wj = w[(size_t)t * k + j];
-        const float4 *yp = reinterpret_cast<const float4 *>(y + ((size_t)t * k + j) * H + h0);
+        const int row = slot[(size_t)t * k + j];
+        const float4 *yp = reinterpret_cast<const float4 *>(y + (size_t)row * H + h0);
         const float4 a = yp[0], b = yp[1];
         const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -71,15 +76,15 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(const float *y_slot, const float *weights, const float *shared, int T,
-                          int H, int k, float routed_scale, void *out, int out_f32,
-                          hipStream_t stream) {
+hipError_t launch_combine(const float *y_seg, const int32_t *slot_of, const float *weights,
+                          const float *shared, int T, int H, int k, float routed_scale, void *out,
+                          int out_f32, hipStream_t stream) {
     const size_t n = (size_t)T * (H / 8);
     if (n == 0)
         return hipSuccess;
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(k_combine, grid, dim3(kThreads), 0, stream, y_slot, weights, shared, T, H,
-                       k, routed_scale, out, out_f32);
+    hipLaunchKernelGGL(k_combine, grid, dim3(kThreads), 0, stream, y_seg, slot_of, weights, shared,
+                       T, H, k, routed_scale, out, out_f32);
     return hipGetLastError();
 }
 

@@ -3,7 +3,8 @@
 // The same products as the staged kernel in gemm.hip,
 //   C[p, n] = sum_k A[row(p), k] * B[e(p), n, k]   (fp32 accumulate),
 // with the same fused epilogues (silu(g) * u for the gated up projection,
-// relu^2 for the non-gated one, fp32 scatter for the down projection), laid
+// relu^2 for the non-gated one, fp32 rows in segment order for the down
+// projection; no output scatter), laid
 // out for the matrix cores and the memory system of one MI355X:
 //
 // * Persistent workgroups. The grid is one workgroup per CU; each walks a
@@ -82,6 +83,19 @@ typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
 __device__ __forceinline__ int slot_of(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
 __device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// LDS accesses of the epilogue, each through a __restrict__ pointer: the
+// compiler waits for every request still in flight into LDS before an LDS
+// access it cannot place in an alias scope, and these give it one.
+__device__ __forceinline__ void park_put16(char *__restrict__ base, int off, u32x4 v) {
+    *(lds_u32x4 *)(base + off) = v;
+}
+__device__ __forceinline__ void park_put8(char *__restrict__ base, int off, u32x2 v) {
+    *(__attribute__((address_space(3))) volatile u32x2 *)(base + off) = v;
+}
+__device__ __forceinline__ u32x4 park_get16(char *__restrict__ base, int off) {
+    return (u32x4) * (lds_u32x4 *)(base + off);
+}
 
 template <int BM>
 struct Geo {
@@ -312,6 +326,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     constexpr int TM = G::TM, TN = G::TN;
     constexpr int kAhead = NS - 1;           // stages requested ahead of the one multiplied
     __shared__ uint4 ring[NS * G::STAGE];
+    // the epilogue's wave-private 4 KB (256-row tiles; 128-row tiles use the
+    // stage multiplied last). An LDS object of its own, so the compiler can
+    // tell its reads from the requests still in flight into the ring.
+    __shared__ uint4 park_lds[BM == 256 ? 4 * 256 : 1];
     __shared__ int s_pre[kMaxE + 1];
     __shared__ int s_off[kMaxE + 1];
     __shared__ int s_wsum[4];
@@ -424,14 +442,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = f32x16{};
-        int orow[TM];                        // output rows of the down projection
-        if (MODE == kDown) {
-#pragma unroll
-            for (int i = 0; i < TM; ++i) {
-                const int pos = row0 + a_tile_row + i * 32 + (lane & 31);
-                orow[i] = pos < row_end ? (p.scatter ? p.scatter[pos] : pos) : -1;
-            }
-        }
         // The last kAhead steps refill with the next tile's first slices;
         // that tile's A offsets are formed just before (its gathered rows
         // were requested a tile ago and the waits of the steps so far have
@@ -464,96 +474,144 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         }
 
         // ---- epilogue. acc[i][j][r]: token (lane % 32) of token tile i,
-        // weight row 8*(r/4) + 4*(lane/32) + r%4 of weight tile j. One
-        // 32x32 tile at a time, with buffer stores whose offset is pushed
-        // past the end of the output for rows past the segment (and columns
-        // past N), which the hardware drops: no branches, so the fences keep
-        // the accumulator reads next to their use.
-        const int nsub = 4 * (lane >> 5);
+        // weight row 8*(r/4) + 4*(lane/32) + r%4 of weight tile j. A lane
+        // holds 4-column pieces of one row, so storing from there writes
+        // 16 or 32 bytes into each of 32 rows per instruction: partial
+        // lines. The results go through a wave-private 4 KB of LDS instead
+        // (256-row tiles: an array of its own; 128-row tiles: the stage
+        // multiplied last, not refilled before the next tile's first
+        // barrier), one 32-row block at a time, and come back as 16-byte
+        // pieces of whole rows: every store instruction writes 8 rows of 128
+        // bytes (fp32, 32 columns) or 4 to 8 rows of 128 to 256 bytes (bf16).
+        // 16-byte chunk c of LDS row r sits at chunk c ^ (r % 8), so the
+        // rows written together and the pieces read together spread over
+        // the banks. Stores past the segment's rows or past N go to an
+        // offset the buffer range check drops: no branches. The area is
+        // wave-private and 4 KB: a 32-row block of 32 fp32 or 64 bf16
+        // columns.
+        char *park;
+        if constexpr (BM == 256) {
+            park = (char *)park_lds + wave * 4096;
+        } else {
+            // every wave is past its reads of that stage (the requests of
+            // the next tile stay in flight)
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            park = (char *)(ring + (sl == 0 ? NS - 1 : sl - 1) * G::STAGE) + wave * 4096;
+        }
+        const int half = lane >> 5;          // which 4 of each 8 columns the lane holds
+        const int prow = lane & 31;          // the row the lane holds
         if (MODE == kDown) {
-            const int n0 = nt * kBN + wn * (kBN / 2) + nsub;
+            const int n0 = nt * kBN + wn * (kBN / 2);
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
-                const bool col_ok = n0 - nsub + j * 32 < p.N;
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
+                for (int j = 0; j < TN; ++j) {
                     const f32x16 &v = acc[i][j];
-                    const uint32_t off = (orow[i] >= 0 && col_ok)
-                                             ? ((uint32_t)orow[i] * (uint32_t)p.ldc + n0 + j * 32) * 4u
-                                             : out_bytes;
+                    // 32 rows x 32 fp32: row r at r * 128 bytes, 8 chunks of 4
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
-                        const f32x4 q4 = {v[4 * gq], v[4 * gq + 1], v[4 * gq + 2], v[4 * gq + 3]};
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, q4), out_rsrc,
-                                                               off + gq * 32, 0, 0);
+                        const int chunk = (2 * gq + half) ^ (prow & 7);
+                        park_put16(park, prow * 128 + chunk * 16,
+                                   __builtin_bit_cast(u32x4, f32x4{v[4 * gq], v[4 * gq + 1],
+                                                                   v[4 * gq + 2], v[4 * gq + 3]}));
+                    }
+                    const int col = n0 + j * 32 + 4 * (lane & 7);
+                    const bool col_ok = col < p.N;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = q * 8 + (lane >> 3);
+                        const int chunk = (lane & 7) ^ (r & 7);
+                        const u32x4 w4 = park_get16(park, r * 128 + chunk * 16);
+                        const int pos = row0 + a_tile_row + i * 32 + r;
+                        const uint32_t off = (pos < row_end && col_ok)
+                                                 ? ((uint32_t)pos * (uint32_t)p.ldc + col) * 4u
+                                                 : out_bytes;
+                        __builtin_amdgcn_raw_buffer_store_b128(w4, out_rsrc, off, 0, 0);
                     }
                     fence();
                 }
             }
         } else {
-            // With 256 token rows a lane holds 256 accumulators and has no
-            // VGPRs left to take them all at once, which is what the register
-            // allocator does at the loop exit; the tiles go through LDS one
-            // at a time instead. The stage multiplied last is not refilled
-            // before the next tile's first barrier.
-            constexpr bool kViaLds = BM == 256;
-            lds_u32x4 *park = (lds_u32x4 *)(ring + (sl == 0 ? NS - 1 : sl - 1) * G::STAGE) + wave * 8 * kWave;
-            if (kViaLds)
-                __syncthreads();             // every wave is past its reads of that stage
+            // per 32-row block, two tiles of 32 output columns at a time:
+            // bf16, written to LDS as rows of 128 bytes (4 KB per wave),
+            // then stored in 16-byte pieces of whole rows
             constexpr int JO = MODE == kGateUp ? TN / 2 : TN;     // output column tiles
+            static_assert(JO % 2 == 0, "output column tiles come in pairs");
             const int ncols = MODE == kGateUp ? p.I : p.N;
             const int n0 = nt * (MODE == kGateUp ? kBN / 2 : kBN) +
-                           wn * (MODE == kGateUp ? kBN / 4 : kBN / 2) + nsub;
+                           wn * (MODE == kGateUp ? kBN / 4 : kBN / 2);
 #pragma unroll
-            for (int j = 0; j < JO; ++j) {
-                const bool col_ok = n0 - nsub + j * 32 < ncols;
+            for (int i = 0; i < TM; ++i) {
 #pragma unroll
-                for (int i = 0; i < TM; ++i) {
-                    const int pos = row0 + a_tile_row + i * 32 + (lane & 31);
-                    f32x16 gv, uv;
-                    if (kViaLds) {
-                        // through this wave's slice of the stage multiplied
-                        // last, 16 bytes per lane per piece (lane-major)
-                        constexpr int JU = MODE == kGateUp ? TN / 2 : 0;
+                for (int jp = 0; jp < JO; jp += 2) {
+                    uint32_t hv[2][8];           // bf16 pairs, the lane's columns of each tile
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            park[q * kWave + lane] = __builtin_bit_cast(
-                                u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                             acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]});
-                            if (MODE == kGateUp)
-                                park[(4 + q) * kWave + lane] = __builtin_bit_cast(
-                                    u32x4, f32x4{acc[i][j + JU][4 * q], acc[i][j + JU][4 * q + 1],
-                                                 acc[i][j + JU][4 * q + 2], acc[i][j + JU][4 * q + 3]});
-                        }
+                    for (int jj = 0; jj < 2; ++jj) {
+                        const int j = jp + jj;
+                        // the accumulators move to VGPRs one tile at a time,
+                        // through LDS (a lane takes back its own 64 bytes)
+                        f32x16 gv, uv;
+                        const int mine = lane * 16;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            park_put16(park, mine + q * 1024,
+                                       __builtin_bit_cast(u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                                                       acc[i][j][4 * q + 2],
+                                                                       acc[i][j][4 * q + 3]}));
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const f32x4 a4 = __builtin_bit_cast(f32x4, (u32x4)park[q * kWave + lane]);
-                            f32x4 b4 = a4;
-                            if (MODE == kGateUp)
-                                b4 = __builtin_bit_cast(f32x4, (u32x4)park[(4 + q) * kWave + lane]);
+                            const f32x4 a4 = __builtin_bit_cast(f32x4, park_get16(park, mine + q * 1024));
 #pragma unroll
-                            for (int c = 0; c < 4; ++c) {
+                            for (int c = 0; c < 4; ++c)
                                 gv[4 * q + c] = a4[c];
-                                uv[4 * q + c] = b4[c];
+                        }
+                        if (MODE == kGateUp) {
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                park_put16(park, mine + q * 1024,
+                                           __builtin_bit_cast(u32x4, f32x4{acc[i][j + TN / 2][4 * q],
+                                                                           acc[i][j + TN / 2][4 * q + 1],
+                                                                           acc[i][j + TN / 2][4 * q + 2],
+                                                                           acc[i][j + TN / 2][4 * q + 3]}));
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const f32x4 b4 = __builtin_bit_cast(f32x4, park_get16(park, mine + q * 1024));
+#pragma unroll
+                                for (int c = 0; c < 4; ++c)
+                                    uv[4 * q + c] = b4[c];
                             }
                         }
-                    } else {
-                        gv = acc[i][j];
-                        uv = acc[i][MODE == kGateUp ? j + TN / 2 : j];
-                        __asm__ volatile("" : "+v"(gv), "+v"(uv));
+#pragma unroll
+                        for (int c = 0; c < 8; ++c) {
+                            const float x0 = MODE == kGateUp ? silu_mul(gv[2 * c], uv[2 * c]) : relu_sq(gv[2 * c]);
+                            const float x1 = MODE == kGateUp ? silu_mul(gv[2 * c + 1], uv[2 * c + 1])
+                                                             : relu_sq(gv[2 * c + 1]);
+                            hv[jj][c] = pack_bf16x2(x0, x1);
+                        }
                     }
-                    const uint32_t off = (pos < row_end && col_ok)
-                                             ? ((uint32_t)pos * (uint32_t)p.ldc + n0 + j * 32) * 2u
-                                             : out_bytes;
+                    // the pair's rows into LDS: tile jj's columns 8 gq + 4 half
+                    // .. + 3 are bytes 16 (4 jj + gq) + 8 half of the row
 #pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        float v[4];
+                    for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            v[c] = MODE == kGateUp ? silu_mul(gv[4 * gq + c], uv[4 * gq + c])
-                                                   : relu_sq(gv[4 * gq + c]);
-                        const u32x2 q2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-                        __builtin_amdgcn_raw_buffer_store_b64(q2, out_rsrc, off + gq * 16, 0, 0);
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const int chunk = (4 * jj + gq) ^ (prow & 7);
+                            park_put8(park, prow * 128 + chunk * 16 + 8 * half,
+                                      u32x2{hv[jj][2 * gq], hv[jj][2 * gq + 1]});
+                        }
+                    // and out in 16-byte pieces of whole rows (8 per row)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int r = q * 8 + (lane >> 3), c = lane & 7;
+                        const int chunk = c ^ (r & 7);
+                        const u32x4 w4 = park_get16(park, r * 128 + chunk * 16);
+                        const int pos = row0 + a_tile_row + i * 32 + r;
+                        const int col = n0 + jp * 32 + 8 * c;
+                        const uint32_t off = (pos < row_end && col < ncols)
+                                                 ? ((uint32_t)pos * (uint32_t)p.ldc + col) * 2u
+                                                 : out_bytes;
+                        __builtin_amdgcn_raw_buffer_store_b128(w4, out_rsrc, off, 0, 0);
                     }
                     fence();
                 }
@@ -652,7 +710,7 @@ bool grouped_supported(const GemmProblem &p) {
     // every A offset (rows of A times lda, in bytes) stays below kPastA
     // and every weight offset within one expert, stay below kPastA
     const long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
-    return !p.affine4 && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
+    return !p.affine4 && p.scatter == nullptr && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
            (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA &&
            (long long)p.N * p.K * 2 < (long long)kPastA;
 }

@@ -71,8 +71,9 @@ hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream);
 bool stream_supported(const GemmProblem &p);
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream);
 
-hipError_t launch_combine(const float *y_slot, const float *weights, const float *shared, int T,
-                          int H, int k, float routed_scale, void *out, int out_f32,
-                          hipStream_t stream);
+// out[t] = routed_scale * sum_j weights[t,j] y_seg[slot_of[t*k+j]] + shared[t]
+hipError_t launch_combine(const float *y_seg, const int32_t *slot_of, const float *weights,
+                          const float *shared, int T, int H, int k, float routed_scale, void *out,
+                          int out_f32, hipStream_t stream);
 
 }  // namespace moe
