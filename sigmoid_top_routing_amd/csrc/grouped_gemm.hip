@@ -549,38 +549,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
                     for (int jj = 0; jj < 2; ++jj) {
                         const int j = jp + jj;
-                        // the accumulators move to VGPRs one tile at a time,
-                        // through LDS (a lane takes back its own 64 bytes)
+                        // the tile's accumulators into VGPRs, one read each:
+                        // written out, so the compiler does not move every
+                        // accumulator of the tile list at once (which spills)
                         f32x16 gv, uv;
-                        const int mine = lane * 16;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            park_put16(park, mine + q * 1024,
-                                       __builtin_bit_cast(u32x4, f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                                                       acc[i][j][4 * q + 2],
-                                                                       acc[i][j][4 * q + 3]}));
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const f32x4 a4 = __builtin_bit_cast(f32x4, park_get16(park, mine + q * 1024));
-#pragma unroll
-                            for (int c = 0; c < 4; ++c)
-                                gv[4 * q + c] = a4[c];
-                        }
-                        if (MODE == kGateUp) {
-#pragma unroll
-                            for (int q = 0; q < 4; ++q)
-                                park_put16(park, mine + q * 1024,
-                                           __builtin_bit_cast(u32x4, f32x4{acc[i][j + TN / 2][4 * q],
-                                                                           acc[i][j + TN / 2][4 * q + 1],
-                                                                           acc[i][j + TN / 2][4 * q + 2],
-                                                                           acc[i][j + TN / 2][4 * q + 3]}));
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) {
-                                const f32x4 b4 = __builtin_bit_cast(f32x4, park_get16(park, mine + q * 1024));
-#pragma unroll
-                                for (int c = 0; c < 4; ++c)
-                                    uv[4 * q + c] = b4[c];
-                            }
+                        for (int r = 0; r < 16; ++r) {
+                            __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(gv[r]) : "a"(acc[i][j][r]));
+                            if (MODE == kGateUp)
+                                __asm__ volatile("v_accvgpr_read_b32 %0, %1"
+                                                 : "=v"(uv[r])
+                                                 : "a"(acc[i][j + TN / 2][r]));
                         }
 #pragma unroll
                         for (int c = 0; c < 8; ++c) {
