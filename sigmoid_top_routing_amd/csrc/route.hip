@@ -16,16 +16,19 @@
 // Two launches: the logits, then the top-k (which for decode-sized batches
 // also adds the slices, k_route_fold).
 //
-// k_logits computes z = x Wr^T as T*E*(H/64) independent fma chains of
-// length 64, each in h order, and adds each (t, e)'s slices in order (see the
-// kernel for the layout). The chains are what bound it: at the prefill
-// shapes they fill the chip's fp32 lanes, at a decode step they are
-// latency-bound, and k_logits_few takes that case.
+// The logits are T*E*(H/64) independent fma chains of length 64, each in h
+// order, and each (t, e)'s slices are added in order. k_logits_ring (H a
+// multiple of 128) and k_logits (other H) run a lane per token; there the
+// broadcast LDS reads of the router rows are what bound them. Batches of at
+// most 8 tokens and 32 experts take k_logits_part (the slices spread over
+// the chip) and k_route_fold; at most 8 tokens with more experts,
+// k_logits_few.
 //
 // k_topk reads z, applies the sigmoid and the bias, and picks the top k of
-// each token with k rounds of a 64-bit (order key, ~index) max over the
-// token's lanes (xor shuffles); then the weights. When one workgroup holds
-// every token (decode-sized batches) it also builds the plan.
+// each token by the 64-bit (order key, ~index) candidates: with one expert
+// per lane each lane counts the larger candidates of its token (its rank),
+// else k rounds of xor-shuffle maxima over the token's lanes; then the
+// weights. When one workgroup holds every token it also builds the plan.
 #include <hip/hip_runtime.h>
 
 #include "device.hpp"
@@ -361,9 +364,10 @@ __global__ __launch_bounds__(kMaxThreads) void k_logits_ring(const uint16_t *__r
     }
 }
 
-// k_logits_few: decode-sized batches (T <= 8, H <= 2048). The chains are
-// the whole cost there (H dependent fmas each, 64 at a time), so the point is to start
-// them early and never stall them: a workgroup owns 8 experts and every
+// k_logits_few: at most 8 tokens with more than 32 experts (H <= 2048).
+// The chains are the whole cost there (a lane runs its (t, e)'s slices one
+// after another), so the point is to start them early and never stall
+// them: a workgroup owns 8 experts and every
 // token, requests all of its rows at once (four h-quarters, in order), and
 // moves quarter q to LDS (x converted to fp32) as soon as it has landed;
 // lanes 0..15 of each wave then run the chains of 2 experts x 8 tokens over
