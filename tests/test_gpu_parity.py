@@ -92,11 +92,12 @@ def test_route_matches_oracle(name):
     check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref)
 
 
-# Batches of at most 8 tokens take the one-workgroup router (E <= 32, H a
-# multiple of 128, H <= 2048: one fma chain per lane, a 5-stage ring over
-# H, fewer h blocks than ring stages at H = 128 and 256), past those limits
-# the 8-experts-per-workgroup decode logits (E > 32) or the tiled logits
-# (H > 2048); every shape here is one of those paths at an edge.
+# Batches of at most 8 tokens and 32 experts take the two-launch decode
+# router (one workgroup per 64-h slice, then the fold, top-k and plan in one
+# workgroup) at any H; with more experts, the 8-experts-per-workgroup decode
+# logits (H a multiple of 128, H <= 2048) or the tiled logits. Every shape
+# here is one of those paths at an edge: one slice, an odd number of
+# slices, a single expert, E just past 32, H past 2048.
 ROUTE_DECODE = {
     "t1_h2048_e32_k4": dict(T=1, H=2048, E=32, k=4),
     "t5_h2048_e32_k4": dict(T=5, H=2048, E=32, k=4),
@@ -109,6 +110,9 @@ ROUTE_DECODE = {
     "t8_h2048_e33_k4": dict(T=8, H=2048, E=33, k=4),
     "t6_h256_e64_k4": dict(T=6, H=256, E=64, k=4),
     "t7_h2176_e32_k4": dict(T=7, H=2176, E=32, k=4),
+    "t4_h64_e5_k2": dict(T=4, H=64, E=5, k=2),
+    "t8_h192_e1_k1": dict(T=8, H=192, E=1, k=1),
+    "t8_h2176_e40_k4": dict(T=8, H=2176, E=40, k=4),
 }
 
 
