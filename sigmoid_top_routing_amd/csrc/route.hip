@@ -822,10 +822,14 @@ void launch_logits(hipStream_t stream, const uint16_t *x, const float *Wr, int T
 
 // Batches of at most 8 tokens and 32 experts take the two-launch decode
 // router, whose scratch holds every slice's partial logits.
-bool decode_router(int T, int E) { return T <= kDecT && E <= kDecE; }
+// (Its loads form 32-bit byte offsets into the router rows, E * H * 4 of
+// them, which must stay below the buffer range of 2^31.)
+bool decode_router(int T, int H, int E) {
+    return T <= kDecT && E <= kDecE && (int64_t)E * H * 4 < ((int64_t)1 << 31);
+}
 
 size_t route_scratch_bytes(int T, int H, int E) {
-    const size_t slices = decode_router(T, E) ? (size_t)(H / 64) : 1;
+    const size_t slices = decode_router(T, H, E) ? (size_t)(H / 64) : 1;
     return slices * T * E * sizeof(float);
 }
 
@@ -838,7 +842,7 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
         return hipSuccess;
     if (H % 64 != 0)
         return hipErrorInvalidValue;
-    if (decode_router(T, E)) {
+    if (decode_router(T, H, E)) {
         // partial logits over the chip, then one workgroup: fold, top-k,
         // weights and (when it fits) the plan
         const int S = H / 64;
