@@ -868,7 +868,10 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
     if (T <= kFewT && H <= kFewMaxH && H % 128 == 0)
         hipLaunchKernelGGL(k_logits_few, dim3((E + kFewE - 1) / kFewE), dim3(kMaxThreads), 0,
                            stream, x, Wr, T, H, E, z_scratch);
-    else if ((int64_t)tblocks * ((E + 7) / 8) >= 128 && H % kRingH == 0)
+    else if ((int64_t)tblocks * ((E + 7) / 8) >= 128 && H % kRingH == 0 &&
+             (int64_t)T * H * 2 < ((int64_t)1 << 31) && (int64_t)E * H * 4 < ((int64_t)1 << 31))
+        // (the ring's requests form 32-bit byte offsets; an offset of 2^31
+        // or more reads zeros)
         hipLaunchKernelGGL(k_logits_ring, dim3(tblocks, (E + 7) / 8), dim3(kMaxThreads), 0, stream,
                            x, Wr, T, H, E, z_scratch);
     else if ((int64_t)tblocks * ((E + 7) / 8) >= 128)
