@@ -109,7 +109,10 @@ typedef struct {
     const uint16_t *shared_down;
 } moe_weights;
 
-/* Bytes of workspace moe_forward() and moe_plan() need for these dims. */
+/* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
+ * 4-bit experts and more than 2 E assignments (T * k > 2 E) this includes
+ * room for the bf16-decoded weights of every expert that can have rows:
+ * min(E, T * k) * max(n_up * H, H * I) * 2 bytes, n_up = 2 I (SwiGLU) or I. */
 int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
 
 /* Router and top-k (TileGym PR #187 "Weight layout and routing"; TensorFold

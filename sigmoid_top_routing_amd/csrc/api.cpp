@@ -41,8 +41,15 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t z, ids, w, counts, offsets, sorted, slot, chunk_counts, h, y, hs, ys, total;
+    size_t z, ids, w, counts, offsets, sorted, slot, chunk_counts, h, y, hs, ys, wdq, total;
 };
+
+// Prompt-sized batches with 4-bit experts decode the weights of the experts
+// with rows to bf16 once per call and run the direct-to-LDS grouped kernel on
+// them; decode-sized ones keep the decode in the staged kernel's loads.
+bool dequant_first(const moe_dims &d) {
+    return d.wfmt == MOE_W_AFFINE4 && (int64_t)d.T * d.k > 2 * (int64_t)d.E;
+}
 
 Layout layout(const moe_dims &d) {
     Layout L{};
@@ -66,6 +73,13 @@ Layout layout(const moe_dims &d) {
     if (d.I_shared > 0) {
         L.hs = take((size_t)d.T * d.I_shared * 2);
         L.ys = take((size_t)d.T * d.H * 4);
+    }
+    if (dequant_first(d)) {
+        // the bf16 weights of the experts with rows, one projection at a time
+        const size_t experts = (size_t)(A < (size_t)d.E ? A : d.E);
+        const size_t n_up = d.act == MOE_ACT_SWIGLU ? 2 * (size_t)d.I : (size_t)d.I;
+        const size_t per = n_up * d.H > (size_t)d.H * d.I ? n_up * d.H : (size_t)d.H * d.I;
+        L.wdq = take(experts * per * 2);
     }
     L.total = off;
     return L;
@@ -338,7 +352,24 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     up.I = I;
     up.C = h;
     up.ldc = I;
-    LAUNCH(run(up));
+    // 4-bit weights, prompt-sized batch (dequant_first): decoded to bf16
+    // first, then the bf16 kernel on the experts with rows
+    uint16_t *wdq = (uint16_t *)(ws + L.wdq);
+    auto dequantized = [&](moe::GemmProblem g) {
+        g.affine4 = 0;
+        g.B = wdq;
+        g.Bscale = nullptr;
+        g.Bbias = nullptr;
+        g.b_compact = 1;
+        return g;
+    };
+    const bool dq = dequant_first(*d) && moe::grouped_supported(dequantized(up));
+    if (dq) {
+        LAUNCH(moe::launch_dequant(up, wdq, stream));
+        LAUNCH(run(dequantized(up)));
+    } else {
+        LAUNCH(run(up));
+    }
     LAUNCH(mark(3));
 
     moe::GemmProblem down{};
@@ -357,7 +388,13 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     down.I = I;
     down.C = y;                        // rows in segment order: the combine gathers them
     down.ldc = H;
-    LAUNCH(run(down));
+    if (dq && moe::grouped_supported(dequantized(down))) {
+        // (the up projection has read wdq by now: same stream)
+        LAUNCH(moe::launch_dequant(down, wdq, stream));
+        LAUNCH(run(dequantized(down)));
+    } else {
+        LAUNCH(run(down));
+    }
     LAUNCH(mark(4));
 
     const float *shared = nullptr;

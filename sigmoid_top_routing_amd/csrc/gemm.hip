@@ -486,6 +486,67 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
     return launch_tile<128, MODE, AFF>(p, stream);
 }
 
+// k_dequant: the 4-bit weights of the experts with rows, decoded once to
+// bf16 for the direct-to-LDS grouped kernel (prompt-sized batches: the
+// decoded rows are then read by every m-tile of the expert from L2 or HBM,
+// instead of being decoded again in each tile's loads). A code word holds 8
+// weights (nibble j at bits 4 j); the decode is the same as the staged
+// kernel's, so both paths multiply the same bf16 weights. The workgroups
+// share the (expert, chunk) items; each thread decodes 4 words per item.
+constexpr int kDqWords = 4;
+
+__global__ __launch_bounds__(kThreads) void k_dequant(GemmProblem p, uint16_t *__restrict__ out) {
+    __shared__ int s_list[256];
+    __shared__ int s_cnt[kThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    // the experts with rows, in expert order
+    const bool busy = tid < p.E && p.offsets[tid + 1] > p.offsets[tid];
+    const uint64_t m = __ballot(busy);
+    if (lane == 0)
+        s_cnt[wave] = __popcll(m);
+    __syncthreads();
+    int rank = __popcll(m & ((1ull << lane) - 1ull)), nb = 0;
+    for (int w = 0; w < kThreads / kWave; ++w) {
+        rank += w < wave ? s_cnt[w] : 0;
+        nb += s_cnt[w];
+    }
+    if (busy)
+        s_list[rank] = tid;
+    __syncthreads();
+    const int K8 = p.K / 8, G = p.K / 64;
+    const size_t words = (size_t)p.N * K8;                 // code words per expert
+    const size_t per_item = (size_t)kThreads * kDqWords;
+    const size_t chunks = (words + per_item - 1) / per_item;
+    const uint32_t *codes = (const uint32_t *)p.B;
+    for (size_t item = blockIdx.x; item < (size_t)nb * chunks; item += gridDim.x) {
+        const int y = (int)(item / chunks);
+        const size_t w0 = (item % chunks) * per_item;
+        const int e = s_list[y];
+#pragma unroll
+        for (int j = 0; j < kDqWords; ++j) {
+            const size_t w = w0 + (size_t)j * kThreads + tid;
+            if (w >= words)
+                break;
+            const size_t n = w / K8, c8 = w % K8;
+            const uint32_t code = codes[(size_t)e * words + w];
+            const size_t g = ((size_t)e * p.N + n) * G + c8 / 8;
+            const float sc = bf16_to_f32(p.Bscale[g]);
+            const float bi = bf16_to_f32(p.Bbias[g]);
+            uint32_t packed[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float lo = __builtin_fmaf(sc, (float)((code >> (8 * c)) & 15u), bi);
+                const float hi = __builtin_fmaf(sc, (float)((code >> (8 * c + 4)) & 15u), bi);
+                packed[c] = pack_bf16x2(lo, hi);
+            }
+            *reinterpret_cast<uint4 *>(out + ((size_t)y * p.N + n) * p.K + c8 * 8) =
+                make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
@@ -503,6 +564,14 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
     case kUpRelu2: return launch_mode<kUpRelu2, false>(p, stream);
     default: return launch_mode<kDown, false>(p, stream);
     }
+}
+
+hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream) {
+    if (!p.affine4 || p.offsets == nullptr || p.E > 256 || p.K % 64 != 0)
+        return hipErrorInvalidValue;
+    // a few workgroups per CU share the items
+    hipLaunchKernelGGL(k_dequant, dim3(1024), dim3(kThreads), 0, stream, p, out);
+    return hipGetLastError();
 }
 
 }  // namespace moe

@@ -332,7 +332,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     __shared__ uint4 park_lds[BM == 256 ? 4 * 256 : 1];
     __shared__ int s_pre[kMaxE + 1];
     __shared__ int s_off[kMaxE + 1];
+    __shared__ int s_rank[kMaxE];            // compact B: a segment's place among those with rows
     __shared__ int s_wsum[4];
+    __shared__ int s_bsum[4];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -358,7 +360,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     }
     if (lane == kWave - 1)
         s_wsum[wave] = incl;
+    const uint64_t busy = __ballot(tid < nseg && tiles > 0);
+    if (lane == 0)
+        s_bsum[wave] = __popcll(busy);
     __syncthreads();
+    if (tid < nseg) {
+        int rank = __popcll(busy & ((1ull << lane) - 1ull));
+        for (int w = 0; w < wave; ++w)
+            rank += s_bsum[w];
+        s_rank[tid] = rank;
+    }
     int total = 0;
     for (int w = 0; w < 4; ++w) {
         if (w < wave)
@@ -392,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         int raw[G::AI];
         const int valid = gathered_rows<BM>(p, row0, row_end, raw);
         a_offsets<BM>(p, raw, valid, req.a_off);
-        b_offsets<BM, MODE>(p, e, nt, req);
+        b_offsets<BM, MODE>(p, p.b_compact ? s_rank[e] : e, nt, req);
     }
     int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
     bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
@@ -468,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                     for (int i = 0; i < G::AI; ++i)
                         __asm__ volatile("" : "+v"(nraw[i]));
                     a_offsets<BM>(p, nraw, nvalid, req.a_off);
-                    b_offsets<BM, MODE>(p, ne, nnt, req);
+                    b_offsets<BM, MODE>(p, p.b_compact ? s_rank[ne] : ne, nnt, req);
                 }
             }
         }

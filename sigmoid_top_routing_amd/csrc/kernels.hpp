@@ -57,9 +57,15 @@ struct GemmProblem {
     void *C;                  // kGateUp / kUpRelu2: bf16 [rows][ldc]; kDown: fp32 [*][ldc]
     int ldc;
     const int32_t *scatter;   // kDown: output row of position p = scatter[p] (NULL: row p)
+    int b_compact;            // B holds only the experts with rows, in expert order
 };
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
+
+// The 4-bit weights of p's experts that have rows (p.affine4, offsets set),
+// decoded once to bf16 (scale * q + bias in fp32, rounded to nearest even)
+// into out: [experts with rows][N][K], in expert order (b_compact).
+hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream);
 
 // The persistent direct-to-LDS kernel (bf16 weights, K a multiple of 32 and
 // at least 128); launch_gemm routes the problems it supports there.
