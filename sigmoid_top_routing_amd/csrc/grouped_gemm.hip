@@ -494,9 +494,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         // barrier), one 32-row block at a time, and come back as 16-byte
         // pieces of whole rows: every store instruction writes 8 rows of 128
         // bytes (fp32, 32 columns) or 4 to 8 rows of 128 to 256 bytes (bf16).
-        // 16-byte chunk c of LDS row r sits at chunk c ^ (r % 8), so the
-        // rows written together and the pieces read together spread over
-        // the banks. Stores past the segment's rows or past N go to an
+        // 16-byte chunk c of LDS row r (128-byte rows: half of the 64 banks)
+        // sits at chunk c ^ ((r / 2) % 8): the 16 rows a 16-lane write
+        // touches, even and odd, then cover every bank once, as do the two
+        // rows a 16-lane read touches. Stores past the segment's rows or past N go to an
         // offset the buffer range check drops: no branches. The area is
         // wave-private and 4 KB: a 32-row block of 32 fp32 or 64 bf16
         // columns.
@@ -522,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                     // 32 rows x 32 fp32: row r at r * 128 bytes, 8 chunks of 4
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
-                        const int chunk = (2 * gq + half) ^ (prow & 7);
+                        const int chunk = (2 * gq + half) ^ ((prow >> 1) & 7);
                         park_put16(park, prow * 128 + chunk * 16,
                                    __builtin_bit_cast(u32x4, f32x4{v[4 * gq], v[4 * gq + 1],
                                                                    v[4 * gq + 2], v[4 * gq + 3]}));
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int r = q * 8 + (lane >> 3);
-                        const int chunk = (lane & 7) ^ (r & 7);
+                        const int chunk = (lane & 7) ^ ((r >> 1) & 7);
                         const u32x4 w4 = park_get16(park, r * 128 + chunk * 16);
                         const int pos = row0 + a_tile_row + i * 32 + r;
                         const uint32_t off = (pos < row_end && col_ok)
@@ -586,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
                         for (int gq = 0; gq < 4; ++gq) {
-                            const int chunk = (4 * jj + gq) ^ (prow & 7);
+                            const int chunk = (4 * jj + gq) ^ ((prow >> 1) & 7);
                             park_put8(park, prow * 128 + chunk * 16 + 8 * half,
                                       u32x2{hv[jj][2 * gq], hv[jj][2 * gq + 1]});
                         }
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int r = q * 8 + (lane >> 3), c = lane & 7;
-                        const int chunk = c ^ (r & 7);
+                        const int chunk = c ^ ((r >> 1) & 7);
                         const u32x4 w4 = park_get16(park, r * 128 + chunk * 16);
                         const int pos = row0 + a_tile_row + i * 32 + r;
                         const int col = n0 + jp * 32 + 8 * c;
