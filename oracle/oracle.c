@@ -9,10 +9,14 @@
  * What the block computes (one token t with input row x_t):
  *   router   z[e]  = sum_h x[t,h] * Wr[e,h]                 fp32, see below
  *            s[e]  = sigmoid(z[e])                          fp32, see below
+ *                    (or the softmax of the row z[0..E-1], the other router
+ *                    family the pages list)
  *            key[e]= s[e] + bias[e]                         fp32
  *   select   ids   = the k experts of largest key           (bias selects only)
  *   weights  w_j   = s[ids_j] / (sum_j s[ids_j] + eps)      unbiased scores
  *   experts  SwiGLU: y = W_d (silu(W_g x) * (W_u x)),  W_gu = [W_g; W_u]
+ *                    with swiglu_limit L > 0: gate pre-activations capped at
+ *                    L, up pre-activations clamped to [-L, L]
  *            relu^2: y = W_d (relu(W_up x))^2
  *   combine  out_t = rsf * sum_j w_j y_{t,j} + shared_t     rsf on the sum
  *            shared_t = W_sd act(W_su x_t), unscaled
@@ -24,7 +28,11 @@
  * the 4-bit weights dequantised exactly); vllm.cpp PR #684 "The seam
  * decision" and the W2 commit (relu^2 expert; routed scale multiplies the
  * finished routed sum before the unscaled shared term is added);
- * bloomery PR #235 "What" (relu^2 keeps a non-finite input non-finite).
+ * bloomery PR #235 "What" (relu^2 keeps a non-finite input non-finite);
+ * TensorFold issue #548, the consolidation proposal (softmax and sigmoid +
+ * bias routers) and the GLM experts' untested paths (swiglu_limit 10: about
+ * 16 % of gate and 33 % of up pre-activations clamp, so the gate is capped on
+ * one side and the up input on both).
  *
  * Precision. Routing is discontinuous in the scores, so the router is not
  * left to float64: the logits, sigmoid and keys are fp32 in a fixed order
@@ -98,7 +106,8 @@ static float router_logit(const uint16_t *x_row, const float *w_row, int H)
     return z;
 }
 
-/* exp in fp32 for v in [-17, 87] (the sigmoid below never asks for more).
+/* exp in fp32 for v in [-87, 87] (the sigmoid and softmax below never ask
+ * for more; e^-87 is still a normal number).
  * Cody-Waite reduction: n = rint(v * log2 e), r = v - n*ln2 with ln2 split
  * into a high part carrying trailing zero bits and a low remainder, so that
  * |r| <= ln2/2 (plus rounding). exp(r) is the Taylor series of e^r through
@@ -135,6 +144,27 @@ float oracle_sigmoid32(float z)
     if (z < -87.0f)
         return 0.0f;
     return 1.0f / (1.0f + oracle_exp32(-z));
+}
+
+/* Softmax of one router row in fp32: m = the largest non-NaN z (-inf if
+ * none); q[e] = e^(z[e] - m), taken as 0 below -87 like the sigmoid's tail;
+ * S = q[0] + q[1] + ... from +0, e ascending; s[e] = q[e] / S, correctly
+ * rounded. A NaN z (or z - m undefined, as for inf - inf) makes its q NaN,
+ * so S and every s of the row are NaN: such a row picks 0, 1, ..., k-1. */
+void oracle_softmax32_row(const float *z, int E, float *s)
+{
+    float m = -INFINITY;
+    for (int e = 0; e < E; ++e)
+        if (z[e] > m)
+            m = z[e];
+    float S = 0.0f;
+    for (int e = 0; e < E; ++e) {
+        float d = z[e] - m;
+        s[e] = (d != d) ? d : (d < -87.0f ? 0.0f : oracle_exp32(d));
+        S = S + s[e];
+    }
+    for (int e = 0; e < E; ++e)
+        s[e] = s[e] / S;
 }
 
 /* Elementwise forms of the two functions above, for sweeps. */
@@ -182,18 +212,23 @@ void oracle_topk(const float *keys, int E, int k, int32_t *ids)
     free(taken);
 }
 
-/* Route one token: fp32 logits, sigmoid and keys; top-k by key; float64
- * weights from the unbiased scores. No routed scaling factor here: it
- * scales the finished routed sum in the combine. */
+/* Route one token: fp32 logits, scores (score_fn 0: sigmoid, 1: softmax)
+ * and keys; top-k by key; float64 weights from the unbiased scores. No
+ * routed scaling factor here: it scales the finished routed sum in the
+ * combine. */
 static void route_row(const uint16_t *x_row, const float *Wr, const float *bias, int H, int E,
-                      int k, int norm_topk, double eps, float *z, float *s, float *key,
-                      int32_t *ids, double *w)
+                      int k, int score_fn, int norm_topk, double eps, float *z, float *s,
+                      float *key, int32_t *ids, double *w)
 {
-    for (int e = 0; e < E; ++e) {
+    for (int e = 0; e < E; ++e)
         z[e] = router_logit(x_row, Wr + (size_t)e * H, H);
-        s[e] = oracle_sigmoid32(z[e]);
+    if (score_fn == 1)
+        oracle_softmax32_row(z, E, s);
+    else
+        for (int e = 0; e < E; ++e)
+            s[e] = oracle_sigmoid32(z[e]);
+    for (int e = 0; e < E; ++e)
         key[e] = s[e] + (bias ? bias[e] : 0.0f);
-    }
     oracle_topk(key, E, k, ids);
     double sum = 0.0;
     for (int j = 0; j < k; ++j)
@@ -204,8 +239,8 @@ static void route_row(const uint16_t *x_row, const float *Wr, const float *bias,
 
 /* Route every token. z, s (each [T,E]) may be NULL. */
 void oracle_route(int T, int H, int E, int k, const uint16_t *x, const float *Wr,
-                  const float *bias, int norm_topk, double eps, float *z_out, float *s_out,
-                  int32_t *ids, double *w, int nthreads)
+                  const float *bias, int score_fn, int norm_topk, double eps, float *z_out,
+                  float *s_out, int32_t *ids, double *w, int nthreads)
 {
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -219,8 +254,8 @@ void oracle_route(int T, int H, int E, int k, const uint16_t *x, const float *Wr
         float *s = z + E, *key = z + 2 * E;
 #pragma omp for schedule(static)
         for (int t = 0; t < T; ++t) {
-            route_row(x + (size_t)t * H, Wr, bias, H, E, k, norm_topk, eps, z, s, key,
-                      ids + (size_t)t * k, w + (size_t)t * k);
+            route_row(x + (size_t)t * H, Wr, bias, H, E, k, score_fn, norm_topk, eps, z, s,
+                      key, ids + (size_t)t * k, w + (size_t)t * k);
             if (z_out)
                 memcpy(z_out + (size_t)t * E, z, sizeof(float) * E);
             if (s_out)
@@ -281,6 +316,8 @@ typedef struct {
     const uint16_t *w_down_scales, *w_down_biases; /* [E,H,I/group] */
     const uint16_t *shared_up;   /* bf16 [n_sup,H]: n_sup = 2*I_s (SwiGLU) or I_s */
     const uint16_t *shared_down; /* bf16 [H,I_s] */
+    int32_t score_fn;   /* 0 sigmoid, 1 softmax */
+    double swiglu_limit;  /* 0: no clamp; else L > 0 for every SwiGLU of the layer */
 } oracle_layer;
 
 /* Row n of a weight matrix with K inputs, as float64. */
@@ -310,20 +347,27 @@ static double dot(const double *a, const double *b, int n)
 }
 
 /* The activation between the two projections, in float64.
- * SwiGLU: silu(g) * u = g / (1 + e^-g) * u.
+ * SwiGLU: silu(g) * u = g / (1 + e^-g) * u; with a limit L > 0 the gate is
+ * first capped at L and the up input clamped to [-L, L] (comparisons, so a
+ * NaN stays NaN).
  * relu^2: (u < 0 ? 0 : u)^2, so NaN and +inf pass through, -inf gives 0. */
-static double activate(int act, double g, double u)
+static double activate(int act, double g, double u, double limit)
 {
-    if (act == 0)
+    if (act == 0) {
+        if (limit > 0.0) {
+            g = (g > limit) ? limit : g;
+            u = (u > limit) ? limit : ((u < -limit) ? -limit : u);
+        }
         return g / (1.0 + exp(-g)) * u;
+    }
     double r = (u < 0.0) ? 0.0 : u;
     return r * r;
 }
 
 /* The activation, exported for direct checks of its special values. */
-double oracle_activate(int act, double g, double u)
+double oracle_activate(int act, double g, double u, double limit)
 {
-    return activate(act, g, u);
+    return activate(act, g, u, limit);
 }
 
 /* One expert MLP on one input row: y[H] = W_d act(W_up xr). scratch holds
@@ -339,7 +383,8 @@ static void expert_mlp(const oracle_layer *L, int e, const double *xr, double *y
         proj[n] = dot(row, xr, H);
     }
     for (int i = 0; i < I; ++i)
-        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[I + i]) : activate(1, 0.0, proj[i]);
+        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[I + i], L->swiglu_limit)
+                                : activate(1, 0.0, proj[i], 0.0);
     for (int h = 0; h < H; ++h) {
         weight_row(L, 0, e, h, H, I, row);
         y[h] = dot(row, proj, I);
@@ -360,7 +405,8 @@ static void shared_mlp(const oracle_layer *L, const double *xr, double *y, doubl
         proj[n] = dot(row, xr, H);
     }
     for (int i = 0; i < Is; ++i)
-        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[Is + i]) : activate(1, 0.0, proj[i]);
+        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[Is + i], L->swiglu_limit)
+                                : activate(1, 0.0, proj[i], 0.0);
     for (int h = 0; h < H; ++h) {
         const uint16_t *w = L->shared_down + (size_t)h * Is;
         for (int c = 0; c < Is; ++c)
@@ -405,8 +451,8 @@ int oracle_forward_tokens(const oracle_layer *L, const int32_t *tokens, int ntok
                 continue;
             }
             const uint16_t *x_row = L->x + (size_t)t * H;
-            route_row(x_row, L->router_w, L->bias, H, E, k, L->norm_topk, L->norm_eps, zsk,
-                      zsk + E, zsk + 2 * E, ids, w);
+            route_row(x_row, L->router_w, L->bias, H, E, k, L->score_fn, L->norm_topk,
+                      L->norm_eps, zsk, zsk + E, zsk + 2 * E, ids, w);
             for (int h = 0; h < H; ++h)
                 xr[h] = (double)bf16_value(x_row[h]);
             for (int h = 0; h < H; ++h)

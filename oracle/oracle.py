@@ -22,6 +22,7 @@ CFLAGS = ["-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast
           "-std=c11", "-Wall", "-Wextra", "-Werror"]
 
 _lib = None
+SCORES = {"sigmoid": 0, "softmax": 1}
 
 
 def compile_source(source: str, out: str, werror: bool = True) -> str:
@@ -49,6 +50,7 @@ class Layer(C.Structure):
         ("w_up", C.c_void_p), ("w_up_scales", C.c_void_p), ("w_up_biases", C.c_void_p),
         ("w_down", C.c_void_p), ("w_down_scales", C.c_void_p), ("w_down_biases", C.c_void_p),
         ("shared_up", C.c_void_p), ("shared_down", C.c_void_p),
+        ("score_fn", C.c_int32), ("swiglu_limit", C.c_double),
     ]
 
 
@@ -68,14 +70,15 @@ def lib():
         L.oracle_exp32_many.argtypes = [p, i, p]
         L.oracle_sigmoid32_many.argtypes = [p, i, p]
         L.oracle_topk.argtypes = [p, i, i, p]
-        L.oracle_route.argtypes = [i, i, i, i, p, p, p, i, C.c_double, p, p, p, p, i]
+        L.oracle_route.argtypes = [i, i, i, i, p, p, p, i, i, C.c_double, p, p, p, p, i]
+        L.oracle_softmax32_row.argtypes = [p, i, p]
         L.oracle_plan.argtypes = [i, i, i, p, p, p, p, p]
         L.oracle_forward_tokens.argtypes = [C.POINTER(Layer), p, i, p, p, p, i]
         L.oracle_forward_tokens.restype = C.c_int
         L.oracle_affine4_decode.argtypes = [p, p, p, i, i, i, p]
         L.oracle_max_threads.restype = C.c_int
         L.oracle_activate.restype = C.c_double
-        L.oracle_activate.argtypes = [i, C.c_double, C.c_double]
+        L.oracle_activate.argtypes = [i, C.c_double, C.c_double, C.c_double]
         _lib = L
     return _lib
 
@@ -106,9 +109,18 @@ def sigmoid32(z) -> np.ndarray:
     return out
 
 
-def activate(act: str, g: float, u: float) -> float:
-    """The expert activation in float64: act "swiglu" -> silu(g)*u, "relu2" -> relu(u)^2."""
-    return lib().oracle_activate(0 if act == "swiglu" else 1, float(g), float(u))
+def activate(act: str, g: float, u: float, limit: float = 0.0) -> float:
+    """The expert activation in float64: act "swiglu" -> silu(g)*u (g capped
+    at limit, u clamped to [-limit, limit] when limit > 0), "relu2" -> relu(u)^2."""
+    return lib().oracle_activate(0 if act == "swiglu" else 1, float(g), float(u), float(limit))
+
+
+def softmax32(z) -> np.ndarray:
+    """Softmax scores of one router row (fp32 in, fp32 out)."""
+    z = _c(np.atleast_1d(z), np.float32)
+    out = np.empty_like(z)
+    lib().oracle_softmax32_row(_ptr(z), z.size, _ptr(out))
+    return out
 
 
 def topk(keys, k: int) -> np.ndarray:
@@ -119,9 +131,9 @@ def topk(keys, k: int) -> np.ndarray:
 
 
 def route(x, router_w, bias, k: int, norm_topk: bool = True, eps: float = 1e-6,
-          want_scores: bool = False, nthreads: int = 0):
-    """Route every token. Returns ids [T,k] int32 and w [T,k] float64, plus
-    z and s [T,E] fp32 when want_scores."""
+          want_scores: bool = False, nthreads: int = 0, score: str = "sigmoid"):
+    """Route every token (score "sigmoid" or "softmax"). Returns ids [T,k]
+    int32 and w [T,k] float64, plus z and s [T,E] fp32 when want_scores."""
     x = _c(x, np.uint16)
     router_w = _c(router_w, np.float32)
     bias = _c(bias, np.float32)
@@ -131,8 +143,8 @@ def route(x, router_w, bias, k: int, norm_topk: bool = True, eps: float = 1e-6,
     w = np.empty((T, k), dtype=np.float64)
     z = np.empty((T, E), dtype=np.float32) if want_scores else None
     s = np.empty((T, E), dtype=np.float32) if want_scores else None
-    lib().oracle_route(T, H, E, k, _ptr(x), _ptr(router_w), _ptr(bias), int(norm_topk), eps,
-                       _ptr(z), _ptr(s), _ptr(ids), _ptr(w), nthreads)
+    lib().oracle_route(T, H, E, k, _ptr(x), _ptr(router_w), _ptr(bias), SCORES[score],
+                       int(norm_topk), eps, _ptr(z), _ptr(s), _ptr(ids), _ptr(w), nthreads)
     if want_scores:
         return ids, w, z, s
     return ids, w
@@ -182,7 +194,9 @@ def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool 
               w_down_scales=arr("w_down_scales", np.uint16),
               w_down_biases=arr("w_down_biases", np.uint16),
               shared_up=arr("shared_up", np.uint16) if wl.I_shared else None,
-              shared_down=arr("shared_down", np.uint16) if wl.I_shared else None)
+              shared_down=arr("shared_down", np.uint16) if wl.I_shared else None,
+              score_fn=SCORES[getattr(wl, "score", "sigmoid")],
+              swiglu_limit=float(getattr(wl, "swiglu_limit", 0.0)))
     n = tokens.size
     out = np.empty((n, wl.H), dtype=np.float64)
     ids = np.empty((n, wl.k), dtype=np.int32)

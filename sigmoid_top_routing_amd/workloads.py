@@ -41,7 +41,9 @@ class Workload:
     """One synthetic MoE-block workload.
 
     act: "swiglu" (gate_up (E, 2I, H), gate rows first) or "relu2"
-    (up (E, I, H)). wfmt: "bf16" or "affine4" (group 64).
+    (up (E, I, H)). wfmt: "bf16" or "affine4" (group 64). score: "sigmoid"
+    or "softmax" router scores. swiglu_limit: 0, or the cap L > 0 of the
+    SwiGLU inputs (gate <= L, |up| <= L).
     """
     name: str
     T: int
@@ -67,12 +69,15 @@ class Workload:
     nan_rows: tuple = ()
     zero_tie_row: int | None = None  # x row of zeros + triple bias tie
     onehot_tie_row: int | None = None  # one-hot x row + two equal logits
+    zero_rows: tuple = ()             # x rows of zeros, bias untouched
     tie_col: int = 7
     scale_lo: float = 0.005
     scale_hi: float = 0.02
     qbias_lo: float = -0.1
     qbias_hi: float = 0.1
     group: int = 64
+    score: str = "sigmoid"
+    swiglu_limit: float = 0.0
 
     @property
     def A(self) -> int:
@@ -116,6 +121,19 @@ MID = {
                              bias_hi=0.1, seed=105, nan_rows=(0, 100, 332), zero_tie_row=7,
                              onehot_tie_row=200, tie_col=3),
     "mid_e256_k8": Workload("mid_e256_k8", T=96, H=192, I=128, E=256, k=8, seed=106),
+    # The softmax router family (TensorFold issue #548, the consolidation
+    # proposal), with NaN rows and exact ties, over 64 experts.
+    # No expert bias (the family has none): every score of an all-zero row
+    # is exactly 1/64, a 64-way tie.
+    "mid_softmax": Workload("mid_softmax", T=400, H=256, I=192, E=64, k=6, score="softmax",
+                            router_std=0.1, bias_lo=0.0, bias_hi=0.0, seed=107,
+                            nan_rows=(3, 250), zero_rows=(11, 300), onehot_tie_row=99),
+    # swiglu_limit 10 with the inputs scaled so that about 16 % of the gate
+    # and 33 % of the up pre-activations clamp (TensorFold issue #548, the
+    # GLM experts' untested paths); the shared expert clamps too.
+    "mid_swiglu_limit": Workload("mid_swiglu_limit", T=300, H=512, I=256, E=16, k=4,
+                                 swiglu_limit=10.0, x_std=22.0, router_std=0.001, I_shared=192,
+                                 seed=108),
 }
 
 
@@ -244,6 +262,7 @@ def _construct_special_rows(wl: Workload, out: dict) -> None:
     """Rows whose routing is fixed by exact arithmetic, not by rounding.
 
     * NaN rows: every x entry is a bf16 NaN, so every router logit is NaN.
+    * Zero rows: every x entry is 0, so every router logit is +0.
     * Zero tie row: x is all zeros, so every logit is +0 and every score
       the same; the bias of experts 1, 4, 6 is set to 0.125, above every
       other bias, which makes a three-way tie at the top.
@@ -257,6 +276,8 @@ def _construct_special_rows(wl: Workload, out: dict) -> None:
     if x is not None:
         for r in wl.nan_rows:
             x[r, :] = BF16_NAN
+        for r in wl.zero_rows:
+            x[r, :] = 0
     if wl.zero_tie_row is not None:
         if x is not None:
             x[wl.zero_tie_row, :] = 0

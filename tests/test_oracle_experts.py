@@ -348,3 +348,71 @@ def test_nan_rows_stay_in_their_rows():
     assert np.isnan(out[list(wl.nan_rows)]).all()
     assert np.isfinite(out[~bad]).all()
     assert (out[wl.zero_tie_row] == 0).all()
+
+
+# ---------------------------------------------------------------- swiglu_limit
+# GLM's experts clamp the SwiGLU inputs at swiglu_limit (TensorFold issue
+# #548, the GLM experts' untested paths: at limit 10 about 16 % of gate and
+# 33 % of up pre-activations clamp, one side for the gate, both for up).
+
+def silu_exp(g):
+    return g / (1.0 + math.exp(-g))
+
+
+def test_swiglu_limit_special_values():
+    nan, inf = float("nan"), float("inf")
+    L = 10.0
+    cases = [  # (g, u, expected)
+        (20.0, 3.0, silu_exp(10.0) * 3.0),      # gate capped above
+        (-20.0, 3.0, silu_exp(-20.0) * 3.0),    # never below
+        (2.0, 15.0, silu_exp(2.0) * 10.0),      # up capped above
+        (2.0, -15.0, silu_exp(2.0) * -10.0),    # and below
+        (9.5, -9.5, silu_exp(9.5) * -9.5),      # inside: untouched
+        (inf, 1.0, silu_exp(10.0)),
+        (1.0, -inf, silu_exp(1.0) * -10.0),
+    ]
+    for g, u, want in cases:
+        assert math.isclose(oracle.activate("swiglu", g, u, L), want, rel_tol=1e-14), (g, u)
+    assert math.isnan(oracle.activate("swiglu", nan, 1.0, L))
+    assert math.isnan(oracle.activate("swiglu", 1.0, nan, L))
+    # limit 0 is no clamp
+    assert math.isclose(oracle.activate("swiglu", 20.0, 15.0, 0.0), silu_exp(20.0) * 15.0,
+                        rel_tol=1e-14)
+    # relu^2 takes no limit
+    assert oracle.activate("relu2", 0.0, 30.0, L) == 900.0
+
+
+def test_swiglu_limit_changes_exactly_the_clamped_tokens():
+    # Tokens none of whose routed or shared pre-activations pass the limit
+    # keep the limit-0 output bit for bit; every other token changes.
+    wl = W.MID["mid_swiglu_limit"].with_(T=40, x_std=6.5)
+    inp = W.generate(wl)
+    toks = np.arange(wl.T)
+    out_l, ids, _ = oracle.forward_tokens(wl, inp, toks, want_routing=True)
+    out_0 = oracle.forward_tokens(wl.with_(swiglu_limit=0.0), inp, toks)
+    x = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    wu = W.bf16_bits_to_f32(inp["w_up"]).astype(np.float64)
+    su = W.bf16_bits_to_f32(inp["shared_up"]).astype(np.float64)
+    L, I, Is = wl.swiglu_limit, wl.I, wl.I_shared
+    changed = 0
+    for t in range(wl.T):
+        pre = [wu[e] @ x[t] for e in ids[t]] + [su @ x[t]]
+        n = [I] * wl.k + [Is]
+        hit = any((p[:m] > L).any() or (np.abs(p[m:]) > L).any() for p, m in zip(pre, n))
+        same = (out_l[t] == out_0[t]).all()
+        assert same != hit, t
+        changed += hit
+    assert 0 < changed < wl.T
+
+
+def test_swiglu_limit_workload_clamps_the_stated_fractions():
+    # the input recipe of the limit case: gate one-sided ~16 %, up two-sided ~33 %
+    wl = W.MID["mid_swiglu_limit"]
+    inp = W.generate(wl)
+    x = W.bf16_bits_to_f32(inp["x"]).astype(np.float64)
+    wu = W.bf16_bits_to_f32(inp["w_up"][:4]).astype(np.float64)
+    g = np.einsum("th,enh->ten", x, wu[:, :wl.I])
+    u = np.einsum("th,enh->ten", x, wu[:, wl.I:])
+    L = wl.swiglu_limit
+    assert 0.13 < (g > L).mean() < 0.19
+    assert 0.28 < (np.abs(u) > L).mean() < 0.38

@@ -32,7 +32,8 @@ MUTANTS = {
         "return r * r;", "return r;",
         ["tests/test_oracle_experts.py::test_activation_special_values"]),
     "gate_up_swapped": (
-        "activate(0, proj[i], proj[I + i])", "activate(0, proj[I + i], proj[i])",
+        "activate(0, proj[i], proj[I + i], L->swiglu_limit)",
+        "activate(0, proj[I + i], proj[i], L->swiglu_limit)",
         ["tests/test_oracle_experts.py::test_hand_layer_closed_form"]),
     "silu_sign": (
         "g / (1.0 + exp(-g)) * u", "g / (1.0 + exp(g)) * u",
@@ -83,6 +84,28 @@ MUTANTS = {
     "affine_group_index": (
         "bf16_value(scale_row[c / group])", "bf16_value(scale_row[c % group])",
         ["tests/test_oracle_experts.py::test_affine4_decode_hand_cases"]),
+    "softmax_no_max_shift": (
+        "float d = z[e] - m;", "float d = z[e];",
+        ["tests/test_oracle_router.py::test_softmax32_exact_points"]),
+    "softmax_sum_descending": (
+        "    for (int e = 0; e < E; ++e) {\n        float d = z[e] - m;",
+        "    for (int e = E - 1; e >= 0; --e) {\n        float d = z[e] - m;",
+        ["tests/test_oracle_router.py::test_softmax32_sum_order_constructed"]),
+    "softmax_last_term_dropped": (
+        "        S = S + s[e];", "        if (e < E - 1)\n            S = S + s[e];",
+        ["tests/test_oracle_router.py::test_softmax32_exact_points"]),
+    "route_ignores_softmax": (
+        "if (score_fn == 1)", "if (score_fn == 2)",
+        ["tests/test_oracle_router.py::test_route_softmax_matches_brute_force_and_closed_weights"]),
+    "limit_gate_two_sided": (
+        "g = (g > limit) ? limit : g;", "g = (g > limit) ? limit : ((g < -limit) ? -limit : g);",
+        ["tests/test_oracle_experts.py::test_swiglu_limit_special_values"]),
+    "limit_up_one_sided": (
+        "u = (u > limit) ? limit : ((u < -limit) ? -limit : u);", "u = (u > limit) ? limit : u;",
+        ["tests/test_oracle_experts.py::test_swiglu_limit_special_values"]),
+    "limit_skips_shared_expert": (
+        "activate(0, proj[i], proj[Is + i], L->swiglu_limit)", "activate(0, proj[i], proj[Is + i], 0.0)",
+        ["tests/test_oracle_experts.py::test_swiglu_limit_changes_exactly_the_clamped_tokens"]),
     "exp_taylor_term_dropped": (
         "    p = fmaf(p, r, 1.0f / 6.0f);        /* 1/3! */\n", "",
         ["tests/test_oracle_router.py::test_exp32_sweep_against_libm"]),

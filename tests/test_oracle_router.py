@@ -257,3 +257,113 @@ def test_weights_sum_invariant_and_no_norm_mode():
     ids2, w2 = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k, norm_topk=False)
     assert (ids2 == ids).all()
     assert (w2 == np.take_along_axis(s, ids, axis=1).astype(np.float64)).all()
+
+
+# ---------------------------------------------------------------- softmax router
+# The other router family the pages list (TensorFold issue #548, the
+# consolidation proposal: softmax, and sigmoid + bias). Its fp32 steps are
+# this project's reading: m = largest non-NaN z, q = e^(z - m) (0 below
+# -87), S = q_0 + q_1 + ... from +0 in expert order, s = q / S.
+
+def test_softmax32_exact_points():
+    # equal logits: every q is e^0 = 1, S = E exactly, s = RN(1/E)
+    for E in (1, 3, 4, 64):
+        s = oracle.softmax32(np.full(E, 0.75, np.float32))
+        assert (s == np.float32(1.0) / np.float32(E)).all(), E
+    # one logit far above the rest: the others fall below -87 and give 0
+    assert list(oracle.softmax32([100.0, 0.0, -5.0])) == [1.0, 0.0, 0.0]
+    assert list(oracle.softmax32([0.0, -87.5])) == [1.0, 0.0]
+    # at -87 exactly the tail is kept: 1 + e^-87 rounds to 1
+    q = oracle.exp32([-87.0])[0]
+    assert q > 0 and list(oracle.softmax32([0.0, -87.0])) == [1.0, q]
+    # two logits ln 3 apart: 3/4 and 1/4 up to the exponential's rounding
+    s = oracle.softmax32([float(np.float32(math.log(3.0))), 0.0]).astype(np.float64)
+    assert abs(s[0] - 0.75) < 2e-7 and abs(s[1] - 0.25) < 2e-7
+
+
+def test_softmax32_nan_and_infinite_rows():
+    for z in ([1.0, np.nan, 0.0], [np.nan] * 5, [np.inf, 0.0], [np.inf, np.inf], [-np.inf] * 3):
+        assert np.isnan(oracle.softmax32(z)).all(), z
+    assert list(oracle.softmax32([-np.inf, 0.0, -np.inf])) == [0.0, 1.0, 0.0]
+
+
+def test_softmax32_sum_order_constructed():
+    # Four experts at -17 (q ~ 0.69 * 2^-24 each) and one at 0 (q = 1): added
+    # after the 1 each small q rounds away; added before it their sum (about
+    # 2.8 * 2^-24) lifts S to 1 + 2^-23. The max last gives S = 1 + 2^-23 in
+    # expert order, the max first S = 1.
+    q = float(oracle.exp32([-17.0])[0])
+    assert 0.5 * 2.0 ** -24 < q < 2.0 ** -24
+    s = oracle.softmax32([0.0, -17.0, -17.0, -17.0, -17.0])
+    assert s[0] == 1.0 and (s[1:] == np.float32(q)).all()
+    s = oracle.softmax32([-17.0, -17.0, -17.0, -17.0, 0.0])
+    big = np.float32(1.0 + 2.0 ** -23)
+    assert s[4] == np.float32(1.0) / big == np.float32(1.0 - 2.0 ** -23)
+    assert (s[:4] == np.float32(q) / big).all()
+
+
+@pytest.mark.parametrize("E", [8, 32, 128, 256])
+def test_softmax32_within_error_bound_of_float64(E):
+    # q carries the exponential's error (<= 1 ulp, swept above) and that of
+    # z - m (|d| u); S adds E - 1 roundings; the division one more.
+    rng = np.random.default_rng(E)
+    for _ in range(50):
+        z = (rng.standard_normal(E) * 3.0).astype(np.float32)
+        s = oracle.softmax32(z).astype(np.float64)
+        d = z.astype(np.float64) - z.max()
+        ref = np.exp(d) / np.exp(d).sum()
+        bound = (E + 4 + 2 * np.abs(d)) * U32 * ref + 1e-37
+        assert (np.abs(s - ref) <= bound).all()
+        assert abs(s.sum() - 1.0) <= 2 * E * U32
+
+
+def test_route_softmax_picks_the_largest_logits():
+    # the softmax is increasing in z: without a bias the picks are the k
+    # largest logits wherever the scores come out distinct
+    wl = W.MID["mid_softmax"]
+    inp = W.generate(wl, experts=False)
+    ids, w, z, s = oracle.route(inp["x"], inp["router_w"], None, wl.k, want_scores=True,
+                                score="softmax")
+    checked = 0
+    for t in range(wl.T):
+        if np.isnan(z[t]).any() or len(set(s[t])) < wl.E:
+            continue
+        assert list(ids[t]) == list(np.argsort(-z[t].astype(np.float64), kind="stable")[:wl.k])
+        checked += 1
+    assert checked > wl.T // 2
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_route_softmax_matches_brute_force_and_closed_weights(bias):
+    wl = W.MID["mid_softmax"]
+    inp = W.generate(wl, experts=False)
+    b = (np.linspace(-0.01, 0.01, wl.E, dtype=np.float32) if bias else None)
+    ids, w, z, s = oracle.route(inp["x"], inp["router_w"], b, wl.k, want_scores=True,
+                                score="softmax")
+    keys = s + (b[None, :] if bias else np.float32(0.0))
+    for t in range(wl.T):
+        assert list(ids[t]) == _brute_topk([float(v) for v in keys[t]], wl.k), t
+    for t in wl.nan_rows:
+        assert list(ids[t]) == list(range(wl.k)) and np.isnan(w[t]).all()
+    if not bias:
+        for t in wl.zero_rows:                  # 64-way tie at 1/64: the lowest ids
+            assert (s[t] == np.float32(1 / 64)).all() and list(ids[t]) == list(range(wl.k))
+            assert np.allclose(w[t], (1 / 64) / (wl.k / 64 + 1e-6), rtol=1e-15)
+        t = wl.onehot_tie_row                   # z = 2 exactly at experts 2 and 5
+        assert z[t, 2] == z[t, 5] == 2.0 and list(ids[t][:2]) == [2, 5] and w[t, 0] == w[t, 1]
+    sel = np.take_along_axis(s, ids, axis=1).astype(np.float64)
+    S = sel.sum(axis=1)
+    ok = ~np.isnan(S)
+    assert np.allclose(w[ok], (sel / (S + 1e-6)[:, None])[ok], rtol=1e-15)
+
+
+def test_route_softmax_all_experts_weights_sum_to_one():
+    # k = E and no eps: the picked scores are the whole row, w = s / sum s
+    wl = W.MID["mid_softmax"]
+    inp = W.generate(wl, experts=False)
+    x = inp["x"][:40]
+    ids, w = oracle.route(x, inp["router_w"][:16], None, 16, eps=0.0, score="softmax")
+    ok = ~np.isnan(w).any(axis=1)
+    assert ok.sum() > 30
+    assert np.allclose(w[ok].sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert (np.sort(ids, axis=1) == np.arange(16)).all()
