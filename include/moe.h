@@ -5,11 +5,14 @@
  * The block, for a token row x_t (H inputs):
  *   z[e]  = sum_h x[t,h] Wr[e,h]           fp32, h ascending, one fmaf per term
  *   s[e]  = 1 / (1 + exp(-z[e]))           fp32 (own exp, correctly rounded division)
+ *           or softmax: q[e] = exp(z[e] - max z) (0 below -87), s[e] = q[e] / sum q,
+ *           the sum from +0 in expert order (score_fn)
  *   ids   = the k experts of largest s[e] + bias[e]; the bias only selects
  *   w_j   = s[ids_j] / (sum_j s[ids_j] + norm_eps)   (or s[ids_j] when norm_topk == 0)
  *   y_j   = W_down[e] act(W_up[e] x_t),  e = ids_j
  *             SwiGLU: W_up = gate_up (E, 2I, H), gate rows first,
- *                     act = silu(gate) * up
+ *                     act = silu(min(gate, L)) * clamp(up, -L, L)
+ *                     (swiglu_limit L; no clamp when L == 0)
  *             relu^2: W_up = up (E, I, H), act = (up < 0 ? 0 : up)^2
  *   out_t = routed_scale * sum_j w_j y_j + shared_t
  *   shared_t = W_sd act(W_su x_t), added unscaled (optional)
@@ -21,7 +24,11 @@
  * commit (relu^2 expert; the routed scale multiplies the finished routed
  * sum, the shared output is added untouched; outputs are f32 or bf16 only);
  * TensorFold issue #548 (one grouped-MoE layer: routing plan plus
- * per-format experts behind one call, decode rows and prompt rows).
+ * per-format experts behind one call, decode rows and prompt rows; the
+ * softmax router family in its consolidation proposal; GLM's swiglu_limit
+ * in its table of untested expert paths, where about 16 % of gate and 33 %
+ * of up pre-activations clamp at limit 10: the gate on one side, up on
+ * both).
  *
  * Conventions for every entry point:
  *  - Tensors are row-major and live in device memory owned by the caller.
@@ -62,6 +69,7 @@ typedef enum {
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
 typedef enum { MOE_W_BF16 = 0, MOE_W_AFFINE4 = 1 } moe_wfmt;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out;
+typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score;
 
 /* Shape and options of one layer call. Limits: T >= 0; 1 <= E <= 256;
  * 1 <= k <= min(E, 8); H, I and I_shared multiples of 64 (I_shared may be
@@ -80,6 +88,9 @@ typedef struct {
     float routed_scale;   /* applied once, to the routed sum only */
     int32_t I_shared;     /* shared-expert intermediate size, 0 = none */
     int32_t out_dtype;    /* moe_out */
+    int32_t score_fn;     /* moe_score: router scores (the bias, if any, still only selects) */
+    float swiglu_limit;   /* 0: none; L > 0 (SwiGLU only, routed and shared experts):
+                             gate capped at L, up clamped to [-L, L], NaN kept */
 } moe_dims;
 
 /* Weights of one layer (device pointers).
@@ -125,7 +136,8 @@ int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
  *           routed_scale is not applied here.
  * Workspace: moe_workspace_bytes(d) (the router uses T*E*4 bytes of it, or
  * T*E*(H/64)*4 when T <= 8 and E <= 32: the partial logits of every slice).
- * Only T, H, E, k, norm_topk and norm_eps of d are read. */
+ * Only T, H, E, k, score_fn, norm_topk and norm_eps of d are read. A NaN
+ * logit makes every softmax score of its row NaN (picks 0, 1, ..., k-1). */
 int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
               const float *expert_bias, int32_t *ids, float *weights, void *workspace,
               size_t workspace_bytes, hipStream_t stream);

@@ -109,6 +109,9 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
             "%s: norm_topk = %d, need 0 or 1", what, d->norm_topk);
     REQUIRE(std::isfinite(d->norm_eps) && d->norm_eps >= 0.0f, MOE_E_SHAPE,
             "%s: norm_eps = %g, need a finite value >= 0", what, (double)d->norm_eps);
+    REQUIRE(d->score_fn == MOE_SCORE_SIGMOID || d->score_fn == MOE_SCORE_SOFTMAX,
+            MOE_E_UNSUPPORTED, "%s: score_fn = %d, need MOE_SCORE_SIGMOID (0) or "
+            "MOE_SCORE_SOFTMAX (1)", what, d->score_fn);
     if (!experts)
         return MOE_OK;
     REQUIRE(d->I > 0 && d->I % 64 == 0 && d->I <= 65536, MOE_E_SHAPE,
@@ -132,6 +135,11 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
             "%s: out_dtype = %d, need MOE_OUT_BF16 (0) or MOE_OUT_F32 (1)", what, d->out_dtype);
     REQUIRE(std::isfinite(d->routed_scale), MOE_E_SHAPE, "%s: routed_scale = %g is not finite",
             what, (double)d->routed_scale);
+    REQUIRE(std::isfinite(d->swiglu_limit) && d->swiglu_limit >= 0.0f, MOE_E_SHAPE,
+            "%s: swiglu_limit = %g, need a finite value >= 0", what, (double)d->swiglu_limit);
+    REQUIRE(d->swiglu_limit == 0.0f || d->act == MOE_ACT_SWIGLU, MOE_E_UNSUPPORTED,
+            "%s: swiglu_limit = %g applies to MOE_ACT_SWIGLU only (act = %d)", what,
+            (double)d->swiglu_limit, d->act);
     return MOE_OK;
 }
 
@@ -215,9 +223,9 @@ int moe_route(const moe_dims *d, const uint16_t *x, const float *router_w,
                            std::make_pair("weights", (const void *)weights),
                            std::make_pair("workspace", (const void *)workspace)})
         TRY(check_device(what, pr.first, pr.second));
-    LAUNCH(moe::launch_route(x, router_w, expert_bias, d->T, d->H, d->E, d->k, d->norm_topk,
-                             d->norm_eps, ids, weights, (float *)workspace, moe::PlanOut{},
-                             nullptr, stream));
+    LAUNCH(moe::launch_route(x, router_w, expert_bias, d->T, d->H, d->E, d->k, d->score_fn,
+                             d->norm_topk, d->norm_eps, ids, weights, (float *)workspace,
+                             moe::PlanOut{}, nullptr, stream));
     return ok();
 }
 
@@ -317,8 +325,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     };
     LAUNCH(mark(0));
     bool plan_done = false;
-    LAUNCH(moe::launch_route(x, w->router_w, w->expert_bias, T, H, E, k, d->norm_topk,
-                             d->norm_eps, ids, wts, (float *)(ws + L.z),
+    LAUNCH(moe::launch_route(x, w->router_w, w->expert_bias, T, H, E, k, d->score_fn,
+                             d->norm_topk, d->norm_eps, ids, wts, (float *)(ws + L.z),
                              moe::PlanOut{counts, offsets, sorted, slot}, &plan_done, stream));
     LAUNCH(mark(1));
     if (!plan_done)
@@ -335,7 +343,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     };
 
     moe::GemmProblem up{};
-    up.mode = d->act == MOE_ACT_SWIGLU ? moe::kGateUp : moe::kUpRelu2;
+    const int gate_mode = d->swiglu_limit > 0.0f ? moe::kGateUpLimit : moe::kGateUp;
+    up.mode = d->act == MOE_ACT_SWIGLU ? gate_mode : moe::kUpRelu2;
     up.affine4 = aff;
     up.A = x;
     up.lda = H;
@@ -352,6 +361,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     up.I = I;
     up.C = h;
     up.ldc = I;
+    up.limit = d->swiglu_limit;
     // 4-bit weights, prompt-sized batch (dequant_first): decoded to bf16
     // first, then the bf16 kernel on the experts with rows
     uint16_t *wdq = (uint16_t *)(ws + L.wdq);
@@ -403,7 +413,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         uint16_t *hs = (uint16_t *)(ws + L.hs);
         float *ys = (float *)(ws + L.ys);
         moe::GemmProblem su{};
-        su.mode = d->act == MOE_ACT_SWIGLU ? moe::kGateUp : moe::kUpRelu2;
+        su.mode = up.mode;
         su.A = x;
         su.lda = H;
         su.rows = T;
@@ -415,6 +425,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         su.I = Is;
         su.C = hs;
         su.ldc = Is;
+        su.limit = up.limit;
         LAUNCH(run(su));
         moe::GemmProblem sd{};
         sd.mode = moe::kDown;

@@ -90,11 +90,33 @@ __device__ __forceinline__ float sigmoid_score(float z) {
     return 1.0f / (1.0f + exp_cw(-z));
 }
 
+// Softmax router term e^d for d = z - (the row's largest logit) <= 0: 0
+// below -87 (the sigmoid's tail rule), NaN stays NaN.
+__device__ __forceinline__ float softmax_term(float d) {
+    if (d != d)
+        return d;
+    if (d < -87.0f)
+        return 0.0f;
+    return exp_cw(d);
+}
+
 // SwiGLU epilogue: silu(g) * u with the hardware exp2 and reciprocal.
 // Not bit-specified; held to the block's output tolerance.
 __device__ __forceinline__ float silu_mul(float g, float u) {
     const float e = __builtin_amdgcn_exp2f(-g * 0x1.715476p+0f);
     return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
+}
+
+// The same with GLM's swiglu_limit L when LIMIT (a separate instantiation,
+// so the unlimited epilogue carries no extra instructions): g capped at L,
+// u clamped to [-L, L], by comparisons, which keep a NaN.
+template <bool LIMIT>
+__device__ __forceinline__ float swiglu(float g, float u, float L) {
+    if constexpr (LIMIT) {
+        g = g > L ? L : g;
+        u = u > L ? L : (u < -L ? -L : u);
+    }
+    return silu_mul(g, u);
 }
 
 // relu^2 epilogue: (u < 0 ? 0 : u)^2 in fp32; NaN and +inf pass through.

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int n_tiles
     row0 = __builtin_amdgcn_readfirstlane(row0);
     row_end = __builtin_amdgcn_readfirstlane(row_end);
     nt = __builtin_amdgcn_readfirstlane(nt);
-    const int n_out0 = nt * (MODE == kGateUp ? BN / 2 : BN);
+    const int n_out0 = nt * (gated(MODE) ? BN / 2 : BN);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int n_tiles
 
     // ---- B rows this thread stages (clamped below N), relative to expert e
     auto b_row = [&](int r) -> int {
-        if (MODE == kGateUp) {
+        if (gated(MODE)) {
             int n = n_out0 + (r % (BN / 2));
             if (n >= p.I)
                 n = p.I - 1;
@@ -313,11 +313,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int n_tiles
     // LDS slot of this lane's fragment piece for each sub-step; the tiles of
     // a wave sit 32 rows apart, which keeps the swizzle and adds 256 slots
     const int a_tile_row = wm * (BM / 2);
-    const int b_row0 = MODE == kGateUp ? wn * (BN / 4) : wn * (BN / 2);
+    const int b_row0 = gated(MODE) ? wn * (BN / 4) : wn * (BN / 2);
     int b_tile_off[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        if (MODE == kGateUp)
+        if (gated(MODE))
             b_tile_off[j] = (j < TN / 2) ? j * 32 : BN / 2 + (j - TN / 2) * 32;
         else
             b_tile_off[j] = j * 32;
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int n_tiles
     // bf16 h: each wave transposes its (BM/2) x CW block through LDS (the
     // operand buffers are idle after the last barrier) so the global stores
     // are whole 16-byte row pieces
-    constexpr int CW = MODE == kGateUp ? BN / 4 : BN / 2;   // output columns per wave
+    constexpr int CW = gated(MODE) ? BN / 4 : BN / 2;   // output columns per wave
     constexpr int CT = CW / 32;                              // 32-col tiles per wave
     uint16_t *hs = (uint16_t *)smem + (size_t)wave * (BM / 2) * CW;
 #pragma unroll
@@ -440,13 +440,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int n_tiles
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = i * 32 + 8 * (r >> 2) + rsub + (r & 3);
-                const float v = MODE == kGateUp ? silu_mul(acc[i][j][r], acc[i][j + TN / 2][r])
-                                                : relu_sq(acc[i][j][r]);
+                constexpr bool LIM = MODE == kGateUpLimit;
+                const float v = gated(MODE)
+                                    ? swiglu<LIM>(acc[i][j][r], acc[i][j + TN / 2][r], p.limit)
+                                    : relu_sq(acc[i][j][r]);
                 hs[row * CW + j * 32 + col] = (uint16_t)f32_to_bf16(v);
             }
     __syncthreads();
     uint16_t *h = (uint16_t *)p.C;
-    const int ncols = MODE == kGateUp ? p.I : p.N;
+    const int ncols = gated(MODE) ? p.I : p.N;
     const int wcol0 = n_out0 + wn * CW;
     constexpr int PIECES = (BM / 2) * CW / 8;                // 16-byte pieces per wave
 #pragma unroll 4
@@ -462,8 +464,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm(GemmProblem p, int n_tiles
 
 template <int BM, int MODE, bool AFF>
 hipError_t launch_tile(const GemmProblem &p, hipStream_t stream) {
-    const int n_cols = MODE == kGateUp ? p.I : p.N;
-    const int n_tile = MODE == kGateUp ? 128 : 256;
+    const int n_cols = gated(MODE) ? p.I : p.N;
+    const int n_tile = gated(MODE) ? 128 : 256;
     const int n_tiles = (n_cols + n_tile - 1) / n_tile;
     const int blocks = grid_blocks<BM>(p, n_tiles);
     if (blocks == 0)
@@ -555,12 +557,14 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
     if (p.affine4) {
         switch (p.mode) {
         case kGateUp: return launch_mode<kGateUp, true>(p, stream);
+        case kGateUpLimit: return launch_mode<kGateUpLimit, true>(p, stream);
         case kUpRelu2: return launch_mode<kUpRelu2, true>(p, stream);
         default: return launch_mode<kDown, true>(p, stream);
         }
     }
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp, false>(p, stream);
+    case kGateUpLimit: return launch_mode<kGateUpLimit, false>(p, stream);
     case kUpRelu2: return launch_mode<kUpRelu2, false>(p, stream);
     default: return launch_mode<kDown, false>(p, stream);
     }

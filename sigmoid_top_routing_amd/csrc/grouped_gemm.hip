@@ -207,7 +207,7 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
         const int r = s >> 2;
         const int c = (s & 3) ^ ((r >> 2) & 3);
         int wr;
-        if (MODE == kGateUp) {
+        if (gated(MODE)) {
             int n = nt * (kBN / 2) + (r & (kBN / 2 - 1));
             if (n >= p.I)
                 n = p.I - 1;
@@ -413,11 +413,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     // LDS slots of this lane's fragment pieces for sub-steps 0 and 1; the
     // tiles of a wave sit 32 rows apart, which keeps the swizzle (+128 slots)
     const int a_tile_row = wm * (BM / 2);
-    const int b_row0 = MODE == kGateUp ? wn * (kBN / 4) : wn * (kBN / 2);
+    const int b_row0 = gated(MODE) ? wn * (kBN / 4) : wn * (kBN / 2);
     int b_toff[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-        if (MODE == kGateUp)
+        if (gated(MODE))
             b_toff[j] = ((j < TN / 2) ? j * 32 : kBN / 2 + (j - TN / 2) * 32) * 4;
         else
             b_toff[j] = j * 32 * 4;
@@ -548,11 +548,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
             // per 32-row block, two tiles of 32 output columns at a time:
             // bf16, written to LDS as rows of 128 bytes (4 KB per wave),
             // then stored in 16-byte pieces of whole rows
-            constexpr int JO = MODE == kGateUp ? TN / 2 : TN;     // output column tiles
+            constexpr int JO = gated(MODE) ? TN / 2 : TN;     // output column tiles
             static_assert(JO % 2 == 0, "output column tiles come in pairs");
-            const int ncols = MODE == kGateUp ? p.I : p.N;
-            const int n0 = nt * (MODE == kGateUp ? kBN / 2 : kBN) +
-                           wn * (MODE == kGateUp ? kBN / 4 : kBN / 2);
+            const int ncols = gated(MODE) ? p.I : p.N;
+            const int n0 = nt * (gated(MODE) ? kBN / 2 : kBN) +
+                           wn * (gated(MODE) ? kBN / 4 : kBN / 2);
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -568,16 +568,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(gv[r]) : "a"(acc[i][j][r]));
-                            if (MODE == kGateUp)
+                            if (gated(MODE))
                                 __asm__ volatile("v_accvgpr_read_b32 %0, %1"
                                                  : "=v"(uv[r])
                                                  : "a"(acc[i][j + TN / 2][r]));
                         }
 #pragma unroll
                         for (int c = 0; c < 8; ++c) {
-                            const float x0 = MODE == kGateUp ? silu_mul(gv[2 * c], uv[2 * c]) : relu_sq(gv[2 * c]);
-                            const float x1 = MODE == kGateUp ? silu_mul(gv[2 * c + 1], uv[2 * c + 1])
-                                                             : relu_sq(gv[2 * c + 1]);
+                            constexpr bool LIM = MODE == kGateUpLimit;
+                            const float x0 = gated(MODE)
+                                                 ? swiglu<LIM>(gv[2 * c], uv[2 * c], p.limit)
+                                                 : relu_sq(gv[2 * c]);
+                            const float x1 = gated(MODE)
+                                                 ? swiglu<LIM>(gv[2 * c + 1], uv[2 * c + 1], p.limit)
+                                                 : relu_sq(gv[2 * c + 1]);
                             hv[jj][c] = pack_bf16x2(x0, x1);
                         }
                     }
@@ -647,8 +651,8 @@ long long tiles_bound(const GemmProblem &p, int &n_tiles) {
         const int nonempty = p.E < p.max_rows ? p.E : p.max_rows;
         mt_max = (p.max_rows + BM - 1) / BM + nonempty;
     }
-    const int n_cols = MODE == kGateUp ? p.I : p.N;
-    const int n_tile = MODE == kGateUp ? kBN / 2 : kBN;
+    const int n_cols = gated(MODE) ? p.I : p.N;
+    const int n_tile = gated(MODE) ? kBN / 2 : kBN;
     n_tiles = (n_cols + n_tile - 1) / n_tile;
     return (long long)mt_max * n_tiles;
 }
@@ -709,6 +713,7 @@ bool grouped_supported(const GemmProblem &p) {
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream) {
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp>(p, stream);
+    case kGateUpLimit: return launch_mode<kGateUpLimit>(p, stream);
     case kUpRelu2: return launch_mode<kUpRelu2>(p, stream);
     default: return launch_mode<kDown>(p, stream);
     }

@@ -23,9 +23,11 @@ constexpr int kFusedPlanMaxA = 1024;
 // every token (decode-sized batches), the top-k launch also writes the plan
 // and *plan_done is set; otherwise the caller runs launch_plan.
 size_t route_scratch_bytes(int T, int H, int E);
+// softmax: 0 sigmoid scores, 1 the softmax of each token's logits.
 hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, int T, int H, int E,
-                        int k, int norm_topk, float eps, int32_t *ids, float *weights,
-                        float *z_scratch, PlanOut plan, bool *plan_done, hipStream_t stream);
+                        int k, int softmax, int norm_topk, float eps, int32_t *ids,
+                        float *weights, float *z_scratch, PlanOut plan, bool *plan_done,
+                        hipStream_t stream);
 
 // Plan scratch: per-chunk expert counts, plan_chunks(A) x E int32.
 int plan_chunk_size(int A);
@@ -35,7 +37,9 @@ hipError_t launch_plan(const int32_t *ids, int A, int E, int32_t *counts, int32_
                        hipStream_t stream);
 
 // Grouped GEMM over expert segments.
-enum GemmMode { kGateUp = 0, kUpRelu2 = 1, kDown = 2 };
+// kGateUpLimit: kGateUp with the SwiGLU inputs clamped at GemmProblem::limit.
+enum GemmMode { kGateUp = 0, kUpRelu2 = 1, kDown = 2, kGateUpLimit = 3 };
+constexpr bool gated(int mode) { return mode == kGateUp || mode == kGateUpLimit; }
 
 struct GemmProblem {
     int mode;                 // GemmMode
@@ -58,6 +62,7 @@ struct GemmProblem {
     int ldc;
     const int32_t *scatter;   // kDown: output row of position p = scatter[p] (NULL: row p)
     int b_compact;            // B holds only the experts with rows, in expert order
+    float limit;              // kGateUpLimit: the SwiGLU input limit L > 0
 };
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);

@@ -9,6 +9,10 @@
 //              alone, are added by the top-k; the width is not given, 64 is
 //              this library's)
 //   s[t,e]   = 1 / (1 + e^-z)           (own exp, correctly rounded division)
+//              or, for the softmax router family (TensorFold issue #548, the
+//              consolidation proposal): m = the row's largest non-NaN z,
+//              q[e] = e^(z[e] - m) (0 below -87), S = q[0] + q[1] + ...
+//              from +0 in expert order, s[t,e] = q[e] / S
 //   key[t,e] = s[t,e] + bias[e]          (the bias only selects)
 //   ids[t,:] = k experts by key, best first; ties to the lower index; NaN last
 //   w[t,j]   = s[t,ids_j] / (sum_j s[t,ids_j] + eps)
@@ -24,7 +28,7 @@
 // the chip) and k_route_fold; at most 8 tokens with more experts,
 // k_logits_few.
 //
-// k_topk reads z, applies the sigmoid and the bias, and picks the top k of
+// k_topk reads z, applies the sigmoid (or softmax) and the bias, and picks the top k of
 // each token by the 64-bit (order key, ~index) candidates: with one expert
 // per lane each lane counts the larger candidates of its token (its rank),
 // else k rounds of xor-shuffle maxima over the token's lanes; then the
@@ -499,9 +503,9 @@ constexpr int kTopkLds = 2 * kFusedPlanMaxA + 2 * 256 + kMaxThreads / kWave;
 // per lane; with one, LPT <= MAXL.
 template <int RE, int MAXL = 64>
 __device__ __forceinline__ void topk_block(const float *z, const float *__restrict__ bias, int T,
-                                           int E, int k, int LPT, int norm_topk, float eps,
-                                           int32_t *__restrict__ ids, float *__restrict__ weights,
-                                           PlanOut plan, int *lds) {
+                                           int E, int k, int LPT, int softmax, int norm_topk,
+                                           float eps, int32_t *__restrict__ ids,
+                                           float *__restrict__ weights, PlanOut plan, int *lds) {
     int *s_ids = lds;
     int *s_rank = s_ids + kFusedPlanMaxA;
     int *s_cnt = s_rank + kFusedPlanMaxA;
@@ -516,11 +520,54 @@ __device__ __forceinline__ void topk_block(const float *z, const float *__restri
 
     float s[RE];
     uint64_t cand[RE];
+    if (softmax) {
+        // the row's largest non-NaN logit (exact: a max over the token's
+        // lanes), the terms e^(z - m), and their sum in expert order: every
+        // lane of the token adds the token's terms from LDS (the region of
+        // the plan's ids, written again only after the barriers below)
+        float zr[RE], q[RE];
+        float m = -__builtin_inff();
+#pragma unroll
+        for (int r = 0; r < RE; ++r) {
+            const int e = eg + r * LPT;
+            const bool real = t < T && e < E;
+            zr[r] = real ? z[(size_t)t * E + e] : 0.0f;
+            m = real && zr[r] > m ? zr[r] : m;
+        }
+        for (int msk = 1; msk < LPT; msk <<= 1) {
+            const float o = __shfl_xor(m, msk, kWave);
+            m = o > m ? o : m;
+        }
+        float *qs = reinterpret_cast<float *>(s_ids) + tb * LPT * RE;   // even: 8-byte aligned
+#pragma unroll
+        for (int r = 0; r < RE; ++r) {
+            const int e = eg + r * LPT;
+            q[r] = t < T && e < E ? softmax_term(zr[r] - m) : 0.0f;
+            qs[e] = q[r];
+        }
+        __syncthreads();
+        float S = 0.0f;
+        for (int e = 0; e < E; e += 2) {
+            const float2 v = *reinterpret_cast<const float2 *>(qs + e);
+            S = S + v.x;
+            S = e + 1 < E ? S + v.y : S;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < RE; ++r)
+            s[r] = q[r] / S;
+    } else {
+#pragma unroll
+        for (int r = 0; r < RE; ++r) {
+            const int e = eg + r * LPT;
+            s[r] = t < T && e < E ? sigmoid_score(z[(size_t)t * E + e]) : 0.0f;
+        }
+    }
 #pragma unroll
     for (int r = 0; r < RE; ++r) {
         const int e = eg + r * LPT;
         const bool real = t < T && e < E;
-        s[r] = real ? sigmoid_score(z[(size_t)t * E + e]) : 0.0f;
+        s[r] = real ? s[r] : 0.0f;
         const float key = s[r] + (bias != nullptr && real ? bias[e] : 0.0f);
         cand[r] = real ? (((uint64_t)order_key(key) << 32) | (uint32_t)(0xffffu - e)) : 0ull;
     }
@@ -661,11 +708,12 @@ __device__ __forceinline__ void topk_block(const float *z, const float *__restri
 template <int RE>
 __global__ __launch_bounds__(kMaxThreads) void k_topk(const float *__restrict__ z,
                                                       const float *__restrict__ bias, int T,
-                                                      int E, int k, int LPT, int norm_topk,
-                                                      float eps, int32_t *__restrict__ ids,
+                                                      int E, int k, int LPT, int softmax,
+                                                      int norm_topk, float eps,
+                                                      int32_t *__restrict__ ids,
                                                       float *__restrict__ weights, PlanOut plan) {
-    __shared__ int lds[kTopkLds];
-    topk_block<RE>(z, bias, T, E, k, LPT, norm_topk, eps, ids, weights, plan, lds);
+    __shared__ __align__(16) int lds[kTopkLds];
+    topk_block<RE>(z, bias, T, E, k, LPT, softmax, norm_topk, eps, ids, weights, plan, lds);
 }
 
 // The router of a decode-sized batch (T <= 8, E <= 32) in two launches.
@@ -767,9 +815,9 @@ constexpr int kFoldBatch = 32;                          // partial loads in flig
 __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 k_route_fold(
     const float *__restrict__ part, const float *__restrict__ bias, int T, int H, int E, int k,
-    int LPT, int norm_topk, float eps, int32_t *__restrict__ ids, float *__restrict__ weights,
-    PlanOut plan) {
-    __shared__ int lds[kDecT * kDecE + kDecE + kTopkLds];
+    int LPT, int softmax, int norm_topk, float eps, int32_t *__restrict__ ids,
+    float *__restrict__ weights, PlanOut plan) {
+    __shared__ __align__(16) int lds[kDecT * kDecE + kDecE + kTopkLds];
     float *zs = reinterpret_cast<float *>(lds);
     float *bs = zs + kDecT * kDecE;                     // the bias, read with the partials
     const int lane = threadIdx.x & (kWave - 1);
@@ -805,8 +853,8 @@ k_route_fold(
     if (tid < E)
         bs[tid] = b;
     __syncthreads();
-    topk_block<1, kDecE>(zs, bias != nullptr ? bs : nullptr, T, E, k, LPT, norm_topk, eps, ids,
-                         weights, plan, lds + kDecT * kDecE + kDecE);
+    topk_block<1, kDecE>(zs, bias != nullptr ? bs : nullptr, T, E, k, LPT, softmax, norm_topk,
+                         eps, ids, weights, plan, lds + kDecT * kDecE + kDecE);
 }
 
 // Two chains per lane when that still leaves a few hundred workgroups,
@@ -834,8 +882,9 @@ size_t route_scratch_bytes(int T, int H, int E) {
 }
 
 hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, int T, int H, int E,
-                        int k, int norm_topk, float eps, int32_t *ids, float *weights,
-                        float *z_scratch, PlanOut plan, bool *plan_done, hipStream_t stream) {
+                        int k, int softmax, int norm_topk, float eps, int32_t *ids,
+                        float *weights, float *z_scratch, PlanOut plan, bool *plan_done,
+                        hipStream_t stream) {
     if (plan_done != nullptr)
         *plan_done = false;
     if (T == 0)
@@ -858,7 +907,7 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
         if (!fuse)
             plan = PlanOut{};
         hipLaunchKernelGGL(k_route_fold, dim3(1), dim3(kMaxThreads), 0, stream, z_scratch, bias, T,
-                           H, E, k, LPT, norm_topk, eps, ids, weights, plan);
+                           H, E, k, LPT, softmax, norm_topk, eps, ids, weights, plan);
         err = hipGetLastError();
         if (err == hipSuccess && plan_done != nullptr)
             *plan_done = fuse;
@@ -895,15 +944,15 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
     switch (RE) {
     case 1:
         hipLaunchKernelGGL(k_topk<1>, grid, dim3(kMaxThreads), 0, stream, z_scratch, bias, T, E,
-                           k, LPT, norm_topk, eps, ids, weights, plan);
+                           k, LPT, softmax, norm_topk, eps, ids, weights, plan);
         break;
     case 2:
         hipLaunchKernelGGL(k_topk<2>, grid, dim3(kMaxThreads), 0, stream, z_scratch, bias, T, E,
-                           k, LPT, norm_topk, eps, ids, weights, plan);
+                           k, LPT, softmax, norm_topk, eps, ids, weights, plan);
         break;
     default:
         hipLaunchKernelGGL(k_topk<4>, grid, dim3(kMaxThreads), 0, stream, z_scratch, bias, T, E,
-                           k, LPT, norm_topk, eps, ids, weights, plan);
+                           k, LPT, softmax, norm_topk, eps, ids, weights, plan);
         break;
     }
     err = hipGetLastError();

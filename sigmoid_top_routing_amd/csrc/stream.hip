@@ -94,7 +94,7 @@ __device__ __forceinline__ void transpose_reduce(float (&v)[V], int lane) {
 
 template <int MODE, int NJ>
 __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
-    constexpr int NR = MODE == kGateUp ? 2 : 1;   // weight rows per unit
+    constexpr int NR = gated(MODE) ? 2 : 1;   // weight rows per unit
     constexpr int UW = units_per_wave<NJ>();
     __shared__ uint4 xs[kTG][NJ * kWave];          // token rows, bf16
     const int lane = threadIdx.x & (kWave - 1);
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
     }
     if (seg0 >= seg1)
         return;                                    // uniform
-    const int units = MODE == kGateUp ? p.I : p.N;
+    const int units = gated(MODE) ? p.I : p.N;
     const int wave = threadIdx.x / kWave;
     const int K = p.K;
     const uint16_t *B = (const uint16_t *)p.B + (size_t)e * p.N * K;
@@ -189,9 +189,9 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
             const int r = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
             if ((lane & 15) == 0 && r < nr && u < units) {
                 const int pos = g0 + r;
-                if (MODE == kGateUp) {
+                if (gated(MODE)) {
                     ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
-                        (uint16_t)f32_to_bf16(silu_mul(v[0], v[1]));
+                        (uint16_t)f32_to_bf16(swiglu<MODE == kGateUpLimit>(v[0], v[1], p.limit));
                 } else if (MODE == kUpRelu2) {
                     ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
                         (uint16_t)f32_to_bf16(relu_sq(v[0]));
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
 
 template <int MODE, int NJ>
 hipError_t launch_nj(const GemmProblem &p, hipStream_t stream) {
-    const int units = MODE == kGateUp ? p.I : p.N;
+    const int units = gated(MODE) ? p.I : p.N;
     const int upb = units_per_block<NJ>();
     const dim3 grid((units + upb - 1) / upb, p.offsets != nullptr ? p.E : 1);
     hipLaunchKernelGGL((k_stream<MODE, NJ>), grid, dim3(kThreads), 0, stream, p);
@@ -234,6 +234,7 @@ bool stream_supported(const GemmProblem &p) {
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream) {
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp>(p, stream);
+    case kGateUpLimit: return launch_mode<kGateUpLimit>(p, stream);
     case kUpRelu2: return launch_mode<kUpRelu2>(p, stream);
     default: return launch_mode<kDown>(p, stream);
     }

@@ -22,6 +22,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_ALIGN",
 ACT = {"swiglu": 0, "relu2": 1}
 WFMT = {"bf16": 0, "affine4": 1}
 OUT = {torch.bfloat16: 0, torch.float32: 1}
+SCORE = {"sigmoid": 0, "softmax": 1}
 
 # every entry point include/moe.h declares
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_plan", "moe_forward", "moe_forward_profiled",
@@ -40,7 +41,8 @@ class Dims(C.Structure):
     _fields_ = [("T", C.c_int32), ("H", C.c_int32), ("I", C.c_int32), ("E", C.c_int32),
                 ("k", C.c_int32), ("act", C.c_int32), ("wfmt", C.c_int32), ("group", C.c_int32),
                 ("norm_topk", C.c_int32), ("norm_eps", C.c_float), ("routed_scale", C.c_float),
-                ("I_shared", C.c_int32), ("out_dtype", C.c_int32)]
+                ("I_shared", C.c_int32), ("out_dtype", C.c_int32), ("score_fn", C.c_int32),
+                ("swiglu_limit", C.c_float)]
 
 
 class Weights(C.Structure):
@@ -93,10 +95,12 @@ def _stream(stream=None):
 
 
 def make_dims(T, H, I, E, k, act="swiglu", wfmt="bf16", rsf=1.0, I_shared=0, norm_topk=True,
-              norm_eps=1e-6, out_dtype=torch.bfloat16) -> Dims:
+              norm_eps=1e-6, out_dtype=torch.bfloat16, score="sigmoid",
+              swiglu_limit=0.0) -> Dims:
     return Dims(T=T, H=H, I=I, E=E, k=k, act=ACT[act], wfmt=WFMT[wfmt],
                 group=64 if wfmt == "affine4" else 0, norm_topk=int(norm_topk),
-                norm_eps=norm_eps, routed_scale=rsf, I_shared=I_shared, out_dtype=OUT[out_dtype])
+                norm_eps=norm_eps, routed_scale=rsf, I_shared=I_shared, out_dtype=OUT[out_dtype],
+                score_fn=SCORE[score], swiglu_limit=swiglu_limit)
 
 
 def workspace_bytes(d: Dims) -> int:
@@ -105,11 +109,11 @@ def workspace_bytes(d: Dims) -> int:
     return n.value
 
 
-def route(x, router_w, bias, k, norm_topk=True, norm_eps=1e-6, stream=None):
+def route(x, router_w, bias, k, norm_topk=True, norm_eps=1e-6, stream=None, score="sigmoid"):
     """ids [T,k] int32 and weights [T,k] fp32 (moe_route)."""
     T, H = x.shape
     E = router_w.shape[0]
-    d = make_dims(T, H, 64, E, k, norm_topk=norm_topk, norm_eps=norm_eps)
+    d = make_dims(T, H, 64, E, k, norm_topk=norm_topk, norm_eps=norm_eps, score=score)
     ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
     w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     nbytes = workspace_bytes(d)
@@ -163,13 +167,16 @@ class MoEBlock:
     I_shared: int = 0
     norm_topk: bool = True
     norm_eps: float = 1e-6
+    score: str = "sigmoid"
+    swiglu_limit: float = 0.0
 
     def __post_init__(self):
         self._ws = None
 
     def dims(self, T, out_dtype=torch.bfloat16) -> Dims:
         return make_dims(T, self.H, self.I, self.E, self.k, self.act, self.wfmt, self.rsf,
-                         self.I_shared, self.norm_topk, self.norm_eps, out_dtype)
+                         self.I_shared, self.norm_topk, self.norm_eps, out_dtype, self.score,
+                         self.swiglu_limit)
 
     def weights(self) -> Weights:
         return Weights(router_w=_ptr(self.router_w), expert_bias=_ptr(self.bias),
@@ -244,7 +251,8 @@ def block_from_arrays(wl, inp: dict, device="cuda") -> MoEBlock:
                     w_down_biases=dev("w_down_biases", True),
                     shared_up=dev("shared_up", True), shared_down=dev("shared_down", True),
                     act=wl.act, wfmt=wl.wfmt, rsf=wl.rsf, I_shared=wl.I_shared,
-                    norm_topk=wl.norm_topk, norm_eps=wl.norm_eps)
+                    norm_topk=wl.norm_topk, norm_eps=wl.norm_eps, score=wl.score,
+                    swiglu_limit=wl.swiglu_limit)
 
 
 def x_to_device(x_bits, device="cuda") -> torch.Tensor:

@@ -93,6 +93,17 @@ def test_unsupported_options_are_refused():
     d = dims()
     d.out_dtype = 5
     assert ws_bytes(d)[0] == -4
+    d = dims()
+    d.score_fn = 2
+    assert ws_bytes(d)[0] == -4
+    assert "score_fn = 2" in lib.load().moe_last_error().decode()
+    d = dims(act="relu2", swiglu_limit=10.0)
+    assert ws_bytes(d)[0] == -4
+    assert "swiglu_limit" in lib.load().moe_last_error().decode()
+    for bad in (-1.0, float("nan"), float("inf")):
+        assert ws_bytes(dims(swiglu_limit=bad))[0] == -2
+    assert ws_bytes(dims(swiglu_limit=10.0))[0] == 0
+    assert ws_bytes(dims(score="softmax"))[0] == 0
 
 
 def _fake(addr):
