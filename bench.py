@@ -119,6 +119,20 @@ def cpu_baseline(wl, inp, budget_s=15.0):
                       f"per token), {dt:.1f} s on {threads} threads"}
 
 
+def variant(wl, args):
+    """The workload with the router scores or SwiGLU limit the flags ask for
+    (its name then says so)."""
+    kw = {}
+    if args.score is not None and args.score != wl.score:
+        kw["score"] = args.score
+    if args.swiglu_limit is not None and args.swiglu_limit != wl.swiglu_limit:
+        kw["swiglu_limit"] = args.swiglu_limit
+    if not kw:
+        return wl
+    tag = "".join(f"+{k}={v}" for k, v in kw.items())
+    return wl.with_(name=wl.name + tag, **kw)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +141,10 @@ def main():
     ap.add_argument("--workload", default="lfm2_prefill_t4096")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--score", choices=("sigmoid", "softmax"), default=None,
+                    help="router scores in place of the workload's own")
+    ap.add_argument("--swiglu-limit", type=float, default=None,
+                    help="SwiGLU input limit in place of the workload's own")
     ap.add_argument("--profile-run", action="store_true",
                     help="untimed calls plus a calibration copy, for rocprofv3 to wrap")
     args = ap.parse_args()
@@ -142,7 +160,7 @@ def main():
     from sigmoid_top_routing_amd import lib
     from sigmoid_top_routing_amd import workloads as W
 
-    wl = W.by_name(args.workload)
+    wl = variant(W.by_name(args.workload), args)
     inp = W.generate(wl)
     block = lib.block_from_arrays(wl, inp)
     x = lib.x_to_device(inp["x"])
@@ -204,6 +222,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
                    "act": wl.act, "weights": wl.wfmt, "rsf": wl.rsf, "I_shared": wl.I_shared,
+                   "score": wl.score, "swiglu_limit": wl.swiglu_limit,
                    "parallelism": "single GPU"},
         "roofline": roof,
         "block": {"tflops": total_f / (ms_per_step * 1e-3) / 1e12,
@@ -211,7 +230,7 @@ def main():
                   "distinct_experts": D, "stages_ms": stages},
     }
 
-    if not args.no_decode and wl.name == "lfm2_prefill_t4096":
+    if not args.no_decode and wl.name.startswith("lfm2_prefill_t4096"):
         result["decode"] = bench_decode(block, W, lib, torch)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, inp)
