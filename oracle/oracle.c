@@ -492,6 +492,51 @@ void oracle_affine4_decode(const uint32_t *codes, const uint16_t *scales, const 
                                                    biases + (size_t)n * G, c, group);
 }
 
+/* ------------------------------------------------------------------ */
+/* the step before the block: fused residual add + RMSNorm             */
+/* ------------------------------------------------------------------ */
+
+/* fp32 -> bf16, round to nearest, ties to even (NaN -> 0x7FC0). */
+static uint16_t bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (f != f)
+        return 0x7FC0;
+    uint32_t lower = u & 0xFFFFu, upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1;
+    return (uint16_t)upper;
+}
+
+/* The shared layer piece that makes the block's input (TensorFold issue
+ * #548, the CUDA claim of the shared layer pieces: RMSNorm and the fused
+ * add + RMSNorm, with a row's bits the same at every row count; TensorFold
+ * PR #1492, the reused addRmsTail norms). Per token row t:
+ *   r[c]        = h[t,c] + residual[t,c]      fp32 sum of the two bf16 values
+ *                                             (r = residual when h is NULL)
+ *   res_out[t,c] = bf16(r[c])                 the residual stream, stored in bf16
+ *   x[t,c]       = r[c] * gamma[c] / sqrt(mean_c r[c]^2 + eps)   float64
+ * The block then takes bf16(x) as its input. */
+void oracle_add_rmsnorm(int T, int H, const uint16_t *h, const uint16_t *res, const uint16_t *gamma,
+                        double eps, uint16_t *res_out, double *x)
+{
+    float *r = (float *)malloc(sizeof(float) * (size_t)H);
+    for (int t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (int c = 0; c < H; ++c) {
+            size_t i = (size_t)t * H + c;
+            r[c] = h ? bf16_value(h[i]) + bf16_value(res[i]) : bf16_value(res[i]);
+            res_out[i] = bf16_round(r[c]);
+            ss += (double)r[c] * (double)r[c];
+        }
+        double inv = 1.0 / sqrt(ss / H + eps);
+        for (int c = 0; c < H; ++c)
+            x[(size_t)t * H + c] = (double)r[c] * inv * (double)bf16_value(gamma[c]);
+    }
+    free(r);
+}
+
 /* Number of threads an OpenMP region here would use. */
 int oracle_max_threads(void)
 {

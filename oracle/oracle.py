@@ -72,6 +72,7 @@ def lib():
         L.oracle_topk.argtypes = [p, i, i, p]
         L.oracle_route.argtypes = [i, i, i, i, p, p, p, i, i, C.c_double, p, p, p, p, i]
         L.oracle_softmax32_row.argtypes = [p, i, p]
+        L.oracle_add_rmsnorm.argtypes = [i, i, p, p, p, C.c_double, p, p]
         L.oracle_plan.argtypes = [i, i, i, p, p, p, p, p]
         L.oracle_forward_tokens.argtypes = [C.POINTER(Layer), p, i, p, p, p, i]
         L.oracle_forward_tokens.restype = C.c_int
@@ -221,3 +222,18 @@ def affine4_decode(codes, scales, biases, group: int = 64) -> np.ndarray:
     out = np.empty((rows, K), dtype=np.float64)
     lib().oracle_affine4_decode(_ptr(codes), _ptr(scales), _ptr(biases), rows, K, group, _ptr(out))
     return out
+
+
+def add_rmsnorm(h, residual, gamma, eps: float = 1e-5):
+    """Fused residual add + RMSNorm: h (or None) and residual bf16 bits
+    [T,H], gamma bf16 bits [H]. Returns the new residual (bf16 bits, [T,H])
+    and x in float64 ([T,H])."""
+    residual = _c(residual, np.uint16)
+    h = _c(h, np.uint16)
+    gamma = _c(gamma, np.uint16)
+    T, H = residual.shape
+    res_out = np.empty((T, H), dtype=np.uint16)
+    x = np.empty((T, H), dtype=np.float64)
+    lib().oracle_add_rmsnorm(T, H, _ptr(h), _ptr(residual), _ptr(gamma), eps, _ptr(res_out),
+                             _ptr(x))
+    return res_out, x

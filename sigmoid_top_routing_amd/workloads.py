@@ -328,6 +328,21 @@ def slice_order_inputs(T: int, H: int, E: int) -> dict:
     return {"x": x, "router_w": wr, "bias": np.zeros(E, np.float32), "pattern": pattern}
 
 
+def norm_inputs(T: int, H: int, seed: int = 0, with_h: bool = True) -> dict:
+    """Inputs of the fused residual add + RMSNorm before the block: h and
+    residual [T,H] bf16 ~ N(0, 1), gamma [H] bf16 ~ N(1, 0.1) (a trained
+    norm scale stays near 1), eps 1e-5. Drawn from
+    SeedSequence([0x5EED, 0x4E0, seed]) children in the order h, residual,
+    gamma."""
+    rh, rr, rg = [np.random.default_rng(c)
+                  for c in np.random.SeedSequence([0x5EED, 0x4E0, seed]).spawn(3)]
+    out = {"residual": _normal_bf16(rr, (T, H), 1.0), "eps": 1e-5}
+    out["h"] = _normal_bf16(rh, (T, H), 1.0) if with_h else None
+    g = rg.standard_normal(H, dtype=np.float32) * np.float32(0.1) + np.float32(1.0)
+    out["gamma"] = f32_to_bf16_bits(g)
+    return out
+
+
 def by_name(name: str) -> Workload:
     for w in CONFIGS:
         if w.name == name:

@@ -106,6 +106,24 @@ MUTANTS = {
     "limit_skips_shared_expert": (
         "activate(0, proj[i], proj[Is + i], L->swiglu_limit)", "activate(0, proj[i], proj[Is + i], 0.0)",
         ["tests/test_oracle_experts.py::test_swiglu_limit_changes_exactly_the_clamped_tokens"]),
+    "norm_eps_dropped": (
+        "double inv = 1.0 / sqrt(ss / H + eps);", "double inv = 1.0 / sqrt(ss / H);",
+        ["tests/test_oracle_norm.py::test_constant_zero_and_tiny_rows_closed_form"]),
+    "norm_mean_over_H_minus_1": (
+        "double inv = 1.0 / sqrt(ss / H + eps);", "double inv = 1.0 / sqrt(ss / (H - 1) + eps);",
+        ["tests/test_oracle_norm.py::test_one_hot_row_pins_the_mean_and_gamma_index"]),
+    "norm_gamma_shifted": (
+        "(double)bf16_value(gamma[c]);", "(double)bf16_value(gamma[(c + 1) % H]);",
+        ["tests/test_oracle_norm.py::test_one_hot_row_pins_the_mean_and_gamma_index"]),
+    "norm_residual_without_h": (
+        "res_out[i] = bf16_round(r[c]);", "res_out[i] = res[i];",
+        ["tests/test_oracle_norm.py::test_residual_is_the_bf16_of_the_sum_ties_to_even"]),
+    "norm_rounding_ties_up": (
+        "if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))", "if (lower >= 0x8000u)",
+        ["tests/test_oracle_norm.py::test_residual_is_the_bf16_of_the_sum_ties_to_even"]),
+    "norm_without_sqrt": (
+        "double inv = 1.0 / sqrt(ss / H + eps);", "double inv = 1.0 / (ss / H + eps);",
+        ["tests/test_oracle_norm.py::test_random_rows_match_the_vector_norm"]),
     "exp_taylor_term_dropped": (
         "    p = fmaf(p, r, 1.0f / 6.0f);        /* 1/3! */\n", "",
         ["tests/test_oracle_router.py::test_exp32_sweep_against_libm"]),
