@@ -184,6 +184,24 @@ int moe_forward_profiled(const moe_dims *d, const moe_weights *w, const uint16_t
                          int32_t *ids_out, float *weights_out, int32_t *offsets_out,
                          hipEvent_t events[MOE_PROFILE_EVENTS]);
 
+/* Fused residual add + RMSNorm, the step that makes the block's input x
+ * (TensorFold issue #548: RMSNorm and the fused add + RMSNorm among the shared
+ * layer pieces, a row's bits the same at every row count; TensorFold PR #1492:
+ * the reused addRmsTail norms). For each of the T rows of H:
+ *   r            = h + residual        fp32 sum of the bf16 values (r = residual if h is NULL)
+ *   residual_out = bf16(r)             round to nearest even: the residual stream
+ *   x            = bf16(r * gamma / sqrt(sum(r^2) / H + eps))
+ *  h, residual, residual_out, x  bf16 [T, H]; gamma bf16 [H]
+ *  h and residual_out may be NULL (then plain RMSNorm, residual not rewritten);
+ *  residual_out may equal residual (in place); no other two may overlap.
+ *  Limits: 0 <= T <= 2^24; H a multiple of 64, at most 8192; eps finite, >= 0.
+ * A row's outputs depend on that row only (one wavefront per row), so they
+ * are the same bits at any T. Same error and stream conventions as above; no
+ * workspace. */
+int moe_add_rmsnorm(int32_t T, int32_t H, const uint16_t *h, const uint16_t *residual,
+                    const uint16_t *gamma, float eps, uint16_t *residual_out, uint16_t *x,
+                    hipStream_t stream);
+
 /* Text of the last error on this thread ("" after a success). */
 const char *moe_last_error(void);
 

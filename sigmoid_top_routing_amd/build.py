@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "plan.hip", "gemm.hip", "grouped_gemm.hip", "stream.hip", "combine.hip",
-           "api.cpp"]
+           "norm.hip", "api.cpp"]
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",

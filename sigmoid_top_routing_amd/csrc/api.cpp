@@ -467,6 +467,32 @@ int moe_forward_profiled(const moe_dims *d, const moe_weights *w, const uint16_t
                         ids_out, weights_out, offsets_out, events);
 }
 
+int moe_add_rmsnorm(int32_t T, int32_t H, const uint16_t *h, const uint16_t *residual,
+                    const uint16_t *gamma, float eps, uint16_t *residual_out, uint16_t *x,
+                    hipStream_t stream) {
+    const char *what = "moe_add_rmsnorm";
+    REQUIRE(T >= 0 && T <= (1 << 24), MOE_E_SHAPE, "%s: T = %d, need 0 <= T <= 2^24", what, T);
+    REQUIRE(H > 0 && H % 64 == 0 && H <= moe::kNormMaxH, MOE_E_SHAPE,
+            "%s: H = %d, need a positive multiple of 64 up to %d", what, H, moe::kNormMaxH);
+    REQUIRE(std::isfinite(eps) && eps >= 0.0f, MOE_E_SHAPE, "%s: eps = %g, need a finite value >= 0",
+            what, (double)eps);
+    if (T == 0)
+        return ok();
+    TRY(check_opt_ptr(what, "h", h));
+    TRY(check_ptr(what, "residual", residual));
+    TRY(check_ptr(what, "gamma", gamma));
+    TRY(check_opt_ptr(what, "residual_out", residual_out));
+    TRY(check_ptr(what, "x", x));
+    for (const auto &pr : {std::make_pair("h", (const void *)h),
+                           std::make_pair("residual", (const void *)residual),
+                           std::make_pair("gamma", (const void *)gamma),
+                           std::make_pair("residual_out", (const void *)residual_out),
+                           std::make_pair("x", (const void *)x)})
+        TRY(check_device(what, pr.first, pr.second));
+    LAUNCH(moe::launch_add_rmsnorm(h, residual, gamma, T, H, eps, residual_out, x, stream));
+    return ok();
+}
+
 const char *moe_last_error(void) { return g_error.c_str(); }
 
 }  // extern "C"

@@ -82,6 +82,14 @@ hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream);
 bool stream_supported(const GemmProblem &p);
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream);
 
+// Fused residual add + RMSNorm of T rows of H (a multiple of 64, at most
+// kNormMaxH): residual_out = bf16(h + residual), x = bf16(r gamma / rms).
+// h and residual_out may be NULL; residual_out may equal residual.
+constexpr int kNormMaxH = 8192;
+hipError_t launch_add_rmsnorm(const uint16_t *h, const uint16_t *residual, const uint16_t *gamma,
+                              int T, int H, float eps, uint16_t *residual_out, uint16_t *x,
+                              hipStream_t stream);
+
 // out[t] = routed_scale * sum_j weights[t,j] y_seg[slot_of[t*k+j]] + shared[t]
 hipError_t launch_combine(const float *y_seg, const int32_t *slot_of, const float *weights,
                           const float *shared, int T, int H, int k, float routed_scale, void *out,

@@ -26,7 +26,7 @@ SCORE = {"sigmoid": 0, "softmax": 1}
 
 # every entry point include/moe.h declares
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_plan", "moe_forward", "moe_forward_profiled",
-           "moe_last_error")
+           "moe_add_rmsnorm", "moe_last_error")
 PROFILE_EVENTS = 7
 STAGES = ("route", "plan", "up", "down", "shared", "combine")
 
@@ -74,6 +74,8 @@ def load():
         L.moe_forward_profiled.argtypes = [C.POINTER(Dims), C.POINTER(Weights), p, p, p,
                                            C.c_size_t, p, p, p, p, C.POINTER(p)]
         L.moe_forward_profiled.restype = i
+        L.moe_add_rmsnorm.argtypes = [C.c_int32, C.c_int32, p, p, p, C.c_float, p, p, p]
+        L.moe_add_rmsnorm.restype = i
         L.moe_last_error.argtypes = []
         L.moe_last_error.restype = C.c_char_p
         _lib = L
@@ -121,6 +123,20 @@ def route(x, router_w, bias, k, norm_topk=True, norm_eps=1e-6, stream=None, scor
     _check(load().moe_route(C.byref(d), _ptr(x), _ptr(router_w), _ptr(bias), _ptr(ids), _ptr(w),
                             _ptr(ws), nbytes, _stream(stream)))
     return ids, w
+
+
+def add_rmsnorm(residual, gamma, eps=1e-5, h=None, residual_out=None, x=None, stream=None):
+    """Fused residual add + RMSNorm (moe_add_rmsnorm): bf16 [T,H] residual and
+    optional h, bf16 [H] gamma. Returns (residual_out, x); pass
+    residual_out=residual to update the residual in place."""
+    T, H = residual.shape
+    if residual_out is None and h is not None:
+        residual_out = torch.empty_like(residual)
+    if x is None:
+        x = torch.empty_like(residual)
+    _check(load().moe_add_rmsnorm(T, H, _ptr(h), _ptr(residual), _ptr(gamma), eps,
+                                  _ptr(residual_out), _ptr(x), _stream(stream)))
+    return residual_out, x
 
 
 def plan(ids, E, fault=None, stream=None):

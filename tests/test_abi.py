@@ -106,6 +106,19 @@ def test_unsupported_options_are_refused():
     assert ws_bytes(dims(score="softmax"))[0] == 0
 
 
+def test_add_rmsnorm_refuses_bad_shapes_and_pointers():
+    L = lib.load()
+    f = L.moe_add_rmsnorm
+    assert f(0, 2048, None, None, None, 1e-5, None, None, None) == 0     # nothing to do
+    for T, H, eps, word in [(4, 100, 1e-5, "H = 100"), (4, 8256, 1e-5, "H = 8256"),
+                            (-1, 64, 1e-5, "T = -1"), (4, 64, float("nan"), "eps")]:
+        assert f(T, H, None, None, None, eps, None, None, None) == -2
+        assert word in L.moe_last_error().decode()
+    assert f(4, 64, None, None, None, 1e-5, None, None, None) == -1
+    assert "residual is NULL" in L.moe_last_error().decode()
+    assert f(4, 64, None, _fake(4096 + 8), _fake(4096), 1e-5, None, _fake(4096), None) == -3
+
+
 def _fake(addr):
     return C.c_void_p(addr)
 
