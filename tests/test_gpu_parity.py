@@ -239,6 +239,29 @@ def test_route_eps_1e20(T, H, E):
         assert abs(w_ref[0, 0] - (0.5 if eps == 1e-20 else 0.092)) < 0.01
 
 
+@pytest.mark.parametrize("score", ["sigmoid", "softmax"])
+def test_route_rows_do_not_depend_on_the_row_count(score):
+    # A token's ids and weights are the same bits whichever router path its
+    # batch takes (TensorFold issue #548: a row's bits the same at every row
+    # count): the decode fold (T <= 8), the register-staged logits (T = 100)
+    # and the LDS ring (T = 4096) all add the same slices in the same order.
+    wl = W.PREFILL.with_(score=score)
+    inp = W.generate(wl, experts=False)
+    wr = torch.from_numpy(inp["router_w"]).to(DEV)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    full = None
+    for T in (4096, 100, 8, 1):
+        x = lib.x_to_device(np.ascontiguousarray(inp["x"][:T]))
+        ids, w = lib.route(x, wr, b, wl.k, score=score)
+        torch.cuda.synchronize()
+        ids, w = ids.cpu().numpy(), w.cpu().numpy()
+        if full is None:
+            full = (ids, w)
+            continue
+        assert (ids == full[0][:T]).all(), T
+        assert (w.view(np.uint32) == full[1][:T].view(np.uint32)).all(), T
+
+
 def test_route_without_bias_and_without_norm():
     wl, inp = small_inputs("mid_swiglu")
     x = lib.x_to_device(inp["x"])
