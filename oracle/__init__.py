@@ -6,5 +6,5 @@ imports it, and it imports nothing from the product.
 """
 from .oracle import (  # noqa: F401
     build, lib, activate, exp32, sigmoid32, softmax32, topk, route, plan, forward_tokens, affine4_decode,
-    max_threads, add_rmsnorm, SOURCE, LIBPATH,
+    max_threads, add_rmsnorm, fp8_decode, SOURCE, LIBPATH,
 )

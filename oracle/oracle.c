@@ -301,7 +301,7 @@ void oracle_plan(int T, int k, int E, const int32_t *ids, int32_t *counts, int32
 typedef struct {
     int32_t T, H, I, E, k;
     int32_t act;        /* 0 SwiGLU, 1 relu^2 */
-    int32_t wfmt;       /* 0 bf16, 1 affine-4 */
+    int32_t wfmt;       /* 0 bf16, 1 affine-4, 2 block-FP8 e4m3 */
     int32_t group;      /* affine-4 group size along the input dimension */
     int32_t norm_topk;
     int32_t I_shared;   /* 0: no shared expert */
@@ -311,14 +311,37 @@ typedef struct {
     const float *router_w;    /* [E,H] */
     const float *bias;        /* [E] or NULL */
     const void *w_up;         /* bf16 [E,n_up,H] or uint32 codes [E,n_up,H/8] */
-    const uint16_t *w_up_scales, *w_up_biases;     /* [E,n_up,H/group] */
+    const void *w_up_scales;  /* affine-4: bf16 [E,n_up,H/group]; FP8: fp32 [E,n_up/128,H/128] */
+    const uint16_t *w_up_biases;                   /* affine-4: bf16 [E,n_up,H/group] */
     const void *w_down;       /* bf16 [E,H,I] or uint32 codes [E,H,I/8] */
-    const uint16_t *w_down_scales, *w_down_biases; /* [E,H,I/group] */
+    const void *w_down_scales;                     /* as w_up_scales, for [E,H,I] */
+    const uint16_t *w_down_biases;
     const uint16_t *shared_up;   /* bf16 [n_sup,H]: n_sup = 2*I_s (SwiGLU) or I_s */
     const uint16_t *shared_down; /* bf16 [H,I_s] */
     int32_t score_fn;   /* 0 sigmoid, 1 softmax */
     double swiglu_limit;  /* 0: no clamp; else L > 0 for every SwiGLU of the layer */
 } oracle_layer;
+
+/* An OCP FP8 E4M3 code (the "fn" variant: no infinities) as float64: sign
+ * bit 7, exponent bits 6..3 with bias 7, mantissa bits 2..0; exponent 0
+ * holds the subnormals m/8 * 2^-6; S.1111.111 is NaN, so the largest
+ * magnitude is 1.75 * 2^8 = 448. Block-FP8 experts (TensorFold issue #548:
+ * the block-FP8 linears and experts on the CUDA branches) store one such
+ * code per weight and one fp32 scale per 128 x 128 block. */
+static double fp8_e4m3_value(uint8_t b)
+{
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+void oracle_fp8_decode(const uint8_t *codes, int n, double *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = fp8_e4m3_value(codes[i]);
+}
 
 /* Row n of a weight matrix with K inputs, as float64. */
 static void weight_row(const oracle_layer *L, int is_up, int e, int n, int N, int K, double *row)
@@ -328,10 +351,17 @@ static void weight_row(const oracle_layer *L, int is_up, int e, int n, int N, in
         const uint16_t *w = (const uint16_t *)(is_up ? L->w_up : L->w_down) + r * K;
         for (int c = 0; c < K; ++c)
             row[c] = (double)bf16_value(w[c]);
+    } else if (L->wfmt == 2) {
+        /* one fp32 scale per 128 x 128 block of the expert's [N, K] matrix */
+        const uint8_t *codes = (const uint8_t *)(is_up ? L->w_up : L->w_down) + r * K;
+        const float *sc = (const float *)(is_up ? L->w_up_scales : L->w_down_scales) +
+                          ((size_t)e * (N / 128) + n / 128) * (K / 128);
+        for (int c = 0; c < K; ++c)
+            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[c / 128];
     } else {
         int G = K / L->group;
         const uint32_t *codes = (const uint32_t *)(is_up ? L->w_up : L->w_down) + r * (K / 8);
-        const uint16_t *sc = (is_up ? L->w_up_scales : L->w_down_scales) + r * G;
+        const uint16_t *sc = (const uint16_t *)(is_up ? L->w_up_scales : L->w_down_scales) + r * G;
         const uint16_t *bi = (is_up ? L->w_up_biases : L->w_down_biases) + r * G;
         for (int c = 0; c < K; ++c)
             row[c] = affine4_value(codes, sc, bi, c, L->group);

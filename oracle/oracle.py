@@ -73,6 +73,7 @@ def lib():
         L.oracle_route.argtypes = [i, i, i, i, p, p, p, i, i, C.c_double, p, p, p, p, i]
         L.oracle_softmax32_row.argtypes = [p, i, p]
         L.oracle_add_rmsnorm.argtypes = [i, i, p, p, p, C.c_double, p, p]
+        L.oracle_fp8_decode.argtypes = [p, i, p]
         L.oracle_plan.argtypes = [i, i, i, p, p, p, p, p]
         L.oracle_forward_tokens.argtypes = [C.POINTER(Layer), p, i, p, p, p, i]
         L.oracle_forward_tokens.restype = C.c_int
@@ -183,16 +184,19 @@ def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool 
         return a.ctypes.data
 
     affine = wl.wfmt == "affine4"
+    fp8 = wl.wfmt == "fp8"
+    code_t = np.uint32 if affine else np.uint8 if fp8 else np.uint16
+    scale_t = np.float32 if fp8 else np.uint16
     L = Layer(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
-              act=0 if wl.act == "swiglu" else 1, wfmt=1 if affine else 0,
+              act=0 if wl.act == "swiglu" else 1, wfmt={"bf16": 0, "affine4": 1, "fp8": 2}[wl.wfmt],
               group=wl.group if affine else 0, norm_topk=int(wl.norm_topk),
               I_shared=wl.I_shared, norm_eps=wl.norm_eps, rsf=wl.rsf,
               x=arr("x", np.uint16), router_w=arr("router_w", np.float32),
               bias=arr("bias", np.float32),
-              w_up=arr("w_up", np.uint32 if affine else np.uint16),
-              w_up_scales=arr("w_up_scales", np.uint16), w_up_biases=arr("w_up_biases", np.uint16),
-              w_down=arr("w_down", np.uint32 if affine else np.uint16),
-              w_down_scales=arr("w_down_scales", np.uint16),
+              w_up=arr("w_up", code_t),
+              w_up_scales=arr("w_up_scales", scale_t), w_up_biases=arr("w_up_biases", np.uint16),
+              w_down=arr("w_down", code_t),
+              w_down_scales=arr("w_down_scales", scale_t),
               w_down_biases=arr("w_down_biases", np.uint16),
               shared_up=arr("shared_up", np.uint16) if wl.I_shared else None,
               shared_down=arr("shared_down", np.uint16) if wl.I_shared else None,
@@ -237,3 +241,11 @@ def add_rmsnorm(h, residual, gamma, eps: float = 1e-5):
     lib().oracle_add_rmsnorm(T, H, _ptr(h), _ptr(residual), _ptr(gamma), eps, _ptr(res_out),
                              _ptr(x))
     return res_out, x
+
+
+def fp8_decode(codes) -> np.ndarray:
+    """OCP FP8 E4M3 codes (uint8) -> float64, exactly."""
+    codes = _c(np.atleast_1d(codes), np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    lib().oracle_fp8_decode(_ptr(codes), codes.size, _ptr(out))
+    return out

@@ -121,6 +121,13 @@ MID = {
                              bias_hi=0.1, seed=105, nan_rows=(0, 100, 332), zero_tie_row=7,
                              onehot_tie_row=200, tie_col=3),
     "mid_e256_k8": Workload("mid_e256_k8", T=96, H=192, I=128, E=256, k=8, seed=106),
+    # Block-FP8 e4m3 experts, one fp32 scale per 128 x 128 block (TensorFold
+    # issue #548: the block-FP8 experts of the CUDA branches), with a
+    # SwiGLU shared expert.
+    "mid_fp8": Workload("mid_fp8", T=500, H=384, I=256, E=16, k=4, wfmt="fp8", scale_lo=0.01,
+                        scale_hi=0.03, I_shared=128, seed=109),
+    "mid_fp8_relu2": Workload("mid_fp8_relu2", T=200, H=256, I=384, E=24, k=6, act="relu2",
+                              wfmt="fp8", rsf=2.5, scale_lo=0.01, scale_hi=0.03, seed=110),
     # The softmax router family (TensorFold issue #548, the consolidation
     # proposal), with NaN rows and exact ties, over 64 experts.
     # No expert bias (the family has none): every score of an all-zero row
@@ -200,6 +207,24 @@ def _words(rng: np.random.Generator, shape) -> np.ndarray:
     return out.reshape(shape)
 
 
+def _fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+    """OCP FP8 E4M3 bytes drawn field by field: sign uniform, exponent field
+    round(N(7, 1.5)) clipped to 0..15 (magnitudes spread around 1 over a few
+    octaves), mantissa uniform on 0..7; the NaN pattern S.1111.111 is
+    replaced by S.1111.110 (448)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for s in range(0, n, CHUNK):
+        m = min(CHUNK, n - s)
+        e = np.clip(np.rint(rng.standard_normal(m, dtype=np.float32) * 1.5 + 7.0), 0, 15)
+        e = e.astype(np.uint8)
+        mant = rng.integers(0, 8, size=m, dtype=np.uint8)
+        sign = rng.integers(0, 2, size=m, dtype=np.uint8)
+        mant[(e == 15) & (mant == 7)] = 6
+        out[s:s + m] = (sign << 7) | (e << 3) | mant
+    return out.reshape(shape)
+
+
 def _children(seed: int):
     return [np.random.default_rng(c) for c in np.random.SeedSequence([0x5EED, seed]).spawn(10)]
 
@@ -248,6 +273,13 @@ def generate(wl: Workload, need_x: bool = True, experts: bool = True) -> dict:
                                                            wl.qbias_lo, wl.qbias_hi))
         out["w_down_biases"] = f32_to_bf16_bits(_uniform_f32(ws[c_qb], (E, H, I // g),
                                                              wl.qbias_lo, wl.qbias_hi))
+    elif wl.wfmt == "fp8":
+        out["w_up"] = _fp8_codes(ws[c_codes], (E, n_up, H))
+        out["w_down"] = _fp8_codes(ws[c_codes], (E, H, I))
+        out["w_up_scales"] = _uniform_f32(ws[c_scales], (E, n_up // 128, H // 128),
+                                          wl.scale_lo, wl.scale_hi)
+        out["w_down_scales"] = _uniform_f32(ws[c_scales], (E, H // 128, I // 128),
+                                            wl.scale_lo, wl.scale_hi)
     else:
         raise ValueError(f"unknown weight format {wl.wfmt!r}")
     if wl.I_shared:

@@ -124,6 +124,19 @@ MUTANTS = {
     "norm_without_sqrt": (
         "double inv = 1.0 / sqrt(ss / H + eps);", "double inv = 1.0 / (ss / H + eps);",
         ["tests/test_oracle_norm.py::test_random_rows_match_the_vector_norm"]),
+    "fp8_exponent_bias_8": (
+        "ldexp(1.0 + (double)m / 8.0, e - 7)", "ldexp(1.0 + (double)m / 8.0, e - 8)",
+        ["tests/test_oracle_fp8.py::test_e4m3_hand_values"]),
+    "fp8_subnormal_scale": (
+        "ldexp((double)m / 8.0, -6)", "ldexp((double)m / 8.0, -7)",
+        ["tests/test_oracle_fp8.py::test_e4m3_hand_values"]),
+    "fp8_no_nan": (
+        "    if (e == 15 && m == 7)\n        return NAN;\n", "",
+        ["tests/test_oracle_fp8.py::test_e4m3_hand_values"]),
+    "fp8_scale_block_transposed": (
+        "((size_t)e * (N / 128) + n / 128) * (K / 128);\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[c / 128];",
+        "(size_t)e * (N / 128) * (K / 128) + n / 128;\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[(c / 128) * (N / 128)];",
+        ["tests/test_oracle_fp8.py::test_fp8_layer_matches_dense_float64"]),
     "exp_taylor_term_dropped": (
         "    p = fmaf(p, r, 1.0f / 6.0f);        /* 1/3! */\n", "",
         ["tests/test_oracle_router.py::test_exp32_sweep_against_libm"]),
