@@ -30,6 +30,12 @@ def test_shapes_and_dtypes():
         if wl.wfmt == "bf16":
             assert inp["w_up"].shape == (wl.E, wl.n_up, wl.H)
             assert inp["w_down"].shape == (wl.E, wl.H, wl.I)
+        elif wl.wfmt == "fp8":
+            assert inp["w_up"].shape == (wl.E, wl.n_up, wl.H) and inp["w_up"].dtype == np.uint8
+            assert inp["w_up_scales"].shape == (wl.E, wl.n_up // 128, wl.H // 128)
+            assert inp["w_down_scales"].dtype == np.float32
+            assert inp["w_down_scales"].shape == (wl.E, wl.H // 128, wl.I // 128)
+            assert not ((inp["w_up"] & 0x7F) == 0x7F).any()      # no NaN codes
         else:
             assert inp["w_up"].shape == (wl.E, wl.n_up, wl.H // 8)
             assert inp["w_up"].dtype == np.uint32
