@@ -67,7 +67,7 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
-typedef enum { MOE_W_BF16 = 0, MOE_W_AFFINE4 = 1 } moe_wfmt;
+typedef enum { MOE_W_BF16 = 0, MOE_W_AFFINE4 = 1, MOE_W_FP8 = 2 } moe_wfmt;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out;
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score;
 
@@ -105,24 +105,32 @@ typedef struct {
  *  w_*_scales / w_*_biases are bf16 [E, N, K/64]; the weight is
  *  scale * code + bias (MLX 4-bit affine, group 64; TensorFold PR #1492
  *  "What").
+ *  For MOE_W_FP8 (block-FP8; TensorFold issue #548, the block-FP8 experts of
+ *  its CUDA branches) they are uint8 OCP E4M3 codes [E, N, K] (sign, 4
+ *  exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
+ *  NaN; largest 448), w_*_scales are fp32 [E, N/128, K/128], one per
+ *  128 x 128 block, the weight is scale * value, and w_*_biases are unused.
+ *  H and I must then be multiples of 128. The experts with rows are decoded
+ *  to bf16 in the workspace, then run on the bf16 kernels.
  *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
  *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared]. */
 typedef struct {
     const float *router_w;
     const float *expert_bias;
     const void *w_up;
-    const uint16_t *w_up_scales;
+    const void *w_up_scales;       /* bf16 (MOE_W_AFFINE4) or fp32 (MOE_W_FP8) */
     const uint16_t *w_up_biases;
     const void *w_down;
-    const uint16_t *w_down_scales;
+    const void *w_down_scales;
     const uint16_t *w_down_biases;
     const uint16_t *shared_up;
     const uint16_t *shared_down;
 } moe_weights;
 
 /* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
- * 4-bit experts and more than 2 E assignments (T * k > 2 E) this includes
- * room for the bf16-decoded weights of every expert that can have rows:
+ * 4-bit experts and more than 2 E assignments (T * k > 2 E), and with
+ * block-FP8 experts at any T, this includes room for the bf16-decoded
+ * weights of every expert that can have rows:
  * min(E, T * k) * max(n_up * H, H * I) * 2 bytes, n_up = 2 I (SwiGLU) or I. */
 int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
 

@@ -47,8 +47,11 @@ struct Layout {
 // Prompt-sized batches with 4-bit experts decode the weights of the experts
 // with rows to bf16 once per call and run the direct-to-LDS grouped kernel on
 // them; decode-sized ones keep the decode in the staged kernel's loads.
+// 4-bit experts of prompt-sized batches, and block-FP8 experts always, are
+// decoded to bf16 before the bf16 kernels run.
 bool dequant_first(const moe_dims &d) {
-    return d.wfmt == MOE_W_AFFINE4 && (int64_t)d.T * d.k > 2 * (int64_t)d.E;
+    return (d.wfmt == MOE_W_AFFINE4 && (int64_t)d.T * d.k > 2 * (int64_t)d.E) ||
+           d.wfmt == MOE_W_FP8;
 }
 
 Layout layout(const moe_dims &d) {
@@ -126,8 +129,16 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
             "%s: 2*max(I, I_shared)*H reaches 2^31 (one expert's weight matrix)", what);
     REQUIRE(d->act == MOE_ACT_SWIGLU || d->act == MOE_ACT_RELU2, MOE_E_UNSUPPORTED,
             "%s: act = %d, need MOE_ACT_SWIGLU (0) or MOE_ACT_RELU2 (1)", what, d->act);
-    REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_AFFINE4, MOE_E_UNSUPPORTED,
-            "%s: wfmt = %d, need MOE_W_BF16 (0) or MOE_W_AFFINE4 (1)", what, d->wfmt);
+    REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_AFFINE4 || d->wfmt == MOE_W_FP8,
+            MOE_E_UNSUPPORTED, "%s: wfmt = %d, need MOE_W_BF16 (0), MOE_W_AFFINE4 (1) or "
+            "MOE_W_FP8 (2)", what, d->wfmt);
+    if (d->wfmt == MOE_W_FP8) {
+        REQUIRE(d->H % 128 == 0 && d->I % 128 == 0, MOE_E_SHAPE,
+                "%s: H = %d, I = %d: block-FP8 experts need multiples of 128", what, d->H, d->I);
+        // the decoded weights run on the MFMA kernel, whose row offsets are 32-bit bytes
+        REQUIRE((int64_t)d->T * d->k * std::max(d->H, d->I) * 2 < ((int64_t)1 << 31),
+                MOE_E_SHAPE, "%s: T*k*max(H, I)*2 reaches 2^31 with block-FP8 experts", what);
+    }
     if (d->wfmt == MOE_W_AFFINE4)
         REQUIRE(d->group == 64, MOE_E_UNSUPPORTED, "%s: group = %d, the 4-bit format needs 64",
                 what, d->group);
@@ -274,6 +285,11 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     TRY(check_ptr(what, "w->w_up", w->w_up));
     TRY(check_ptr(what, "w->w_down", w->w_down));
     const bool aff = d->wfmt == MOE_W_AFFINE4;
+    const bool fp8 = d->wfmt == MOE_W_FP8;
+    if (fp8) {
+        TRY(check_ptr(what, "w->w_up_scales", w->w_up_scales));
+        TRY(check_ptr(what, "w->w_down_scales", w->w_down_scales));
+    }
     if (aff) {
         TRY(check_ptr(what, "w->w_up_scales", w->w_up_scales));
         TRY(check_ptr(what, "w->w_up_biases", w->w_up_biases));
@@ -296,8 +312,9 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     TRY(check_ptr(what, "out", out));
     TRY(check_ptr(what, "workspace", workspace));
     const void *dev[] = {x, out, workspace, w->router_w, w->expert_bias, w->w_up, w->w_down,
-                         aff ? w->w_up_scales : nullptr, aff ? w->w_up_biases : nullptr,
-                         aff ? w->w_down_scales : nullptr, aff ? w->w_down_biases : nullptr,
+                         aff || fp8 ? w->w_up_scales : nullptr, aff ? w->w_up_biases : nullptr,
+                         aff || fp8 ? w->w_down_scales : nullptr,
+                         aff ? w->w_down_biases : nullptr,
                          d->I_shared ? w->shared_up : nullptr,
                          d->I_shared ? w->shared_down : nullptr, ids_out, weights_out,
                          offsets_out};
@@ -346,6 +363,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     const int gate_mode = d->swiglu_limit > 0.0f ? moe::kGateUpLimit : moe::kGateUp;
     up.mode = d->act == MOE_ACT_SWIGLU ? gate_mode : moe::kUpRelu2;
     up.affine4 = aff;
+    up.fp8 = d->wfmt == MOE_W_FP8;
     up.A = x;
     up.lda = H;
     up.gather = sorted;
@@ -354,8 +372,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     up.E = E;
     up.max_rows = A;
     up.B = w->w_up;
-    up.Bscale = w->w_up_scales;
-    up.Bbias = w->w_up_biases;
+    up.Bscale = (const uint16_t *)w->w_up_scales;
+    up.Bbias = (const uint16_t *)w->w_up_biases;
     up.N = d->act == MOE_ACT_SWIGLU ? 2 * I : I;
     up.K = H;
     up.I = I;
@@ -367,6 +385,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     uint16_t *wdq = (uint16_t *)(ws + L.wdq);
     auto dequantized = [&](moe::GemmProblem g) {
         g.affine4 = 0;
+        g.fp8 = 0;
         g.B = wdq;
         g.Bscale = nullptr;
         g.Bbias = nullptr;
@@ -385,14 +404,15 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     moe::GemmProblem down{};
     down.mode = moe::kDown;
     down.affine4 = aff;
+    down.fp8 = up.fp8;
     down.A = h;
     down.lda = I;
     down.offsets = offsets;
     down.E = E;
     down.max_rows = A;
     down.B = w->w_down;
-    down.Bscale = w->w_down_scales;
-    down.Bbias = w->w_down_biases;
+    down.Bscale = (const uint16_t *)w->w_down_scales;
+    down.Bbias = (const uint16_t *)w->w_down_biases;
     down.N = H;
     down.K = I;
     down.I = I;

@@ -549,9 +549,76 @@ __global__ __launch_bounds__(kThreads) void k_dequant(GemmProblem p, uint16_t *_
     }
 }
 
+// Block-FP8 weights of the experts with rows, decoded to bf16 in expert
+// order (b_compact), like k_dequant: OCP E4M3 codes (sign, 4 exponent bits
+// with bias 7, 3 mantissa bits; exponent 0 holds m * 2^-9; S.1111.111 is
+// NaN), each times the fp32 scale of its 128 x 128 block, rounded once to
+// bf16. A thread decodes 16 consecutive codes of a row (one 16-byte load,
+// one scale) per item.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const uint32_t sign = (b & 0x80u) << 24;
+    float v = e != 0 ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                     : (float)m * 0x1p-9f;
+    v = (e == 15u && m == 7u) ? __builtin_nanf("") : v;
+    return __uint_as_float(__float_as_uint(v) | sign);
+}
+
+__global__ __launch_bounds__(kThreads) void k_dequant_fp8(GemmProblem p,
+                                                          uint16_t *__restrict__ out) {
+    __shared__ int s_list[256];
+    __shared__ int s_cnt[kThreads / kWave];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const bool busy = tid < p.E && p.offsets[tid + 1] > p.offsets[tid];
+    const uint64_t m = __ballot(busy);
+    if (lane == 0)
+        s_cnt[wave] = __popcll(m);
+    __syncthreads();
+    int rank = __popcll(m & ((1ull << lane) - 1ull)), nb = 0;
+    for (int w = 0; w < kThreads / kWave; ++w) {
+        rank += w < wave ? s_cnt[w] : 0;
+        nb += s_cnt[w];
+    }
+    if (busy)
+        s_list[rank] = tid;
+    __syncthreads();
+    const int K16 = p.K / 16, KB = p.K / 128, NB = p.N / 128;
+    const size_t pieces = (size_t)p.N * K16;               // 16-code pieces per expert
+    const size_t chunks = (pieces + kThreads - 1) / kThreads;
+    const uint8_t *codes = (const uint8_t *)p.B;
+    const float *scales = (const float *)p.Bscale;
+    for (size_t item = blockIdx.x; item < (size_t)nb * chunks; item += gridDim.x) {
+        const int y = (int)(item / chunks);
+        const size_t q = (item % chunks) * kThreads + tid;
+        if (q >= pieces)
+            continue;
+        const int e = s_list[y];
+        const size_t n = q / K16, c16 = q % K16;
+        const uint4 v = *reinterpret_cast<const uint4 *>(codes + ((size_t)e * p.N + n) * p.K +
+                                                         c16 * 16);
+        const float sc = scales[((size_t)e * NB + n / 128) * KB + c16 / 8];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            packed[2 * i] = pack_bf16x2(e4m3_to_f32(w[i] & 0xffu) * sc,
+                                        e4m3_to_f32((w[i] >> 8) & 0xffu) * sc);
+            packed[2 * i + 1] = pack_bf16x2(e4m3_to_f32((w[i] >> 16) & 0xffu) * sc,
+                                            e4m3_to_f32(w[i] >> 24) * sc);
+        }
+        uint4 *o = reinterpret_cast<uint4 *>(out + ((size_t)y * p.N + n) * p.K + c16 * 16);
+        o[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        o[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
+    if (p.fp8)
+        return hipErrorInvalidValue;             // decoded by launch_dequant first
     if (grouped_supported(p))
         return launch_grouped(p, stream);
     if (p.affine4) {
@@ -571,6 +638,12 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream) {
+    if (p.fp8) {
+        if (p.offsets == nullptr || p.E > 256 || p.K % 128 != 0 || p.N % 128 != 0)
+            return hipErrorInvalidValue;
+        hipLaunchKernelGGL(k_dequant_fp8, dim3(1024), dim3(kThreads), 0, stream, p, out);
+        return hipGetLastError();
+    }
     if (!p.affine4 || p.offsets == nullptr || p.E > 256 || p.K % 64 != 0)
         return hipErrorInvalidValue;
     // a few workgroups per CU share the items

@@ -705,7 +705,7 @@ bool grouped_supported(const GemmProblem &p) {
     // every A offset (rows of A times lda, in bytes) stays below kPastA
     // and every weight offset within one expert, stay below kPastA
     const long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
-    return !p.affine4 && p.scatter == nullptr && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
+    return !p.affine4 && !p.fp8 && p.scatter == nullptr && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
            (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA &&
            (long long)p.N * p.K * 2 < (long long)kPastA;
 }

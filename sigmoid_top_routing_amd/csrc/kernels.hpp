@@ -44,6 +44,8 @@ constexpr bool gated(int mode) { return mode == kGateUp || mode == kGateUpLimit;
 struct GemmProblem {
     int mode;                 // GemmMode
     int affine4;              // B is 4-bit affine (codes + bf16 scale / bias, group 64)
+    int fp8;                  // B is block-FP8 e4m3 (bytes + fp32 scale per 128 x 128 block):
+                              // only launch_dequant reads it
     const uint16_t *A;        // bf16 rows, lda elements apart
     int lda;
     const int32_t *gather;    // A row of position p = gather[p] / gather_div (NULL: row p)
@@ -53,7 +55,7 @@ struct GemmProblem {
     int E;
     int max_rows;             // bound on offsets[E] (sizes the grid)
     const void *B;            // [E][N][K] bf16, or uint32 codes [E][N][K/8]
-    const uint16_t *Bscale;   // [E][N][K/64] (affine-4)
+    const uint16_t *Bscale;   // [E][N][K/64] (affine-4); fp32 [E][N/128][K/128] (fp8)
     const uint16_t *Bbias;
     int N;                    // rows of B per expert
     int K;
@@ -67,9 +69,10 @@ struct GemmProblem {
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
 
-// The 4-bit weights of p's experts that have rows (p.affine4, offsets set),
-// decoded once to bf16 (scale * q + bias in fp32, rounded to nearest even)
-// into out: [experts with rows][N][K], in expert order (b_compact).
+// The 4-bit (p.affine4) or block-FP8 (p.fp8) weights of p's experts that
+// have rows (offsets set), decoded once to bf16 (scale * q + bias, or
+// scale * e4m3 value, in fp32, rounded to nearest even) into out:
+// [experts with rows][N][K], in expert order (b_compact).
 hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream);
 
 // The persistent direct-to-LDS kernel (bf16 weights, K a multiple of 32 and

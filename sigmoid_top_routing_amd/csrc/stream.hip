@@ -228,7 +228,7 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 }  // namespace
 
 bool stream_supported(const GemmProblem &p) {
-    return !p.affine4 && p.K <= 4096;
+    return !p.affine4 && !p.fp8 && !p.b_compact && p.K <= 4096;
 }
 
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream) {

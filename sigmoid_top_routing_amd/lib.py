@@ -20,7 +20,7 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_ALIGN",
           -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
 ACT = {"swiglu": 0, "relu2": 1}
-WFMT = {"bf16": 0, "affine4": 1}
+WFMT = {"bf16": 0, "affine4": 1, "fp8": 2}
 OUT = {torch.bfloat16: 0, torch.float32: 1}
 SCORE = {"sigmoid": 0, "softmax": 1}
 
@@ -260,10 +260,12 @@ def block_from_arrays(wl, inp: dict, device="cuda") -> MoEBlock:
         t = t.to(device)
         return t.view(torch.bfloat16) if as_bf16 else t
     aff = wl.wfmt == "affine4"
+    fp8 = wl.wfmt == "fp8"
     return MoEBlock(H=wl.H, I=wl.I, E=wl.E, k=wl.k, router_w=dev("router_w"), bias=dev("bias"),
-                    w_up=dev("w_up", not aff), w_down=dev("w_down", not aff),
-                    w_up_scales=dev("w_up_scales", True), w_up_biases=dev("w_up_biases", True),
-                    w_down_scales=dev("w_down_scales", True),
+                    w_up=dev("w_up", not (aff or fp8)), w_down=dev("w_down", not (aff or fp8)),
+                    w_up_scales=dev("w_up_scales", not fp8),
+                    w_up_biases=dev("w_up_biases", True),
+                    w_down_scales=dev("w_down_scales", not fp8),
                     w_down_biases=dev("w_down_biases", True),
                     shared_up=dev("shared_up", True), shared_down=dev("shared_down", True),
                     act=wl.act, wfmt=wl.wfmt, rsf=wl.rsf, I_shared=wl.I_shared,

@@ -124,10 +124,10 @@ MID = {
     # Block-FP8 e4m3 experts, one fp32 scale per 128 x 128 block (TensorFold
     # issue #548: the block-FP8 experts of the CUDA branches), with a
     # SwiGLU shared expert.
-    "mid_fp8": Workload("mid_fp8", T=500, H=384, I=256, E=16, k=4, wfmt="fp8", scale_lo=0.01,
-                        scale_hi=0.03, I_shared=128, seed=109),
+    "mid_fp8": Workload("mid_fp8", T=500, H=384, I=256, E=16, k=4, wfmt="fp8", scale_lo=1e-4,
+                        scale_hi=3e-4, I_shared=128, seed=109),
     "mid_fp8_relu2": Workload("mid_fp8_relu2", T=200, H=256, I=384, E=24, k=6, act="relu2",
-                              wfmt="fp8", rsf=2.5, scale_lo=0.01, scale_hi=0.03, seed=110),
+                              wfmt="fp8", rsf=2.5, scale_lo=1e-4, scale_hi=3e-4, seed=110),
     # The softmax router family (TensorFold issue #548, the consolidation
     # proposal), with NaN rows and exact ties, over 64 experts.
     # No expert bias (the family has none): every score of an all-zero row
@@ -147,6 +147,17 @@ MID = {
 # --------------------------------------------------------------------------
 # bf16 helpers (storage format only)
 # --------------------------------------------------------------------------
+
+# Full-size workloads beyond the five above, for the next formats: the
+# LFM2-MoE shapes with block-FP8 experts, at prefill and decode sizes.
+EXTRA = {
+    "lfm2_fp8_prefill_t4096": Workload("lfm2_fp8_prefill_t4096", T=4096, H=2048, I=1792, E=32,
+                                       k=4, wfmt="fp8", scale_lo=1e-4, scale_hi=3e-4, seed=111),
+    "lfm2_fp8_decode_t8": Workload("lfm2_fp8_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
+                                   wfmt="fp8", scale_lo=1e-4, scale_hi=3e-4, seed=112,
+                                   weight_seed=111),
+}
+
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 to bf16 (round to nearest, ties to even); NaN -> 0x7FC0."""
@@ -208,15 +219,16 @@ def _words(rng: np.random.Generator, shape) -> np.ndarray:
 
 
 def _fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
-    """OCP FP8 E4M3 bytes drawn field by field: sign uniform, exponent field
-    round(N(7, 1.5)) clipped to 0..15 (magnitudes spread around 1 over a few
-    octaves), mantissa uniform on 0..7; the NaN pattern S.1111.111 is
-    replaced by S.1111.110 (448)."""
+    """OCP FP8 E4M3 bytes drawn field by field, shaped like weights quantized
+    with a per-block absmax scale (the block's largest weight near code 448,
+    the bulk a few octaves below): sign uniform, exponent field
+    round(N(13, 1)) clipped to 0..15, mantissa uniform on 0..7; the NaN
+    pattern S.1111.111 is replaced by S.1111.110 (448)."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint8)
     for s in range(0, n, CHUNK):
         m = min(CHUNK, n - s)
-        e = np.clip(np.rint(rng.standard_normal(m, dtype=np.float32) * 1.5 + 7.0), 0, 15)
+        e = np.clip(np.rint(rng.standard_normal(m, dtype=np.float32) + 13.0), 0, 15)
         e = e.astype(np.uint8)
         mant = rng.integers(0, 8, size=m, dtype=np.uint8)
         sign = rng.integers(0, 2, size=m, dtype=np.uint8)
@@ -381,4 +393,6 @@ def by_name(name: str) -> Workload:
             return w
     if name in MID:
         return MID[name]
+    if name in EXTRA:
+        return EXTRA[name]
     raise KeyError(name)
