@@ -65,6 +65,19 @@ static float bf16_value(uint16_t b)
     return f;
 }
 
+/* fp32 -> bf16, round to nearest, ties to even (NaN -> 0x7FC0). */
+static uint16_t bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if (f != f)
+        return 0x7FC0;
+    uint32_t lower = u & 0xFFFFu, upper = u >> 16;
+    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
+        upper += 1;
+    return (uint16_t)upper;
+}
+
 /* MLX-style 4-bit affine weight, exactly: element c of row n is
  * scale[n][c/64] * q + bias[n][c/64], q the nibble at bits 4*(c%8) of word
  * c/8 (TensorFold PR #1492 "What": MLX 4-bit affine experts; packing is
@@ -510,6 +523,127 @@ int oracle_forward_tokens(const oracle_layer *L, const int32_t *tokens, int ntok
     return bad ? -1 : 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* fp32 mimic of the engine's own order, for bitwise pins only          */
+/* ------------------------------------------------------------------ */
+
+/* The pages pin the combine's fp32 order bit for bit, not by tolerance
+ * (vllm.cpp PR #684, the review-repairs commit: folding the routed scale
+ * into each expert weight stayed green while every case compared with a
+ * tolerance, and was pinned on decimal-grid data that separates the two
+ * forms; the W2 commit: the routed scale multiplies the finished routed sum,
+ * the shared output is added untouched; relu^2 and silu * up widen to fp32
+ * and round once). This mimic is that order, for one token:
+ *   acc = +0; acc = fmaf(w_j, y_j, acc) for j = 0, 1, ..., k-1
+ *   acc = acc * rsf;  acc = acc + shared;  out = acc           (fp32)
+ * and, when fold != 0, the folded form the pin must tell apart:
+ *   acc = +0; acc = fmaf(rsf * w_j, y_j, acc) for j ascending; acc = acc + shared.
+ * It does not grade outputs (oracle_forward_tokens does); it is run on data
+ * built so that every projection has at most one non-zero term, which makes
+ * y_j and the shared output exact whatever order a kernel sums in. */
+void oracle_combine32(int ntok, int H, int k, const float *w, const float *y,
+                      const float *shared, float rsf, int fold, float *out)
+{
+    for (int t = 0; t < ntok; ++t)
+        for (int h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int j = 0; j < k; ++j) {
+                float wj = w[(size_t)t * k + j];
+                if (fold)
+                    wj = rsf * wj;
+                acc = fmaf(wj, y[((size_t)t * k + j) * H + h], acc);
+            }
+            if (!fold)
+                acc = acc * rsf;
+            if (shared)
+                acc = acc + shared[(size_t)t * H + h];
+            out[(size_t)t * H + h] = acc;
+        }
+}
+
+/* The activation epilogue in fp32 on fp32 pre-activations, rounded once to
+ * bf16 by round-to-nearest-even (the W2 commit: widen, compute, round once).
+ *   relu^2 (act 1): r = (u < 0 ? 0 : u), bf16(r * r)
+ *   SwiGLU (act 0): bf16((g * sigmoid32(g)) * u)
+ * The engine's silu takes its exponential and reciprocal from the hardware;
+ * the two agree bit for bit only where the fp32 sigmoid is exactly 1 (gates
+ * above 17), which is where the SwiGLU pins put their gates. */
+uint16_t oracle_epilogue32(int act, float g, float u)
+{
+    if (act == 1) {
+        float r = (u < 0.0f) ? 0.0f : u;
+        return bf16_round(r * r);
+    }
+    return bf16_round((g * oracle_sigmoid32(g)) * u);
+}
+
+/* fp32 of an exact float64 value; counts the values that are not exact. */
+static float exact32(double v, int *inexact)
+{
+    float f = (float)v;
+    if (v == v && (double)f != v)
+        *inexact += 1;
+    return f;
+}
+
+/* The per-assignment rows the engine's down projection writes, in fp32, and
+ * the shared expert's fp32 output, for the listed tokens and the given picks
+ * (ids [ntok, k]): the projections are float64 dot products rounded to fp32,
+ * the epilogue is oracle_epilogue32. y_out [ntok, k, H]; shared_out [ntok, H]
+ * (when the layer has a shared expert). Returns the number of projection
+ * values that were not exact in fp32 (the pins need 0: then no summation
+ * order can change a bit). bf16 experts only. */
+int oracle_expert_rows32(const oracle_layer *L, const int32_t *tokens, int ntok,
+                         const int32_t *ids, float *y_out, float *shared_out)
+{
+    int H = L->H, I = L->I, k = L->k, Is = L->I_shared;
+    int wide = (I > Is ? I : Is);
+    double *xr = (double *)malloc(sizeof(double) * (size_t)H);
+    double *row = (double *)malloc(sizeof(double) * (size_t)(H > wide ? H : wide));
+    double *hv = (double *)malloc(sizeof(double) * (size_t)wide);
+    float *pre = (float *)malloc(sizeof(float) * (size_t)2 * wide);
+    int inexact = 0;
+    for (int i = 0; i < ntok; ++i) {
+        const uint16_t *x_row = L->x + (size_t)tokens[i] * H;
+        for (int h = 0; h < H; ++h)
+            xr[h] = (double)bf16_value(x_row[h]);
+        for (int j = 0; j <= k; ++j) {
+            int shared = (j == k);
+            if (shared && Is == 0)
+                break;
+            int In = shared ? Is : I;
+            int n_up = (L->act == 0) ? 2 * In : In;
+            for (int n = 0; n < n_up; ++n) {
+                if (shared) {
+                    const uint16_t *w = L->shared_up + (size_t)n * H;
+                    for (int c = 0; c < H; ++c)
+                        row[c] = (double)bf16_value(w[c]);
+                } else {
+                    weight_row(L, 1, ids[(size_t)i * k + j], n, n_up, H, row);
+                }
+                pre[n] = exact32(dot(row, xr, H), &inexact);
+            }
+            for (int n = 0; n < In; ++n)
+                hv[n] = (double)bf16_value(L->act == 0
+                                               ? oracle_epilogue32(0, pre[n], pre[In + n])
+                                               : oracle_epilogue32(1, 0.0f, pre[n]));
+            float *yo = shared ? shared_out + (size_t)i * H : y_out + ((size_t)i * k + j) * H;
+            for (int h = 0; h < H; ++h) {
+                if (shared) {
+                    const uint16_t *w = L->shared_down + (size_t)h * Is;
+                    for (int c = 0; c < Is; ++c)
+                        row[c] = (double)bf16_value(w[c]);
+                } else {
+                    weight_row(L, 0, ids[(size_t)i * k + j], h, H, I, row);
+                }
+                yo[h] = exact32(dot(row, hv, In), &inexact);
+            }
+        }
+    }
+    free(xr); free(row); free(hv); free(pre);
+    return inexact;
+}
+
 /* Decode rows r0..r0+nr-1 of an affine-4 matrix with K inputs to float64. */
 void oracle_affine4_decode(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                            int rows, int K, int group, double *out)
@@ -526,18 +660,6 @@ void oracle_affine4_decode(const uint32_t *codes, const uint16_t *scales, const 
 /* the step before the block: fused residual add + RMSNorm             */
 /* ------------------------------------------------------------------ */
 
-/* fp32 -> bf16, round to nearest, ties to even (NaN -> 0x7FC0). */
-static uint16_t bf16_round(float f)
-{
-    uint32_t u;
-    memcpy(&u, &f, 4);
-    if (f != f)
-        return 0x7FC0;
-    uint32_t lower = u & 0xFFFFu, upper = u >> 16;
-    if (lower > 0x8000u || (lower == 0x8000u && (upper & 1u)))
-        upper += 1;
-    return (uint16_t)upper;
-}
 
 /* The shared layer piece that makes the block's input (TensorFold issue
  * #548, the CUDA claim of the shared layer pieces: RMSNorm and the fused

@@ -81,6 +81,11 @@ def lib():
         L.oracle_max_threads.restype = C.c_int
         L.oracle_activate.restype = C.c_double
         L.oracle_activate.argtypes = [i, C.c_double, C.c_double, C.c_double]
+        L.oracle_combine32.argtypes = [i, i, i, p, p, p, C.c_float, i, p]
+        L.oracle_epilogue32.restype = C.c_uint16
+        L.oracle_epilogue32.argtypes = [i, C.c_float, C.c_float]
+        L.oracle_expert_rows32.restype = C.c_int
+        L.oracle_expert_rows32.argtypes = [C.POINTER(Layer), p, i, p, p, p]
         _lib = L
     return _lib
 
@@ -166,15 +171,8 @@ def plan(ids, E: int):
     return counts, offsets, srt, slot
 
 
-def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool = False):
-    """The block's float64 output rows for ``tokens`` ([n, H] float64).
-
-    ``wl`` carries the shapes and flags (a workloads.Workload or anything
-    with the same attributes); ``inp`` the arrays from workloads.generate.
-    """
-    tokens = _c(np.atleast_1d(tokens), np.int32)
-    keep = {}
-
+def _layer(wl, inp: dict, keep: dict) -> Layer:
+    """The oracle_layer struct of a workload's arrays (kept alive in keep)."""
     def arr(name, dtype):
         a = inp.get(name)
         if a is None:
@@ -187,21 +185,34 @@ def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool 
     fp8 = wl.wfmt == "fp8"
     code_t = np.uint32 if affine else np.uint8 if fp8 else np.uint16
     scale_t = np.float32 if fp8 else np.uint16
-    L = Layer(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
-              act=0 if wl.act == "swiglu" else 1, wfmt={"bf16": 0, "affine4": 1, "fp8": 2}[wl.wfmt],
-              group=wl.group if affine else 0, norm_topk=int(wl.norm_topk),
-              I_shared=wl.I_shared, norm_eps=wl.norm_eps, rsf=wl.rsf,
-              x=arr("x", np.uint16), router_w=arr("router_w", np.float32),
-              bias=arr("bias", np.float32),
-              w_up=arr("w_up", code_t),
-              w_up_scales=arr("w_up_scales", scale_t), w_up_biases=arr("w_up_biases", np.uint16),
-              w_down=arr("w_down", code_t),
-              w_down_scales=arr("w_down_scales", scale_t),
-              w_down_biases=arr("w_down_biases", np.uint16),
-              shared_up=arr("shared_up", np.uint16) if wl.I_shared else None,
-              shared_down=arr("shared_down", np.uint16) if wl.I_shared else None,
-              score_fn=SCORES[getattr(wl, "score", "sigmoid")],
-              swiglu_limit=float(getattr(wl, "swiglu_limit", 0.0)))
+    return Layer(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
+                 act=0 if wl.act == "swiglu" else 1,
+                 wfmt={"bf16": 0, "affine4": 1, "fp8": 2}[wl.wfmt],
+                 group=wl.group if affine else 0, norm_topk=int(wl.norm_topk),
+                 I_shared=wl.I_shared, norm_eps=wl.norm_eps, rsf=wl.rsf,
+                 x=arr("x", np.uint16), router_w=arr("router_w", np.float32),
+                 bias=arr("bias", np.float32),
+                 w_up=arr("w_up", code_t),
+                 w_up_scales=arr("w_up_scales", scale_t),
+                 w_up_biases=arr("w_up_biases", np.uint16),
+                 w_down=arr("w_down", code_t),
+                 w_down_scales=arr("w_down_scales", scale_t),
+                 w_down_biases=arr("w_down_biases", np.uint16),
+                 shared_up=arr("shared_up", np.uint16) if wl.I_shared else None,
+                 shared_down=arr("shared_down", np.uint16) if wl.I_shared else None,
+                 score_fn=SCORES[getattr(wl, "score", "sigmoid")],
+                 swiglu_limit=float(getattr(wl, "swiglu_limit", 0.0)))
+
+
+def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool = False):
+    """The block's float64 output rows for ``tokens`` ([n, H] float64).
+
+    ``wl`` carries the shapes and flags (a workloads.Workload or anything
+    with the same attributes); ``inp`` the arrays from workloads.generate.
+    """
+    tokens = _c(np.atleast_1d(tokens), np.int32)
+    keep = {}
+    L = _layer(wl, inp, keep)
     n = tokens.size
     out = np.empty((n, wl.H), dtype=np.float64)
     ids = np.empty((n, wl.k), dtype=np.int32)
@@ -213,6 +224,50 @@ def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool 
     if want_routing:
         return out, ids, w
     return out
+
+
+def combine32(w, y, shared, rsf: float, fold: bool = False) -> np.ndarray:
+    """fp32 mimic of the engine's combine, for bitwise pins: w [n,k] fp32,
+    y [n,k,H] fp32, shared [n,H] fp32 or None. out = (fma chain of w_j y_j,
+    j ascending) * rsf + shared; fold=True gives the folded form
+    (fma chain of (rsf w_j) y_j) + shared instead."""
+    w = _c(w, np.float32)
+    y = _c(y, np.float32)
+    shared = _c(shared, np.float32)
+    n, k, H = y.shape
+    assert w.shape == (n, k)
+    out = np.empty((n, H), dtype=np.float32)
+    lib().oracle_combine32(n, H, k, _ptr(w), _ptr(y), _ptr(shared), C.c_float(rsf), int(fold),
+                           _ptr(out))
+    return out
+
+
+def epilogue32(act: str, g, u) -> np.ndarray:
+    """fp32 epilogue rounded once to bf16 (bits): relu^2 of u, or
+    (g * sigmoid32(g)) * u for SwiGLU."""
+    g = np.broadcast_to(np.asarray(g, np.float32), np.shape(u)).ravel()
+    u = np.asarray(u, np.float32).ravel()
+    a = 0 if act == "swiglu" else 1
+    f = lib().oracle_epilogue32
+    return np.array([f(a, C.c_float(gi), C.c_float(ui)) for gi, ui in zip(g, u)], dtype=np.uint16)
+
+
+def expert_rows32(wl, inp: dict, tokens, ids):
+    """Per-assignment fp32 down rows y [n,k,H] and the shared expert's fp32
+    output [n,H] (or None) for ``tokens`` routed to ``ids`` [n,k], with the
+    fp32 epilogue rounded once to bf16 between the projections. Returns
+    (y, shared, inexact): inexact counts projection values that were not
+    exact in fp32 (0 on data with one non-zero term per dot product)."""
+    tokens = _c(np.atleast_1d(tokens), np.int32)
+    ids = _c(ids, np.int32)
+    keep = {}
+    L = _layer(wl, inp, keep)
+    n = tokens.size
+    assert ids.shape == (n, wl.k)
+    y = np.empty((n, wl.k, wl.H), dtype=np.float32)
+    sh = np.empty((n, wl.H), dtype=np.float32) if wl.I_shared else None
+    inexact = lib().oracle_expert_rows32(C.byref(L), _ptr(tokens), n, _ptr(ids), _ptr(y), _ptr(sh))
+    return y, sh, inexact
 
 
 def affine4_decode(codes, scales, biases, group: int = 64) -> np.ndarray:

@@ -70,6 +70,8 @@ class Workload:
     zero_tie_row: int | None = None  # x row of zeros + triple bias tie
     onehot_tie_row: int | None = None  # one-hot x row + two equal logits
     zero_rows: tuple = ()             # x rows of zeros, bias untouched
+    posinf_rows: tuple = ()           # x rows with +inf at column tie_col
+    neginf_rows: tuple = ()           # x rows with -inf at column tie_col
     tie_col: int = 7
     scale_lo: float = 0.005
     scale_hi: float = 0.02
@@ -121,6 +123,16 @@ MID = {
                              bias_hi=0.1, seed=105, nan_rows=(0, 100, 332), zero_tie_row=7,
                              onehot_tie_row=200, tie_col=3),
     "mid_e256_k8": Workload("mid_e256_k8", T=96, H=192, I=128, E=256, k=8, seed=106),
+    # 4-bit experts whose down projection has K = I = 64 (the staged kernel
+    # with the decode in its loads, at prompt and decode sizes)
+    "mid_affine4_i64": Workload("mid_affine4_i64", T=200, H=256, I=64, E=8, k=2,
+                                wfmt="affine4", seed=113),
+    # relu^2 experts on rows with a NaN, +inf or -inf input (bloomery PR #235:
+    # relu^2 keeps a non-finite input non-finite), with a shared expert
+    "mid_relu2_nonfinite": Workload("mid_relu2_nonfinite", T=160, H=256, I=192, E=16, k=4,
+                                    act="relu2", rsf=2.5, I_shared=128, seed=114,
+                                    nan_rows=(1, 90), posinf_rows=(3, 100), neginf_rows=(5, 150),
+                                    tie_col=11),
     # Block-FP8 e4m3 experts, one fp32 scale per 128 x 128 block (TensorFold
     # issue #548: the block-FP8 experts of the CUDA branches), with a
     # SwiGLU shared expert.
@@ -156,6 +168,14 @@ EXTRA = {
     "lfm2_fp8_decode_t8": Workload("lfm2_fp8_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
                                    wfmt="fp8", scale_lo=1e-4, scale_hi=3e-4, seed=112,
                                    weight_seed=111),
+    # The decode step on the 4-bit weights: with the +2.0 boost as configured
+    # (every token picks the four boosted experts), and without it (the same
+    # expert weights and base bias, so the picks spread over the experts).
+    "affine4_decode_t8": Workload("affine4_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
+                                  wfmt="affine4", seed=5, weight_seed=4, boost=2.0,
+                                  boosted=(3, 11, 19, 27)),
+    "affine4_flat_decode_t8": Workload("affine4_flat_decode_t8", T=8, H=2048, I=1792, E=32,
+                                       k=4, wfmt="affine4", seed=5, weight_seed=4),
 }
 
 
@@ -307,6 +327,8 @@ def _construct_special_rows(wl: Workload, out: dict) -> None:
 
     * NaN rows: every x entry is a bf16 NaN, so every router logit is NaN.
     * Zero rows: every x entry is 0, so every router logit is +0.
+    * +inf / -inf rows: x has +inf (-inf) at column tie_col, so a logit is
+      +inf or -inf by the sign of that router weight.
     * Zero tie row: x is all zeros, so every logit is +0 and every score
       the same; the bias of experts 1, 4, 6 is set to 0.125, above every
       other bias, which makes a three-way tie at the top.
@@ -322,6 +344,10 @@ def _construct_special_rows(wl: Workload, out: dict) -> None:
             x[r, :] = BF16_NAN
         for r in wl.zero_rows:
             x[r, :] = 0
+        for r in wl.posinf_rows:
+            x[r, wl.tie_col] = 0x7F80
+        for r in wl.neginf_rows:
+            x[r, wl.tie_col] = 0xFF80
     if wl.zero_tie_row is not None:
         if x is not None:
             x[wl.zero_tie_row, :] = 0
@@ -370,6 +396,87 @@ def slice_order_inputs(T: int, H: int, E: int) -> dict:
     for t in range(T):
         x[t, :] = f32_to_bf16_bits(np.full(1, 2.0 ** (t % 3), np.float32))[0]
     return {"x": x, "router_w": wr, "bias": np.zeros(E, np.float32), "pattern": pattern}
+
+
+def _grid_bf16(rng: np.random.Generator, shape, lo: float, hi: float,
+               signed: bool = True) -> np.ndarray:
+    """bf16 bits of magnitudes drawn uniformly in [lo, hi) (never zero), with
+    a uniform random sign when signed."""
+    v = _uniform_f32(rng, shape, lo, hi)
+    if signed:
+        v = np.where(rng.integers(0, 2, size=v.shape) == 1, -v, v).astype(np.float32)
+    return f32_to_bf16_bits(v)
+
+
+def exact_inputs(wl: Workload, nonfinite: bool = False) -> dict:
+    """Inputs on which every expert projection has at most one non-zero
+    term, so a projection's value is one product of two bf16 numbers (exact
+    in fp32) whatever order a kernel sums in. What is left to pin bit for bit
+    is then the engine's own fp32 order: the activation epilogue and its one
+    rounding to bf16, and the combine.
+
+    * x: token t is one-hot, 1.0 at column onehot_col(t) = (37 t) mod H.
+    * router weight N(0, 0.5) fp32 and expert bias U(bias_lo, bias_hi), so
+      the logit of expert e is its router weight at the token's column.
+    * up weights (relu^2 and the up half of gate_up): magnitudes U[0.25, 4)
+      with random signs; SwiGLU gate rows: U[24, 64), where the fp32 sigmoid
+      is exactly 1, so silu(g) u is the fp32 product g u.
+    * down weights: row n of expert e has one non-zero, at column
+      (7 n + 3 e) mod I, magnitude U[0.25, 4) with a random sign. The shared
+      expert is built the same way (as expert E).
+    * nonfinite (relu^2 only): up weight (e, n, c) set to -inf for e = 1,
+      +inf for e = 2 and NaN for e = 3, with n = 5 and c the column of token
+      e; the router weight of expert e at that column is set to 10, so that
+      token (and every token sharing its column) picks expert e first. A
+      token routed to such an expert from another column multiplies the
+      non-finite weight by 0 (NaN); the token on the column gets -inf, +inf
+      or NaN as its pre-activation.
+    Draws come from SeedSequence([0x5EED, 0xB17, seed]) children in the
+    order x-free: router, bias, up, down, shared up, shared down."""
+    E, H, I, T = wl.E, wl.H, wl.I, wl.T
+    rr, rb, ru, rd, rsu, rsd = [np.random.default_rng(c) for c in
+                                np.random.SeedSequence([0x5EED, 0xB17, wl.seed]).spawn(6)]
+    out = {}
+    x = np.zeros((T, H), np.uint16)
+    x[np.arange(T), onehot_col(np.arange(T), H)] = BF16_ONE
+    out["x"] = x
+    out["router_w"] = _normal_f32(rr, (E, H), 0.5)
+    out["bias"] = _uniform_f32(rb, (E,), wl.bias_lo, wl.bias_hi)
+
+    def up_rows(rng, experts, n_rows, I_):
+        if wl.act == "swiglu":
+            gate = _grid_bf16(rng, (experts, I_, H), 24.0, 64.0, signed=False)
+            up = _grid_bf16(rng, (experts, I_, H), 0.25, 4.0)
+            return np.concatenate([gate, up], axis=1)
+        return _grid_bf16(rng, (experts, n_rows, H), 0.25, 4.0)
+
+    def down_rows(rng, experts, I_, e0=0):
+        d = np.zeros((experts, H, I_), np.uint16)
+        vals = _grid_bf16(rng, (experts, H), 0.25, 4.0)
+        n = np.arange(H)
+        for e in range(experts):
+            d[e, n, (7 * n + 3 * (e0 + e)) % I_] = vals[e]
+        return d
+
+    out["w_up"] = up_rows(ru, E, wl.n_up, I)
+    out["w_down"] = down_rows(rd, E, I)
+    if wl.I_shared:
+        n_sup = 2 * wl.I_shared if wl.act == "swiglu" else wl.I_shared
+        out["shared_up"] = up_rows(rsu, 1, n_sup, wl.I_shared)[0]
+        out["shared_down"] = down_rows(rsd, 1, wl.I_shared, e0=E)[0]
+    if nonfinite:
+        assert wl.act == "relu2" and E > 3 and T > 3
+        bits = {1: 0xFF80, 2: 0x7F80, 3: BF16_NAN}      # -inf, +inf, NaN
+        for e, b in bits.items():
+            c = onehot_col(e, H)
+            out["w_up"][e, 5, c] = b
+            out["router_w"][e, c] = np.float32(10.0)
+    return out
+
+
+def onehot_col(t, H: int):
+    """Column of the single 1.0 of token t in exact_inputs."""
+    return (37 * np.asarray(t)) % H
 
 
 def norm_inputs(T: int, H: int, seed: int = 0, with_h: bool = True) -> dict:

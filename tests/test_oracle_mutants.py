@@ -137,6 +137,37 @@ MUTANTS = {
         "((size_t)e * (N / 128) + n / 128) * (K / 128);\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[c / 128];",
         "(size_t)e * (N / 128) * (K / 128) + n / 128;\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[(c / 128) * (N / 128)];",
         ["tests/test_oracle_fp8.py::test_fp8_layer_matches_dense_float64"]),
+    "mimic_combine_descending": (
+        "            for (int j = 0; j < k; ++j) {\n                float wj = w[",
+        "            for (int j = k - 1; j >= 0; --j) {\n                float wj = w[",
+        ["tests/test_oracle_mimic.py::test_combine_is_an_fma_chain_over_j_ascending"]),
+    "mimic_combine_unfused": (
+        "acc = fmaf(wj, y[((size_t)t * k + j) * H + h], acc);",
+        "acc = wj * y[((size_t)t * k + j) * H + h] + acc;",
+        ["tests/test_oracle_mimic.py::test_combine_is_an_fma_chain_over_j_ascending"]),
+    "mimic_shared_before_scale": (
+        "            if (!fold)\n                acc = acc * rsf;\n            if (shared)\n"
+        "                acc = acc + shared[(size_t)t * H + h];",
+        "            if (shared)\n                acc = acc + shared[(size_t)t * H + h];\n"
+        "            if (!fold)\n                acc = acc * rsf;",
+        ["tests/test_oracle_mimic.py::test_routed_scale_once_after_the_sum_and_shared_unscaled"]),
+    "mimic_always_folded": (
+        ("                if (fold)\n                    wj = rsf * wj;",
+         "            if (!fold)\n                acc = acc * rsf;\n"),
+        ("                wj = rsf * wj;", ""),
+        ["tests/test_oracle_mimic.py::test_routed_scale_once_after_the_sum_and_shared_unscaled"]),
+    "mimic_epilogue_truncates": (
+        "        return bf16_round(r * r);",
+        "        float q = r * r;\n        uint32_t b;\n        memcpy(&b, &q, 4);\n"
+        "        return (uint16_t)(b >> 16);",
+        ["tests/test_oracle_mimic.py::test_epilogue_rounding_ties_to_even_by_exact_arithmetic"]),
+    "mimic_relu_by_fmax": (
+        "float r = (u < 0.0f) ? 0.0f : u;\n        return bf16_round",
+        "float r = fmaxf(u, 0.0f);\n        return bf16_round",
+        ["tests/test_oracle_mimic.py::test_epilogue_relu2_special_values_and_rounding"]),
+    "mimic_swiglu_gate_up_swapped": (
+        "bf16_round((g * oracle_sigmoid32(g)) * u)", "bf16_round((u * oracle_sigmoid32(u)) * g)",
+        ["tests/test_oracle_mimic.py::test_epilogue_saturated_swiglu_is_the_product"]),
     "exp_taylor_term_dropped": (
         "    p = fmaf(p, r, 1.0f / 6.0f);        /* 1/3! */\n", "",
         ["tests/test_oracle_router.py::test_exp32_sweep_against_libm"]),
