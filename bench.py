@@ -16,7 +16,13 @@ Besides the whole-block throughput the line carries:
   cpu_baseline  the float64 CPU oracle on a sample of the same tokens;
   decode        the T=8 decode step on the same weights (HBM-bound), with
                 the 256 MB last-level cache flushed (by reading 512 MB)
-                before every call.
+                before every call;
+  add_rmsnorm   the fused residual add + RMSNorm that makes the block's input;
+  configs       the other workloads, each with its step time, algorithmic
+                bytes and flops and their fractions of the HBM and bf16 MFMA
+                peaks: the tiny block, the relu^2 block with a shared expert,
+                the 4-bit block, and the 4-bit decode step (T = 8) without
+                and with the four boosted experts.
 """
 from __future__ import annotations
 
@@ -100,8 +106,22 @@ def profile_run(args):
     print(f"profile run: {args.steps} calls of {wl.name}, copy of {COPY_BYTES} bytes", flush=True)
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, inp, budget_s=15.0):
+    """The float64 oracle on a sample of the workload's tokens, on every
+    thread OpenMP gives it (the host cores this process may run on), plus
+    the whole tiny workload on one thread."""
     import oracle
+    from sigmoid_top_routing_amd import workloads as W
     threads = oracle.max_threads()
     rng = np.random.default_rng(1234)
     n0 = max(threads, 4)
@@ -114,9 +134,18 @@ def cpu_baseline(wl, inp, budget_s=15.0):
     t0 = time.perf_counter()
     oracle.forward_tokens(wl, inp, toks)
     dt = time.perf_counter() - t0
+    tiny = W.TINY
+    tin = W.generate(tiny)
+    t1 = time.perf_counter()
+    oracle.forward_tokens(tiny, tin, np.arange(tiny.T), nthreads=1)
+    dt1 = time.perf_counter() - t1
+    oracle.forward_tokens(tiny, tin, np.arange(1), nthreads=threads)   # restores the count
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n} of the {wl.T} tokens of {wl.name} (routing and float64 experts "
-                      f"per token), {dt:.1f} s on {threads} threads"}
+                      f"per token), {dt:.1f} s on {threads} threads",
+            "host_cores": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
+            "tiny_one_thread": {"workload": tiny.name, "tokens": tiny.T, "s": dt1,
+                                "tokens_per_s": tiny.T / dt1}}
 
 
 def variant(wl, args):
@@ -231,8 +260,18 @@ def main():
     }
 
     if not args.no_decode and wl.name.startswith("lfm2_prefill_t4096"):
-        result["decode"] = bench_decode(block, W, lib, torch)
+        print("bench: decode, add + RMSNorm and the other configurations", file=sys.stderr,
+              flush=True)
+        result["decode"] = bench_step(W.DECODE, W, lib, torch, block=block, flush=True)
         result["add_rmsnorm"] = bench_norm(wl.T, wl.H, W, lib, torch)
+        result["configs"] = {}
+        for tag, name, flush in (("tiny", "tiny_t64_e8_k2", False),
+                                 ("relu2", "nemotron_relu2_t2048", False),
+                                 ("affine4", "affine4_t1024", False),
+                                 ("affine4_decode", "affine4_flat_decode_t8", True),
+                                 ("affine4_decode_boosted", "affine4_decode_t8", True)):
+            result["configs"][tag] = bench_step(W.by_name(name), W, lib, torch, flush=flush)
+            print(f"bench: {tag} done", file=sys.stderr, flush=True)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(result))
@@ -269,24 +308,38 @@ def bench_norm(T, H, W, lib, torch, steps=20):
             "frac_hbm": gbs / PEAK_HBM_GBS, "timing": "median of %d calls, cache evicted" % steps}
 
 
-def bench_decode(block, W, lib, torch, steps=20):
-    """T=8 on the prefill weights. Between calls a 512 MB buffer is read
-    (twice the 256 MB last-level cache), so the expert weights come from HBM;
-    it is read rather than written so no dirty lines are left to be written
-    back during the timed call."""
-    wl = W.DECODE
-    inp = W.generate(wl, experts=False)
+def shared_bytes(wl):
+    if not wl.I_shared:
+        return 0
+    n_sup = 2 * wl.I_shared if wl.act == "swiglu" else wl.I_shared
+    return 2 * (n_sup + wl.I_shared) * wl.H
+
+
+def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20):
+    """One workload's step, each call between its own event pair on the
+    current stream (the median call is reported), then the stage breakdown
+    from calls with the stage events inside (each record adds a few
+    microseconds of queue time, so the step time is taken without them).
+    flush: before every call a 512 MB buffer is read (twice the 256 MB
+    last-level cache) so the expert weights come from HBM; it is read rather
+    than written so no dirty lines are written back during the timed call.
+    block: the weights already on the device (the workload's x is drawn on
+    its own seed). Algorithmic work: the MFMA flops of the routed and shared
+    projections, and the bytes of the D distinct experts touched (as stored),
+    the shared expert, the router weight, x and the bf16 output."""
+    inp = W.generate(wl, experts=block is None)
+    if block is None:
+        block = lib.block_from_arrays(wl, inp)
     x = lib.x_to_device(inp["x"])
     ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
-    flush = torch.ones(64 << 20, dtype=torch.int64, device="cuda")
+    buf = torch.ones(64 << 20, dtype=torch.int64, device="cuda") if flush else None
     for _ in range(3):
         block.forward(x, out=out, ids_out=ids)
-    # the step alone: one event pair around a plain call (each event recorded
-    # inside the step would add a few microseconds of queue time)
     times = []
     for _ in range(steps):
-        flush.sum()
+        if buf is not None:
+            buf.sum()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
@@ -294,21 +347,29 @@ def bench_decode(block, W, lib, torch, steps=20):
         b.record()
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b))
-    # the stage breakdown, from calls with the stage events inside
     ups = []
     for _ in range(steps):
-        flush.sum()
+        if buf is not None:
+            buf.sum()
         ev = lib.StageEvents()
         block.forward(x, out=out, ids_out=ids, events=ev)
         torch.cuda.synchronize()
         ups.append(ev.stage_ms())
     D = int(np.unique(ids.cpu().numpy()).size)
     eb_up, eb_down = expert_bytes(wl)
-    algo = D * (eb_up + eb_down) + wl.E * wl.H * 4 + 2 * wl.T * wl.H * 2
-    t = float(np.median(times))
-    return {"workload": wl.name, "T": wl.T, "distinct_experts": D, "us_per_step": 1e3 * t,
-            "tokens_per_s": wl.T / (t * 1e-3), "algorithmic_bytes": algo,
-            "GBps": algo / (t * 1e-3) / 1e9, "frac_hbm": algo / (t * 1e-3) / 1e9 / PEAK_HBM_GBS,
+    algo = (D * (eb_up + eb_down) + shared_bytes(wl) + wl.E * wl.H * 4 +
+            2 * wl.T * wl.H * 2)
+    flops = sum(flops_of(wl))
+    t = float(np.median(times)) * 1e-3
+    gbs = algo / t / 1e9
+    tfs = flops / t / 1e12
+    return {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
+            "act": wl.act, "weights": wl.wfmt, "I_shared": wl.I_shared,
+            "distinct_experts": D, "us_per_step": 1e6 * t, "tokens_per_s": wl.T / t,
+            "algorithmic_bytes": algo, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
+            "flops": flops, "tflops": tfs, "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS,
+            "cache_evicted": bool(flush),
+            "timing": "median of %d calls, one event pair each" % steps,
             "stages_us_with_events": {k: 1e3 * float(np.median([u[k] for u in ups]))
                                       for k in lib.STAGES}}
 

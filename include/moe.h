@@ -3,7 +3,13 @@
  * AMD Instinct MI355X (gfx950).
  *
  * The block, for a token row x_t (H inputs):
- *   z[e]  = sum_h x[t,h] Wr[e,h]           fp32, h ascending, one fmaf per term
+ *   z[e]  = p_0 + p_1 + ... + p_{H/64-1}   fp32, added in ascending j from +0, where
+ *   p_j   = x[t,64j] Wr[e,64j] + ... + x[t,64j+63] Wr[e,64j+63]
+ *                                          fp32, one fmaf per term, h ascending, from +0
+ *           (the router's K slices are 64 wide and fixed by H alone; TensorFold
+ *           issue #548, the Nemotron score top-k that adds the router's K
+ *           slices itself, and the kernel rule that slices come from the
+ *           weight's shape, so a row's bits do not depend on the batch)
  *   s[e]  = 1 / (1 + exp(-z[e]))           fp32 (own exp, correctly rounded division)
  *           or softmax: q[e] = exp(z[e] - max z) (0 below -87), s[e] = q[e] / sum q,
  *           the sum from +0 in expert order (score_fn)

@@ -439,11 +439,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     for (int m = 0; m < G::NF; ++m)
         read_frag<BM>(ring, f, 0, m, a_slot[0], b_slot[0], b_toff);
 
-    // the output as a buffer resource: offsets at or past out_bytes are dropped
-    const uint32_t out_rows = p.offsets ? p.max_rows : p.rows;
-    const uint32_t out_bytes = out_rows * (uint32_t)p.ldc * (MODE == kDown ? 4u : 2u);
-    const __amdgpu_buffer_rsrc_t out_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc(p.C, (short)0, (int)out_bytes, kBufferWord3);
+    // Each tile stores through a buffer resource based at its own first
+    // output row and spanning its rows that lie in the segment: offsets stay
+    // below BM rows of ldc elements (< 2^26 bytes) however large the output
+    // is, and an offset at or past the span (padding rows, columns past N)
+    // is dropped by the range check.
+    constexpr uint32_t kElt = MODE == kDown ? 4u : 2u;
+    const uint32_t kDropped = 0x80000000u;   // past every tile's span
 
     f32x16 acc[TM][TN];
     int sl = 0;                              // ring slot of the next step (steps done % NS)
@@ -513,6 +515,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         }
         const int half = lane >> 5;          // which 4 of each 8 columns the lane holds
         const int prow = lane & 31;          // the row the lane holds
+        const int span_rows = min(row_end - row0, BM);
+        const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (char *)p.C + (size_t)row0 * (size_t)p.ldc * kElt, (short)0,
+            (int)((uint32_t)span_rows * (uint32_t)p.ldc * kElt), kBufferWord3);
         if (MODE == kDown) {
             const int n0 = nt * kBN + wn * (kBN / 2);
 #pragma unroll
@@ -535,10 +541,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                         const int r = q * 8 + (lane >> 3);
                         const int chunk = (lane & 7) ^ ((r >> 1) & 7);
                         const u32x4 w4 = park_get16(park, r * 128 + chunk * 16);
-                        const int pos = row0 + a_tile_row + i * 32 + r;
-                        const uint32_t off = (pos < row_end && col_ok)
-                                                 ? ((uint32_t)pos * (uint32_t)p.ldc + col) * 4u
-                                                 : out_bytes;
+                        const int prel = a_tile_row + i * 32 + r;   // row within the tile
+                        const uint32_t off = (row0 + prel < row_end && col_ok)
+                                                 ? ((uint32_t)prel * (uint32_t)p.ldc + col) * 4u
+                                                 : kDropped;
                         __builtin_amdgcn_raw_buffer_store_b128(w4, out_rsrc, off, 0, 0);
                     }
                     fence();
@@ -601,11 +607,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                         const int r = q * 8 + (lane >> 3), c = lane & 7;
                         const int chunk = c ^ ((r >> 1) & 7);
                         const u32x4 w4 = park_get16(park, r * 128 + chunk * 16);
-                        const int pos = row0 + a_tile_row + i * 32 + r;
+                        const int prel = a_tile_row + i * 32 + r;   // row within the tile
                         const int col = n0 + jp * 32 + 8 * c;
-                        const uint32_t off = (pos < row_end && col < ncols)
-                                                 ? ((uint32_t)pos * (uint32_t)p.ldc + col) * 2u
-                                                 : out_bytes;
+                        const uint32_t off = (row0 + prel < row_end && col < ncols)
+                                                 ? ((uint32_t)prel * (uint32_t)p.ldc + col) * 2u
+                                                 : kDropped;
                         __builtin_amdgcn_raw_buffer_store_b128(w4, out_rsrc, off, 0, 0);
                     }
                     fence();
@@ -702,9 +708,12 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 }  // namespace
 
 bool grouped_supported(const GemmProblem &p) {
-    // every A offset (rows of A times lda, in bytes) stays below kPastA
-    // and every weight offset within one expert, stay below kPastA
-    const long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
+    // every A offset (rows of A times lda, in bytes) and every weight offset
+    // within one expert stay below kPastA; the rows of a gathered A are the
+    // positions divided by gather_div (the tokens of the up projection)
+    long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
+    if (p.gather != nullptr && p.gather_div > 1)
+        a_rows = (a_rows + p.gather_div - 1) / p.gather_div;
     return !p.affine4 && !p.fp8 && p.scatter == nullptr && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
            (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA &&
            (long long)p.N * p.K * 2 < (long long)kPastA;

@@ -65,6 +65,13 @@ def test_workspace_bytes_grows_with_the_problem():
     assert rc == 0 and shared > small
 
 
+def test_workspace_bytes_past_4gib_of_down_rows():
+    # T*k*H*4 = 4.59e9 bytes of per-assignment fp32 rows: the layout is in
+    # size_t and the call is accepted (T*k*H stays below 2^31 elements)
+    rc, n = ws_bytes(dims(T=140000, H=2048, I=128, E=8, k=4))
+    assert rc == 0 and n > 140000 * 4 * 2048 * 4 > (1 << 32)
+
+
 @pytest.mark.parametrize("bad,code,word", [
     (dict(H=100), -2, "H = 100"),
     (dict(H=0), -2, "H = 0"),

@@ -384,7 +384,9 @@ DECODE_CASES = [("tiny_t64_e8_k2", 8), ("tiny_t64_e8_k2", 1), ("mid_swiglu", 8),
                 ("mid_e256_k8", 64), ("mid_e256_k8", 7), ("mid_nan_ties", 4),
                 ("mid_swiglu_bigseg", 2), ("mid_softmax", 8), ("mid_softmax", 2),
                 ("mid_swiglu_limit", 8), ("mid_swiglu_limit", 1), ("mid_fp8", 4), ("mid_fp8", 1),
-                ("mid_fp8_relu2", 8)]
+                ("mid_fp8_relu2", 8), ("mid_affine4", 8), ("mid_affine4", 1),
+                ("mid_affine4_relu2", 8), ("mid_affine4_relu2", 3), ("mid_affine4_i64", 8),
+                ("mid_relu2_nonfinite", 8)]
 
 
 @pytest.mark.parametrize("name,T", DECODE_CASES)
@@ -460,6 +462,28 @@ def test_edge_cases(case):
     assert (ids16 == ids).all()
     check_out(out32, ref, tol_for(wl))
     assert (W.f32_to_bf16_bits(out32) == W.f32_to_bf16_bits(out16)).all()
+
+
+def test_forward_past_4gib_of_down_rows():
+    # The down projection's fp32 rows (T*k*H*4 = 4.59e9 bytes) pass 2^32
+    # bytes, so a store offset formed from the start of that buffer would
+    # wrap; rows past 2^32 bytes (slots >= 2^32 / (4 H)) are checked on the
+    # tokens that own them, plus a random sample.
+    wl = W.Workload("big_down_rows", T=140000, H=2048, I=128, E=8, k=4, seed=220)
+    inp = W.generate(wl)
+    out, ids, w, offs = run_forward(wl, inp)
+    ids_ref, w_ref = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k)
+    check_routing(ids, w, ids_ref, w_ref)
+    _, o_ref, _, slot_ref = oracle.plan(ids_ref, wl.E)
+    assert (offs == o_ref).all()
+    far = np.nonzero((slot_ref.reshape(wl.T, wl.k) >= (1 << 32) // (4 * wl.H)).any(axis=1))[0]
+    assert far.size > 1000
+    rng = np.random.default_rng(12)
+    toks = np.unique(np.concatenate([far[-8:], rng.choice(far, 24), rng.integers(0, wl.T, 8),
+                                     [wl.T - 1]]))
+    ref = oracle.forward_tokens(wl, inp, toks)
+    check_out(out[toks], ref, tol_for(wl))
+    assert np.isfinite(out).all()
 
 
 def test_zero_tokens():
