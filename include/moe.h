@@ -198,6 +198,25 @@ int moe_forward_profiled(const moe_dims *d, const moe_weights *w, const uint16_t
                          int32_t *ids_out, float *weights_out, int32_t *offsets_out,
                          hipEvent_t events[MOE_PROFILE_EVENTS]);
 
+/* moe_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same block and the same kernels, with the workspace taken
+ * from a static device array of MOE_NOALLOC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on until the process ends. The entry point
+ * calls no allocator. Inputs and outputs are as for moe_forward; the
+ * current device must be the one the stream and the tensors belong to.
+ * Calls whose workspace (moe_workspace_bytes) exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES are refused with MOE_E_WORKSPACE before
+ * anything is enqueued (4-bit experts of prompt-sized batches and block-FP8
+ * experts need room for decoded weights and usually are). Every call on one
+ * GPU shares that GPU's scratch: calls that overlap on one GPU (on
+ * different streams, or from different threads) race and must not be
+ * issued. A call does not rely on anything a previous call left there. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_dims *d, const moe_weights *w, const uint16_t *x, void *out,
+                        hipStream_t stream, int32_t *ids_out, float *weights_out,
+                        int32_t *offsets_out);
+
 /* Fused residual add + RMSNorm, the step that makes the block's input x
  * (TensorFold issue #548: RMSNorm and the fused add + RMSNorm among the shared
  * layer pieces, a row's bits the same at every row count; TensorFold PR #1492:

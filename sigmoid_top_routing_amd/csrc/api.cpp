@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "moe.h"
@@ -277,7 +278,8 @@ namespace {
 
 int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, const uint16_t *x,
                  void *out, void *workspace, size_t workspace_bytes, hipStream_t stream,
-                 int32_t *ids_out, float *weights_out, int32_t *offsets_out, hipEvent_t *events) {
+                 int32_t *ids_out, float *weights_out, int32_t *offsets_out, hipEvent_t *events,
+                 bool workspace_is_scratch = false) {
     TRY(check_dims(what, d, true));
     REQUIRE(w != nullptr, MOE_E_NULL, "%s: weights is NULL", what);
     TRY(check_ptr(what, "w->router_w", w->router_w));
@@ -311,7 +313,9 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     TRY(check_ptr(what, "x", x));
     TRY(check_ptr(what, "out", out));
     TRY(check_ptr(what, "workspace", workspace));
-    const void *dev[] = {x, out, workspace, w->router_w, w->expert_bias, w->w_up, w->w_down,
+    // (the static scratch is a device global, not an allocation the
+    // runtime's pointer query knows)
+    const void *dev[] = {x, out, workspace_is_scratch ? nullptr : workspace, w->router_w, w->expert_bias, w->w_up, w->w_down,
                          aff || fp8 ? w->w_up_scales : nullptr, aff ? w->w_up_biases : nullptr,
                          aff || fp8 ? w->w_down_scales : nullptr,
                          aff ? w->w_down_biases : nullptr,
@@ -485,6 +489,70 @@ int moe_forward_profiled(const moe_dims *d, const moe_weights *w, const uint16_t
                          hipEvent_t events[MOE_PROFILE_EVENTS]) {
     return forward_impl("moe_forward_profiled", d, w, x, out, workspace, workspace_bytes, stream,
                         ids_out, weights_out, offsets_out, events);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of moe_forward_noalloc: a file-scope device array, so the entry
+// point needs no allocation. Each GPU the library runs on holds its own copy
+// (at its own address) until the process ends. In host code `scratch` names
+// a host-side stand-in, never the device memory: its device address is
+// looked up once per device with hipGetSymbolAddress, and only that address
+// is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_dev[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on its first use).
+int scratch_address(const char *what, void **ptr) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MOE_E_HIP, "%s: hipGetDevice failed: %s", what, hipGetErrorString(e));
+    }
+    REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_E_UNSUPPORTED,
+            "%s: device %d, need an index below %d", what, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *p = nullptr;
+        const hipError_t se = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (se != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return fail(MOE_E_HIP, "%s: hipGetSymbolAddress(scratch) failed on device %d: %s",
+                        what, dev, hipGetErrorString(se));
+        }
+        g_scratch_dev[dev] = p;
+    }
+    *ptr = g_scratch_dev[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_noalloc(const moe_dims *d, const moe_weights *w, const uint16_t *x, void *out,
+                        hipStream_t stream, int32_t *ids_out, float *weights_out,
+                        int32_t *offsets_out) {
+    const char *what = "moe_forward_noalloc";
+    TRY(check_dims(what, d, true));
+    const size_t need = layout(*d).total;
+    REQUIRE(need <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_E_WORKSPACE,
+            "%s: this call needs %zu bytes of scratch; the static scratch holds %zu "
+            "(MOE_NOALLOC_SCRATCH_BYTES): call moe_forward with a workspace instead",
+            what, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    if (d->T == 0)      // checks the arguments, enqueues nothing
+        return forward_impl(what, d, w, x, out, nullptr, (size_t)MOE_NOALLOC_SCRATCH_BYTES,
+                            stream, ids_out, weights_out, offsets_out, nullptr, true);
+    void *ws = nullptr;
+    TRY(scratch_address(what, &ws));
+    return forward_impl(what, d, w, x, out, ws, (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream,
+                        ids_out, weights_out, offsets_out, nullptr, true);
 }
 
 int moe_add_rmsnorm(int32_t T, int32_t H, const uint16_t *h, const uint16_t *residual,

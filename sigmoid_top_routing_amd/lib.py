@@ -26,7 +26,8 @@ SCORE = {"sigmoid": 0, "softmax": 1}
 
 # every entry point include/moe.h declares
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_plan", "moe_forward", "moe_forward_profiled",
-           "moe_add_rmsnorm", "moe_last_error")
+           "moe_forward_noalloc", "moe_add_rmsnorm", "moe_last_error")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 PROFILE_EVENTS = 7
 STAGES = ("route", "plan", "up", "down", "shared", "combine")
 
@@ -74,6 +75,9 @@ def load():
         L.moe_forward_profiled.argtypes = [C.POINTER(Dims), C.POINTER(Weights), p, p, p,
                                            C.c_size_t, p, p, p, p, C.POINTER(p)]
         L.moe_forward_profiled.restype = i
+        L.moe_forward_noalloc.argtypes = [C.POINTER(Dims), C.POINTER(Weights), p, p, p, p, p,
+                                          p]
+        L.moe_forward_noalloc.restype = i
         L.moe_add_rmsnorm.argtypes = [C.c_int32, C.c_int32, p, p, p, C.c_float, p, p, p]
         L.moe_add_rmsnorm.restype = i
         L.moe_last_error.argtypes = []
@@ -226,6 +230,21 @@ class MoEBlock:
             _check(load().moe_forward(*args))
         else:
             _check(load().moe_forward_profiled(*args, events.handles()))
+        return out
+
+
+    def forward_noalloc(self, x, out_dtype=torch.bfloat16, out=None, ids_out=None,
+                        weights_out=None, offsets_out=None, stream=None):
+        """out [T,H] through moe_forward_noalloc: the library's static scratch
+        instead of a workspace (no allocation inside the call)."""
+        T = x.shape[0]
+        d = self.dims(T, out_dtype)
+        if out is None:
+            out = torch.empty((T, self.H), dtype=out_dtype, device=x.device)
+        w = self.weights()
+        _check(load().moe_forward_noalloc(C.byref(d), C.byref(w), _ptr(x), _ptr(out),
+                                          _stream(stream), _ptr(ids_out), _ptr(weights_out),
+                                          _ptr(offsets_out)))
         return out
 
 

@@ -170,6 +170,29 @@ def test_forward_refuses_null_misaligned_and_short_workspace():
     assert rc == -1 and "shared_up" in L.moe_last_error().decode()
 
 
+def test_noalloc_refuses_problems_past_its_scratch_before_any_launch():
+    # moe_forward_noalloc takes its workspace from a static device array of
+    # MOE_NOALLOC_SCRATCH_BYTES; a call that needs more is refused on the host
+    L = lib.load()
+    w = lib.Weights(router_w=0x1000, w_up=0x2000, w_down=0x3000)
+    big = dims(T=4096, H=2048, I=1792, E=32, k=4)
+    assert lib.workspace_bytes(big) > lib.NOALLOC_SCRATCH_BYTES
+    rc = L.moe_forward_noalloc(C.byref(big), C.byref(w), _fake(0x1000), _fake(0x1000), None,
+                               None, None, None)
+    msg = L.moe_last_error().decode()
+    assert rc == -5 and "MOE_NOALLOC_SCRATCH_BYTES" in msg and str(lib.NOALLOC_SCRATCH_BYTES) in msg
+    # 4-bit experts of a prompt-sized batch need room for their decoded weights
+    q4 = dims(T=1024, H=2048, I=1792, E=32, k=4, wfmt="affine4")
+    rc = L.moe_forward_noalloc(C.byref(q4), C.byref(w), _fake(0x1000), _fake(0x1000), None,
+                               None, None, None)
+    assert rc == -5
+    # zero tokens: arguments checked, nothing enqueued, no device touched
+    z = dims(T=0)
+    assert L.moe_forward_noalloc(C.byref(z), C.byref(w), None, None, None, None, None,
+                                 None) == 0
+    assert L.moe_forward_noalloc(C.byref(z), None, None, None, None, None, None, None) == -1
+
+
 def test_zero_tokens_enqueue_nothing():
     L = lib.load()
     d = dims(T=0)
