@@ -21,8 +21,9 @@ Besides the whole-block throughput the line carries:
   configs       the other workloads, each with its step time, algorithmic
                 bytes and flops and their fractions of the HBM and bf16 MFMA
                 peaks: the tiny block, the relu^2 block with a shared expert,
-                the 4-bit block, and the 4-bit decode step (T = 8) without
-                and with the four boosted experts.
+                the 4-bit block, the 4-bit decode step (T = 8) without
+                and with the four boosted experts, and the block-FP8 decode
+                step.
 """
 from __future__ import annotations
 
@@ -61,6 +62,9 @@ def expert_bytes(wl):
     if wl.wfmt == "affine4":
         up = wl.n_up * wl.H // 2 + 2 * 2 * wl.n_up * (wl.H // 64)
         down = wl.H * wl.I // 2 + 2 * 2 * wl.H * (wl.I // 64)
+    elif wl.wfmt == "fp8":
+        up = wl.n_up * wl.H + 4 * (wl.n_up // 128) * (wl.H // 128)
+        down = wl.H * wl.I + 4 * (wl.H // 128) * (wl.I // 128)
     else:
         up = 2 * wl.n_up * wl.H
         down = 2 * wl.H * wl.I
@@ -269,7 +273,8 @@ def main():
                                  ("relu2", "nemotron_relu2_t2048", False),
                                  ("affine4", "affine4_t1024", False),
                                  ("affine4_decode", "affine4_flat_decode_t8", True),
-                                 ("affine4_decode_boosted", "affine4_decode_t8", True)):
+                                 ("affine4_decode_boosted", "affine4_decode_t8", True),
+                                 ("fp8_decode", "lfm2_fp8_decode_t8", True)):
             result["configs"][tag] = bench_step(W.by_name(name), W, lib, torch, flush=flush)
             print(f"bench: {tag} done", file=sys.stderr, flush=True)
     if not args.no_cpu:

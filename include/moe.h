@@ -116,7 +116,9 @@ typedef struct {
  *  exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
  *  NaN; largest 448), w_*_scales are fp32 [E, N/128, K/128], one per
  *  128 x 128 block, the weight is scale * value, and w_*_biases are unused.
- *  H and I must then be multiples of 128. The experts with rows are decoded
+ *  H and I must then be multiples of 128. Decode-sized batches stream the
+ *  codes (one byte per weight) and apply each block's scale in fp32 to the
+ *  partial sum of its 128 inputs; larger ones decode the experts with rows
  *  to bf16 in the workspace, then run on the bf16 kernels.
  *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
  *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared]. */
@@ -134,10 +136,11 @@ typedef struct {
 } moe_weights;
 
 /* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
- * 4-bit experts and more than 2 E assignments (T * k > 2 E), and with
- * block-FP8 experts at any T, this includes room for the bf16-decoded
- * weights of every expert that can have rows:
- * min(E, T * k) * max(n_up * H, H * I) * 2 bytes, n_up = 2 I (SwiGLU) or I. */
+ * 4-bit or block-FP8 experts and more than 2 E assignments (T * k > 2 E),
+ * and with block-FP8 experts whose max(H, I) exceeds 4096 at any T, this
+ * includes room for the bf16-decoded weights of every expert that can have
+ * rows: min(E, T * k) * max(n_up * H, H * I) * 2 bytes, n_up = 2 I (SwiGLU)
+ * or I. Decode-sized batches (T * k <= 2 E) stream the codes instead. */
 int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
 
 /* Router and top-k (TileGym PR #187 "Weight layout and routing"; TensorFold

@@ -45,14 +45,27 @@ struct Layout {
     size_t z, ids, w, counts, offsets, sorted, slot, chunk_counts, h, y, hs, ys, wdq, total;
 };
 
-// Prompt-sized batches with 4-bit experts decode the weights of the experts
-// with rows to bf16 once per call and run the direct-to-LDS grouped kernel on
-// them; decode-sized ones keep the decode in the staged kernel's loads.
-// 4-bit experts of prompt-sized batches, and block-FP8 experts always, are
-// decoded to bf16 before the bf16 kernels run.
+// Decode-sized batches (at most two assignments per expert on average)
+// stream each touched expert's weights once; larger ones take the MFMA tiles
+// (TensorFold issue #548: decode rows and prompt rows).
+bool decode_sized(const moe_dims &d) { return (int64_t)d.T * d.k <= 2 * (int64_t)d.E; }
+
+// Quantized experts the decode form streams at their stored width (the
+// projections' K within its limits).
+bool quant_streams(const moe_dims &d) {
+    const int kmax = std::max(d.H, d.I);
+    return decode_sized(d) && ((d.wfmt == MOE_W_AFFINE4 && kmax <= moe::kStreamMaxKAffine4) ||
+                               (d.wfmt == MOE_W_FP8 && kmax <= moe::kStreamMaxKFp8));
+}
+
+// 4-bit experts of prompt-sized batches, and block-FP8 experts the decode
+// form does not stream, are decoded to bf16 (the weights of the experts with
+// rows, once per call) before the bf16 MFMA kernel runs. Decode-sized 4-bit
+// batches the stream does not take keep the decode in the staged kernel's
+// loads.
 bool dequant_first(const moe_dims &d) {
-    return (d.wfmt == MOE_W_AFFINE4 && (int64_t)d.T * d.k > 2 * (int64_t)d.E) ||
-           d.wfmt == MOE_W_FP8;
+    return (d.wfmt == MOE_W_AFFINE4 && !decode_sized(d)) ||
+           (d.wfmt == MOE_W_FP8 && !quant_streams(d));
 }
 
 Layout layout(const moe_dims &d) {
@@ -354,10 +367,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         LAUNCH(moe::launch_plan(ids, A, E, counts, offsets, sorted, slot, nullptr,
                                 (int32_t *)(ws + L.chunk_counts), stream));
     LAUNCH(mark(2));
-    // Decode-sized batches (at most two assignments per expert on average)
-    // stream each touched expert's weights once; larger ones take the MFMA
-    // tiles (TensorFold issue #548: decode rows and prompt rows).
-    const bool decode_form = A <= 2 * E;
+    const bool decode_form = decode_sized(*d);
     auto run = [&](const moe::GemmProblem &g) {
         return decode_form && moe::stream_supported(g) ? moe::launch_stream(g, stream)
                                                        : moe::launch_gemm(g, stream);

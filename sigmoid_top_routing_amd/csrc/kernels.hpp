@@ -82,6 +82,10 @@ hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream);
 
 // The same problem in the weight-streaming (decode) form: few A rows per
 // expert, every touched weight row read once, v_dot2 accumulation.
+// Largest K the quantized decode form takes (4 steps of 16 code bytes per
+// lane: 8192 4-bit weights, 4096 FP8 weights).
+constexpr int kStreamMaxKAffine4 = 8192;
+constexpr int kStreamMaxKFp8 = 4096;
 bool stream_supported(const GemmProblem &p);
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream);
 

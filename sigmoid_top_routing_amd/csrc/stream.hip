@@ -65,31 +65,32 @@ __device__ __forceinline__ float dot8(const uint4 &w, const uint4 &x, float c) {
 // times across lanes (xor 32, 16, ...), then sum the KEEP survivors over the
 // remaining lanes. Afterwards v[0..KEEP-1] of every lane are full sums of
 // the values whose index is given by the lane's bits 5, 4, ... (most
-// significant first) times KEEP.
-template <int V, int KEEP>
-__device__ __forceinline__ void transpose_reduce(float (&v)[V], int lane) {
-    int c = V;
-    int m = 32;
+// significant first) times KEEP. Written as compile-time recursion, so every
+// array index and xor mask is a constant (a runtime half would turn each
+// v[j + half] into a chain of compares and selects).
+template <int C, int KEEP, int M, int V>
+__device__ __forceinline__ void transpose_reduce_step(float (&v)[V], int lane) {
+    if constexpr (C > KEEP) {
+        constexpr int half = C / 2;
+        const bool hi = (lane & M) != 0;
 #pragma unroll
-    for (int step = 0; (V >> step) > KEEP; ++step) {
-        const bool hi = (lane & m) != 0;
-        const int half = c / 2;
-#pragma unroll
-        for (int j = 0; j < V / 2; ++j) {
-            if (j < half) {
-                const float give = hi ? v[j] : v[j + half];
-                const float keep = hi ? v[j + half] : v[j];
-                v[j] = keep + __shfl_xor(give, m, kWave);
-            }
+        for (int j = 0; j < half; ++j) {
+            const float give = hi ? v[j] : v[j + half];
+            const float keep = hi ? v[j + half] : v[j];
+            v[j] = keep + __shfl_xor(give, M, kWave);
         }
-        c = half;
-        m >>= 1;
-    }
-    for (; m >= 1; m >>= 1) {
+        transpose_reduce_step<half, KEEP, M / 2, V>(v, lane);
+    } else if constexpr (M >= 1) {
 #pragma unroll
         for (int j = 0; j < KEEP; ++j)
-            v[j] += __shfl_xor(v[j], m, kWave);
+            v[j] += __shfl_xor(v[j], M, kWave);
+        transpose_reduce_step<C, KEEP, M / 2, V>(v, lane);
     }
+}
+
+template <int V, int KEEP>
+__device__ __forceinline__ void transpose_reduce(float (&v)[V], int lane) {
+    transpose_reduce_step<V, KEEP, 32, V>(v, lane);
 }
 
 template <int MODE, int NJ>
@@ -204,6 +205,281 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Quantized weights in the decode form: the codes are streamed at their
+// stored width and decoded in registers, so a step reads each touched
+// expert's bytes once (TensorFold PR #1492, "What": the MLX 4-bit affine
+// experts with group 64; TensorFold issue #548: block-FP8 experts with one
+// fp32 scale per 128 x 128 block, and one decode-row kernel per format).
+//
+// A lane loads 16 bytes of codes per row and step j: 32 weights of 4-bit
+// codes (elements 32 l + 2048 j .. + 31, inside one group of 64), or 16
+// FP8 weights (elements 16 l + 1024 j .. + 15, inside one 128-wide K block).
+// So each lane partial has a single scale, applied in fp32 to the partial:
+//   4-bit:  w = s q + b, and sum_c w_c x_c = s (A - 128 X) + b X with
+//           A = sum_c (128 + q_c) x_c and X = sum_c x_c over the lane's 32
+//           elements. 128 + q is a bf16 whose bits are 0x4300 | q, so the
+//           codes become bf16 pairs with two integer ops and A is a chain of
+//           v_dot2_f32_bf16, like the bf16 kernel; X comes from the same
+//           x reads (a dot2 chain with 1.0 pairs), once per token row and
+//           step for all of the wave's units.
+//   FP8:    w = s v, and sum_c w_c x_c = s (sum_c v_c x_c): every E4M3 value
+//           is a bf16 value, so v is converted exactly (two per
+//           instruction) and the sum is a v_dot2_f32_bf16 chain.
+// The lane partials are then reduced across the wave as in k_stream.
+constexpr int kFmtAffine4 = 1;
+constexpr int kFmtFp8 = 2;
+
+template <int FMT>
+struct QFmt {
+    static constexpr int EPL = FMT == kFmtAffine4 ? 32 : 16;   // weights per lane per step
+    static constexpr int EPJ = EPL * kWave;                    // weights per wave per step
+    static constexpr int CPL = EPL / 8;                        // 16-byte x chunks per lane
+};
+
+// LDS slot of x chunk c (8 bf16) of a staged row: lane l reads chunks
+// CPL l + i; the low bits are XORed with bits 4.. of the chunk so the 16
+// lanes of one ds_read_b128 pass hit 16 distinct 16-byte bank groups.
+template <int CPL>
+__device__ __forceinline__ int qslot(int c) {
+    return CPL == 1 ? c : ((c & ~(CPL - 1)) | ((c & (CPL - 1)) ^ ((c >> 4) & (CPL - 1))));
+}
+
+// 4-bit codes of one word -> four bf16 pairs (128 + q): pair b holds nibbles
+// 2b (low half) and 2b + 1 (high half). v_perm_b32 puts byte b of w (low
+// nibble: code 2b) in byte 0 and byte b of w >> 4 (low nibble: code 2b + 1)
+// in byte 2 (selectors 0..3 pick bytes of its second operand, 4..7 of its
+// first, 12 gives 0x00); the mask keeps those two nibbles under 0x4300.
+__device__ __forceinline__ void q4_pairs(uint32_t w, uint32_t (&pr)[4]) {
+    const uint32_t hi = w >> 4;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint32_t t = __builtin_amdgcn_perm(hi, w, 0x0C000C00u | ((4u + b) << 16) | b);
+        pr[b] = (t & 0x000F000Fu) | 0x43004300u;
+    }
+}
+
+// Units per wave: two, or one at four steps of codes (the registers hold
+// every step's codes). Four and eight weight rows per wave measured the same
+// and slower (fewer waves fit a CU).
+template <int NJ, int NR>
+constexpr int q_units_per_wave() { return NJ >= 4 ? 1 : 2; }
+
+template <int MODE, int FMT, int NJ>
+__global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
+    using Q = QFmt<FMT>;
+    constexpr int NR = gated(MODE) ? 2 : 1;       // weight rows per unit
+    constexpr int UW = q_units_per_wave<NJ, NR>();   // units per wave
+    constexpr int XC = NJ * Q::EPJ / 8;           // x chunks per staged row
+    __shared__ uint4 xs[kTG][XC];                 // token rows, bf16, swizzled chunks
+    const int lane = threadIdx.x & (kWave - 1);
+    int e = 0, seg0 = 0, seg1 = p.rows;
+    if (p.offsets != nullptr) {
+        e = -1;
+        int want = blockIdx.y;
+        for (int base = 0; base < p.E && e < 0; base += kWave) {
+            const int x = base + lane;
+            const int lo = x < p.E ? p.offsets[x] : 0;
+            const int hi = x < p.E ? p.offsets[x + 1] : 0;
+            const bool busy = hi > lo;
+            const uint64_t m = __ballot(busy);
+            const int below = __popcll(m & ((1ull << lane) - 1ull));
+            const uint64_t hit = __ballot(busy && below == want);
+            if (hit != 0) {
+                const int src = __ffsll((unsigned long long)hit) - 1;
+                e = base + src;
+                seg0 = __shfl(lo, src, kWave);
+                seg1 = __shfl(hi, src, kWave);
+            }
+            want -= __popcll(m);
+        }
+        e = __builtin_amdgcn_readfirstlane(e);
+        if (e < 0)
+            return;                                // uniform
+        seg0 = __builtin_amdgcn_readfirstlane(seg0);
+        seg1 = __builtin_amdgcn_readfirstlane(seg1);
+    }
+    if (seg0 >= seg1)
+        return;                                    // uniform
+    const int units = gated(MODE) ? p.I : p.N;
+    const int wave = threadIdx.x / kWave;
+    const int K = p.K;
+    const int ub = blockIdx.x * (kThreads / kWave) * UW + wave * UW;
+
+    // this wave's code rows and the scale (and bias) of each lane partial,
+    // requested before anything else
+    uint4 w[UW][NR][NJ];
+    float sc[UW][NR][NJ], bi[UW][NR][NJ];
+    const size_t erow = (size_t)e * p.N;
+#pragma unroll
+    for (int i = 0; i < UW; ++i) {
+        const int u = ub + i;
+#pragma unroll
+        for (int s = 0; s < NR; ++s) {
+            const int n = s == 0 ? u : p.I + u;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int kk = j * Q::EPJ + lane * Q::EPL;     // first weight of the lane
+                const bool in = u < units && kk < K;
+                sc[i][s][j] = 0.0f;
+                bi[i][s][j] = 0.0f;
+                if (FMT == kFmtAffine4) {
+                    const uint8_t *row = (const uint8_t *)p.B + (erow + n) * (size_t)(K / 2);
+                    w[i][s][j] = in ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                          reinterpret_cast<const u32x4 *>(row + kk / 2)))
+                                    : make_uint4(0, 0, 0, 0);
+                    if (in) {
+                        const size_t g = (erow + n) * (size_t)(K / 64) + kk / 64;
+                        sc[i][s][j] = bf16_to_f32(p.Bscale[g]);
+                        bi[i][s][j] = bf16_to_f32(p.Bbias[g]);
+                    }
+                } else {
+                    const uint8_t *row = (const uint8_t *)p.B + (erow + n) * (size_t)K;
+                    w[i][s][j] = in ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
+                                          reinterpret_cast<const u32x4 *>(row + kk)))
+                                    : make_uint4(0, 0, 0, 0);
+                    if (in)
+                        sc[i][s][j] = reinterpret_cast<const float *>(p.Bscale)
+                            [((size_t)e * (p.N / 128) + n / 128) * (size_t)(K / 128) + kk / 128];
+                }
+            }
+        }
+    }
+
+    for (int g0 = seg0; g0 < seg1; g0 += kTG) {
+        const int nr = min(kTG, seg1 - g0);
+        if (g0 != seg0)
+            __syncthreads();                       // the previous group is read
+        for (int idx = threadIdx.x; idx < kTG * XC; idx += kThreads) {
+            const int r = idx / XC, c = idx % XC;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (r < nr && c * 8 < K) {
+                const int pos = g0 + r;
+                const int arow = p.gather ? p.gather[pos] / p.gather_div : pos;
+                v = *reinterpret_cast<const uint4 *>(p.A + (size_t)arow * p.lda + c * 8);
+            }
+            xs[r][qslot<Q::CPL>(c)] = v;
+        }
+        __syncthreads();
+        // v[i][r * NR + s]: unit i, token row r, weight row s
+        float v[UW][kTG * NR];
+#pragma unroll
+        for (int i = 0; i < UW; ++i)
+#pragma unroll
+            for (int q = 0; q < kTG * NR; ++q)
+                v[i][q] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            // step j of every unit's rows decoded to bf16 pairs once
+            uint32_t pr[UW][NR][Q::EPL / 2];
+#pragma unroll
+            for (int i = 0; i < UW; ++i)
+#pragma unroll
+                for (int s = 0; s < NR; ++s) {
+                    const uint32_t cw[4] = {w[i][s][j].x, w[i][s][j].y, w[i][s][j].z,
+                                            w[i][s][j].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (FMT == kFmtAffine4) {
+                            uint32_t four[4];
+                            q4_pairs(cw[q], four);
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                pr[i][s][4 * q + b] = four[b];
+                        } else {
+                            pr[i][s][2 * q] = __builtin_bit_cast(
+                                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[q], 1.0f, false));
+                            pr[i][s][2 * q + 1] = __builtin_bit_cast(
+                                uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[q], 1.0f, true));
+                        }
+                    }
+                }
+#pragma unroll
+            for (int r = 0; r < kTG; ++r) {
+                if (r < nr) {                      // uniform
+                    // the lane's x values of this step, read once for every unit
+                    uint4 xv[Q::CPL];
+#pragma unroll
+                    for (int c = 0; c < Q::CPL; ++c)
+                        xv[c] = xs[r][qslot<Q::CPL>((j * kWave + lane) * Q::CPL + c)];
+                    // 4-bit: X = the sum of those x values
+                    float X = 0.0f;
+                    if constexpr (FMT == kFmtAffine4) {
+#pragma unroll
+                        for (int c = 0; c < Q::CPL; ++c)
+                            X = dot8(make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u,
+                                                0x3F803F80u), xv[c], X);
+                    }
+#pragma unroll
+                    for (int i = 0; i < UW; ++i)
+#pragma unroll
+                        for (int s = 0; s < NR; ++s) {
+                            float a = 0.0f;
+#pragma unroll
+                            for (int c = 0; c < Q::CPL; ++c)
+                                a = dot8(make_uint4(pr[i][s][4 * c], pr[i][s][4 * c + 1],
+                                                    pr[i][s][4 * c + 2], pr[i][s][4 * c + 3]),
+                                         xv[c], a);
+                            if constexpr (FMT == kFmtAffine4)
+                                v[i][r * NR + s] += sc[i][s][j] * __builtin_fmaf(-128.0f, X, a) +
+                                                    bi[i][s][j] * X;
+                            else
+                                v[i][r * NR + s] += sc[i][s][j] * a;
+                        }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < UW; ++i) {
+            const int u = ub + i;
+            transpose_reduce<kTG * NR, NR>(v[i], lane);
+            const int r = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+            if ((lane & 15) == 0 && r < nr && u < units) {
+                const int pos = g0 + r;
+                if (gated(MODE)) {
+                    ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] = (uint16_t)f32_to_bf16(
+                        swiglu<MODE == kGateUpLimit>(v[i][0], v[i][1], p.limit));
+                } else if (MODE == kUpRelu2) {
+                    ((uint16_t *)p.C)[(size_t)pos * p.ldc + u] =
+                        (uint16_t)f32_to_bf16(relu_sq(v[i][0]));
+                } else {
+                    const int orow = p.scatter ? p.scatter[pos] : pos;
+                    ((float *)p.C)[(size_t)orow * p.ldc + u] = v[i][0];
+                }
+            }
+        }
+    }
+}
+
+template <int MODE, int FMT, int NJ>
+hipError_t launch_q(const GemmProblem &p, hipStream_t stream) {
+    const int units = gated(MODE) ? p.I : p.N;
+    const int upb = (kThreads / kWave) * q_units_per_wave<NJ, gated(MODE) ? 2 : 1>();
+    const dim3 grid((units + upb - 1) / upb, p.offsets != nullptr ? p.E : 1);
+    hipLaunchKernelGGL((k_stream_q<MODE, FMT, NJ>), grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int MODE, int FMT>
+hipError_t launch_q_mode(const GemmProblem &p, hipStream_t stream) {
+    const int nj = (p.K + QFmt<FMT>::EPJ - 1) / QFmt<FMT>::EPJ;
+    if (nj <= 1)
+        return launch_q<MODE, FMT, 1>(p, stream);
+    if (nj <= 2)
+        return launch_q<MODE, FMT, 2>(p, stream);
+    return launch_q<MODE, FMT, 4>(p, stream);
+}
+
+template <int FMT>
+hipError_t launch_q_fmt(const GemmProblem &p, hipStream_t stream) {
+    switch (p.mode) {
+    case kGateUp: return launch_q_mode<kGateUp, FMT>(p, stream);
+    case kGateUpLimit: return launch_q_mode<kGateUpLimit, FMT>(p, stream);
+    case kUpRelu2: return launch_q_mode<kUpRelu2, FMT>(p, stream);
+    default: return launch_q_mode<kDown, FMT>(p, stream);
+    }
+}
+
 template <int MODE, int NJ>
 hipError_t launch_nj(const GemmProblem &p, hipStream_t stream) {
     const int units = gated(MODE) ? p.I : p.N;
@@ -228,10 +504,22 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 }  // namespace
 
 bool stream_supported(const GemmProblem &p) {
-    return !p.affine4 && !p.fp8 && !p.b_compact && p.K <= 4096;
+    if (p.b_compact || p.scatter != nullptr)
+        return false;
+    static_assert(kStreamMaxKAffine4 == 4 * QFmt<kFmtAffine4>::EPJ, "4-bit steps");
+    static_assert(kStreamMaxKFp8 == 4 * QFmt<kFmtFp8>::EPJ, "FP8 steps");
+    if (p.affine4)      // 4 code words per lane and step; groups of 64
+        return p.K % 64 == 0 && p.K <= kStreamMaxKAffine4;
+    if (p.fp8)          // 128 x 128 scale blocks
+        return p.K % 128 == 0 && p.N % 128 == 0 && p.K <= kStreamMaxKFp8;
+    return p.K <= 4096;
 }
 
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream) {
+    if (p.affine4)
+        return launch_q_fmt<kFmtAffine4>(p, stream);
+    if (p.fp8)
+        return launch_q_fmt<kFmtFp8>(p, stream);
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp>(p, stream);
     case kGateUpLimit: return launch_mode<kGateUpLimit>(p, stream);

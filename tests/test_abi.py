@@ -113,9 +113,14 @@ def test_unsupported_options_are_refused():
     assert ws_bytes(dims(score="softmax"))[0] == 0
     assert ws_bytes(dims(wfmt="fp8", H=192))[0] == -2
     assert "multiples of 128" in lib.load().moe_last_error().decode()
-    rc, n8 = ws_bytes(dims(wfmt="fp8", T=1, H=256, I=256, E=8, k=2))
-    rc16, n16 = ws_bytes(dims(T=1, H=256, I=256, E=8, k=2))
-    assert rc == rc16 == 0 and n8 >= n16 + 2 * 512 * 256 * 2     # two experts decoded
+    # a prompt-sized FP8 batch holds the decoded weights of its experts; a
+    # decode-sized one streams the codes and needs no more than bf16
+    rc, n8 = ws_bytes(dims(wfmt="fp8", T=64, H=256, I=256, E=8, k=2))
+    rc16, n16 = ws_bytes(dims(T=64, H=256, I=256, E=8, k=2))
+    assert rc == rc16 == 0 and n8 >= n16 + 8 * 512 * 256 * 2     # eight experts decoded
+    rc, n8 = ws_bytes(dims(wfmt="fp8", T=8, H=256, I=256, E=8, k=2))
+    rc16, n16 = ws_bytes(dims(T=8, H=256, I=256, E=8, k=2))
+    assert rc == rc16 == 0 and n8 == n16
 
 
 def test_add_rmsnorm_refuses_bad_shapes_and_pointers():
