@@ -22,6 +22,8 @@
  *             relu^2: W_up = up (E, I, H), act = (up < 0 ? 0 : up)^2
  *   out_t = routed_scale * sum_j w_j y_j + shared_t
  *   shared_t = W_sd act(W_su x_t), added unscaled (optional)
+ *   (or, with fold_routed_scale and no shared expert,
+ *    out_t = sum_j (routed_scale w_j) y_j)
  * Sources: TileGym PR #187, "Weight layout and routing" (gate_up layout,
  * sigmoid routing, bias used only for selection, sum + 1e-6, then the routed
  * scaling factor); TensorFold PR #1492, "What" and "Verification" (fp32
@@ -97,6 +99,13 @@ typedef struct {
     int32_t score_fn;     /* moe_score: router scores (the bias, if any, still only selects) */
     float swiglu_limit;   /* 0: none; L > 0 (SwiGLU only, routed and shared experts):
                              gate capped at L, up clamped to [-L, L], NaN kept */
+    int32_t fold_routed_scale; /* 0: routed_scale multiplies the finished routed sum
+                             (the Nemotron-H order); 1: Laguna's fold, routed_scale
+                             multiplies each expert weight inside the sum, the
+                             fp32 product routed_scale * w_j taken once per term
+                             (vllm.cpp PR #684, the review-repairs commit: equal in
+                             exact arithmetic, different fp32 bits; legal only
+                             without a shared expert, so I_shared must be 0) */
 } moe_dims;
 
 /* Weights of one layer (device pointers).
@@ -181,7 +190,9 @@ int moe_plan(const moe_dims *d, const int32_t *ids, int32_t *counts, int32_t *of
  *  x    bf16 [T, H]
  *  out  [T, H], bf16 or fp32 by d->out_dtype: each element is computed in
  *       fp32 as routed_scale * (fma chain of w_j * y_j, j ascending), plus
- *       the shared expert's output, and rounded once.
+ *       the shared expert's output, and rounded once; with
+ *       d->fold_routed_scale, as the fma chain of (routed_scale * w_j) * y_j,
+ *       j ascending. weights_out holds the unscaled w_j either way.
  *  ids_out, weights_out ([T, k]) and offsets_out ([E+1]) may be NULL; when
  *  given they receive the routing and the plan offsets of this call.
  * Workspace: moe_workspace_bytes(d). */

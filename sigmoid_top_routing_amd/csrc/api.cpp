@@ -165,6 +165,11 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
     REQUIRE(d->swiglu_limit == 0.0f || d->act == MOE_ACT_SWIGLU, MOE_E_UNSUPPORTED,
             "%s: swiglu_limit = %g applies to MOE_ACT_SWIGLU only (act = %d)", what,
             (double)d->swiglu_limit, d->act);
+    REQUIRE(d->fold_routed_scale == 0 || d->fold_routed_scale == 1, MOE_E_UNSUPPORTED,
+            "%s: fold_routed_scale = %d, need 0 or 1", what, d->fold_routed_scale);
+    REQUIRE(d->fold_routed_scale == 0 || d->I_shared == 0, MOE_E_UNSUPPORTED,
+            "%s: fold_routed_scale = 1 with I_shared = %d: the fold is legal only without "
+            "a shared expert", what, d->I_shared);
     return MOE_OK;
 }
 
@@ -478,7 +483,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         shared = ys;
     }
     LAUNCH(mark(5));
-    LAUNCH(moe::launch_combine(y, slot, wts, shared, T, H, k, d->routed_scale, out,
+    LAUNCH(moe::launch_combine(y, slot, wts, shared, T, H, k, d->routed_scale,
+                               d->fold_routed_scale != 0, out,
                                d->out_dtype == MOE_OUT_F32, stream));
     LAUNCH(mark(6));
     return ok();

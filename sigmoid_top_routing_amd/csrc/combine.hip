@@ -10,6 +10,12 @@
 // ("Weight layout and routing"): the routed scaling factor comes after the
 // normalised weights.
 //
+// With fold (Laguna's order, only without a shared expert) the scale goes
+// into each weight instead: acc = fma(routed_scale * w[t,j], y, acc), j
+// ascending, and nothing after; the product is rounded once per term, so the
+// bits differ from the order above (vllm.cpp PR #684, the review-repairs
+// commit). A separate instantiation, so the default order's code is unchanged.
+//
 // y holds the down projection's rows in segment order (assignment a at row
 // slot_of[a], the plan's position), so the expert kernels write whole rows
 // where their tiles are and the combine gathers a token's k rows. Each
@@ -26,6 +32,7 @@ namespace {
 
 constexpr int kThreads = 256;
 
+template <bool FOLD>
 __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ y,
                                                       const int32_t *__restrict__ slot,
                                                       const float *__restrict__ w,
@@ -43,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ 
     for (int c = 0; c < 8; ++c)
         acc[c] = 0.0f;
     for (int j = 0; j < k; ++j) {
-        const float wj = w[(size_t)t * k + j];
+        const float wj = FOLD ? rsf * w[(size_t)t * k + j] : w[(size_t)t * k + j];
         const int row = slot[(size_t)t * k + j];
         const float4 *yp = reinterpret_cast<const float4 *>(y + (size_t)row * H + h0);
         const float4 a = yp[0], b = yp[1];
@@ -52,9 +59,11 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ 
         for (int c = 0; c < 8; ++c)
             acc[c] = __builtin_fmaf(wj, v[c], acc[c]);
     }
+    if (!FOLD) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-        acc[c] = acc[c] * rsf;
+        for (int c = 0; c < 8; ++c)
+            acc[c] = acc[c] * rsf;
+    }
     if (shared != nullptr) {
         const float4 *sp = reinterpret_cast<const float4 *>(shared + (size_t)t * H + h0);
         const float4 a = sp[0], b = sp[1];
@@ -77,14 +86,18 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ 
 }  // namespace
 
 hipError_t launch_combine(const float *y_seg, const int32_t *slot_of, const float *weights,
-                          const float *shared, int T, int H, int k, float routed_scale, void *out,
-                          int out_f32, hipStream_t stream) {
+                          const float *shared, int T, int H, int k, float routed_scale, bool fold,
+                          void *out, int out_f32, hipStream_t stream) {
     const size_t n = (size_t)T * (H / 8);
     if (n == 0)
         return hipSuccess;
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
-    hipLaunchKernelGGL(k_combine, grid, dim3(kThreads), 0, stream, y_seg, slot_of, weights, shared,
-                       T, H, k, routed_scale, out, out_f32);
+    if (fold)
+        hipLaunchKernelGGL(k_combine<true>, grid, dim3(kThreads), 0, stream, y_seg, slot_of,
+                           weights, shared, T, H, k, routed_scale, out, out_f32);
+    else
+        hipLaunchKernelGGL(k_combine<false>, grid, dim3(kThreads), 0, stream, y_seg, slot_of,
+                           weights, shared, T, H, k, routed_scale, out, out_f32);
     return hipGetLastError();
 }
 

@@ -97,9 +97,10 @@ hipError_t launch_add_rmsnorm(const uint16_t *h, const uint16_t *residual, const
                               int T, int H, float eps, uint16_t *residual_out, uint16_t *x,
                               hipStream_t stream);
 
-// out[t] = routed_scale * sum_j weights[t,j] y_seg[slot_of[t*k+j]] + shared[t]
+// out[t] = routed_scale * sum_j weights[t,j] y_seg[slot_of[t*k+j]] + shared[t], or with
+// fold, sum_j (routed_scale * weights[t,j]) y_seg[slot_of[t*k+j]] (no shared term)
 hipError_t launch_combine(const float *y_seg, const int32_t *slot_of, const float *weights,
-                          const float *shared, int T, int H, int k, float routed_scale, void *out,
-                          int out_f32, hipStream_t stream);
+                          const float *shared, int T, int H, int k, float routed_scale, bool fold,
+                          void *out, int out_f32, hipStream_t stream);
 
 }  // namespace moe

@@ -110,6 +110,13 @@ def test_unsupported_options_are_refused():
     for bad in (-1.0, float("nan"), float("inf")):
         assert ws_bytes(dims(swiglu_limit=bad))[0] == -2
     assert ws_bytes(dims(swiglu_limit=10.0))[0] == 0
+    # Laguna's fold of the routed scale: only without a shared expert
+    assert ws_bytes(dims(fold_routed_scale=True))[0] == 0
+    assert ws_bytes(dims(fold_routed_scale=True, I_shared=64))[0] == -4
+    assert "shared expert" in lib.load().moe_last_error().decode()
+    d = dims()
+    d.fold_routed_scale = 2
+    assert ws_bytes(d)[0] == -4
     assert ws_bytes(dims(score="softmax"))[0] == 0
     assert ws_bytes(dims(wfmt="fp8", H=192))[0] == -2
     assert "multiples of 128" in lib.load().moe_last_error().decode()

@@ -29,18 +29,24 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 
+# name: (workload, non-finite up weights, Laguna's fold of the routed scale)
 CASES = {
     # relu^2 experts, routed scale 2.5, a relu^2 shared expert
     "relu2_shared": (W.Workload("pin_relu2", T=300, H=256, I=192, E=16, k=4, act="relu2",
                                 rsf=2.5, I_shared=128, bias_lo=-0.1, bias_hi=0.1, seed=500),
-                     False),
+                     False, False),
     # SwiGLU with saturated gates, a decimal routed scale, a SwiGLU shared expert
     "swiglu_shared": (W.Workload("pin_swiglu", T=300, H=256, I=128, E=16, k=4, rsf=0.7,
-                                 I_shared=64, bias_lo=-0.1, bias_hi=0.1, seed=501), False),
+                                 I_shared=64, bias_lo=-0.1, bias_hi=0.1, seed=501), False, False),
     # relu^2 of -inf, +inf and NaN pre-activations (and NaN from inf * 0)
     "relu2_nonfinite": (W.Workload("pin_relu2_nonfinite", T=300, H=256, I=192, E=16, k=4,
                                    act="relu2", rsf=1.5, bias_lo=-0.1, bias_hi=0.1, seed=502),
-                        True),
+                        True, False),
+    # Laguna's fold (no shared expert): the scale inside each term, which
+    # must then give the folded bits and not the engine's
+    "swiglu_laguna_fold": (W.Workload("pin_swiglu_fold", T=300, H=256, I=128, E=16, k=4,
+                                      rsf=2.5, bias_lo=-0.1, bias_hi=0.1, seed=503),
+                           False, True),
 }
 
 
@@ -61,13 +67,14 @@ RUNS = [(c, T) for c in sorted(CASES) for T in (None, 8, 1) if not (CASES[c][1] 
 
 @pytest.mark.parametrize("case,T", RUNS)
 def test_fp32_output_is_the_engine_order_bit_for_bit(case, T):
-    wl, nonfinite = CASES[case]
+    wl, nonfinite, fold = CASES[case]
     inp = W.exact_inputs(wl, nonfinite=nonfinite)
     if T is not None:
         assert T * wl.k <= 2 * wl.E          # the decode form
         wl = wl.with_(T=T)
         inp = dict(inp, x=np.ascontiguousarray(inp["x"][:T]))
     block = lib.block_from_arrays(wl, inp)
+    block.fold_routed_scale = fold
     x = lib.x_to_device(inp["x"])
     ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device=DEV)
     w = torch.empty((wl.T, wl.k), dtype=torch.float32, device=DEV)
@@ -84,10 +91,11 @@ def test_fp32_output_is_the_engine_order_bit_for_bit(case, T):
     toks = np.arange(wl.T)
     y, shared, inexact = oracle.expert_rows32(wl, inp, toks, ids)
     assert inexact == 0
-    want = oracle.combine32(w, y, shared, wl.rsf)
+    engine = oracle.combine32(w, y, shared, wl.rsf)
     folded = oracle.combine32(w, y, shared, wl.rsf, fold=True)
-    fin = np.isfinite(want) & np.isfinite(folded)
-    sep = (want[fin].view(np.uint32) != folded[fin].view(np.uint32)).mean()
+    want = folded if fold else engine
+    fin = np.isfinite(engine) & np.isfinite(folded)
+    sep = (engine[fin].view(np.uint32) != folded[fin].view(np.uint32)).mean()
     assert sep > 0.05, f"the data separates only {sep:.1%} of the elements"
     if nonfinite and T is None:
         assert np.isnan(want).any() and np.isinf(want).any() and np.isfinite(want).any()
