@@ -91,8 +91,9 @@ COPY_BYTES = 256 << 20
 
 def profile_run(args):
     """Untimed calls for a profiler to wrap: `steps` forward calls of the
-    workload, then one device-to-device copy of COPY_BYTES bytes that scales
-    the HBM byte counters."""
+    workload, then two copies of COPY_BYTES bytes that scale the HBM byte
+    counters: the runtime's device-to-device copy, and an elementwise copy
+    (x * 1 in fp32, 16-byte loads and stores like the library's kernels)."""
     import torch
     from sigmoid_top_routing_amd import lib
     from sigmoid_top_routing_amd import workloads as W
@@ -106,6 +107,7 @@ def profile_run(args):
     src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
     dst.copy_(src)
+    torch.mul(src.view(torch.float32), 1.0, out=dst.view(torch.float32))
     torch.cuda.synchronize()
     print(f"profile run: {args.steps} calls of {wl.name}, copy of {COPY_BYTES} bytes", flush=True)
 

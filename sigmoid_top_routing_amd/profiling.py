@@ -95,15 +95,16 @@ def per_dispatch(db: str, counter: str):
     return [(names[d], d, v) for d, v in vals.items()]
 
 
-def traffic(fetch_db, write_db, kernel, copy_bytes):
+def traffic(fetch_db, write_db, kernel, copy_bytes, copy_kernel=COPY_KERNEL):
     """HBM bytes per launch of `kernel` (a substring of its name), scaled by
-    the largest plain copy of copy_bytes bytes."""
+    the largest plain copy (copy_kernel, a substring of its name) of
+    copy_bytes bytes."""
     res = {}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         rows = per_dispatch(db, counter)
-        copies = [v for n, _, v in rows if COPY_KERNEL in n]
+        copies = [v for n, _, v in rows if copy_kernel in n]
         if not copies:
-            raise SystemExit(f"{db}: no {COPY_KERNEL} dispatch to scale {counter} by")
+            raise SystemExit(f"{db}: no {copy_kernel} dispatch to scale {counter} by")
         factor = max(copies) * 1024.0 / copy_bytes       # counter bytes per real byte
         mine = [v for n, _, v in rows if kernel in n]
         if not mine:
@@ -130,6 +131,8 @@ def main(argv=None):
     a.add_argument("--tag", required=True)
     a.add_argument("--workload", required=True)
     a.add_argument("--copy-bytes", type=int, required=True)
+    a.add_argument("--copy-kernel", default=COPY_KERNEL,
+                   help="substring of the calibrating copy kernel's name")
     a.add_argument("--source", action="append", default=[])
     a.add_argument("--out", default=os.path.join(ROOT, "profiles", "traffic.json"))
     args = ap.parse_args(argv)
@@ -141,7 +144,9 @@ def main(argv=None):
                             if c not in ("dispatches", "avg_us"))
             print(f"{k}: dispatches={cs['dispatches']} avg_us={cs['avg_us']:.2f} {vals}")
     else:
-        rec = traffic(args.fetch_db, args.write_db, args.kernel, args.copy_bytes)
+        rec = traffic(args.fetch_db, args.write_db, args.kernel, args.copy_bytes,
+                      args.copy_kernel)
+        rec["copy_kernel"] = args.copy_kernel
         rec["kernel"] = args.kernel
         rec["source_digest"] = source_digest(*args.source) if args.source else None
         rec["sources"] = args.source
