@@ -333,6 +333,7 @@ typedef struct {
     const uint16_t *shared_down; /* bf16 [H,I_s] */
     int32_t score_fn;   /* 0 sigmoid, 1 softmax */
     double swiglu_limit;  /* 0: no clamp; else L > 0 for every SwiGLU of the layer */
+    int32_t round_h;    /* 1: the activation between the projections stored as bf16 */
 } oracle_layer;
 
 /* An OCP FP8 E4M3 code (the "fn" variant: no infinities) as float64: sign
@@ -413,6 +414,16 @@ double oracle_activate(int act, double g, double u, double limit)
     return activate(act, g, u, limit);
 }
 
+/* The activation between the two projections as the path stores it when
+ * round_h is set: rounded to fp32, then to bf16 by round-to-nearest-even
+ * (the MoE kernels' intermediate is a bf16 tensor, vllm.cpp PR #684, the
+ * W2 commit: the relu^2 arm rounds once on the store). Otherwise the value
+ * itself: the definition keeps it exact. */
+static double stored_h(const oracle_layer *L, double h)
+{
+    return L->round_h ? (double)bf16_value(bf16_round((float)h)) : h;
+}
+
 /* One expert MLP on one input row: y[H] = W_d act(W_up xr). scratch holds
  * 2*I + max(H, I) doubles. */
 static void expert_mlp(const oracle_layer *L, int e, const double *xr, double *y, double *scratch)
@@ -426,8 +437,8 @@ static void expert_mlp(const oracle_layer *L, int e, const double *xr, double *y
         proj[n] = dot(row, xr, H);
     }
     for (int i = 0; i < I; ++i)
-        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[I + i], L->swiglu_limit)
-                                : activate(1, 0.0, proj[i], 0.0);
+        proj[i] = stored_h(L, (L->act == 0) ? activate(0, proj[i], proj[I + i], L->swiglu_limit)
+                                            : activate(1, 0.0, proj[i], 0.0));
     for (int h = 0; h < H; ++h) {
         weight_row(L, 0, e, h, H, I, row);
         y[h] = dot(row, proj, I);
@@ -448,8 +459,8 @@ static void shared_mlp(const oracle_layer *L, const double *xr, double *y, doubl
         proj[n] = dot(row, xr, H);
     }
     for (int i = 0; i < Is; ++i)
-        proj[i] = (L->act == 0) ? activate(0, proj[i], proj[Is + i], L->swiglu_limit)
-                                : activate(1, 0.0, proj[i], 0.0);
+        proj[i] = stored_h(L, (L->act == 0) ? activate(0, proj[i], proj[Is + i], L->swiglu_limit)
+                                            : activate(1, 0.0, proj[i], 0.0));
     for (int h = 0; h < H; ++h) {
         const uint16_t *w = L->shared_down + (size_t)h * Is;
         for (int c = 0; c < Is; ++c)

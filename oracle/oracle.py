@@ -50,7 +50,7 @@ class Layer(C.Structure):
         ("w_up", C.c_void_p), ("w_up_scales", C.c_void_p), ("w_up_biases", C.c_void_p),
         ("w_down", C.c_void_p), ("w_down_scales", C.c_void_p), ("w_down_biases", C.c_void_p),
         ("shared_up", C.c_void_p), ("shared_down", C.c_void_p),
-        ("score_fn", C.c_int32), ("swiglu_limit", C.c_double),
+        ("score_fn", C.c_int32), ("swiglu_limit", C.c_double), ("round_h", C.c_int32),
     ]
 
 
@@ -171,7 +171,7 @@ def plan(ids, E: int):
     return counts, offsets, srt, slot
 
 
-def _layer(wl, inp: dict, keep: dict) -> Layer:
+def _layer(wl, inp: dict, keep: dict, round_h: bool = False) -> Layer:
     """The oracle_layer struct of a workload's arrays (kept alive in keep)."""
     def arr(name, dtype):
         a = inp.get(name)
@@ -201,18 +201,22 @@ def _layer(wl, inp: dict, keep: dict) -> Layer:
                  shared_up=arr("shared_up", np.uint16) if wl.I_shared else None,
                  shared_down=arr("shared_down", np.uint16) if wl.I_shared else None,
                  score_fn=SCORES[getattr(wl, "score", "sigmoid")],
-                 swiglu_limit=float(getattr(wl, "swiglu_limit", 0.0)))
+                 swiglu_limit=float(getattr(wl, "swiglu_limit", 0.0)),
+                 round_h=int(round_h))
 
 
-def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool = False):
+def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool = False,
+                   round_h: bool = False):
     """The block's float64 output rows for ``tokens`` ([n, H] float64).
 
     ``wl`` carries the shapes and flags (a workloads.Workload or anything
     with the same attributes); ``inp`` the arrays from workloads.generate.
+    round_h: the activation between the projections rounded to bf16, as the
+    path stores it (everything else stays float64).
     """
     tokens = _c(np.atleast_1d(tokens), np.int32)
     keep = {}
-    L = _layer(wl, inp, keep)
+    L = _layer(wl, inp, keep, round_h)
     n = tokens.size
     out = np.empty((n, wl.H), dtype=np.float64)
     ids = np.empty((n, wl.k), dtype=np.int32)

@@ -22,8 +22,10 @@ ROOT = os.path.dirname(HERE)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["route.hip", "plan.hip", "gemm.hip", "grouped_gemm.hip", "stream.hip", "combine.hip",
-           "norm.hip", "api.cpp"]
+SOURCES = ["route.hip", "plan.hip", "gemm.hip", "grouped_gemm.hip", "grouped_gemm_f8.hip",
+           "stream.hip", "combine.hip", "norm.hip", "api.cpp"]
+# Per-source flags: the FP8 grouped GEMM keeps its MFMA accumulators in VGPRs.
+SOURCE_FLAGS = {"grouped_gemm_f8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -36,7 +38,8 @@ FLAGS = [
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

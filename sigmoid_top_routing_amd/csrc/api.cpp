@@ -58,14 +58,21 @@ bool quant_streams(const moe_dims &d) {
                                (d.wfmt == MOE_W_FP8 && kmax <= moe::kStreamMaxKFp8));
 }
 
-// 4-bit experts of prompt-sized batches, and block-FP8 experts the decode
-// form does not stream, are decoded to bf16 (the weights of the experts with
-// rows, once per call) before the bf16 MFMA kernel runs. Decode-sized 4-bit
-// batches the stream does not take keep the decode in the staged kernel's
-// loads.
+// Block-FP8 experts the persistent MFMA kernel reads at their stored width
+// (one byte per weight, the block scales applied to the fp32 sums): the
+// scales of a row block's K-blocks fit one per lane (K <= 64 x 128).
+bool fp8_tiles(const moe_dims &d) {
+    return d.wfmt == MOE_W_FP8 && d.H <= 64 * 128 && d.I <= 64 * 128;
+}
+
+// 4-bit experts of prompt-sized batches, and block-FP8 experts that neither
+// the decode form nor the FP8 tiles take, are decoded to bf16 (the weights
+// of the experts with rows, once per call) before the bf16 MFMA kernel
+// runs. Decode-sized 4-bit batches the stream does not take keep the decode
+// in the staged kernel's loads.
 bool dequant_first(const moe_dims &d) {
     return (d.wfmt == MOE_W_AFFINE4 && !decode_sized(d)) ||
-           (d.wfmt == MOE_W_FP8 && !quant_streams(d));
+           (d.wfmt == MOE_W_FP8 && !quant_streams(d) && !fp8_tiles(d));
 }
 
 Layout layout(const moe_dims &d) {

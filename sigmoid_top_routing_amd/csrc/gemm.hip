@@ -617,10 +617,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant_fp8(GemmProblem p,
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
-    if (p.fp8)
-        return hipErrorInvalidValue;             // decoded by launch_dequant first
     if (grouped_supported(p))
-        return launch_grouped(p, stream);
+        return launch_grouped(p, stream);        // FP8 included (its own tiles)
+    if (p.fp8)
+        return hipErrorInvalidValue;             // otherwise decoded by launch_dequant first
     if (p.affine4) {
         switch (p.mode) {
         case kGateUp: return launch_mode<kGateUp, true>(p, stream);

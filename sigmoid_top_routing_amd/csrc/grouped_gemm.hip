@@ -97,16 +97,19 @@ __device__ __forceinline__ u32x4 park_get16(char *__restrict__ base, int off) {
     return (u32x4) * (lds_u32x4 *)(base + off);
 }
 
-template <int BM>
+// F8: block-FP8 weights, one byte each in the stages (32-byte rows per
+// K-slice instead of 64).
+template <int BM, bool F8 = false>
 struct Geo {
     static constexpr int TM = BM / 64;            // 32-token MFMA tiles per wave
     static constexpr int TN = kBN / 64;           // 32-weight-row MFMA tiles per wave
+    static constexpr int BROW = F8 ? 2 : 4;       // 16-byte slots per weight row of a stage
     static constexpr int AI = BM * 4 / kThreads;  // A requests per thread per stage
-    static constexpr int BI = kBN * 4 / kThreads; // B requests per thread per stage
+    static constexpr int BI = kBN * BROW / kThreads; // B requests per thread per stage
     static constexpr int PER = AI + BI;
-    static constexpr int STAGE = (BM + kBN) * 4;  // 16-byte slots per stage
+    static constexpr int STAGE = BM * 4 + kBN * BROW;  // 16-byte slots per stage
     static constexpr int NQ = TM * TN;            // MFMAs per sub-step
-    static constexpr int NF = TM + TN;            // fragment reads per sub-step
+    static constexpr int NF = TM + TN;            // fragment reads per sub-step (bf16)
 };
 
 // Where the tiles of one launch are: the prefix of tiles over the segments
@@ -185,27 +188,54 @@ __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)
 }
 
 // Request state of the tile whose slices are being fetched.
-template <int BM>
+template <int BM, bool F8>
 struct Req {
     const char *b_base;               // uniform: the expert's weight rows
     uint32_t a_off[Geo<BM>::AI];      // per thread, bytes at K-slice 0
-    uint32_t b_off[Geo<BM>::BI];
+    uint32_t b_off[Geo<BM, F8>::BI];
+    float scale[F8 ? 2 : 1];          // F8: lane b holds the scale of K-block b of each
+                                      // weight-row block of the wave (gate, up)
 };
 
 // The weight side of a tile's requests: the expert's base and, per B piece
 // of this thread, the byte offset of its row and chunk at K-slice 0 (rows
 // past N are clamped to a valid row).
-template <int BM, int MODE>
-__device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, Req<BM> &q) {
-    using G = Geo<BM>;
+//
+// F8 stage rows are 32 bytes, two 16-byte chunks: chunk c of row r sits at
+// slot 2 r + (c ^ bit 3 of r). A fragment read (16 lanes, 16 consecutive
+// rows, one chunk each) then covers the 64 banks once. The F8 request also
+// loads the tile's block scales: for each weight-row block of the wave
+// (SwiGLU: the gate rows and the up rows; otherwise the wave's 128 rows),
+// lane b takes the scale of K-block b.
+template <int BM, int MODE, bool F8>
+__device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, Req<BM, F8> &q) {
+    using G = Geo<BM, F8>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    q.b_base = (const char *)p.B + (size_t)e * p.N * p.K * 2;
+    q.b_base = (const char *)p.B + (size_t)e * p.N * p.K * (F8 ? 1 : 2);
+    if constexpr (F8) {
+        const int nb = p.K / 128;           // K-blocks (at most 64: one per lane)
+        const int wn = wave & 1;
+        const int rb_max = p.N / 128 - 1;
+        int rb[2];
+        if (gated(MODE)) {
+            rb[0] = nt;                     // gate rows nt*128 + wn*64 .. + 63
+            rb[1] = p.I / 128 + nt;         // the up rows I + the same
+        } else {
+            rb[0] = min(nt * 2 + wn, rb_max);  // past N: clamped, never stored
+            rb[1] = rb[0];
+        }
+        const float *sc = (const float *)p.Bscale + (size_t)e * (p.N / 128) * nb;
+        const int b = lane < nb ? lane : nb - 1;
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            q.scale[g] = sc[(size_t)rb[g] * nb + b];
+    }
 #pragma unroll
     for (int i = 0; i < G::BI; ++i) {
         const int s = (wave * G::BI + i) * kWave + lane;
-        const int r = s >> 2;
-        const int c = (s & 3) ^ ((r >> 2) & 3);
+        const int r = F8 ? s >> 1 : s >> 2;
+        const int c = F8 ? (s & 1) ^ ((r >> 3) & 1) : (s & 3) ^ ((r >> 2) & 3);
         int wr;
         if (gated(MODE)) {
             int n = nt * (kBN / 2) + (r & (kBN / 2 - 1));
@@ -217,32 +247,58 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
             if (wr >= p.N)
                 wr = p.N - 1;
         }
-        q.b_off[i] = ((uint32_t)wr * (uint32_t)p.K + c * 8) * 2u;
+        q.b_off[i] = F8 ? (uint32_t)wr * (uint32_t)p.K + c * 16
+                        : ((uint32_t)wr * (uint32_t)p.K + c * 8) * 2u;
     }
 }
 
 // Piece m (A pieces first, then B pieces) of K-slice ks into one stage.
-template <int BM, int MODE>
+template <int BM, int MODE, bool F8>
 __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmProblem &p,
-                                        const Req<BM> &q, int ks, int m) {
-    using G = Geo<BM>;
+                                        const Req<BM, F8> &q, int ks, int m) {
+    using G = Geo<BM, F8>;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const uint32_t kb = (uint32_t)ks * (kBK * 2);
     if (m < G::AI) {
         // pieces of padding rows (offset kPastA) read as zeros
-        buffer_to_lds16(p.A, stage + (wave * G::AI + m) * kWave, q.a_off[m] + kb);
+        buffer_to_lds16(p.A, stage + (wave * G::AI + m) * kWave, q.a_off[m] + (uint32_t)ks * (kBK * 2));
     } else {
         const int i = m - G::AI;
-        buffer_to_lds16(q.b_base, stage + BM * 4 + (wave * G::BI + i) * kWave, q.b_off[i] + kb);
+        buffer_to_lds16(q.b_base, stage + BM * 4 + (wave * G::BI + i) * kWave,
+                        q.b_off[i] + (uint32_t)ks * (kBK * (F8 ? 1 : 2)));
     }
 }
 
-// Fragment registers: slot 0 and 1 of a double buffer over sub-steps.
-template <int BM>
+// Fragment registers: slot 0 and 1 of a double buffer over sub-steps. F8
+// also holds the raw bytes of each weight fragment: 16 bytes per lane, both
+// sub-steps of a step (bytes 0-7 sub-step 0, 8-15 sub-step 1).
+template <int BM, bool F8 = false>
 struct Frags {
     bf16x8 a[2][Geo<BM>::TM];
     bf16x8 b[2][Geo<BM>::TN];
+    u32x4 braw[F8 ? Geo<BM>::TN : 1];
 };
+
+// One 16-byte fragment read of a stage, through a __restrict__ pointer of
+// its own (as read_frag): the read then carries an alias scope, which lets
+// the compiler tell it from the requests still in flight into other stages.
+__device__ __forceinline__ u32x4 lds_frag(const uint4 *__restrict__ S, int slot) {
+    return __builtin_bit_cast(u32x4, S[slot]);
+}
+
+// Slot `slot`'s weight fragment j from the raw FP8 bytes: e4m3 to bf16 is
+// exact (every e4m3 value, NaN included, is a bf16 value); the block scale
+// is applied to the fp32 sums, not here.
+template <int BM>
+__device__ __forceinline__ void cvt_b(Frags<BM, true> &f, int slot, int j) {
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const uint32_t w = f.braw[j][2 * slot + q];
+        o[2 * q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+        o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    }
+    f.b[slot][j] = __builtin_bit_cast(bf16x8, (u32x4){o[0], o[1], o[2], o[3]});
+}
 
 // Fragment m from a stage into a slot, in the order the MFMAs of a sub-step
 // first use them (they run weight tile j fastest): A tile 0, B tiles 0 ..
@@ -267,7 +323,7 @@ __device__ __forceinline__ void read_frag(const uint4 *__restrict__ S, Frags<BM>
 template <int BM, int MODE, int NS>
 __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uint4 *__restrict__ Snext,
                                           uint4 *__restrict__ Sfill, const GemmProblem &p,
-                                          const Req<BM> &q, int ks, Frags<BM> &f,
+                                          const Req<BM, false> &q, int ks, Frags<BM> &f,
                                           f32x16 (&acc)[Geo<BM>::TM][Geo<BM>::TN],
                                           const int (&a_slot)[2], const int (&b_slot)[2],
                                           const int *b_toff) {
@@ -301,7 +357,76 @@ __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uin
             if (m < G::NF)
                 read_frag<BM>(Snext, f, 0, m, a_slot[0], b_slot[0], b_toff);
             else
-                request<BM, MODE>(Sfill, p, q, ks, m - G::NF);
+                request<BM, MODE, false>(Sfill, p, q, ks, m - G::NF);
+        }
+        fence();
+    }
+}
+
+// The same step on FP8 weights. The weight fragments of both sub-steps come
+// in one 16-byte read per lane (in the previous step's sub-step 1) and are
+// converted to bf16 during the step. With that layout, lane half
+// h of sub-step kk covers K = 16 h + 8 kk .. + 7 of the slice, so the token
+// fragments are read from chunk 2 h + kk.
+//
+// On the first step of a K-block (`rescale`), each accumulator tile is
+// multiplied, just before its first MFMA of the block, by r = (scale of the
+// previous K-block) / (scale of this one), per weight-row block of the wave
+// (r_gate, r_up): the sums are then kept in units of the current block's
+// scale, and the finished sum is multiplied by the last block's scale. That
+// is sum_b s_b P_b (P_b the block's exact-weight fp32 partial), with one
+// extra rounding per block instead of a second set of accumulators.
+template <int BM, int MODE, int NS>
+__device__ __forceinline__ void ring_step_f8(const uint4 *__restrict__ S, const uint4 *__restrict__ Snext,
+                                             uint4 *__restrict__ Sfill, const GemmProblem &p,
+                                             const Req<BM, true> &q, int ks, Frags<BM, true> &f,
+                                             f32x16 (&acc)[Geo<BM>::TM][Geo<BM>::TN],
+                                             const int (&a_slot)[2], int b_slot, const int *b_toff,
+                                             bool rescale, float r_gate, float r_up) {
+    using G = Geo<BM, true>;
+    constexpr int TM = G::TM, TN = G::TN;
+    fence();
+    // sub-step 0: MFMAs on slot 0, each weight fragment converted just
+    // before its first MFMA; token fragments of sub-step 1 into slot 1 and
+    // its weight fragments converted. (Converting slot 0 at the end of the
+    // previous step instead makes the compiler wait for every request in
+    // flight before the first LDS read of the step.)
+#pragma unroll
+    for (int n = 0; n < G::NQ; ++n) {
+        const int i = n / TN, j = n % TN;
+        if (n < TN)
+            cvt_b<BM>(f, 0, j);
+        if (rescale) {
+            const float r = (gated(MODE) && j >= TN / 2) ? r_up : r_gate;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] *= r;
+        }
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[0][j], f.a[0][i], acc[i][j], 0, 0, 0);
+        if (n < TM)
+            f.a[1][n] = __builtin_bit_cast(bf16x8, lds_frag(S, a_slot[1] + n * 128));
+        else if (n - TM < TN)
+            cvt_b<BM>(f, 1, n - TM);
+        fence();
+    }
+    wait_vmcnt<(NS - 3) * G::PER>();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    // sub-step 1: MFMAs on slot 1; the next step's token fragments and raw
+    // weight bytes, and the refill of the stage read in the previous step
+    constexpr int NM = TM + TN + G::PER;
+#pragma unroll
+    for (int n = 0; n < G::NQ; ++n) {
+        const int i = n / TN, j = n % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[1][j], f.a[1][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int m = n * NM / G::NQ; m < (n + 1) * NM / G::NQ; ++m) {
+            if (m < TM)
+                f.a[0][m] = __builtin_bit_cast(bf16x8, lds_frag(Snext, a_slot[0] + m * 128));
+            else if (m < TM + TN)
+                f.braw[m - TM] = lds_frag(Snext, b_slot + b_toff[m - TM]);
+            else
+                request<BM, MODE, true>(Sfill, p, q, ks, m - TM - TN);
         }
         fence();
     }
@@ -309,20 +434,20 @@ __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uin
 
 // Prologue: the first NS - 1 slices of the first tile into stages 0 ..
 // NS - 2.
-template <int BM, int MODE, int NS>
+template <int BM, int MODE, int NS, bool F8>
 __device__ __forceinline__ void prime(uint4 *__restrict__ ring, const GemmProblem &p,
-                                      const Req<BM> &q) {
-    using G = Geo<BM>;
+                                      const Req<BM, F8> &q) {
+    using G = Geo<BM, F8>;
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
 #pragma unroll
         for (int m = 0; m < G::PER; ++m)
-            request<BM, MODE>(ring + st * G::STAGE, p, q, st, m);
+            request<BM, MODE, F8>(ring + st * G::STAGE, p, q, st, m);
 }
 
-template <int BM, int MODE, int NS>
+template <int BM, int MODE, int NS, bool F8>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_tiles) {
-    using G = Geo<BM>;
+    using G = Geo<BM, F8>;
     constexpr int TM = G::TM, TN = G::TN;
     constexpr int kAhead = NS - 1;           // stages requested ahead of the one multiplied
     __shared__ uint4 ring[NS * G::STAGE];
@@ -398,12 +523,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     int e, row0, row_end, nt;                // the tile being multiplied
     if (!place<BM>(tl, 0, e, row0, row_end, nt))
         return;                              // uniform
-    Req<BM> req;                             // the tile being fetched
+    Req<BM, F8> req;                         // the tile being fetched
     {
         int raw[G::AI];
         const int valid = gathered_rows<BM>(p, row0, row_end, raw);
         a_offsets<BM>(p, raw, valid, req.a_off);
-        b_offsets<BM, MODE>(p, p.b_compact ? s_rank[e] : e, nt, req);
+        b_offsets<BM, MODE, F8>(p, p.b_compact ? s_rank[e] : e, nt, req);
     }
     int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
     bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
@@ -425,19 +550,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     int a_slot[2], b_slot[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
+        // F8: lane half h of sub-step kk covers chunk 2 h + kk of the slice
+        const int ch = F8 ? 2 * (lane >> 5) + kk : kk * 2 + (lane >> 5);
         a_slot[kk] = slot_of(a_tile_row + (lane & 31), ch);
         b_slot[kk] = BM * 4 + slot_of(b_row0 + (lane & 31), ch);
     }
+    if constexpr (F8) {
+        // the lane's 16-byte chunk (lane / 32) of its 32-byte row; tiles 32
+        // rows apart keep the swizzle
+        const int rr = b_row0 + (lane & 31);
+        b_slot[0] = BM * 4 + rr * 2 + ((lane >> 5) ^ ((rr >> 3) & 1));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            b_toff[j] /= 2;
+    }
 
     const int KT = p.K / kBK;
-    prime<BM, MODE, NS>(ring, p, req);
+    prime<BM, MODE, NS, F8>(ring, p, req);
     wait_vmcnt<(NS - 2) * G::PER>();
     __builtin_amdgcn_s_barrier();
-    Frags<BM> f;
+    Frags<BM, F8> f;
+    if constexpr (F8) {
 #pragma unroll
-    for (int m = 0; m < G::NF; ++m)
-        read_frag<BM>(ring, f, 0, m, a_slot[0], b_slot[0], b_toff);
+        for (int i = 0; i < TM; ++i)
+            f.a[0][i] = __builtin_bit_cast(bf16x8, ring[a_slot[0] + i * 128]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            f.braw[j] = __builtin_bit_cast(u32x4, ring[b_slot[0] + b_toff[j]]);
+    } else {
+#pragma unroll
+        for (int m = 0; m < G::NF; ++m)
+            read_frag<BM>(ring, f, 0, m, a_slot[0], b_slot[0], b_toff);
+    }
 
     // Each tile stores through a buffer resource based at its own first
     // output row and spanning its rows that lie in the segment: offsets stay
@@ -455,6 +599,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
             for (int j = 0; j < TN; ++j)
                 acc[i][j] = f32x16{};
+        // F8: this tile's block scales (lane b: K-block b) and the units the
+        // sums are kept in (the scale of the K-block being multiplied)
+        float sc_gate = 0.0f, sc_up = 0.0f, rho_gate = 0.0f, rho_up = 0.0f;
+        if constexpr (F8) {
+            sc_gate = req.scale[0];
+            sc_up = req.scale[1];
+            rho_gate = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_gate), 0));
+            rho_up = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_up), 0));
+        }
         // The last kAhead steps refill with the next tile's first slices;
         // that tile's A offsets are formed just before (its gathered rows
         // were requested a tile ago and the waits of the steps so far have
@@ -469,8 +622,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
             uint4 *Sn = ring + sn * G::STAGE;
             uint4 *Sf = ring + sf * G::STAGE;
             sl = sn;
-            ring_step<BM, MODE, NS>(S, Sn, Sf, p, req, kt + kAhead < KT ? kt + kAhead : kt + kAhead - KT,
-                                f, acc, a_slot, b_slot, b_toff);
+            const int ks = kt + kAhead < KT ? kt + kAhead : kt + kAhead - KT;
+            if constexpr (F8) {
+                // first step of K-block b > 0: r = (previous block's scale) /
+                // (this block's scale); uniform. The step index passes through
+                // an empty asm so the loop is not peeled at kt = 0: a second
+                // inlined copy of the step makes the compiler wait for every
+                // request in flight before its LDS reads.
+                int kq = kt;
+                __asm__ volatile("" : "+s"(kq));
+                const bool rescale = kq > 0 && (kq & 3) == 0;
+                float r_gate = 1.0f, r_up = 1.0f;
+                if (rescale) {
+                    const int b = kq >> 2;
+                    const float s_gate = __builtin_bit_cast(
+                        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_gate), b));
+                    r_gate = rho_gate / s_gate;
+                    rho_gate = s_gate;
+                    if (gated(MODE)) {
+                        const float s_up = __builtin_bit_cast(
+                            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc_up), b));
+                        r_up = rho_up / s_up;
+                        rho_up = s_up;
+                    }
+                }
+                ring_step_f8<BM, MODE, NS>(S, Sn, Sf, p, req, ks, f, acc, a_slot, b_slot[0], b_toff,
+                                           rescale, r_gate, r_up);
+            } else {
+                ring_step<BM, MODE, NS>(S, Sn, Sf, p, req, ks, f, acc, a_slot, b_slot, b_toff);
+            }
             if (kt == KT - kAhead - 1) {
                 // a tile past the end re-requests this one (in bounds, never
                 // multiplied)
@@ -481,7 +661,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                     for (int i = 0; i < G::AI; ++i)
                         __asm__ volatile("" : "+v"(nraw[i]));
                     a_offsets<BM>(p, nraw, nvalid, req.a_off);
-                    b_offsets<BM, MODE>(p, p.b_compact ? s_rank[ne] : ne, nnt, req);
+                    b_offsets<BM, MODE, F8>(p, p.b_compact ? s_rank[ne] : ne, nnt, req);
                 }
             }
         }
@@ -525,7 +705,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    const f32x16 &v = acc[i][j];
+                    // F8: the finished sum in units of the last block's scale
+                    const f32x16 v = F8 ? acc[i][j] * rho_gate : acc[i][j];
                     // 32 rows x 32 fp32: row r at r * 128 bytes, 8 chunks of 4
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
@@ -573,11 +754,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                         f32x16 gv, uv;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
-                            __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(gv[r]) : "a"(acc[i][j][r]));
-                            if (gated(MODE))
-                                __asm__ volatile("v_accvgpr_read_b32 %0, %1"
-                                                 : "=v"(uv[r])
-                                                 : "a"(acc[i][j + TN / 2][r]));
+                            if constexpr (F8) {
+                                gv[r] = acc[i][j][r] * rho_gate;
+                                if (gated(MODE))
+                                    uv[r] = acc[i][j + TN / 2][r] * rho_up;
+                            } else {
+                                __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(gv[r]) : "a"(acc[i][j][r]));
+                                if (gated(MODE))
+                                    __asm__ volatile("v_accvgpr_read_b32 %0, %1"
+                                                     : "=v"(uv[r])
+                                                     : "a"(acc[i][j + TN / 2][r]));
+                            }
                         }
 #pragma unroll
                         for (int c = 0; c < 8; ++c) {
@@ -663,7 +850,7 @@ long long tiles_bound(const GemmProblem &p, int &n_tiles) {
     return (long long)mt_max * n_tiles;
 }
 
-template <int BM, int MODE>
+template <int BM, int MODE, bool F8 = false>
 hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
     int n_tiles = 0;
     const long long work = tiles_bound<BM, MODE>(p, n_tiles);
@@ -680,16 +867,17 @@ hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
     // the deep ring for 128-row tiles where K has the slices to fill it
     if constexpr (BM == 128) {
         if (p.K / kBK >= kStagesDeep) {
-            hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesDeep>), dim3(blocks), dim3(kThreads), 0,
+            hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesDeep, F8>), dim3(blocks), dim3(kThreads), 0,
                                stream, p, n_tiles);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesSmall>), dim3(blocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesSmall, F8>), dim3(blocks), dim3(kThreads), 0, stream,
                        p, n_tiles);
     return hipGetLastError();
 }
 
+#ifndef MOE_GROUPED_F8_UNIT
 template <int MODE>
 hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
     int segs = 1;
@@ -705,8 +893,24 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
     return launch_bm<128, MODE>(p, stream);
 }
 
+#endif
+
 }  // namespace
 
+#ifdef MOE_GROUPED_F8_UNIT
+// FP8 weights: 128-row tiles, whose 128 accumulators per lane stay in VGPRs
+// (this unit is compiled with the MFMAs' VGPR form) so the per-K-block
+// rescale is one multiply per accumulator; the raw weight bytes fit beside
+// them.
+hipError_t launch_grouped_f8(const GemmProblem &p, hipStream_t stream) {
+    switch (p.mode) {
+    case kGateUp: return launch_bm<128, kGateUp, true>(p, stream);
+    case kGateUpLimit: return launch_bm<128, kGateUpLimit, true>(p, stream);
+    case kUpRelu2: return launch_bm<128, kUpRelu2, true>(p, stream);
+    default: return launch_bm<128, kDown, true>(p, stream);
+    }
+}
+#else
 bool grouped_supported(const GemmProblem &p) {
     // every A offset (rows of A times lda, in bytes) and every weight offset
     // within one expert stay below kPastA; the rows of a gathered A are the
@@ -714,12 +918,18 @@ bool grouped_supported(const GemmProblem &p) {
     long long a_rows = p.offsets != nullptr ? p.max_rows : p.rows;
     if (p.gather != nullptr && p.gather_div > 1)
         a_rows = (a_rows + p.gather_div - 1) / p.gather_div;
-    return !p.affine4 && !p.fp8 && p.scatter == nullptr && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
+    // FP8: 128 x 128 scale blocks (a gated N splits at I, a multiple of 128),
+    // at most 64 K-blocks (one per lane), the caller's weights as stored
+    const bool fp8_ok = !p.fp8 || (p.K % 128 == 0 && p.K / 128 <= kWave && p.N % 128 == 0 &&
+                                   (!gated(p.mode) || p.I % 128 == 0) && !p.b_compact);
+    return !p.affine4 && fp8_ok && p.scatter == nullptr && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
            (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA &&
-           (long long)p.N * p.K * 2 < (long long)kPastA;
+           (long long)p.N * p.K * (p.fp8 ? 1 : 2) < (long long)kPastA;
 }
 
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream) {
+    if (p.fp8)
+        return launch_grouped_f8(p, stream);
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp>(p, stream);
     case kGateUpLimit: return launch_mode<kGateUpLimit>(p, stream);
@@ -727,5 +937,6 @@ hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream) {
     default: return launch_mode<kDown>(p, stream);
     }
 }
+#endif
 
 }  // namespace moe

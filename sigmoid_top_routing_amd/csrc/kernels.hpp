@@ -45,7 +45,8 @@ struct GemmProblem {
     int mode;                 // GemmMode
     int affine4;              // B is 4-bit affine (codes + bf16 scale / bias, group 64)
     int fp8;                  // B is block-FP8 e4m3 (bytes + fp32 scale per 128 x 128 block):
-                              // only launch_dequant reads it
+                              // the persistent kernel (grouped_supported), the stream
+                              // (stream_supported) or launch_dequant reads it
     const uint16_t *A;        // bf16 rows, lda elements apart
     int lda;
     const int32_t *gather;    // A row of position p = gather[p] / gather_div (NULL: row p)
@@ -79,6 +80,8 @@ hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t strea
 // at least 128); launch_gemm routes the problems it supports there.
 bool grouped_supported(const GemmProblem &p);
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream);
+// Its block-FP8 form (grouped_gemm_f8.hip); launch_grouped calls it.
+hipError_t launch_grouped_f8(const GemmProblem &p, hipStream_t stream);
 
 // The same problem in the weight-streaming (decode) form: few A rows per
 // expert, every touched weight row read once, v_dot2 accumulation.

@@ -75,6 +75,9 @@ class Workload:
     tie_col: int = 7
     scale_lo: float = 0.005
     scale_hi: float = 0.02
+    fp8_exp_mu: float = 13.0          # block-FP8 codes: exponent field round(N(mu, sd))
+    fp8_exp_sd: float = 1.0
+    fp8_nan: tuple = ()               # (expert, row) of w_down rows holding one e4m3 NaN
     qbias_lo: float = -0.1
     qbias_hi: float = 0.1
     group: int = 64
@@ -138,8 +141,17 @@ MID = {
     # SwiGLU shared expert.
     "mid_fp8": Workload("mid_fp8", T=500, H=384, I=256, E=16, k=4, wfmt="fp8", scale_lo=1e-4,
                         scale_hi=3e-4, I_shared=128, seed=109),
+    # relu^2 block-FP8 experts, with e4m3 NaN codes (S.1111.111) in three
+    # down rows: the tokens routed to those experts get NaN in that column
     "mid_fp8_relu2": Workload("mid_fp8_relu2", T=200, H=256, I=384, E=24, k=6, act="relu2",
-                              wfmt="fp8", rsf=2.5, scale_lo=1e-4, scale_hi=3e-4, seed=110),
+                              wfmt="fp8", rsf=2.5, scale_lo=1e-4, scale_hi=3e-4, seed=110,
+                              fp8_nan=((0, 5), (3, 100), (7, 200))),
+    # Block-FP8 codes over a wide range (exponent field N(7, 1.5), scales
+    # 0.01-0.03): weights from about 1e-4 to 13, whose products reach far
+    # past the bulk; the shapes of mid_fp8.
+    "mid_fp8_wide": Workload("mid_fp8_wide", T=500, H=384, I=256, E=16, k=4, wfmt="fp8",
+                             scale_lo=0.01, scale_hi=0.03, fp8_exp_mu=7.0, fp8_exp_sd=1.5,
+                             I_shared=128, seed=115),
     # The softmax router family (TensorFold issue #548, the consolidation
     # proposal), with NaN rows and exact ties, over 64 experts.
     # No expert bias (the family has none): every score of an all-zero row
@@ -238,17 +250,18 @@ def _words(rng: np.random.Generator, shape) -> np.ndarray:
     return out.reshape(shape)
 
 
-def _fp8_codes(rng: np.random.Generator, shape) -> np.ndarray:
+def _fp8_codes(rng: np.random.Generator, shape, mu: float = 13.0, sd: float = 1.0) -> np.ndarray:
     """OCP FP8 E4M3 bytes drawn field by field, shaped like weights quantized
-    with a per-block absmax scale (the block's largest weight near code 448,
-    the bulk a few octaves below): sign uniform, exponent field
-    round(N(13, 1)) clipped to 0..15, mantissa uniform on 0..7; the NaN
-    pattern S.1111.111 is replaced by S.1111.110 (448)."""
+    with a per-block absmax scale (by default the block's largest weight
+    near code 448, the bulk a few octaves below): sign uniform, exponent
+    field round(N(mu, sd)) clipped to 0..15, mantissa uniform on 0..7; the
+    NaN pattern S.1111.111 is replaced by S.1111.110 (448)."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint8)
+    mu32, sd32 = np.float32(mu), np.float32(sd)
     for s in range(0, n, CHUNK):
         m = min(CHUNK, n - s)
-        e = np.clip(np.rint(rng.standard_normal(m, dtype=np.float32) + 13.0), 0, 15)
+        e = np.clip(np.rint(rng.standard_normal(m, dtype=np.float32) * sd32 + mu32), 0, 15)
         e = e.astype(np.uint8)
         mant = rng.integers(0, 8, size=m, dtype=np.uint8)
         sign = rng.integers(0, 2, size=m, dtype=np.uint8)
@@ -306,8 +319,12 @@ def generate(wl: Workload, need_x: bool = True, experts: bool = True) -> dict:
         out["w_down_biases"] = f32_to_bf16_bits(_uniform_f32(ws[c_qb], (E, H, I // g),
                                                              wl.qbias_lo, wl.qbias_hi))
     elif wl.wfmt == "fp8":
-        out["w_up"] = _fp8_codes(ws[c_codes], (E, n_up, H))
-        out["w_down"] = _fp8_codes(ws[c_codes], (E, H, I))
+        mu, sd = wl.fp8_exp_mu, wl.fp8_exp_sd
+        out["w_up"] = _fp8_codes(ws[c_codes], (E, n_up, H), mu, sd)
+        out["w_down"] = _fp8_codes(ws[c_codes], (E, H, I), mu, sd)
+        for i, (e, h) in enumerate(wl.fp8_nan):
+            # one NaN code per listed down row, alternating sign
+            out["w_down"][e, h, (7 * h + e) % I] = 0x7F if i % 2 == 0 else 0xFF
         out["w_up_scales"] = _uniform_f32(ws[c_scales], (E, n_up // 128, H // 128),
                                           wl.scale_lo, wl.scale_hi)
         out["w_down_scales"] = _uniform_f32(ws[c_scales], (E, H // 128, I // 128),

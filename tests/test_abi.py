@@ -120,14 +120,17 @@ def test_unsupported_options_are_refused():
     assert ws_bytes(dims(score="softmax"))[0] == 0
     assert ws_bytes(dims(wfmt="fp8", H=192))[0] == -2
     assert "multiples of 128" in lib.load().moe_last_error().decode()
-    # a prompt-sized FP8 batch holds the decoded weights of its experts; a
-    # decode-sized one streams the codes and needs no more than bf16
-    rc, n8 = ws_bytes(dims(wfmt="fp8", T=64, H=256, I=256, E=8, k=2))
-    rc16, n16 = ws_bytes(dims(T=64, H=256, I=256, E=8, k=2))
-    assert rc == rc16 == 0 and n8 >= n16 + 8 * 512 * 256 * 2     # eight experts decoded
-    rc, n8 = ws_bytes(dims(wfmt="fp8", T=8, H=256, I=256, E=8, k=2))
-    rc16, n16 = ws_bytes(dims(T=8, H=256, I=256, E=8, k=2))
-    assert rc == rc16 == 0 and n8 == n16
+    # FP8 codes are read at their stored width at prompt sizes (the MFMA
+    # tiles) and at decode sizes (the stream): no more workspace than bf16.
+    # Past 64 K-blocks (K > 8192) the tiles do not take them and a prompt-sized
+    # batch holds the decoded weights of its experts.
+    for T in (64, 8):
+        rc, n8 = ws_bytes(dims(wfmt="fp8", T=T, H=256, I=256, E=8, k=2))
+        rc16, n16 = ws_bytes(dims(T=T, H=256, I=256, E=8, k=2))
+        assert rc == rc16 == 0 and n8 == n16
+    rc, n8 = ws_bytes(dims(wfmt="fp8", T=64, H=8320, I=128, E=8, k=2))
+    rc16, n16 = ws_bytes(dims(T=64, H=8320, I=128, E=8, k=2))
+    assert rc == rc16 == 0 and n8 >= n16 + 8 * 256 * 8320 * 2     # eight experts decoded
 
 
 def test_add_rmsnorm_refuses_bad_shapes_and_pointers():

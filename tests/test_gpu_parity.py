@@ -7,10 +7,15 @@ stated acceptance):
   * weights: NaN in the same places, elsewhere |gpu - ref| <= 1e-6 |ref|
     (fp32 with at most k + 2 roundings against float64);
   * outputs: NaN in the same places; over the finite entries
-    max |gpu - ref| <= 2e-2 rms(ref) for bf16 experts and 5e-2 rms(ref) for
-    4-bit and block-FP8 experts (their weights are rounded to bf16 once
-    decoded; an emulation of exactly those roundings gives 1.6 to 2.1 % of
-    rms on the FP8 test layers). A bf16 output may also differ by the rounding of the
+    max |gpu - ref| <= 2e-2 rms(ref) for bf16 and block-FP8 experts (e4m3
+    values are bf16 values and the block scales multiply fp32 sums, so the
+    weights are exact) and 5e-2 rms(ref) for 4-bit experts (decoded to bf16
+    at prompt sizes). Block-FP8 codes over a wide range (mid_fp8_wide) reach
+    4.3 % of rms through the bf16 activation between the projections alone
+    (the stored intermediate of every format; an emulation with exact
+    weights and that one rounding gives 4.27 %): they are held to 2e-2
+    against the oracle with that rounding applied (round_h) and to 6e-2
+    against the exact definition. A bf16 output may also differ by the rounding of the
     exact value itself to bf16 (outputs are f32 or bf16, vllm.cpp PR #684):
     where the routing concentrates on one expert (the softmax router) the
     largest outputs reach 9 rms, and their own half-ulp alone is 2.4 % of rms.
@@ -33,9 +38,25 @@ FULL = [w.name for w in W.CONFIGS[1:]] + sorted(W.EXTRA)
 
 
 def tol_for(wl):
-    # weights decoded to bf16 before the MFMAs (4-bit and block-FP8) take the
-    # quantized-format bar
-    return 5e-2 if wl.wfmt in ("affine4", "fp8") else 2e-2
+    # 4-bit weights decoded to bf16 before the MFMAs take the quantized-format
+    # bar; block-FP8 weights are exact
+    return 5e-2 if wl.wfmt == "affine4" else 2e-2
+
+
+WIDE_FP8_DEF_BAR = 6e-2
+
+
+def refs_for(wl, inp, toks, want_routing=False):
+    """The (reference, bar) pairs an output is held to, and the oracle's
+    routing when asked: the definition at the format's bar, or for
+    wide-range FP8 codes the stored-activation oracle at 2e-2 and the
+    definition at WIDE_FP8_DEF_BAR."""
+    ref, ids, w = oracle.forward_tokens(wl, inp, toks, want_routing=True)
+    pairs = [(ref, tol_for(wl))]
+    if wl.wfmt == "fp8" and wl.fp8_exp_sd > 1.0:
+        pairs = [(oracle.forward_tokens(wl, inp, toks, round_h=True), 2e-2),
+                 (ref, WIDE_FP8_DEF_BAR)]
+    return (pairs, ids, w) if want_routing else pairs
 
 
 def poisoned(shape, dtype):
@@ -356,11 +377,12 @@ def run_forward(wl, inp, out_dtype=torch.bfloat16, x_bits=None, block=None):
 def test_forward_matches_oracle_every_token(name, out_dtype):
     wl, inp = small_inputs(name)
     out, ids, w, offs = run_forward(wl, inp, out_dtype)
-    ref, ids_ref, w_ref = oracle.forward_tokens(wl, inp, np.arange(wl.T), want_routing=True)
+    refs, ids_ref, w_ref = refs_for(wl, inp, np.arange(wl.T), want_routing=True)
     check_routing(ids, w, ids_ref, w_ref)
     _, o_ref, _, _ = oracle.plan(ids_ref, wl.E)
     assert (offs == o_ref).all()
-    check_out(out, ref, tol_for(wl), rounded_to_bf16=out_dtype == torch.bfloat16)
+    for ref, tol in refs:
+        check_out(out, ref, tol, rounded_to_bf16=out_dtype == torch.bfloat16)
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -374,8 +396,8 @@ def test_forward_full_size_sampled(name):
     assert (offs == o_ref).all()
     rng = np.random.default_rng(11)
     toks = np.unique(np.concatenate([[0, wl.T - 1], rng.integers(0, wl.T, size=30)]))
-    ref = oracle.forward_tokens(wl, inp, toks)
-    check_out(out[toks], ref, tol_for(wl))
+    for ref, tol in refs_for(wl, inp, toks):
+        check_out(out[toks], ref, tol)
     assert np.isfinite(out).all()
 
 
@@ -384,7 +406,8 @@ DECODE_CASES = [("tiny_t64_e8_k2", 8), ("tiny_t64_e8_k2", 1), ("mid_swiglu", 8),
                 ("mid_e256_k8", 64), ("mid_e256_k8", 7), ("mid_nan_ties", 4),
                 ("mid_swiglu_bigseg", 2), ("mid_softmax", 8), ("mid_softmax", 2),
                 ("mid_swiglu_limit", 8), ("mid_swiglu_limit", 1), ("mid_fp8", 4), ("mid_fp8", 1),
-                ("mid_fp8_relu2", 8), ("mid_affine4", 8), ("mid_affine4", 1),
+                ("mid_fp8_relu2", 8), ("mid_fp8_wide", 8), ("mid_fp8_wide", 2),
+                ("mid_affine4", 8), ("mid_affine4", 1),
                 ("mid_affine4_relu2", 8), ("mid_affine4_relu2", 3), ("mid_affine4_i64", 8),
                 ("mid_relu2_nonfinite", 8)]
 
@@ -399,12 +422,13 @@ def test_decode_sized_batches(name, T):
     inpT = dict(inp)
     inpT["x"] = np.ascontiguousarray(inp["x"][:T])
     out, ids, w, offs = run_forward(wlT, inpT)
-    ref, ids_ref, w_ref = oracle.forward_tokens(wlT, inpT, np.arange(T), want_routing=True)
+    refs, ids_ref, w_ref = refs_for(wlT, inpT, np.arange(T), want_routing=True)
     check_routing(ids, w, ids_ref, w_ref)
     _, o_ref, _, _ = oracle.plan(ids_ref, wl.E)
     assert (offs == o_ref).all()
     out32, _, _, _ = run_forward(wlT, inpT, torch.float32)
-    check_out(out32, ref, tol_for(wl))
+    for ref, tol in refs:
+        check_out(out32, ref, tol)
     assert (W.f32_to_bf16_bits(out32) == W.f32_to_bf16_bits(out)).all()
 
 

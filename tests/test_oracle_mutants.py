@@ -137,6 +137,18 @@ MUTANTS = {
         "((size_t)e * (N / 128) + n / 128) * (K / 128);\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[c / 128];",
         "(size_t)e * (N / 128) * (K / 128) + n / 128;\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[(c / 128) * (N / 128)];",
         ["tests/test_oracle_fp8.py::test_fp8_layer_matches_dense_float64"]),
+    "round_h_ignored": (
+        "return L->round_h ? (double)bf16_value(bf16_round((float)h)) : h;", "return h;",
+        ["tests/test_oracle_round_h.py::test_round_h_hand_values_routed_and_shared"]),
+    "round_h_truncates": (
+        "return L->round_h ? (double)bf16_value(bf16_round((float)h)) : h;",
+        "float f = (float)h; uint32_t b; memcpy(&b, &f, 4); b &= 0xFFFF0000u; memcpy(&f, &b, 4);\n"
+        "    return L->round_h ? (double)f : h;",
+        ["tests/test_oracle_round_h.py::test_round_h_hand_values_routed_and_shared"]),
+    "round_h_shared_skipped": (
+        "proj[i] = stored_h(L, (L->act == 0) ? activate(0, proj[i], proj[Is + i], L->swiglu_limit)",
+        "proj[i] = ((L->act == 0) ? activate(0, proj[i], proj[Is + i], L->swiglu_limit)",
+        ["tests/test_oracle_round_h.py::test_round_h_hand_values_routed_and_shared"]),
     "mimic_combine_descending": (
         "            for (int j = 0; j < k; ++j) {\n                float wj = w[",
         "            for (int j = k - 1; j >= 0; --j) {\n                float wj = w[",
