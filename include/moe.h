@@ -106,6 +106,16 @@ typedef struct {
                              (vllm.cpp PR #684, the review-repairs commit: equal in
                              exact arithmetic, different fp32 bits; legal only
                              without a shared expert, so I_shared must be 0) */
+    int32_t row_invariant; /* 0: decode-sized batches (T * k <= 2 E) take the
+                             weight-streaming form, whose fp32 sums differ from the
+                             MFMA tiles' in the last bits; 1: every batch takes the
+                             MFMA tiles (4-bit experts decoded to bf16 first), so a
+                             token's output bits do not depend on how many tokens
+                             share the call (TensorFold issue #548, the kernel
+                             registry's family rule), at the tiles' cost for decode
+                             batches. Holds while every projection fits the tiles:
+                             T*k*max(H, I)*2 < 2^31 and, for block-FP8, H and I at
+                             most 8192. */
 } moe_dims;
 
 /* Weights of one layer (device pointers).

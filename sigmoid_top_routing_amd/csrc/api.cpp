@@ -48,7 +48,10 @@ struct Layout {
 // Decode-sized batches (at most two assignments per expert on average)
 // stream each touched expert's weights once; larger ones take the MFMA tiles
 // (TensorFold issue #548: decode rows and prompt rows).
-bool decode_sized(const moe_dims &d) { return (int64_t)d.T * d.k <= 2 * (int64_t)d.E; }
+// With row_invariant no batch is: every one takes the tiles.
+bool decode_sized(const moe_dims &d) {
+    return !d.row_invariant && (int64_t)d.T * d.k <= 2 * (int64_t)d.E;
+}
 
 // Quantized experts the decode form streams at their stored width (the
 // projections' K within its limits).
@@ -174,6 +177,8 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
             (double)d->swiglu_limit, d->act);
     REQUIRE(d->fold_routed_scale == 0 || d->fold_routed_scale == 1, MOE_E_UNSUPPORTED,
             "%s: fold_routed_scale = %d, need 0 or 1", what, d->fold_routed_scale);
+    REQUIRE(d->row_invariant == 0 || d->row_invariant == 1, MOE_E_UNSUPPORTED,
+            "%s: row_invariant = %d, need 0 or 1", what, d->row_invariant);
     REQUIRE(d->fold_routed_scale == 0 || d->I_shared == 0, MOE_E_UNSUPPORTED,
             "%s: fold_routed_scale = 1 with I_shared = %d: the fold is legal only without "
             "a shared expert", what, d->I_shared);

@@ -43,7 +43,8 @@ class Dims(C.Structure):
                 ("k", C.c_int32), ("act", C.c_int32), ("wfmt", C.c_int32), ("group", C.c_int32),
                 ("norm_topk", C.c_int32), ("norm_eps", C.c_float), ("routed_scale", C.c_float),
                 ("I_shared", C.c_int32), ("out_dtype", C.c_int32), ("score_fn", C.c_int32),
-                ("swiglu_limit", C.c_float), ("fold_routed_scale", C.c_int32)]
+                ("swiglu_limit", C.c_float), ("fold_routed_scale", C.c_int32),
+                ("row_invariant", C.c_int32)]
 
 
 class Weights(C.Structure):
@@ -102,12 +103,12 @@ def _stream(stream=None):
 
 def make_dims(T, H, I, E, k, act="swiglu", wfmt="bf16", rsf=1.0, I_shared=0, norm_topk=True,
               norm_eps=1e-6, out_dtype=torch.bfloat16, score="sigmoid",
-              swiglu_limit=0.0, fold_routed_scale=False) -> Dims:
+              swiglu_limit=0.0, fold_routed_scale=False, row_invariant=False) -> Dims:
     return Dims(T=T, H=H, I=I, E=E, k=k, act=ACT[act], wfmt=WFMT[wfmt],
                 group=64 if wfmt == "affine4" else 0, norm_topk=int(norm_topk),
                 norm_eps=norm_eps, routed_scale=rsf, I_shared=I_shared, out_dtype=OUT[out_dtype],
                 score_fn=SCORE[score], swiglu_limit=swiglu_limit,
-                fold_routed_scale=int(fold_routed_scale))
+                fold_routed_scale=int(fold_routed_scale), row_invariant=int(row_invariant))
 
 
 def workspace_bytes(d: Dims) -> int:
@@ -191,6 +192,7 @@ class MoEBlock:
     score: str = "sigmoid"
     swiglu_limit: float = 0.0
     fold_routed_scale: bool = False
+    row_invariant: bool = False
 
     def __post_init__(self):
         self._ws = None
@@ -198,7 +200,7 @@ class MoEBlock:
     def dims(self, T, out_dtype=torch.bfloat16) -> Dims:
         return make_dims(T, self.H, self.I, self.E, self.k, self.act, self.wfmt, self.rsf,
                          self.I_shared, self.norm_topk, self.norm_eps, out_dtype, self.score,
-                         self.swiglu_limit, self.fold_routed_scale)
+                         self.swiglu_limit, self.fold_routed_scale, self.row_invariant)
 
     def weights(self) -> Weights:
         return Weights(router_w=_ptr(self.router_w), expert_bias=_ptr(self.bias),

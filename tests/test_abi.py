@@ -117,6 +117,15 @@ def test_unsupported_options_are_refused():
     d = dims()
     d.fold_routed_scale = 2
     assert ws_bytes(d)[0] == -4
+    # one family of bits at every row count: 0 or 1; with it a decode-sized
+    # 4-bit batch decodes its experts to bf16 for the tiles
+    d = dims()
+    d.row_invariant = 2
+    assert ws_bytes(d)[0] == -4
+    assert "row_invariant" in lib.load().moe_last_error().decode()
+    rc, n_stream = ws_bytes(dims(wfmt="affine4", T=8, H=256, I=256, E=8, k=2))
+    rc1, n_tiles = ws_bytes(dims(wfmt="affine4", T=8, H=256, I=256, E=8, k=2, row_invariant=True))
+    assert rc == rc1 == 0 and n_tiles >= n_stream + 8 * 512 * 256 * 2
     assert ws_bytes(dims(score="softmax"))[0] == 0
     assert ws_bytes(dims(wfmt="fp8", H=192))[0] == -2
     assert "multiples of 128" in lib.load().moe_last_error().decode()
