@@ -42,7 +42,8 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-    size_t z, ids, w, counts, offsets, sorted, slot, chunk_counts, h, y, hs, ys, wdq, total;
+    size_t z, ids, w, counts, offsets, seg_offsets, sorted, slot, chunk_counts, h, y, hs, ys, wdq,
+        total;
 };
 
 // Decode-sized batches (at most two assignments per expert on average)
@@ -78,9 +79,30 @@ bool dequant_first(const moe_dims &d) {
            (d.wfmt == MOE_W_FP8 && !quant_streams(d) && !fp8_tiles(d));
 }
 
+// The shared expert as m plan segments of the routed experts' width
+// (I_shared = m I), run inside the routed experts' grouped launches: every
+// token is a row of each segment, segment v taking gate/up rows v I .. and
+// down columns v I .. of the shared weights (vllm.cpp PR #684, the 9-slot
+// plan of the top-k plus the shared id). Prompt-sized batches on the MFMA
+// tiles with bf16 or decoded 4-bit experts; 0 otherwise (the shared expert
+// then runs as its own dense projections).
+int shared_segments(const moe_dims &d) {
+    if (d.I_shared <= 0 || d.I_shared % d.I != 0 || decode_sized(d) || d.wfmt == MOE_W_FP8)
+        return 0;
+    const int m = d.I_shared / d.I;
+    const int64_t rows = (int64_t)d.T * d.k + (int64_t)m * d.T;   // plan positions
+    const int64_t up_rows = (rows + d.k - 1) / d.k;                // bound of the gathered rows
+    if (d.E + m > 256 || d.H < 128 || d.I < 128 || up_rows * d.H * 2 >= ((int64_t)1 << 31) ||
+        rows * d.I * 2 >= ((int64_t)1 << 31))
+        return 0;
+    return m;
+}
+
 Layout layout(const moe_dims &d) {
     Layout L{};
     const size_t A = (size_t)d.T * d.k;
+    const int m = shared_segments(d);
+    const size_t R = A + (size_t)m * d.T;      // plan positions, shared segments included
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -92,12 +114,14 @@ Layout layout(const moe_dims &d) {
     L.w = take(A * 4);
     L.counts = take((size_t)d.E * 4);
     L.offsets = take((size_t)(d.E + 1) * 4);
-    L.sorted = take(A * 4);
+    if (m > 0)
+        L.seg_offsets = take((size_t)(d.E + m + 1) * 4);
+    L.sorted = take(R * 4);
     L.slot = take(A * 4);
     L.chunk_counts = take((size_t)moe::plan_chunks((int)A) * d.E * 4);
-    L.h = take(A * d.I * 2);
-    L.y = take(A * d.H * 4);
-    if (d.I_shared > 0) {
+    L.h = take(R * d.I * 2);
+    L.y = take(R * d.H * 4);
+    if (d.I_shared > 0 && m == 0) {
         L.hs = take((size_t)d.T * d.I_shared * 2);
         L.ys = take((size_t)d.T * d.H * 4);
     }
@@ -369,6 +393,9 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     int32_t *slot = (int32_t *)(ws + L.slot);
     uint16_t *h = (uint16_t *)(ws + L.h);
     float *y = (float *)(ws + L.y);
+    const int m = shared_segments(*d);
+    int32_t *seg_off = m > 0 ? (int32_t *)(ws + L.seg_offsets) : offsets;
+    const int R = A + m * T;                 // plan positions, shared segments included
 
     auto mark = [&](int i) -> hipError_t {
         return (events != nullptr && events[i] != nullptr) ? hipEventRecord(events[i], stream)
@@ -376,13 +403,16 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     };
     LAUNCH(mark(0));
     bool plan_done = false;
+    // (the router builds the plan itself only without shared segments)
     LAUNCH(moe::launch_route(x, w->router_w, w->expert_bias, T, H, E, k, d->score_fn,
                              d->norm_topk, d->norm_eps, ids, wts, (float *)(ws + L.z),
-                             moe::PlanOut{counts, offsets, sorted, slot}, &plan_done, stream));
+                             m > 0 ? moe::PlanOut{} : moe::PlanOut{counts, offsets, sorted, slot},
+                             &plan_done, stream));
     LAUNCH(mark(1));
     if (!plan_done)
         LAUNCH(moe::launch_plan(ids, A, E, counts, offsets, sorted, slot, nullptr,
-                                (int32_t *)(ws + L.chunk_counts), stream));
+                                (int32_t *)(ws + L.chunk_counts), stream,
+                                m > 0 ? seg_off : nullptr, m, T));
     LAUNCH(mark(2));
     const bool decode_form = decode_sized(*d);
     auto run = [&](const moe::GemmProblem &g) {
@@ -399,9 +429,18 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     up.lda = H;
     up.gather = sorted;
     up.gather_div = k;
-    up.offsets = offsets;
+    up.offsets = seg_off;
     up.E = E;
-    up.max_rows = A;
+    up.max_rows = R;
+    if (m > 0) {
+        // segment E + v: gate rows v I .. (up rows I_shared + v I ..) of the
+        // shared up projection
+        up.B2 = (const uint16_t *)w->shared_up;
+        up.E2 = m;
+        up.b2_ld = H;
+        up.b2_up = d->I_shared;
+        up.b2_vstride = (long long)I * H;
+    }
     up.B = w->w_up;
     up.Bscale = (const uint16_t *)w->w_up_scales;
     up.Bbias = (const uint16_t *)w->w_up_biases;
@@ -438,9 +477,16 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     down.fp8 = up.fp8;
     down.A = h;
     down.lda = I;
-    down.offsets = offsets;
+    down.offsets = seg_off;
     down.E = E;
-    down.max_rows = A;
+    down.max_rows = R;
+    if (m > 0) {
+        // segment E + v: columns v I .. v I + I - 1 of the shared down projection
+        down.B2 = (const uint16_t *)w->shared_down;
+        down.E2 = m;
+        down.b2_ld = d->I_shared;
+        down.b2_vstride = I;
+    }
     down.B = w->w_down;
     down.Bscale = (const uint16_t *)w->w_down_scales;
     down.Bbias = (const uint16_t *)w->w_down_biases;
@@ -459,7 +505,12 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     LAUNCH(mark(4));
 
     const float *shared = nullptr;
-    if (d->I_shared > 0) {
+    int shared_terms = 1;
+    if (m > 0) {
+        // the segments' rows follow the routed ones: m partial outputs per token
+        shared = y + (size_t)A * H;
+        shared_terms = m;
+    } else if (d->I_shared > 0) {
         const int Is = d->I_shared;
         uint16_t *hs = (uint16_t *)(ws + L.hs);
         float *ys = (float *)(ws + L.ys);
@@ -495,7 +546,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         shared = ys;
     }
     LAUNCH(mark(5));
-    LAUNCH(moe::launch_combine(y, slot, wts, shared, T, H, k, d->routed_scale,
+    LAUNCH(moe::launch_combine(y, slot, wts, shared, shared_terms, T, H, k, d->routed_scale,
                                d->fold_routed_scale != 0, out,
                                d->out_dtype == MOE_OUT_F32, stream));
     LAUNCH(mark(6));

@@ -3,6 +3,9 @@
 //   acc = 0; acc = fma(w[t,j], y[slot_of[t*k+j], h], acc) for j = 0..k-1 (ascending)
 //   acc = acc * routed_scale          (the routed sum is scaled once, here)
 //   acc = acc + shared[t, h]          (the shared expert is added unscaled)
+// When the shared expert ran as m plan segments of the routed experts' width
+// (I_shared = m I), its output is the sum of m partial rows, added first in
+// ascending order: s = shared_0[t, h] + ... + shared_{m-1}[t, h], acc + s.
 //   out[t, h] = round(acc)            (bf16 nearest-even, or fp32 as is)
 // vllm.cpp PR #684 (W2 commit): the routed scale multiplies the finished
 // routed sum before the shared output is added; folding it into each weight
@@ -36,9 +39,9 @@ template <bool FOLD>
 __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ y,
                                                       const int32_t *__restrict__ slot,
                                                       const float *__restrict__ w,
-                                                      const float *__restrict__ shared, int T,
-                                                      int H, int k, float rsf, void *out,
-                                                      int out_f32) {
+                                                      const float *__restrict__ shared,
+                                                      int shared_terms, int T, int H, int k,
+                                                      float rsf, void *out, int out_f32) {
     const int per_tok = H / 8;
     const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
     if (idx >= (size_t)T * per_tok)
@@ -65,12 +68,19 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ 
             acc[c] = acc[c] * rsf;
     }
     if (shared != nullptr) {
-        const float4 *sp = reinterpret_cast<const float4 *>(shared + (size_t)t * H + h0);
-        const float4 a = sp[0], b = sp[1];
-        const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        float s[8];
+        for (int v = 0; v < shared_terms; ++v) {
+            const float4 *sp =
+                reinterpret_cast<const float4 *>(shared + ((size_t)v * T + t) * H + h0);
+            const float4 a = sp[0], b = sp[1];
+            const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                s[c] = v == 0 ? e[c] : s[c] + e[c];
+        }
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-            acc[c] = acc[c] + v[c];
+            acc[c] = acc[c] + s[c];
     }
     if (out_f32) {
         float4 *op = reinterpret_cast<float4 *>((float *)out + (size_t)t * H + h0);
@@ -86,18 +96,21 @@ __global__ __launch_bounds__(kThreads) void k_combine(const float *__restrict__ 
 }  // namespace
 
 hipError_t launch_combine(const float *y_seg, const int32_t *slot_of, const float *weights,
-                          const float *shared, int T, int H, int k, float routed_scale, bool fold,
-                          void *out, int out_f32, hipStream_t stream) {
+                          const float *shared, int shared_terms, int T, int H, int k,
+                          float routed_scale, bool fold, void *out, int out_f32,
+                          hipStream_t stream) {
     const size_t n = (size_t)T * (H / 8);
     if (n == 0)
         return hipSuccess;
+    if (shared != nullptr && shared_terms < 1)
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)((n + kThreads - 1) / kThreads));
     if (fold)
         hipLaunchKernelGGL(k_combine<true>, grid, dim3(kThreads), 0, stream, y_seg, slot_of,
-                           weights, shared, T, H, k, routed_scale, out, out_f32);
+                           weights, shared, shared_terms, T, H, k, routed_scale, out, out_f32);
     else
         hipLaunchKernelGGL(k_combine<false>, grid, dim3(kThreads), 0, stream, y_seg, slot_of,
-                           weights, shared, T, H, k, routed_scale, out, out_f32);
+                           weights, shared, shared_terms, T, H, k, routed_scale, out, out_f32);
     return hipGetLastError();
 }
 

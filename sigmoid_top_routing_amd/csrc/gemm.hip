@@ -619,6 +619,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_fp8(GemmProblem p,
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
     if (grouped_supported(p))
         return launch_grouped(p, stream);        // FP8 included (its own tiles)
+    if (p.E2 > 0)
+        return hipErrorInvalidValue;             // shared segments: the persistent kernel only
     if (p.fp8)
         return hipErrorInvalidValue;             // otherwise decoded by launch_dequant first
     if (p.affine4) {

@@ -212,7 +212,12 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
     using G = Geo<BM, F8>;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    q.b_base = (const char *)p.B + (size_t)e * p.N * p.K * (F8 ? 1 : 2);
+    // segments past the experts: the shared expert's slices (bf16 only)
+    const bool sh = !F8 && e >= p.E;
+    q.b_base = sh ? (const char *)(p.B2 + (size_t)(e - p.E) * p.b2_vstride)
+                  : (const char *)p.B + (size_t)e * p.N * p.K * (F8 ? 1 : 2);
+    const uint32_t ld = sh ? (uint32_t)p.b2_ld : (uint32_t)p.K;
+    const int up_rows = sh ? p.b2_up : p.I;
     if constexpr (F8) {
         const int nb = p.K / 128;           // K-blocks (at most 64: one per lane)
         const int wn = wave & 1;
@@ -241,14 +246,13 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
             int n = nt * (kBN / 2) + (r & (kBN / 2 - 1));
             if (n >= p.I)
                 n = p.I - 1;
-            wr = r < kBN / 2 ? n : p.I + n;
+            wr = r < kBN / 2 ? n : up_rows + n;
         } else {
             wr = nt * kBN + r;
             if (wr >= p.N)
                 wr = p.N - 1;
         }
-        q.b_off[i] = F8 ? (uint32_t)wr * (uint32_t)p.K + c * 16
-                        : ((uint32_t)wr * (uint32_t)p.K + c * 8) * 2u;
+        q.b_off[i] = F8 ? (uint32_t)wr * ld + c * 16 : ((uint32_t)wr * ld + c * 8) * 2u;
     }
 }
 
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     const int wm = wave >> 1, wn = wave & 1;
 
     // ---- tiles per segment and their prefix
-    const int nseg = p.offsets ? p.E : 1;
+    const int nseg = p.offsets ? p.E + p.E2 : 1;
     int tiles = 0;
     if (tid < nseg) {
         const int lo = p.offsets ? p.offsets[tid] : 0;
@@ -528,7 +532,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         int raw[G::AI];
         const int valid = gathered_rows<BM>(p, row0, row_end, raw);
         a_offsets<BM>(p, raw, valid, req.a_off);
-        b_offsets<BM, MODE, F8>(p, p.b_compact ? s_rank[e] : e, nt, req);
+        b_offsets<BM, MODE, F8>(p, p.b_compact && e < p.E ? s_rank[e] : e, nt, req);
     }
     int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
     bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
@@ -661,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                     for (int i = 0; i < G::AI; ++i)
                         __asm__ volatile("" : "+v"(nraw[i]));
                     a_offsets<BM>(p, nraw, nvalid, req.a_off);
-                    b_offsets<BM, MODE, F8>(p, p.b_compact ? s_rank[ne] : ne, nnt, req);
+                    b_offsets<BM, MODE, F8>(p, p.b_compact && ne < p.E ? s_rank[ne] : ne, nnt, req);
                 }
             }
         }
@@ -841,7 +845,8 @@ long long tiles_bound(const GemmProblem &p, int &n_tiles) {
     if (p.offsets == nullptr) {
         mt_max = (p.rows + BM - 1) / BM;
     } else {
-        const int nonempty = p.E < p.max_rows ? p.E : p.max_rows;
+        const int segs = p.E + p.E2;
+        const int nonempty = segs < p.max_rows ? segs : p.max_rows;
         mt_max = (p.max_rows + BM - 1) / BM + nonempty;
     }
     const int n_cols = gated(MODE) ? p.I : p.N;
@@ -882,7 +887,7 @@ template <int MODE>
 hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
     int segs = 1;
     if (p.offsets != nullptr)
-        segs = p.E < p.max_rows ? p.E : p.max_rows;
+        segs = p.E + p.E2 < p.max_rows ? p.E + p.E2 : p.max_rows;
     const int rows = p.offsets != nullptr ? p.max_rows : p.rows;
     const int avg = segs > 0 ? rows / segs : 0;
     // 256-row tiles for long segments, unless a dense problem then has fewer
@@ -922,8 +927,15 @@ bool grouped_supported(const GemmProblem &p) {
     // at most 64 K-blocks (one per lane), the caller's weights as stored
     const bool fp8_ok = !p.fp8 || (p.K % 128 == 0 && p.K / 128 <= kWave && p.N % 128 == 0 &&
                                    (!gated(p.mode) || p.I % 128 == 0) && !p.b_compact);
-    return !p.affine4 && fp8_ok && p.scatter == nullptr && p.K % kBK == 0 && p.K / kBK >= kStagesSmall &&
-           (p.offsets == nullptr || p.E <= kMaxE) && a_rows * p.lda * 2 < (long long)kPastA &&
+    // shared segments: bf16 weights beside bf16 (or decoded) experts, every
+    // weight offset of a slice below kPastA
+    const long long b2_rows = gated(p.mode) ? (long long)p.b2_up + p.I : p.N;
+    const bool e2_ok = p.E2 == 0 ||
+                       (p.E2 > 0 && !p.fp8 && p.offsets != nullptr && p.B2 != nullptr &&
+                        b2_rows * p.b2_ld * 2 < (long long)kPastA && p.b2_ld >= p.K);
+    return !p.affine4 && fp8_ok && e2_ok && p.scatter == nullptr && p.K % kBK == 0 &&
+           p.K / kBK >= kStagesSmall && (p.offsets == nullptr || p.E + p.E2 <= kMaxE) &&
+           a_rows * p.lda * 2 < (long long)kPastA &&
            (long long)p.N * p.K * (p.fp8 ? 1 : 2) < (long long)kPastA;
 }
 

@@ -32,9 +32,14 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
 // Plan scratch: per-chunk expert counts, plan_chunks(A) x E int32.
 int plan_chunk_size(int A);
 int plan_chunks(int A);
+// seg_offsets (optional): [E + shared_segs + 1], the offsets followed by
+// shared_segs segments of T rows each (the shared expert as plan segments,
+// all T tokens in each); sorted then holds A + shared_segs * T entries, the
+// shared positions A + v T + t holding t * k (token t through the gather).
 hipError_t launch_plan(const int32_t *ids, int A, int E, int32_t *counts, int32_t *offsets,
                        int32_t *sorted, int32_t *slot_of, int32_t *fault, int32_t *chunk_counts,
-                       hipStream_t stream);
+                       hipStream_t stream, int32_t *seg_offsets = nullptr, int shared_segs = 0,
+                       int T = 0);
 
 // Grouped GEMM over expert segments.
 // kGateUpLimit: kGateUp with the SwiGLU inputs clamped at GemmProblem::limit.
@@ -66,6 +71,15 @@ struct GemmProblem {
     const int32_t *scatter;   // kDown: output row of position p = scatter[p] (NULL: row p)
     int b_compact;            // B holds only the experts with rows, in expert order
     float limit;              // kGateUpLimit: the SwiGLU input limit L > 0
+    // Segments E .. E + E2 - 1 after the experts (the shared expert as plan
+    // segments; bf16, the persistent kernel only): segment E + v reads its
+    // weights at B2 + v * b2_vstride elements, rows b2_ld elements apart,
+    // and (gated) its up rows b2_up rows after its gate rows.
+    const uint16_t *B2;
+    int E2;
+    int b2_ld;
+    int b2_up;
+    long long b2_vstride;
 };
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
@@ -100,10 +114,13 @@ hipError_t launch_add_rmsnorm(const uint16_t *h, const uint16_t *residual, const
                               int T, int H, float eps, uint16_t *residual_out, uint16_t *x,
                               hipStream_t stream);
 
-// out[t] = routed_scale * sum_j weights[t,j] y_seg[slot_of[t*k+j]] + shared[t], or with
-// fold, sum_j (routed_scale * weights[t,j]) y_seg[slot_of[t*k+j]] (no shared term)
+// out[t] = routed_scale * sum_j weights[t,j] y_seg[slot_of[t*k+j]] + s[t], or with
+// fold, sum_j (routed_scale * weights[t,j]) y_seg[slot_of[t*k+j]] (no shared term);
+// s[t] = shared[t] + shared[T + t] + ... over shared_terms rows T*H apart (v
+// ascending; one term: the shared output itself).
 hipError_t launch_combine(const float *y_seg, const int32_t *slot_of, const float *weights,
-                          const float *shared, int T, int H, int k, float routed_scale, bool fold,
-                          void *out, int out_f32, hipStream_t stream);
+                          const float *shared, int shared_terms, int T, int H, int k,
+                          float routed_scale, bool fold, void *out, int out_f32,
+                          hipStream_t stream);
 
 }  // namespace moe

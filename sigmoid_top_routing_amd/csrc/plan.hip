@@ -24,10 +24,22 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxChunks = 64;
 
+// Also the shared segments (host-known, independent of the ids): the
+// bounds after offsets[E] and the gather entries of their positions.
 __global__ __launch_bounds__(kThreads) void k_plan_count(const int32_t *__restrict__ ids, int A,
                                                          int E, int chunk,
                                                          int32_t *__restrict__ chunk_counts,
-                                                         int32_t *__restrict__ fault) {
+                                                         int32_t *__restrict__ fault,
+                                                         int32_t *__restrict__ sorted,
+                                                         int32_t *__restrict__ seg_offsets,
+                                                         int shared_segs, int T, int k) {
+    if (shared_segs > 0) {
+        const int n = shared_segs * T;
+        for (int i = blockIdx.x * kThreads + threadIdx.x; i < n; i += gridDim.x * kThreads)
+            sorted[A + i] = (i % T) * k;
+        if (blockIdx.x == 0 && threadIdx.x < shared_segs)
+            seg_offsets[E + 1 + threadIdx.x] = A + (threadIdx.x + 1) * T;
+    }
     __shared__ int cnt[256];
     __shared__ int bad;
     const int tid = threadIdx.x;
@@ -54,7 +66,8 @@ __global__ __launch_bounds__(kThreads) void k_plan_count(const int32_t *__restri
 __global__ __launch_bounds__(kThreads) void k_plan_scatter(
     const int32_t *__restrict__ ids, int A, int E, int chunk, int nchunks,
     const int32_t *__restrict__ chunk_counts, int32_t *__restrict__ counts,
-    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ slot_of) {
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted, int32_t *__restrict__ slot_of,
+    int32_t *__restrict__ seg_offsets) {
     __shared__ int run[256];
     __shared__ int wsum[4];
     __shared__ int wcnt[4][256];
@@ -93,6 +106,11 @@ __global__ __launch_bounds__(kThreads) void k_plan_scatter(
         offsets[tid] = excl;
         if (tid == E - 1)
             offsets[E] = incl;
+        if (seg_offsets != nullptr) {
+            seg_offsets[tid] = excl;
+            if (tid == E - 1)
+                seg_offsets[E] = incl;
+        }
     }
     run[tid] = excl + before;
 #pragma unroll
@@ -155,15 +173,19 @@ int plan_chunks(int A) {
 
 hipError_t launch_plan(const int32_t *ids, int A, int E, int32_t *counts, int32_t *offsets,
                        int32_t *sorted, int32_t *slot_of, int32_t *fault, int32_t *chunk_counts,
-                       hipStream_t stream) {
+                       hipStream_t stream, int32_t *seg_offsets, int shared_segs, int T) {
+    if (shared_segs < 0 || shared_segs > kThreads || (shared_segs > 0 && seg_offsets == nullptr) ||
+        (shared_segs > 0 && (T <= 0 || A % T != 0)))
+        return hipErrorInvalidValue;
     const int chunk = plan_chunk_size(A);
     const int nb = plan_chunks(A);
     if (nb > 0)
         hipLaunchKernelGGL(k_plan_count, dim3(nb), dim3(kThreads), 0, stream, ids, A, E, chunk,
-                           chunk_counts, fault);
+                           chunk_counts, fault, sorted, seg_offsets, shared_segs, T,
+                           shared_segs > 0 ? A / T : 0);
     // with no assignments one block still writes zero counts and offsets
     hipLaunchKernelGGL(k_plan_scatter, dim3(nb > 0 ? nb : 1), dim3(kThreads), 0, stream, ids, A,
-                       E, chunk, nb, chunk_counts, counts, offsets, sorted, slot_of);
+                       E, chunk, nb, chunk_counts, counts, offsets, sorted, slot_of, seg_offsets);
     return hipGetLastError();
 }
 

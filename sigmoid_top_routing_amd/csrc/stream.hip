@@ -504,7 +504,7 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 }  // namespace
 
 bool stream_supported(const GemmProblem &p) {
-    if (p.b_compact || p.scatter != nullptr)
+    if (p.b_compact || p.scatter != nullptr || p.E2 > 0)
         return false;
     static_assert(kStreamMaxKAffine4 == 4 * QFmt<kFmtAffine4>::EPJ, "4-bit steps");
     static_assert(kStreamMaxKFp8 == 4 * QFmt<kFmtFp8>::EPJ, "FP8 steps");

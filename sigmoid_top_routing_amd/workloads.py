@@ -136,6 +136,17 @@ MID = {
                                     act="relu2", rsf=2.5, I_shared=128, seed=114,
                                     nan_rows=(1, 90), posinf_rows=(3, 100), neginf_rows=(5, 150),
                                     tie_col=11),
+    # Shared experts a whole number of routed widths wide (I_shared = m I):
+    # at prompt sizes they run as m plan segments inside the routed launches
+    # (relu^2 m = 2 as in Nemotron-H; SwiGLU m = 3 with the input limit;
+    # 4-bit routed experts beside a bf16 shared expert, m = 1).
+    "mid_relu2_shared_seg": Workload("mid_relu2_shared_seg", T=300, H=256, I=192, E=16, k=4,
+                                     act="relu2", rsf=2.5, I_shared=384, seed=116),
+    "mid_swiglu_shared_seg3": Workload("mid_swiglu_shared_seg3", T=200, H=256, I=128, E=12, k=3,
+                                       rsf=1.25, I_shared=384, swiglu_limit=7.0, x_std=8.0,
+                                       seed=117),
+    "mid_affine4_shared_seg": Workload("mid_affine4_shared_seg", T=200, H=256, I=128, E=8, k=2,
+                                       wfmt="affine4", I_shared=128, seed=118),
     # Block-FP8 e4m3 experts, one fp32 scale per 128 x 128 block (TensorFold
     # issue #548: the block-FP8 experts of the CUDA branches), with a
     # SwiGLU shared expert.

@@ -42,6 +42,11 @@ CASES = {
     "relu2_nonfinite": (W.Workload("pin_relu2_nonfinite", T=300, H=256, I=192, E=16, k=4,
                                    act="relu2", rsf=1.5, bias_lo=-0.1, bias_hi=0.1, seed=502),
                         True, False),
+    # relu^2 with a shared expert twice the routed width: at the prompt size
+    # it runs as two plan segments whose partial rows the combine adds
+    "relu2_shared_seg": (W.Workload("pin_relu2_seg", T=300, H=256, I=128, E=16, k=4,
+                                    act="relu2", rsf=2.5, I_shared=256, bias_lo=-0.1,
+                                    bias_hi=0.1, seed=504), False, False),
     # Laguna's fold (no shared expert): the scale inside each term, which
     # must then give the folded bits and not the engine's
     "swiglu_laguna_fold": (W.Workload("pin_swiglu_fold", T=300, H=256, I=128, E=16, k=4,

@@ -409,7 +409,8 @@ DECODE_CASES = [("tiny_t64_e8_k2", 8), ("tiny_t64_e8_k2", 1), ("mid_swiglu", 8),
                 ("mid_fp8_relu2", 8), ("mid_fp8_wide", 8), ("mid_fp8_wide", 2),
                 ("mid_affine4", 8), ("mid_affine4", 1),
                 ("mid_affine4_relu2", 8), ("mid_affine4_relu2", 3), ("mid_affine4_i64", 8),
-                ("mid_relu2_nonfinite", 8)]
+                ("mid_relu2_nonfinite", 8), ("mid_relu2_shared_seg", 8),
+                ("mid_swiglu_shared_seg3", 8), ("mid_affine4_shared_seg", 8)]
 
 
 @pytest.mark.parametrize("name,T", DECODE_CASES)
