@@ -135,10 +135,15 @@ typedef struct {
  *  exponent bits with bias 7, 3 mantissa bits; no infinities; S.1111.111 is
  *  NaN; largest 448), w_*_scales are fp32 [E, N/128, K/128], one per
  *  128 x 128 block, the weight is scale * value, and w_*_biases are unused.
- *  H and I must then be multiples of 128. Decode-sized batches stream the
- *  codes (one byte per weight) and apply each block's scale in fp32 to the
- *  partial sum of its 128 inputs; larger ones decode the experts with rows
- *  to bf16 in the workspace, then run on the bf16 kernels.
+ *  H and I must then be multiples of 128, and every scale finite and
+ *  non-zero (as an absmax quantizer's scales are; a zero or non-finite scale
+ *  gives undefined outputs). The codes are read at one byte per weight and
+ *  converted exactly to bf16 (every E4M3 value is a bf16 value); the block
+ *  scales multiply fp32 sums: decode-sized batches stream the codes and
+ *  scale each lane's partial over 16 inputs of one block, larger ones run
+ *  the MFMA tiles, whose running sums are rescaled at each 128-wide K-block
+ *  boundary. With H or I above 8192 a prompt-sized batch decodes the experts
+ *  with rows to bf16 (scale * value rounded) in the workspace first.
  *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
  *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared]. */
 typedef struct {
@@ -155,11 +160,13 @@ typedef struct {
 } moe_weights;
 
 /* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
- * 4-bit or block-FP8 experts and more than 2 E assignments (T * k > 2 E),
- * and with block-FP8 experts whose max(H, I) exceeds 4096 at any T, this
- * includes room for the bf16-decoded weights of every expert that can have
- * rows: min(E, T * k) * max(n_up * H, H * I) * 2 bytes, n_up = 2 I (SwiGLU)
- * or I. Decode-sized batches (T * k <= 2 E) stream the codes instead. */
+ * 4-bit experts and more than 2 E assignments (T * k > 2 E) or row_invariant,
+ * and with block-FP8 experts whose max(H, I) exceeds 8192 (and, at decode
+ * sizes, 4096), this includes room for the bf16-decoded weights of every
+ * expert that can have rows: min(E, T * k) * max(n_up * H, H * I) * 2 bytes,
+ * n_up = 2 I (SwiGLU) or I. Otherwise the codes are read as stored. With a
+ * shared expert whose I_shared is a whole number m of I, prompt-sized
+ * batches also hold its m segments' rows: m*T more rows of h and y. */
 int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
 
 /* Router and top-k (TileGym PR #187 "Weight layout and routing"; TensorFold
@@ -202,7 +209,11 @@ int moe_plan(const moe_dims *d, const int32_t *ids, int32_t *counts, int32_t *of
  *       fp32 as routed_scale * (fma chain of w_j * y_j, j ascending), plus
  *       the shared expert's output, and rounded once; with
  *       d->fold_routed_scale, as the fma chain of (routed_scale * w_j) * y_j,
- *       j ascending. weights_out holds the unscaled w_j either way.
+ *       j ascending. weights_out holds the unscaled w_j either way. When
+ *       I_shared is a whole number m of I, prompt-sized batches run the
+ *       shared expert as m segments of every token inside the routed
+ *       experts' launches (the plan's extra slots), and its output is the
+ *       sum of the m partial rows, v ascending.
  *  ids_out, weights_out ([T, k]) and offsets_out ([E+1]) may be NULL; when
  *  given they receive the routing and the plan offsets of this call.
  * Workspace: moe_workspace_bytes(d). */
