@@ -22,8 +22,9 @@ Besides the whole-block throughput the line carries:
                 bytes and flops and their fractions of the HBM and bf16 MFMA
                 peaks: the tiny block, the relu^2 block with a shared expert,
                 the 4-bit block, the 4-bit decode step (T = 8) without
-                and with the four boosted experts, and the block-FP8 decode
-                step.
+                and with the four boosted experts, the block-FP8 prefill and
+                decode steps, and the bf16 decode step with row_invariant
+                (every batch on the MFMA tiles).
 """
 from __future__ import annotations
 
@@ -276,9 +277,12 @@ def main():
                                  ("affine4", "affine4_t1024", False),
                                  ("affine4_decode", "affine4_flat_decode_t8", True),
                                  ("affine4_decode_boosted", "affine4_decode_t8", True),
+                                 ("fp8", "lfm2_fp8_prefill_t4096", False),
                                  ("fp8_decode", "lfm2_fp8_decode_t8", True)):
             result["configs"][tag] = bench_step(W.by_name(name), W, lib, torch, flush=flush)
             print(f"bench: {tag} done", file=sys.stderr, flush=True)
+        result["configs"]["decode_row_invariant"] = bench_step(W.DECODE, W, lib, torch, block=block,
+                                                               flush=True, row_invariant=True)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(result))
@@ -322,7 +326,7 @@ def shared_bytes(wl):
     return 2 * (n_sup + wl.I_shared) * wl.H
 
 
-def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20):
+def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20, row_invariant=False):
     """One workload's step, each call between its own event pair on the
     current stream (the median call is reported), then the stage breakdown
     from calls with the stage events inside (each record adds a few
@@ -331,12 +335,15 @@ def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20):
     last-level cache) so the expert weights come from HBM; it is read rather
     than written so no dirty lines are written back during the timed call.
     block: the weights already on the device (the workload's x is drawn on
-    its own seed). Algorithmic work: the MFMA flops of the routed and shared
+    its own seed). row_invariant: the call with that option (the block's
+    own setting is restored afterwards). Algorithmic work: the MFMA flops of the routed and shared
     projections, and the bytes of the D distinct experts touched (as stored),
     the shared expert, the router weight, x and the bf16 output."""
     inp = W.generate(wl, experts=block is None)
     if block is None:
         block = lib.block_from_arrays(wl, inp)
+    saved = block.row_invariant
+    block.row_invariant = row_invariant
     x = lib.x_to_device(inp["x"])
     ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
@@ -362,6 +369,7 @@ def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20):
         block.forward(x, out=out, ids_out=ids, events=ev)
         torch.cuda.synchronize()
         ups.append(ev.stage_ms())
+    block.row_invariant = saved
     D = int(np.unique(ids.cpu().numpy()).size)
     eb_up, eb_down = expert_bytes(wl)
     algo = (D * (eb_up + eb_down) + shared_bytes(wl) + wl.E * wl.H * 4 +
@@ -375,7 +383,7 @@ def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20):
             "distinct_experts": D, "us_per_step": 1e6 * t, "tokens_per_s": wl.T / t,
             "algorithmic_bytes": algo, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
             "flops": flops, "tflops": tfs, "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS,
-            "cache_evicted": bool(flush),
+            "cache_evicted": bool(flush), "row_invariant": bool(row_invariant),
             "timing": "median of %d calls, one event pair each" % steps,
             "stages_us_with_events": {k: 1e3 * float(np.median([u[k] for u in ups]))
                                       for k in lib.STAGES}}

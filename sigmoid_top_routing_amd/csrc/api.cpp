@@ -222,10 +222,45 @@ int check_opt_ptr(const char *what, const char *name, const void *p) {
     return MOE_OK;
 }
 
+// Device allocations this thread has validated: a pointer inside one is not
+// queried again. A call makes up to 16 pointer checks, which cost more host
+// time than the launches of a decode step; the weights, workspace and
+// outputs of a layer repeat from call to call, so after the first call none
+// is queried. (A pointer into memory freed since is not caught; that is
+// undefined anyway.)
+struct DevRange {
+    uintptr_t lo, hi;
+};
+constexpr int kDevRanges = 64;
+thread_local DevRange t_dev_ranges[kDevRanges];
+thread_local int t_dev_count = 0;
+thread_local int t_dev_next = 0;
+
+bool known_device(const void *p) {
+    const uintptr_t a = (uintptr_t)p;
+    for (int i = 0; i < t_dev_count; ++i)
+        if (a >= t_dev_ranges[i].lo && a < t_dev_ranges[i].hi)
+            return true;
+    return false;
+}
+
+void remember_device(const void *p) {
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p) != hipSuccess || size == 0) {
+        (void)hipGetLastError();
+        return;
+    }
+    t_dev_ranges[t_dev_next] = DevRange{(uintptr_t)base, (uintptr_t)base + size};
+    t_dev_next = (t_dev_next + 1) % kDevRanges;
+    if (t_dev_count < kDevRanges)
+        ++t_dev_count;
+}
+
 // Device memory check, the last check before launching (it is the only one
 // that asks the HIP runtime).
 int check_device(const char *what, const char *name, const void *p) {
-    if (p == nullptr)
+    if (p == nullptr || known_device(p))
         return MOE_OK;
     hipPointerAttribute_t attr;
     const hipError_t e = hipPointerGetAttributes(&attr, p);
@@ -236,6 +271,7 @@ int check_device(const char *what, const char *name, const void *p) {
     }
     REQUIRE(attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged, MOE_E_SHAPE,
             "%s: %s = %p is not device memory", what, name, p);
+    remember_device(p);
     return MOE_OK;
 }
 
