@@ -334,6 +334,8 @@ typedef struct {
     int32_t score_fn;   /* 0 sigmoid, 1 softmax */
     double swiglu_limit;  /* 0: no clamp; else L > 0 for every SwiGLU of the layer */
     int32_t round_h;    /* 1: the activation between the projections stored as bf16 */
+    const float *w_up_global;    /* NVFP4: fp32 [E], the global scale of each expert's up matrix */
+    const float *w_down_global;  /* NVFP4: fp32 [E], of each expert's down matrix */
 } oracle_layer;
 
 /* An OCP FP8 E4M3 code (the "fn" variant: no infinities) as float64: sign
@@ -357,6 +359,32 @@ void oracle_fp8_decode(const uint8_t *codes, int n, double *out)
         out[i] = fp8_e4m3_value(codes[i]);
 }
 
+/* An FP4 E2M1 code (4 bits: sign bit 3, exponent bits 2..1 with bias 1,
+ * mantissa bit 0) as float64: exponent 0 holds the subnormal m/2; otherwise
+ * 2^(e-1) (1 + m/2). No infinities or NaN: the magnitudes are 0, 0.5, 1,
+ * 1.5, 2, 3, 4 and 6. NVFP4 experts (TensorFold issue #548, the core/quant
+ * split: ModelOpt NVFP4, uint8 [N, K/2], an e4m3 scale every 16 inputs and
+ * a global scale) store two such codes per byte. */
+static double fp4_e2m1_value(unsigned q)
+{
+    int s = (q >> 3) & 1, e = (q >> 1) & 3, m = q & 1;
+    double v = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* Element c of an NVFP4 row: code byte c/2, low nibble for even c (this
+ * project's stated packing, as for the 4-bit affine format). */
+static unsigned fp4_code(const uint8_t *row, int c)
+{
+    return (row[c / 2] >> (4 * (c % 2))) & 15u;
+}
+
+void oracle_fp4_decode(const uint8_t *bytes, int n, double *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = fp4_e2m1_value(fp4_code(bytes, i));
+}
+
 /* Row n of a weight matrix with K inputs, as float64. */
 static void weight_row(const oracle_layer *L, int is_up, int e, int n, int N, int K, double *row)
 {
@@ -365,6 +393,14 @@ static void weight_row(const oracle_layer *L, int is_up, int e, int n, int N, in
         const uint16_t *w = (const uint16_t *)(is_up ? L->w_up : L->w_down) + r * K;
         for (int c = 0; c < K; ++c)
             row[c] = (double)bf16_value(w[c]);
+    } else if (L->wfmt == 3) {
+        /* weight = e2m1 code x its 16-wide group's e4m3 scale x the matrix's
+         * global scale */
+        const uint8_t *codes = (const uint8_t *)(is_up ? L->w_up : L->w_down) + r * (K / 2);
+        const uint8_t *sc = (const uint8_t *)(is_up ? L->w_up_scales : L->w_down_scales) + r * (K / 16);
+        const double g = (double)(is_up ? L->w_up_global : L->w_down_global)[e];
+        for (int c = 0; c < K; ++c)
+            row[c] = fp4_e2m1_value(fp4_code(codes, c)) * fp8_e4m3_value(sc[c / 16]) * g;
     } else if (L->wfmt == 2) {
         /* one fp32 scale per 128 x 128 block of the expert's [N, K] matrix */
         const uint8_t *codes = (const uint8_t *)(is_up ? L->w_up : L->w_down) + r * K;

@@ -51,6 +51,7 @@ class Layer(C.Structure):
         ("w_down", C.c_void_p), ("w_down_scales", C.c_void_p), ("w_down_biases", C.c_void_p),
         ("shared_up", C.c_void_p), ("shared_down", C.c_void_p),
         ("score_fn", C.c_int32), ("swiglu_limit", C.c_double), ("round_h", C.c_int32),
+        ("w_up_global", C.c_void_p), ("w_down_global", C.c_void_p),
     ]
 
 
@@ -74,6 +75,7 @@ def lib():
         L.oracle_softmax32_row.argtypes = [p, i, p]
         L.oracle_add_rmsnorm.argtypes = [i, i, p, p, p, C.c_double, p, p]
         L.oracle_fp8_decode.argtypes = [p, i, p]
+        L.oracle_fp4_decode.argtypes = [p, i, p]
         L.oracle_plan.argtypes = [i, i, i, p, p, p, p, p]
         L.oracle_forward_tokens.argtypes = [C.POINTER(Layer), p, i, p, p, p, i]
         L.oracle_forward_tokens.restype = C.c_int
@@ -183,11 +185,12 @@ def _layer(wl, inp: dict, keep: dict, round_h: bool = False) -> Layer:
 
     affine = wl.wfmt == "affine4"
     fp8 = wl.wfmt == "fp8"
-    code_t = np.uint32 if affine else np.uint8 if fp8 else np.uint16
-    scale_t = np.float32 if fp8 else np.uint16
+    nvfp4 = wl.wfmt == "nvfp4"
+    code_t = np.uint32 if affine else np.uint8 if (fp8 or nvfp4) else np.uint16
+    scale_t = np.float32 if fp8 else np.uint8 if nvfp4 else np.uint16
     return Layer(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
                  act=0 if wl.act == "swiglu" else 1,
-                 wfmt={"bf16": 0, "affine4": 1, "fp8": 2}[wl.wfmt],
+                 wfmt={"bf16": 0, "affine4": 1, "fp8": 2, "nvfp4": 3}[wl.wfmt],
                  group=wl.group if affine else 0, norm_topk=int(wl.norm_topk),
                  I_shared=wl.I_shared, norm_eps=wl.norm_eps, rsf=wl.rsf,
                  x=arr("x", np.uint16), router_w=arr("router_w", np.float32),
@@ -202,7 +205,9 @@ def _layer(wl, inp: dict, keep: dict, round_h: bool = False) -> Layer:
                  shared_down=arr("shared_down", np.uint16) if wl.I_shared else None,
                  score_fn=SCORES[getattr(wl, "score", "sigmoid")],
                  swiglu_limit=float(getattr(wl, "swiglu_limit", 0.0)),
-                 round_h=int(round_h))
+                 round_h=int(round_h),
+                 w_up_global=arr("w_up_global", np.float32),
+                 w_down_global=arr("w_down_global", np.float32))
 
 
 def forward_tokens(wl, inp: dict, tokens, nthreads: int = 0, want_routing: bool = False,
@@ -307,4 +312,14 @@ def fp8_decode(codes) -> np.ndarray:
     codes = _c(np.atleast_1d(codes), np.uint8)
     out = np.empty(codes.shape, dtype=np.float64)
     lib().oracle_fp8_decode(_ptr(codes), codes.size, _ptr(out))
+    return out
+
+
+def fp4_decode(packed, n: int) -> np.ndarray:
+    """The first n FP4 E2M1 values of a packed byte array (element c in byte
+    c // 2, low nibble first), as float64."""
+    packed = _c(np.asarray(packed).reshape(-1), np.uint8)
+    assert 0 <= n <= 2 * packed.size
+    out = np.empty(n, dtype=np.float64)
+    lib().oracle_fp4_decode(_ptr(packed), n, _ptr(out))
     return out

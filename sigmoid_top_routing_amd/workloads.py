@@ -78,6 +78,8 @@ class Workload:
     fp8_exp_mu: float = 13.0          # block-FP8 codes: exponent field round(N(mu, sd))
     fp8_exp_sd: float = 1.0
     fp8_nan: tuple = ()               # (expert, row) of w_down rows holding one e4m3 NaN
+    global_lo: float = 3e-5           # NVFP4: global scale of each expert matrix, U(lo, hi)
+    global_hi: float = 8e-5
     qbias_lo: float = -0.1
     qbias_hi: float = 0.1
     group: int = 64
@@ -163,6 +165,13 @@ MID = {
     "mid_fp8_wide": Workload("mid_fp8_wide", T=500, H=384, I=256, E=16, k=4, wfmt="fp8",
                              scale_lo=0.01, scale_hi=0.03, fp8_exp_mu=7.0, fp8_exp_sd=1.5,
                              I_shared=128, seed=115),
+    # NVFP4 experts (TensorFold issue #548, the core/quant split: ModelOpt
+    # NVFP4, uint8 [N, K/2], an e4m3 scale every 16 inputs, a global scale),
+    # with a bf16 SwiGLU shared expert, and relu^2 NVFP4 experts.
+    "mid_nvfp4": Workload("mid_nvfp4", T=300, H=384, I=256, E=16, k=4, wfmt="nvfp4",
+                          I_shared=128, seed=119),
+    "mid_nvfp4_relu2": Workload("mid_nvfp4_relu2", T=200, H=256, I=384, E=24, k=6, act="relu2",
+                                wfmt="nvfp4", rsf=2.5, seed=120),
     # The softmax router family (TensorFold issue #548, the consolidation
     # proposal), with NaN rows and exact ties, over 64 experts.
     # No expert bias (the family has none): every score of an all-zero row
@@ -188,6 +197,10 @@ MID = {
 EXTRA = {
     "lfm2_fp8_prefill_t4096": Workload("lfm2_fp8_prefill_t4096", T=4096, H=2048, I=1792, E=32,
                                        k=4, wfmt="fp8", scale_lo=1e-4, scale_hi=3e-4, seed=111),
+    "lfm2_nvfp4_prefill_t4096": Workload("lfm2_nvfp4_prefill_t4096", T=4096, H=2048, I=1792,
+                                         E=32, k=4, wfmt="nvfp4", seed=121),
+    "lfm2_nvfp4_decode_t8": Workload("lfm2_nvfp4_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
+                                     wfmt="nvfp4", seed=122, weight_seed=121),
     "lfm2_fp8_decode_t8": Workload("lfm2_fp8_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
                                    wfmt="fp8", scale_lo=1e-4, scale_hi=3e-4, seed=112,
                                    weight_seed=111),
@@ -281,6 +294,26 @@ def _fp8_codes(rng: np.random.Generator, shape, mu: float = 13.0, sd: float = 1.
     return out.reshape(shape)
 
 
+def _bytes(rng: np.random.Generator, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint8)
+    for s in range(0, n, CHUNK):
+        m = min(CHUNK, n - s)
+        out[s:s + m] = rng.integers(0, 256, size=m, dtype=np.uint8)
+    return out.reshape(shape)
+
+
+def _e4m3_scales(rng: np.random.Generator, shape, mu: float, sd: float) -> np.ndarray:
+    """Positive OCP E4M3 scale codes: exponent field round(N(mu, sd))
+    clipped to 0..15, mantissa uniform, never the NaN pattern."""
+    n = int(np.prod(shape))
+    e = np.clip(np.rint(rng.standard_normal(n, dtype=np.float32) * np.float32(sd) +
+                        np.float32(mu)), 0, 15).astype(np.uint8)
+    mant = rng.integers(0, 8, size=n, dtype=np.uint8)
+    mant[(e == 15) & (mant == 7)] = 6
+    return ((e << 3) | mant).reshape(shape)
+
+
 def _children(seed: int):
     return [np.random.default_rng(c) for c in np.random.SeedSequence([0x5EED, seed]).spawn(10)]
 
@@ -329,6 +362,18 @@ def generate(wl: Workload, need_x: bool = True, experts: bool = True) -> dict:
                                                            wl.qbias_lo, wl.qbias_hi))
         out["w_down_biases"] = f32_to_bf16_bits(_uniform_f32(ws[c_qb], (E, H, I // g),
                                                              wl.qbias_lo, wl.qbias_hi))
+    elif wl.wfmt == "nvfp4":
+        # codes: two uniform E2M1 codes per byte; per 16 inputs an E4M3 scale
+        # drawn like absmax-scaled blocks (near 448 by default); per expert
+        # matrix a global scale
+        out["w_up"] = _bytes(ws[c_codes], (E, n_up, H // 2))
+        out["w_down"] = _bytes(ws[c_codes], (E, H, I // 2))
+        out["w_up_scales"] = _e4m3_scales(ws[c_scales], (E, n_up, H // 16), wl.fp8_exp_mu,
+                                          wl.fp8_exp_sd)
+        out["w_down_scales"] = _e4m3_scales(ws[c_scales], (E, H, I // 16), wl.fp8_exp_mu,
+                                            wl.fp8_exp_sd)
+        out["w_up_global"] = _uniform_f32(ws[c_qb], (E,), wl.global_lo, wl.global_hi)
+        out["w_down_global"] = _uniform_f32(ws[c_qb], (E,), wl.global_lo, wl.global_hi)
     elif wl.wfmt == "fp8":
         mu, sd = wl.fp8_exp_mu, wl.fp8_exp_sd
         out["w_up"] = _fp8_codes(ws[c_codes], (E, n_up, H), mu, sd)

@@ -137,6 +137,18 @@ MUTANTS = {
         "((size_t)e * (N / 128) + n / 128) * (K / 128);\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[c / 128];",
         "(size_t)e * (N / 128) * (K / 128) + n / 128;\n        for (int c = 0; c < K; ++c)\n            row[c] = fp8_e4m3_value(codes[c]) * (double)sc[(c / 128) * (N / 128)];",
         ["tests/test_oracle_fp8.py::test_fp8_layer_matches_dense_float64"]),
+    "fp4_high_nibble_first": (
+        "return (row[c / 2] >> (4 * (c % 2))) & 15u;", "return (row[c / 2] >> (4 * (1 - c % 2))) & 15u;",
+        ["tests/test_oracle_nvfp4.py::test_packing_is_low_nibble_first"]),
+    "fp4_exponent_bias_0": (
+        "ldexp(1.0 + 0.5 * m, e - 1)", "ldexp(1.0 + 0.5 * m, e)",
+        ["tests/test_oracle_nvfp4.py::test_e2m1_hand_values"]),
+    "nvfp4_group_32": (
+        "fp8_e4m3_value(sc[c / 16]) * g;", "fp8_e4m3_value(sc[c / 32]) * g;",
+        ["tests/test_oracle_nvfp4.py::test_nvfp4_layer_matches_dense_float64"]),
+    "nvfp4_global_dropped": (
+        "fp8_e4m3_value(sc[c / 16]) * g;", "fp8_e4m3_value(sc[c / 16]);",
+        ["tests/test_oracle_nvfp4.py::test_hand_layer"]),
     "round_h_ignored": (
         "return L->round_h ? (double)bf16_value(bf16_round((float)h)) : h;", "return h;",
         ["tests/test_oracle_round_h.py::test_round_h_hand_values_routed_and_shared"]),

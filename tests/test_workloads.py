@@ -36,6 +36,15 @@ def test_shapes_and_dtypes():
             assert inp["w_down_scales"].dtype == np.float32
             assert inp["w_down_scales"].shape == (wl.E, wl.H // 128, wl.I // 128)
             assert not ((inp["w_up"] & 0x7F) == 0x7F).any()      # no NaN codes
+        elif wl.wfmt == "nvfp4":
+            assert inp["w_up"].shape == (wl.E, wl.n_up, wl.H // 2) and inp["w_up"].dtype == np.uint8
+            assert inp["w_down"].shape == (wl.E, wl.H, wl.I // 2)
+            assert inp["w_up_scales"].shape == (wl.E, wl.n_up, wl.H // 16)
+            assert inp["w_down_scales"].shape == (wl.E, wl.H, wl.I // 16)
+            assert inp["w_up_scales"].dtype == np.uint8
+            assert not (inp["w_up_scales"] & 0x80).any()          # positive scales
+            assert not ((inp["w_up_scales"] & 0x7F) == 0x7F).any()  # never NaN
+            assert inp["w_up_global"].shape == (wl.E,) and inp["w_up_global"].dtype == np.float32
         else:
             assert inp["w_up"].shape == (wl.E, wl.n_up, wl.H // 8)
             assert inp["w_up"].dtype == np.uint32
