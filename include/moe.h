@@ -75,7 +75,7 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
-typedef enum { MOE_W_BF16 = 0, MOE_W_AFFINE4 = 1, MOE_W_FP8 = 2 } moe_wfmt;
+typedef enum { MOE_W_BF16 = 0, MOE_W_AFFINE4 = 1, MOE_W_FP8 = 2, MOE_W_NVFP4 = 3 } moe_wfmt;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out;
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score;
 
@@ -144,6 +144,19 @@ typedef struct {
  *  the MFMA tiles, whose running sums are rescaled at each 128-wide K-block
  *  boundary. With H or I above 8192 a prompt-sized batch decodes the experts
  *  with rows to bf16 (scale * value rounded) in the workspace first.
+ *  For MOE_W_NVFP4 (ModelOpt NVFP4; TensorFold issue #548, the core/quant
+ *  split: uint8 [N, K/2], an e4m3 scale every 16 inputs, a global scale)
+ *  they are uint8 [E, N, K/2], two FP4 E2M1 codes per byte (sign bit 3,
+ *  exponent bits 2..1 with bias 1, mantissa bit 0: magnitudes 0, 0.5, 1,
+ *  1.5, 2, 3, 4, 6), element c of a row in byte c/2, low nibble first (this
+ *  library's stated packing); w_*_scales are OCP E4M3 bytes [E, N, K/16],
+ *  one per 16 inputs; w_up_global / w_down_global are fp32 [E], one per
+ *  expert matrix (the fused gate_up matrix has one); the weight is
+ *  e2m1 * scale * global, and w_*_biases are unused. Every e2m1 * scale
+ *  product is exact in bf16: decode-sized batches stream the codes and
+ *  scale each 16-input partial in fp32, larger ones decode the experts with
+ *  rows to bf16 (exactly) in the workspace; the global scale multiplies
+ *  the fp32 sums of each row.
  *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
  *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared]. */
 typedef struct {
@@ -157,10 +170,13 @@ typedef struct {
     const uint16_t *w_down_biases;
     const uint16_t *shared_up;
     const uint16_t *shared_down;
+    const float *w_up_global;      /* MOE_W_NVFP4: fp32 [E]; otherwise unused */
+    const float *w_down_global;
 } moe_weights;
 
 /* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
- * 4-bit experts and more than 2 E assignments (T * k > 2 E) or row_invariant,
+ * 4-bit or NVFP4 experts and more than 2 E assignments (T * k > 2 E) or
+ * row_invariant,
  * and with block-FP8 experts whose max(H, I) exceeds 8192 (and, at decode
  * sizes, 4096), this includes room for the bf16-decoded weights of every
  * expert that can have rows: min(E, T * k) * max(n_up * H, H * I) * 2 bytes,

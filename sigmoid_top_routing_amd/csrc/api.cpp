@@ -59,7 +59,8 @@ bool decode_sized(const moe_dims &d) {
 bool quant_streams(const moe_dims &d) {
     const int kmax = std::max(d.H, d.I);
     return decode_sized(d) && ((d.wfmt == MOE_W_AFFINE4 && kmax <= moe::kStreamMaxKAffine4) ||
-                               (d.wfmt == MOE_W_FP8 && kmax <= moe::kStreamMaxKFp8));
+                               (d.wfmt == MOE_W_FP8 && kmax <= moe::kStreamMaxKFp8) ||
+                               (d.wfmt == MOE_W_NVFP4 && kmax <= moe::kStreamMaxKNvfp4));
 }
 
 // Block-FP8 experts the persistent MFMA kernel reads at their stored width
@@ -76,7 +77,8 @@ bool fp8_tiles(const moe_dims &d) {
 // in the staged kernel's loads.
 bool dequant_first(const moe_dims &d) {
     return (d.wfmt == MOE_W_AFFINE4 && !decode_sized(d)) ||
-           (d.wfmt == MOE_W_FP8 && !quant_streams(d) && !fp8_tiles(d));
+           (d.wfmt == MOE_W_FP8 && !quant_streams(d) && !fp8_tiles(d)) ||
+           (d.wfmt == MOE_W_NVFP4 && !quant_streams(d));
 }
 
 // The shared expert as m plan segments of the routed experts' width
@@ -177,9 +179,10 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
             "%s: 2*max(I, I_shared)*H reaches 2^31 (one expert's weight matrix)", what);
     REQUIRE(d->act == MOE_ACT_SWIGLU || d->act == MOE_ACT_RELU2, MOE_E_UNSUPPORTED,
             "%s: act = %d, need MOE_ACT_SWIGLU (0) or MOE_ACT_RELU2 (1)", what, d->act);
-    REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_AFFINE4 || d->wfmt == MOE_W_FP8,
-            MOE_E_UNSUPPORTED, "%s: wfmt = %d, need MOE_W_BF16 (0), MOE_W_AFFINE4 (1) or "
-            "MOE_W_FP8 (2)", what, d->wfmt);
+    REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_AFFINE4 || d->wfmt == MOE_W_FP8 ||
+                d->wfmt == MOE_W_NVFP4,
+            MOE_E_UNSUPPORTED, "%s: wfmt = %d, need MOE_W_BF16 (0), MOE_W_AFFINE4 (1), "
+            "MOE_W_FP8 (2) or MOE_W_NVFP4 (3)", what, d->wfmt);
     if (d->wfmt == MOE_W_FP8) {
         REQUIRE(d->H % 128 == 0 && d->I % 128 == 0, MOE_E_SHAPE,
                 "%s: H = %d, I = %d: block-FP8 experts need multiples of 128", what, d->H, d->I);
@@ -378,9 +381,14 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     TRY(check_ptr(what, "w->w_down", w->w_down));
     const bool aff = d->wfmt == MOE_W_AFFINE4;
     const bool fp8 = d->wfmt == MOE_W_FP8;
-    if (fp8) {
+    const bool nv4 = d->wfmt == MOE_W_NVFP4;
+    if (fp8 || nv4) {
         TRY(check_ptr(what, "w->w_up_scales", w->w_up_scales));
         TRY(check_ptr(what, "w->w_down_scales", w->w_down_scales));
+    }
+    if (nv4) {
+        REQUIRE(w->w_up_global != nullptr && w->w_down_global != nullptr, MOE_E_NULL,
+                "%s: NVFP4 experts need w->w_up_global and w->w_down_global", what);
     }
     if (aff) {
         TRY(check_ptr(what, "w->w_up_scales", w->w_up_scales));
@@ -406,16 +414,18 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     // (the static scratch is a device global, not an allocation the
     // runtime's pointer query knows)
     const void *dev[] = {x, out, workspace_is_scratch ? nullptr : workspace, w->router_w, w->expert_bias, w->w_up, w->w_down,
-                         aff || fp8 ? w->w_up_scales : nullptr, aff ? w->w_up_biases : nullptr,
-                         aff || fp8 ? w->w_down_scales : nullptr,
+                         aff || fp8 || nv4 ? w->w_up_scales : nullptr, aff ? w->w_up_biases : nullptr,
+                         aff || fp8 || nv4 ? w->w_down_scales : nullptr,
                          aff ? w->w_down_biases : nullptr,
                          d->I_shared ? w->shared_up : nullptr,
                          d->I_shared ? w->shared_down : nullptr, ids_out, weights_out,
-                         offsets_out};
+                         offsets_out, nv4 ? w->w_up_global : nullptr,
+                         nv4 ? w->w_down_global : nullptr};
     const char *dev_names[] = {"x", "out", "workspace", "w->router_w", "w->expert_bias",
                                "w->w_up", "w->w_down", "w->w_up_scales", "w->w_up_biases",
                                "w->w_down_scales", "w->w_down_biases", "w->shared_up",
-                               "w->shared_down", "ids_out", "weights_out", "offsets_out"};
+                               "w->shared_down", "ids_out", "weights_out", "offsets_out",
+                               "w->w_up_global", "w->w_down_global"};
     for (size_t i = 0; i < sizeof dev / sizeof dev[0]; ++i)
         TRY(check_device(what, dev_names[i], dev[i]));
 
@@ -461,6 +471,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     up.mode = d->act == MOE_ACT_SWIGLU ? gate_mode : moe::kUpRelu2;
     up.affine4 = aff;
     up.fp8 = d->wfmt == MOE_W_FP8;
+    up.nvfp4 = nv4;
+    up.Bglobal = nv4 ? w->w_up_global : nullptr;
     up.A = x;
     up.lda = H;
     up.gather = sorted;
@@ -492,6 +504,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     auto dequantized = [&](moe::GemmProblem g) {
         g.affine4 = 0;
         g.fp8 = 0;
+        g.nvfp4 = 0;                 // (an NVFP4 global scale stays in Bglobal)
         g.B = wdq;
         g.Bscale = nullptr;
         g.Bbias = nullptr;
@@ -511,6 +524,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     down.mode = moe::kDown;
     down.affine4 = aff;
     down.fp8 = up.fp8;
+    down.nvfp4 = nv4;
+    down.Bglobal = nv4 ? w->w_down_global : nullptr;
     down.A = h;
     down.lda = I;
     down.offsets = seg_off;

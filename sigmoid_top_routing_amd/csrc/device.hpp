@@ -55,6 +55,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return pack_bf16x2(f, 0.0f) & 0xffffu;
 }
 
+// The four bytes of w, each two FP4 E2M1 codes (low nibble first), as four
+// bf16 pairs: gfx950's v_cvt_scalef32_pk_bf16_fp4 with scale 1, which gives
+// every E2M1 value exactly (checked on all 256 bytes in each byte position,
+// -0 kept). The byte select is an immediate, hence the four spelled-out calls.
+__device__ __forceinline__ void fp4_pairs(uint32_t w, uint32_t (&pr)[4]) {
+    pr[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0));
+    pr[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1));
+    pr[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2));
+    pr[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3));
+}
+
 // e^v in fp32 for v in [-17, 87]: v = n ln2 + r with n = rint(v log2 e)
 // and a two-part ln2 (the high part has nine zero low bits), then the
 // Taylor polynomial of e^r to degree 7 in Horner form and a scaling by 2^n.

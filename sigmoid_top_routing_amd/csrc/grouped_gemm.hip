@@ -699,6 +699,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         }
         const int half = lane >> 5;          // which 4 of each 8 columns the lane holds
         const int prow = lane & 31;          // the row the lane holds
+        // a per-expert scale of the sums (NVFP4's global scale), uniform
+        const bool gscaled = !F8 && p.Bglobal != nullptr && e < p.E;
+        const float gsc = gscaled ? p.Bglobal[e] : 1.0f;
         const int span_rows = min(row_end - row0, BM);
         const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             (char *)p.C + (size_t)row0 * (size_t)p.ldc * kElt, (short)0,
@@ -710,7 +713,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
                     // F8: the finished sum in units of the last block's scale
-                    const f32x16 v = F8 ? acc[i][j] * rho_gate : acc[i][j];
+                    f32x16 v = F8 ? acc[i][j] * rho_gate : acc[i][j];
+                    if (gscaled)
+                        v = v * gsc;
                     // 32 rows x 32 fp32: row r at r * 128 bytes, 8 chunks of 4
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
@@ -769,6 +774,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                                                      : "=v"(uv[r])
                                                      : "a"(acc[i][j + TN / 2][r]));
                             }
+                        }
+                        if (gscaled) {
+                            gv = gv * gsc;
+                            if (gated(MODE))
+                                uv = uv * gsc;
                         }
 #pragma unroll
                         for (int c = 0; c < 8; ++c) {
@@ -933,7 +943,7 @@ bool grouped_supported(const GemmProblem &p) {
     const bool e2_ok = p.E2 == 0 ||
                        (p.E2 > 0 && !p.fp8 && p.offsets != nullptr && p.B2 != nullptr &&
                         b2_rows * p.b2_ld * 2 < (long long)kPastA && p.b2_ld >= p.K);
-    return !p.affine4 && fp8_ok && e2_ok && p.scatter == nullptr && p.K % kBK == 0 &&
+    return !p.affine4 && !p.nvfp4 && fp8_ok && e2_ok && p.scatter == nullptr && p.K % kBK == 0 &&
            p.K / kBK >= kStagesSmall && (p.offsets == nullptr || p.E + p.E2 <= kMaxE) &&
            a_rows * p.lda * 2 < (long long)kPastA &&
            (long long)p.N * p.K * (p.fp8 ? 1 : 2) < (long long)kPastA;

@@ -52,6 +52,9 @@ struct GemmProblem {
     int fp8;                  // B is block-FP8 e4m3 (bytes + fp32 scale per 128 x 128 block):
                               // the persistent kernel (grouped_supported), the stream
                               // (stream_supported) or launch_dequant reads it
+    int nvfp4;                // B is NVFP4: e2m1 codes [E][N][K/2] (low nibble first), an
+                              // e4m3 scale byte per 16 inputs [E][N][K/16]: the stream or
+                              // launch_dequant reads it
     const uint16_t *A;        // bf16 rows, lda elements apart
     int lda;
     const int32_t *gather;    // A row of position p = gather[p] / gather_div (NULL: row p)
@@ -80,14 +83,20 @@ struct GemmProblem {
     int b2_ld;
     int b2_up;
     long long b2_vstride;
+    // Per-expert fp32 scale of the sums (NVFP4's global scale; NULL: none),
+    // applied before the epilogue, indexed by expert (not by compact rank);
+    // the persistent kernel and the quantized stream apply it.
+    const float *Bglobal;
 };
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
 
-// The 4-bit (p.affine4) or block-FP8 (p.fp8) weights of p's experts that
-// have rows (offsets set), decoded once to bf16 (scale * q + bias, or
-// scale * e4m3 value, in fp32, rounded to nearest even) into out:
-// [experts with rows][N][K], in expert order (b_compact).
+// The 4-bit (p.affine4), block-FP8 (p.fp8) or NVFP4 (p.nvfp4) weights of
+// p's experts that have rows (offsets set), decoded once to bf16 (scale * q
+// + bias, scale * e4m3 value, or e4m3 scale * e2m1 value, in fp32, rounded
+// to nearest even; the NVFP4 product is exact in bf16 and its global scale
+// is left to Bglobal) into out: [experts with rows][N][K], in expert order
+// (b_compact).
 hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream);
 
 // The persistent direct-to-LDS kernel (bf16 weights, K a multiple of 32 and
@@ -103,6 +112,7 @@ hipError_t launch_grouped_f8(const GemmProblem &p, hipStream_t stream);
 // lane: 8192 4-bit weights, 4096 FP8 weights).
 constexpr int kStreamMaxKAffine4 = 8192;
 constexpr int kStreamMaxKFp8 = 4096;
+constexpr int kStreamMaxKNvfp4 = 8192;
 bool stream_supported(const GemmProblem &p);
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream);
 

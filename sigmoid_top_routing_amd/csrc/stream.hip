@@ -226,13 +226,20 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
 //   FP8:    w = s v, and sum_c w_c x_c = s (sum_c v_c x_c): every E4M3 value
 //           is a bf16 value, so v is converted exactly (two per
 //           instruction) and the sum is a v_dot2_f32_bf16 chain.
+//   NVFP4:  32 E2M1 codes per lane and step (16 bytes), two 16-wide groups
+//           with an E4M3 scale each: w = s_g v G, and the lane adds
+//           s_0 (sum over group 0 of v x) + s_1 (sum over group 1), v
+//           converted exactly (v_cvt_scalef32_pk_bf16_fp4, two per
+//           instruction); the expert's global scale G multiplies the
+//           reduced sum.
 // The lane partials are then reduced across the wave as in k_stream.
 constexpr int kFmtAffine4 = 1;
 constexpr int kFmtFp8 = 2;
+constexpr int kFmtNvfp4 = 3;
 
 template <int FMT>
 struct QFmt {
-    static constexpr int EPL = FMT == kFmtAffine4 ? 32 : 16;   // weights per lane per step
+    static constexpr int EPL = FMT == kFmtFp8 ? 16 : 32;       // weights per lane per step
     static constexpr int EPJ = EPL * kWave;                    // weights per wave per step
     static constexpr int CPL = EPL / 8;                        // 16-byte x chunks per lane
 };
@@ -323,15 +330,24 @@ __global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
                 const bool in = u < units && kk < K;
                 sc[i][s][j] = 0.0f;
                 bi[i][s][j] = 0.0f;
-                if (FMT == kFmtAffine4) {
+                if (FMT == kFmtAffine4 || FMT == kFmtNvfp4) {
                     const uint8_t *row = (const uint8_t *)p.B + (erow + n) * (size_t)(K / 2);
                     w[i][s][j] = in ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
                                           reinterpret_cast<const u32x4 *>(row + kk / 2)))
                                     : make_uint4(0, 0, 0, 0);
-                    if (in) {
+                    if (in && FMT == kFmtAffine4) {
                         const size_t g = (erow + n) * (size_t)(K / 64) + kk / 64;
                         sc[i][s][j] = bf16_to_f32(p.Bscale[g]);
                         bi[i][s][j] = bf16_to_f32(p.Bbias[g]);
+                    } else if (in) {
+                        // the E4M3 scales of the lane's two 16-wide groups
+                        // (sc: group 0, bi: group 1)
+                        const uint32_t two = *reinterpret_cast<const uint16_t *>(
+                            (const uint8_t *)p.Bscale + (erow + n) * (size_t)(K / 16) + kk / 16);
+                        const uint32_t pr = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(two, 1.0f, false));
+                        sc[i][s][j] = bf16_to_f32(pr & 0xffffu);
+                        bi[i][s][j] = bf16_to_f32(pr >> 16);
                     }
                 } else {
                     const uint8_t *row = (const uint8_t *)p.B + (erow + n) * (size_t)K;
@@ -386,6 +402,13 @@ __global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
 #pragma unroll
                             for (int b = 0; b < 4; ++b)
                                 pr[i][s][4 * q + b] = four[b];
+                        } else if constexpr (FMT == kFmtNvfp4) {
+                            // byte b: codes 2b (low nibble) and 2b + 1
+                            uint32_t four[4];
+                            fp4_pairs(cw[q], four);
+#pragma unroll
+                            for (int b = 0; b < 4; ++b)
+                                pr[i][s][4 * q + b] = four[b];
                         } else {
                             pr[i][s][2 * q] = __builtin_bit_cast(
                                 uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(cw[q], 1.0f, false));
@@ -414,6 +437,23 @@ __global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
                     for (int i = 0; i < UW; ++i)
 #pragma unroll
                         for (int s = 0; s < NR; ++s) {
+                            if constexpr (FMT == kFmtNvfp4) {
+                                // chunks 0, 1: group 0; chunks 2, 3: group 1
+                                float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+                                for (int c = 0; c < 2; ++c)
+                                    a0 = dot8(make_uint4(pr[i][s][4 * c], pr[i][s][4 * c + 1],
+                                                         pr[i][s][4 * c + 2], pr[i][s][4 * c + 3]),
+                                              xv[c], a0);
+#pragma unroll
+                                for (int c = 2; c < 4; ++c)
+                                    a1 = dot8(make_uint4(pr[i][s][4 * c], pr[i][s][4 * c + 1],
+                                                         pr[i][s][4 * c + 2], pr[i][s][4 * c + 3]),
+                                              xv[c], a1);
+                                v[i][r * NR + s] += sc[i][s][j] * a0;
+                                v[i][r * NR + s] += bi[i][s][j] * a1;
+                                continue;
+                            }
                             float a = 0.0f;
 #pragma unroll
                             for (int c = 0; c < Q::CPL; ++c)
@@ -429,10 +469,17 @@ __global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
                 }
             }
         }
+        // the expert's global scale of the sums (NVFP4), uniform
+        const float G = (FMT == kFmtNvfp4 && p.Bglobal != nullptr) ? p.Bglobal[e] : 1.0f;
 #pragma unroll
         for (int i = 0; i < UW; ++i) {
             const int u = ub + i;
             transpose_reduce<kTG * NR, NR>(v[i], lane);
+            if constexpr (FMT == kFmtNvfp4) {
+#pragma unroll
+                for (int q = 0; q < NR; ++q)
+                    v[i][q] *= G;
+            }
             const int r = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
             if ((lane & 15) == 0 && r < nr && u < units) {
                 const int pos = g0 + r;
@@ -504,8 +551,10 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 }  // namespace
 
 bool stream_supported(const GemmProblem &p) {
-    if (p.b_compact || p.scatter != nullptr || p.E2 > 0)
+    if (p.b_compact || p.scatter != nullptr || p.E2 > 0 || (p.Bglobal != nullptr && !p.nvfp4))
         return false;
+    if (p.nvfp4)        // 4 code words per lane and step; groups of 16
+        return p.K % 32 == 0 && p.K <= kStreamMaxKNvfp4;
     static_assert(kStreamMaxKAffine4 == 4 * QFmt<kFmtAffine4>::EPJ, "4-bit steps");
     static_assert(kStreamMaxKFp8 == 4 * QFmt<kFmtFp8>::EPJ, "FP8 steps");
     if (p.affine4)      // 4 code words per lane and step; groups of 64
@@ -520,6 +569,8 @@ hipError_t launch_stream(const GemmProblem &p, hipStream_t stream) {
         return launch_q_fmt<kFmtAffine4>(p, stream);
     if (p.fp8)
         return launch_q_fmt<kFmtFp8>(p, stream);
+    if (p.nvfp4)
+        return launch_q_fmt<kFmtNvfp4>(p, stream);
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp>(p, stream);
     case kGateUpLimit: return launch_mode<kGateUpLimit>(p, stream);

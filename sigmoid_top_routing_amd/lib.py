@@ -20,7 +20,7 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_ALIGN",
           -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
 ACT = {"swiglu": 0, "relu2": 1}
-WFMT = {"bf16": 0, "affine4": 1, "fp8": 2}
+WFMT = {"bf16": 0, "affine4": 1, "fp8": 2, "nvfp4": 3}
 OUT = {torch.bfloat16: 0, torch.float32: 1}
 SCORE = {"sigmoid": 0, "softmax": 1}
 
@@ -50,7 +50,8 @@ class Dims(C.Structure):
 class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "router_w", "expert_bias", "w_up", "w_up_scales", "w_up_biases", "w_down",
-        "w_down_scales", "w_down_biases", "shared_up", "shared_down")]
+        "w_down_scales", "w_down_biases", "shared_up", "shared_down", "w_up_global",
+        "w_down_global")]
 
 
 _lib = None
@@ -181,6 +182,8 @@ class MoEBlock:
     w_up_biases: torch.Tensor | None = None
     w_down_scales: torch.Tensor | None = None
     w_down_biases: torch.Tensor | None = None
+    w_up_global: torch.Tensor | None = None      # NVFP4: fp32 [E]
+    w_down_global: torch.Tensor | None = None
     shared_up: torch.Tensor | None = None
     shared_down: torch.Tensor | None = None
     act: str = "swiglu"
@@ -211,13 +214,14 @@ class MoEBlock:
     def _weight_ptrs(self):
         return (_ptr(self.router_w), _ptr(self.bias), _ptr(self.w_up), _ptr(self.w_up_scales),
                 _ptr(self.w_up_biases), _ptr(self.w_down), _ptr(self.w_down_scales),
-                _ptr(self.w_down_biases), _ptr(self.shared_up), _ptr(self.shared_down))
+                _ptr(self.w_down_biases), _ptr(self.shared_up), _ptr(self.shared_down),
+                _ptr(self.w_up_global), _ptr(self.w_down_global))
 
     def weights(self) -> Weights:
-        (rw, b, wu, wus, wub, wd, wds, wdb, su, sd) = self._weight_ptrs()
+        (rw, b, wu, wus, wub, wd, wds, wdb, su, sd, ug, dg) = self._weight_ptrs()
         return Weights(router_w=rw, expert_bias=b, w_up=wu, w_up_scales=wus, w_up_biases=wub,
                        w_down=wd, w_down_scales=wds, w_down_biases=wdb, shared_up=su,
-                       shared_down=sd)
+                       shared_down=sd, w_up_global=ug, w_down_global=dg)
 
     def _marshalled(self, T, out_dtype):
         """(dims, weights, workspace bytes) of a call: built once per shape,
@@ -305,12 +309,15 @@ def block_from_arrays(wl, inp: dict, device="cuda") -> MoEBlock:
         return t.view(torch.bfloat16) if as_bf16 else t
     aff = wl.wfmt == "affine4"
     fp8 = wl.wfmt == "fp8"
+    nv4 = wl.wfmt == "nvfp4"
+    quant = aff or fp8 or nv4
     return MoEBlock(H=wl.H, I=wl.I, E=wl.E, k=wl.k, router_w=dev("router_w"), bias=dev("bias"),
-                    w_up=dev("w_up", not (aff or fp8)), w_down=dev("w_down", not (aff or fp8)),
-                    w_up_scales=dev("w_up_scales", not fp8),
+                    w_up=dev("w_up", not quant), w_down=dev("w_down", not quant),
+                    w_up_scales=dev("w_up_scales", aff),
                     w_up_biases=dev("w_up_biases", True),
-                    w_down_scales=dev("w_down_scales", not fp8),
+                    w_down_scales=dev("w_down_scales", aff),
                     w_down_biases=dev("w_down_biases", True),
+                    w_up_global=dev("w_up_global"), w_down_global=dev("w_down_global"),
                     shared_up=dev("shared_up", True), shared_down=dev("shared_down", True),
                     act=wl.act, wfmt=wl.wfmt, rsf=wl.rsf, I_shared=wl.I_shared,
                     norm_topk=wl.norm_topk, norm_eps=wl.norm_eps, score=wl.score,

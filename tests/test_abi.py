@@ -126,6 +126,14 @@ def test_unsupported_options_are_refused():
     rc, n_stream = ws_bytes(dims(wfmt="affine4", T=8, H=256, I=256, E=8, k=2))
     rc1, n_tiles = ws_bytes(dims(wfmt="affine4", T=8, H=256, I=256, E=8, k=2, row_invariant=True))
     assert rc == rc1 == 0 and n_tiles >= n_stream + 8 * 512 * 256 * 2
+    # NVFP4: decode-sized batches stream the codes (no more than bf16); a
+    # prompt-sized batch decodes its experts to bf16 first
+    rc, nq = ws_bytes(dims(wfmt="nvfp4", T=8, H=256, I=256, E=8, k=2))
+    rc16, n16 = ws_bytes(dims(T=8, H=256, I=256, E=8, k=2))
+    assert rc == rc16 == 0 and nq == n16
+    rc, nq = ws_bytes(dims(wfmt="nvfp4", T=64, H=256, I=256, E=8, k=2))
+    rc16, n16 = ws_bytes(dims(T=64, H=256, I=256, E=8, k=2))
+    assert rc == rc16 == 0 and nq >= n16 + 8 * 512 * 256 * 2
     assert ws_bytes(dims(score="softmax"))[0] == 0
     assert ws_bytes(dims(wfmt="fp8", H=192))[0] == -2
     assert "multiples of 128" in lib.load().moe_last_error().decode()
@@ -187,6 +195,13 @@ def test_forward_refuses_null_misaligned_and_short_workspace():
     rc = L.moe_forward(C.byref(da), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
                        1 << 30, None, None, None, None)
     assert rc == -1 and "scales" in L.moe_last_error().decode()
+    # NVFP4 weights without their global scales
+    dn = dims(wfmt="nvfp4")
+    wn = lib.Weights(router_w=0x1000, w_up=0x2000, w_down=0x3000, w_up_scales=0x4000,
+                     w_down_scales=0x5000)
+    rc = L.moe_forward(C.byref(dn), C.byref(wn), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       1 << 30, None, None, None, None)
+    assert rc == -1 and "w_up_global" in L.moe_last_error().decode()
     # a shared expert without its weights
     ds = dims(I_shared=64)
     rc = L.moe_forward(C.byref(ds), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),

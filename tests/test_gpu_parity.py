@@ -7,10 +7,11 @@ stated acceptance):
   * weights: NaN in the same places, elsewhere |gpu - ref| <= 1e-6 |ref|
     (fp32 with at most k + 2 roundings against float64);
   * outputs: NaN in the same places; over the finite entries
-    max |gpu - ref| <= 2e-2 rms(ref) for bf16 and block-FP8 experts (e4m3
-    values are bf16 values and the block scales multiply fp32 sums, so the
-    weights are exact) and 5e-2 rms(ref) for 4-bit experts (decoded to bf16
-    at prompt sizes). Block-FP8 codes over a wide range (mid_fp8_wide) reach
+    max |gpu - ref| <= 2e-2 rms(ref) for bf16, block-FP8 and NVFP4 experts
+    (e4m3 values are bf16 values and the block scales multiply fp32 sums; an
+    e2m1 value times its e4m3 scale is exact in bf16 and the global scale
+    multiplies fp32 sums: the weights are exact) and 5e-2 rms(ref) for 4-bit
+    experts (decoded to bf16 at prompt sizes). Block-FP8 codes over a wide range (mid_fp8_wide) reach
     4.3 % of rms through the bf16 activation between the projections alone
     (the stored intermediate of every format; an emulation with exact
     weights and that one rounding gives 4.27 %): they are held to 2e-2
@@ -410,6 +411,7 @@ DECODE_CASES = [("tiny_t64_e8_k2", 8), ("tiny_t64_e8_k2", 1), ("mid_swiglu", 8),
                 ("mid_affine4", 8), ("mid_affine4", 1),
                 ("mid_affine4_relu2", 8), ("mid_affine4_relu2", 3), ("mid_affine4_i64", 8),
                 ("mid_relu2_nonfinite", 8), ("mid_relu2_shared_seg", 8),
+                ("mid_nvfp4", 8), ("mid_nvfp4", 1), ("mid_nvfp4_relu2", 8),
                 ("mid_swiglu_shared_seg3", 8), ("mid_affine4_shared_seg", 8)]
 
 
