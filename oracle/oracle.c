@@ -379,6 +379,19 @@ static unsigned fp4_code(const uint8_t *row, int c)
     return (row[c / 2] >> (4 * (c % 2))) & 15u;
 }
 
+/* An OCP MX E8M0 scale byte: 2^(b - 127); 0xFF is NaN. MXFP4 experts (the
+ * MX formats the pages name beside NVFP4) hold one per 32 E2M1 codes. */
+static double e8m0_value(uint8_t b)
+{
+    return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+void oracle_e8m0_decode(const uint8_t *bytes, int n, double *out)
+{
+    for (int i = 0; i < n; ++i)
+        out[i] = e8m0_value(bytes[i]);
+}
+
 void oracle_fp4_decode(const uint8_t *bytes, int n, double *out)
 {
     for (int i = 0; i < n; ++i)
@@ -401,6 +414,12 @@ static void weight_row(const oracle_layer *L, int is_up, int e, int n, int N, in
         const double g = (double)(is_up ? L->w_up_global : L->w_down_global)[e];
         for (int c = 0; c < K; ++c)
             row[c] = fp4_e2m1_value(fp4_code(codes, c)) * fp8_e4m3_value(sc[c / 16]) * g;
+    } else if (L->wfmt == 4) {
+        /* MXFP4: weight = e2m1 code x the E8M0 scale of its 32 inputs */
+        const uint8_t *codes = (const uint8_t *)(is_up ? L->w_up : L->w_down) + r * (K / 2);
+        const uint8_t *sc = (const uint8_t *)(is_up ? L->w_up_scales : L->w_down_scales) + r * (K / 32);
+        for (int c = 0; c < K; ++c)
+            row[c] = fp4_e2m1_value(fp4_code(codes, c)) * e8m0_value(sc[c / 32]);
     } else if (L->wfmt == 2) {
         /* one fp32 scale per 128 x 128 block of the expert's [N, K] matrix */
         const uint8_t *codes = (const uint8_t *)(is_up ? L->w_up : L->w_down) + r * K;

@@ -76,6 +76,7 @@ def lib():
         L.oracle_add_rmsnorm.argtypes = [i, i, p, p, p, C.c_double, p, p]
         L.oracle_fp8_decode.argtypes = [p, i, p]
         L.oracle_fp4_decode.argtypes = [p, i, p]
+        L.oracle_e8m0_decode.argtypes = [p, i, p]
         L.oracle_plan.argtypes = [i, i, i, p, p, p, p, p]
         L.oracle_forward_tokens.argtypes = [C.POINTER(Layer), p, i, p, p, p, i]
         L.oracle_forward_tokens.restype = C.c_int
@@ -185,12 +186,12 @@ def _layer(wl, inp: dict, keep: dict, round_h: bool = False) -> Layer:
 
     affine = wl.wfmt == "affine4"
     fp8 = wl.wfmt == "fp8"
-    nvfp4 = wl.wfmt == "nvfp4"
-    code_t = np.uint32 if affine else np.uint8 if (fp8 or nvfp4) else np.uint16
-    scale_t = np.float32 if fp8 else np.uint8 if nvfp4 else np.uint16
+    fp4 = wl.wfmt in ("nvfp4", "mxfp4")
+    code_t = np.uint32 if affine else np.uint8 if (fp8 or fp4) else np.uint16
+    scale_t = np.float32 if fp8 else np.uint8 if fp4 else np.uint16
     return Layer(T=wl.T, H=wl.H, I=wl.I, E=wl.E, k=wl.k,
                  act=0 if wl.act == "swiglu" else 1,
-                 wfmt={"bf16": 0, "affine4": 1, "fp8": 2, "nvfp4": 3}[wl.wfmt],
+                 wfmt={"bf16": 0, "affine4": 1, "fp8": 2, "nvfp4": 3, "mxfp4": 4}[wl.wfmt],
                  group=wl.group if affine else 0, norm_topk=int(wl.norm_topk),
                  I_shared=wl.I_shared, norm_eps=wl.norm_eps, rsf=wl.rsf,
                  x=arr("x", np.uint16), router_w=arr("router_w", np.float32),
@@ -322,4 +323,12 @@ def fp4_decode(packed, n: int) -> np.ndarray:
     assert 0 <= n <= 2 * packed.size
     out = np.empty(n, dtype=np.float64)
     lib().oracle_fp4_decode(_ptr(packed), n, _ptr(out))
+    return out
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """OCP MX E8M0 scale bytes -> float64: 2^(b - 127), 0xFF NaN."""
+    codes = _c(np.atleast_1d(codes), np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    lib().oracle_e8m0_decode(_ptr(codes), codes.size, _ptr(out))
     return out

@@ -80,6 +80,9 @@ class Workload:
     fp8_nan: tuple = ()               # (expert, row) of w_down rows holding one e4m3 NaN
     global_lo: float = 3e-5           # NVFP4: global scale of each expert matrix, U(lo, hi)
     global_hi: float = 8e-5
+    mx_exp_mu: float = 120.0          # MXFP4: E8M0 scale byte round(N(mu, sd))
+    mx_exp_sd: float = 1.0
+    mx_nan: tuple = ()                # (expert, row) of w_down rows with one NaN scale (0xFF)
     qbias_lo: float = -0.1
     qbias_hi: float = 0.1
     group: int = 64
@@ -172,6 +175,14 @@ MID = {
                           I_shared=128, seed=119),
     "mid_nvfp4_relu2": Workload("mid_nvfp4_relu2", T=200, H=256, I=384, E=24, k=6, act="relu2",
                                 wfmt="nvfp4", rsf=2.5, seed=120),
+    # MXFP4 experts (the OCP MX format: E2M1 codes, an E8M0 scale every 32
+    # inputs), relu^2 with a NaN scale in two down rows, and SwiGLU with a
+    # bf16 shared expert.
+    "mid_mxfp4": Workload("mid_mxfp4", T=300, H=384, I=256, E=16, k=4, wfmt="mxfp4",
+                          I_shared=128, seed=123),
+    "mid_mxfp4_relu2": Workload("mid_mxfp4_relu2", T=200, H=256, I=384, E=24, k=6,
+                                act="relu2", wfmt="mxfp4", rsf=2.5, seed=124,
+                                mx_nan=((1, 7), (5, 130))),
     # The softmax router family (TensorFold issue #548, the consolidation
     # proposal), with NaN rows and exact ties, over 64 experts.
     # No expert bias (the family has none): every score of an all-zero row
@@ -201,6 +212,8 @@ EXTRA = {
                                          E=32, k=4, wfmt="nvfp4", seed=121),
     "lfm2_nvfp4_decode_t8": Workload("lfm2_nvfp4_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
                                      wfmt="nvfp4", seed=122, weight_seed=121),
+    "lfm2_mxfp4_decode_t8": Workload("lfm2_mxfp4_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
+                                     wfmt="mxfp4", seed=125),
     "lfm2_fp8_decode_t8": Workload("lfm2_fp8_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
                                    wfmt="fp8", scale_lo=1e-4, scale_hi=3e-4, seed=112,
                                    weight_seed=111),
@@ -374,6 +387,20 @@ def generate(wl: Workload, need_x: bool = True, experts: bool = True) -> dict:
                                             wl.fp8_exp_sd)
         out["w_up_global"] = _uniform_f32(ws[c_qb], (E,), wl.global_lo, wl.global_hi)
         out["w_down_global"] = _uniform_f32(ws[c_qb], (E,), wl.global_lo, wl.global_hi)
+    elif wl.wfmt == "mxfp4":
+        # codes as NVFP4; per 32 inputs an E8M0 scale 2^(b - 127)
+        out["w_up"] = _bytes(ws[c_codes], (E, n_up, H // 2))
+        out["w_down"] = _bytes(ws[c_codes], (E, H, I // 2))
+
+        def e8m0(rng, shape):
+            n = int(np.prod(shape))
+            b = np.rint(rng.standard_normal(n, dtype=np.float32) * np.float32(wl.mx_exp_sd) +
+                        np.float32(wl.mx_exp_mu))
+            return np.clip(b, 1, 254).astype(np.uint8).reshape(shape)
+        out["w_up_scales"] = e8m0(ws[c_scales], (E, n_up, H // 32))
+        out["w_down_scales"] = e8m0(ws[c_scales], (E, H, I // 32))
+        for e, h in wl.mx_nan:
+            out["w_down_scales"][e, h, (3 * h + e) % (I // 32)] = 0xFF
     elif wl.wfmt == "fp8":
         mu, sd = wl.fp8_exp_mu, wl.fp8_exp_sd
         out["w_up"] = _fp8_codes(ws[c_codes], (E, n_up, H), mu, sd)

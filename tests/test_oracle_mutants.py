@@ -149,6 +149,15 @@ MUTANTS = {
     "nvfp4_global_dropped": (
         "fp8_e4m3_value(sc[c / 16]) * g;", "fp8_e4m3_value(sc[c / 16]);",
         ["tests/test_oracle_nvfp4.py::test_hand_layer"]),
+    "mxfp4_group_16": (
+        "e8m0_value(sc[c / 32]);", "e8m0_value(sc[c / 16]);",
+        ["tests/test_oracle_nvfp4.py::test_mxfp4_layer_matches_dense_float64"]),
+    "e8m0_bias_128": (
+        "ldexp(1.0, (int)b - 127);", "ldexp(1.0, (int)b - 128);",
+        ["tests/test_oracle_nvfp4.py::test_e8m0_hand_values"]),
+    "e8m0_no_nan": (
+        "return b == 0xFF ? NAN : ldexp", "return b == 0x1FF ? NAN : ldexp",
+        ["tests/test_oracle_nvfp4.py::test_e8m0_hand_values"]),
     "round_h_ignored": (
         "return L->round_h ? (double)bf16_value(bf16_round((float)h)) : h;", "return h;",
         ["tests/test_oracle_round_h.py::test_round_h_hand_values_routed_and_shared"]),

@@ -109,3 +109,86 @@ def test_nvfp4_layer_matches_dense_float64(name):
             sd = W.bf16_bits_to_f32(inp["shared_down"]).astype(np.float64)
             ref[i] += sd @ act(su @ x[i], wl.I_shared)
     assert np.allclose(out, ref, rtol=1e-10, atol=1e-12 * np.abs(ref).max())
+
+
+# ---------------------------------------------------------------- MXFP4
+# OCP MX: the same E2M1 codes with an E8M0 scale every 32 inputs,
+# 2^(b - 127), 0xFF NaN, and no global scale.
+
+def test_e8m0_hand_values():
+    got = oracle.e8m0_decode(np.array([127, 128, 120, 1, 0, 254, 255], np.uint8))
+    assert got[:6].tolist() == [1.0, 2.0, 2.0 ** -7, 2.0 ** -126, 2.0 ** -127, 2.0 ** 127]
+    assert np.isnan(got[6])
+
+
+def test_mxfp4_hand_layer():
+    H = I = 64
+    wl = W.Workload("pin_mxfp4", T=2, H=H, I=I, E=2, k=1, act="relu2", wfmt="mxfp4",
+                    norm_topk=False)
+    x = np.zeros((2, H), np.float32)
+    x[:, 0] = 1.0
+    router = np.zeros((2, H), np.float32)
+    router[1, 0] = -1.0
+    w_up = np.zeros((2, I, H // 2), np.uint8)
+    w_down = np.zeros((2, H, I // 2), np.uint8)
+    up_sc = np.full((2, I, H // 32), 127, np.uint8)
+    down_sc = np.full((2, H, I // 32), 127, np.uint8)
+    w_up[0, 0, 0] = 0x05                          # 3.0
+    up_sc[0, 0, 0] = 126                          # x 1/2 = 1.5; relu^2 2.25
+    w_down[0, 0, 0] = 0x02                        # 1.0
+    down_sc[0, 0, 0] = 125                        # x 1/4
+    down_sc[0, 0, 1] = 255                        # NaN scale on inputs 32..63 of down row 0
+    up_sc[0, 1, 1] = 255                          # and on up row 1, inputs 32..63
+    inp = {"x": W.f32_to_bf16_bits(x), "router_w": router, "bias": np.zeros(2, np.float32),
+           "w_up": w_up, "w_down": w_down, "w_up_scales": up_sc, "w_down_scales": down_sc}
+    out = oracle.forward_tokens(wl, inp, np.arange(2))
+    # up row 1 is NaN (NaN scale x 0 codes), so down row 0 and every other
+    # down row meet a NaN activation: every output is NaN ...
+    assert np.isnan(out).all()
+    # ... and without the NaN scales the one path is worked out by hand
+    up_sc[0, 1, 1] = 127
+    down_sc[0, 0, 1] = 127
+    out = oracle.forward_tokens(wl, inp, np.arange(2))
+    expect = np.zeros((2, wl.H))
+    expect[:, 0] = 0.5 * 0.25 * 1.5 ** 2
+    assert (out == expect).all()
+
+
+@pytest.mark.parametrize("name", ["mid_mxfp4", "mid_mxfp4_relu2"])
+def test_mxfp4_layer_matches_dense_float64(name):
+    wl = W.by_name(name)
+    inp = W.generate(wl)
+    toks = np.arange(12)
+    out, ids, w = oracle.forward_tokens(wl, inp, toks, want_routing=True)
+
+    def dense(codes, scales):
+        v = _np_fp4(codes, 2 * codes.shape[2])
+        s = np.where(scales == 255, np.nan, np.ldexp(1.0, scales.astype(np.int64) - 127))
+        return v * np.repeat(s, 32, axis=2)
+
+    wu = dense(inp["w_up"], inp["w_up_scales"])
+    wd = dense(inp["w_down"], inp["w_down_scales"])
+    x = W.bf16_bits_to_f32(inp["x"][toks]).astype(np.float64)
+
+    def act(p, n):
+        if wl.act == "swiglu":
+            g, u = p[:n], p[n:]
+            return g / (1.0 + np.exp(-g)) * u
+        r = np.where(p < 0, 0.0, p)
+        return r * r
+
+    ref = np.zeros((toks.size, wl.H))
+    for i in range(toks.size):
+        for j in range(wl.k):
+            e = ids[i, j]
+            ref[i] += w[i, j] * (wd[e] @ act(wu[e] @ x[i], wl.I))
+        ref[i] *= wl.rsf
+        if wl.I_shared:
+            su = W.bf16_bits_to_f32(inp["shared_up"]).astype(np.float64)
+            sd = W.bf16_bits_to_f32(inp["shared_down"]).astype(np.float64)
+            ref[i] += sd @ act(su @ x[i], wl.I_shared)
+    nan = np.isnan(ref)
+    assert (np.isnan(out) == nan).all()
+    if wl.mx_nan:
+        assert nan.any()
+    assert np.allclose(out[~nan], ref[~nan], rtol=1e-10, atol=1e-12 * np.abs(ref[~nan]).max())

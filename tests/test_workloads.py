@@ -36,6 +36,11 @@ def test_shapes_and_dtypes():
             assert inp["w_down_scales"].dtype == np.float32
             assert inp["w_down_scales"].shape == (wl.E, wl.H // 128, wl.I // 128)
             assert not ((inp["w_up"] & 0x7F) == 0x7F).any()      # no NaN codes
+        elif wl.wfmt == "mxfp4":
+            assert inp["w_up"].shape == (wl.E, wl.n_up, wl.H // 2) and inp["w_up"].dtype == np.uint8
+            assert inp["w_up_scales"].shape == (wl.E, wl.n_up, wl.H // 32)
+            assert inp["w_down_scales"].shape == (wl.E, wl.H, wl.I // 32)
+            assert (inp["w_up_scales"] != 255).all()              # NaN only where planted
         elif wl.wfmt == "nvfp4":
             assert inp["w_up"].shape == (wl.E, wl.n_up, wl.H // 2) and inp["w_up"].dtype == np.uint8
             assert inp["w_down"].shape == (wl.E, wl.H, wl.I // 2)
