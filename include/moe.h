@@ -75,7 +75,13 @@ typedef enum {
 } moe_status;
 
 typedef enum { MOE_ACT_SWIGLU = 0, MOE_ACT_RELU2 = 1 } moe_act;
-typedef enum { MOE_W_BF16 = 0, MOE_W_AFFINE4 = 1, MOE_W_FP8 = 2, MOE_W_NVFP4 = 3 } moe_wfmt;
+typedef enum {
+    MOE_W_BF16 = 0,
+    MOE_W_AFFINE4 = 1,
+    MOE_W_FP8 = 2,
+    MOE_W_NVFP4 = 3,
+    MOE_W_MXFP4 = 4
+} moe_wfmt;
 typedef enum { MOE_OUT_BF16 = 0, MOE_OUT_F32 = 1 } moe_out;
 typedef enum { MOE_SCORE_SIGMOID = 0, MOE_SCORE_SOFTMAX = 1 } moe_score;
 
@@ -157,6 +163,14 @@ typedef struct {
  *  scale each 16-input partial in fp32, larger ones decode the experts with
  *  rows to bf16 (exactly) in the workspace; the global scale multiplies
  *  the fp32 sums of each row.
+ *  For MOE_W_MXFP4 (the OCP microscaling sibling of NVFP4: the same E2M1
+ *  codes with a power-of-two scale per 32 instead of an E4M3 one per 16) the
+ *  codes are packed as for NVFP4, w_*_scales are E8M0 bytes [E, N, K/32],
+ *  2^(b - 127) each (0xFF is NaN), one per 32 inputs, the weight is
+ *  e2m1 * scale, exact in bf16 (for scale bytes below 253), and
+ *  w_*_biases and the global scales are unused. Decode-sized batches
+ *  stream the codes and scale each lane's 32-input partial in fp32; larger
+ *  ones decode the experts with rows to bf16 first.
  *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
  *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared]. */
 typedef struct {
@@ -175,7 +189,7 @@ typedef struct {
 } moe_weights;
 
 /* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
- * 4-bit or NVFP4 experts and more than 2 E assignments (T * k > 2 E) or
+ * 4-bit, NVFP4 or MXFP4 experts and more than 2 E assignments (T * k > 2 E) or
  * row_invariant,
  * and with block-FP8 experts whose max(H, I) exceeds 8192 (and, at decode
  * sizes, 4096), this includes room for the bf16-decoded weights of every

@@ -380,7 +380,8 @@ static unsigned fp4_code(const uint8_t *row, int c)
 }
 
 /* An OCP MX E8M0 scale byte: 2^(b - 127); 0xFF is NaN. MXFP4 experts (the
- * MX formats the pages name beside NVFP4) hold one per 32 E2M1 codes. */
+ * OCP microscaling sibling of the NVFP4 layout the pages serve: the same
+ * E2M1 codes, a power-of-two scale per 32) hold one per 32 E2M1 codes. */
 static double e8m0_value(uint8_t b)
 {
     return b == 0xFF ? NAN : ldexp(1.0, (int)b - 127);

@@ -60,7 +60,8 @@ bool quant_streams(const moe_dims &d) {
     const int kmax = std::max(d.H, d.I);
     return decode_sized(d) && ((d.wfmt == MOE_W_AFFINE4 && kmax <= moe::kStreamMaxKAffine4) ||
                                (d.wfmt == MOE_W_FP8 && kmax <= moe::kStreamMaxKFp8) ||
-                               (d.wfmt == MOE_W_NVFP4 && kmax <= moe::kStreamMaxKNvfp4));
+                               (d.wfmt == MOE_W_NVFP4 && kmax <= moe::kStreamMaxKNvfp4) ||
+                               (d.wfmt == MOE_W_MXFP4 && kmax <= moe::kStreamMaxKMxfp4));
 }
 
 // Block-FP8 experts the persistent MFMA kernel reads at their stored width
@@ -78,7 +79,7 @@ bool fp8_tiles(const moe_dims &d) {
 bool dequant_first(const moe_dims &d) {
     return (d.wfmt == MOE_W_AFFINE4 && !decode_sized(d)) ||
            (d.wfmt == MOE_W_FP8 && !quant_streams(d) && !fp8_tiles(d)) ||
-           (d.wfmt == MOE_W_NVFP4 && !quant_streams(d));
+           ((d.wfmt == MOE_W_NVFP4 || d.wfmt == MOE_W_MXFP4) && !quant_streams(d));
 }
 
 // The shared expert as m plan segments of the routed experts' width
@@ -180,9 +181,9 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
     REQUIRE(d->act == MOE_ACT_SWIGLU || d->act == MOE_ACT_RELU2, MOE_E_UNSUPPORTED,
             "%s: act = %d, need MOE_ACT_SWIGLU (0) or MOE_ACT_RELU2 (1)", what, d->act);
     REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_AFFINE4 || d->wfmt == MOE_W_FP8 ||
-                d->wfmt == MOE_W_NVFP4,
+                d->wfmt == MOE_W_NVFP4 || d->wfmt == MOE_W_MXFP4,
             MOE_E_UNSUPPORTED, "%s: wfmt = %d, need MOE_W_BF16 (0), MOE_W_AFFINE4 (1), "
-            "MOE_W_FP8 (2) or MOE_W_NVFP4 (3)", what, d->wfmt);
+            "MOE_W_FP8 (2), MOE_W_NVFP4 (3) or MOE_W_MXFP4 (4)", what, d->wfmt);
     if (d->wfmt == MOE_W_FP8) {
         REQUIRE(d->H % 128 == 0 && d->I % 128 == 0, MOE_E_SHAPE,
                 "%s: H = %d, I = %d: block-FP8 experts need multiples of 128", what, d->H, d->I);
@@ -382,7 +383,8 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     const bool aff = d->wfmt == MOE_W_AFFINE4;
     const bool fp8 = d->wfmt == MOE_W_FP8;
     const bool nv4 = d->wfmt == MOE_W_NVFP4;
-    if (fp8 || nv4) {
+    const bool mx4 = d->wfmt == MOE_W_MXFP4;
+    if (fp8 || nv4 || mx4) {
         TRY(check_ptr(what, "w->w_up_scales", w->w_up_scales));
         TRY(check_ptr(what, "w->w_down_scales", w->w_down_scales));
     }
@@ -414,8 +416,9 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     // (the static scratch is a device global, not an allocation the
     // runtime's pointer query knows)
     const void *dev[] = {x, out, workspace_is_scratch ? nullptr : workspace, w->router_w, w->expert_bias, w->w_up, w->w_down,
-                         aff || fp8 || nv4 ? w->w_up_scales : nullptr, aff ? w->w_up_biases : nullptr,
-                         aff || fp8 || nv4 ? w->w_down_scales : nullptr,
+                         aff || fp8 || nv4 || mx4 ? w->w_up_scales : nullptr,
+                         aff ? w->w_up_biases : nullptr,
+                         aff || fp8 || nv4 || mx4 ? w->w_down_scales : nullptr,
                          aff ? w->w_down_biases : nullptr,
                          d->I_shared ? w->shared_up : nullptr,
                          d->I_shared ? w->shared_down : nullptr, ids_out, weights_out,
@@ -472,6 +475,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     up.affine4 = aff;
     up.fp8 = d->wfmt == MOE_W_FP8;
     up.nvfp4 = nv4;
+    up.mxfp4 = mx4;
     up.Bglobal = nv4 ? w->w_up_global : nullptr;
     up.A = x;
     up.lda = H;
@@ -505,6 +509,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         g.affine4 = 0;
         g.fp8 = 0;
         g.nvfp4 = 0;                 // (an NVFP4 global scale stays in Bglobal)
+        g.mxfp4 = 0;
         g.B = wdq;
         g.Bscale = nullptr;
         g.Bbias = nullptr;
@@ -525,6 +530,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     down.affine4 = aff;
     down.fp8 = up.fp8;
     down.nvfp4 = nv4;
+    down.mxfp4 = mx4;
     down.Bglobal = nv4 ? w->w_down_global : nullptr;
     down.A = h;
     down.lda = I;

@@ -55,6 +55,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
     return pack_bf16x2(f, 0.0f) & 0xffffu;
 }
 
+// An OCP MX E8M0 scale byte as fp32: 2^(b - 127) (b = 0: 2^-127, a
+// subnormal), 0xFF NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
+    const float v = b != 0 ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+    return b == 0xFFu ? __builtin_nanf("") : v;
+}
+
 // The four bytes of w, each two FP4 E2M1 codes (low nibble first), as four
 // bf16 pairs: gfx950's v_cvt_scalef32_pk_bf16_fp4 with scale 1, which gives
 // every E2M1 value exactly (checked on all 256 bytes in each byte position,

@@ -621,6 +621,9 @@ __global__ __launch_bounds__(kThreads) void k_dequant_fp8(GemmProblem p,
 // rounding to bf16 is exact; the matrix's global scale is applied to the
 // GEMM's fp32 sums (Bglobal). A thread decodes one 16-input group (8 code
 // bytes, one scale byte) per item.
+// MX: MXFP4, an E8M0 scale per 32 inputs (the group's scale is that of
+// its 32-wide block), no global scale.
+template <bool MX>
 __global__ __launch_bounds__(kThreads) void k_dequant_nvfp4(GemmProblem p,
                                                             uint16_t *__restrict__ out) {
     __shared__ int s_list[256];
@@ -654,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nvfp4(GemmProblem p,
         const int e = s_list[y];
         const size_t g = (size_t)e * pieces + q;           // the group's index in the expert array
         const uint2 v = *reinterpret_cast<const uint2 *>(codes + g * 8);
-        const float sc = e4m3_to_f32(scales[g]);
+        const float sc = MX ? e8m0_to_f32(scales[g / 2]) : e4m3_to_f32(scales[g]);
         const uint32_t w[2] = {v.x, v.y};
         uint32_t packed[8];
 #pragma unroll
@@ -677,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_nvfp4(GemmProblem p,
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
     if (grouped_supported(p))
         return launch_grouped(p, stream);        // FP8 included (its own tiles)
-    if (p.E2 > 0 || p.Bglobal != nullptr || p.nvfp4)
+    if (p.E2 > 0 || p.Bglobal != nullptr || p.nvfp4 || p.mxfp4)
         return hipErrorInvalidValue;             // shared segments, global scales: the
                                                  // persistent kernel only
     if (p.fp8)
@@ -699,10 +702,13 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream) {
-    if (p.nvfp4) {
-        if (p.offsets == nullptr || p.E > 256 || p.K % 16 != 0)
+    if (p.nvfp4 || p.mxfp4) {
+        if (p.offsets == nullptr || p.E > 256 || p.K % (p.mxfp4 ? 32 : 16) != 0)
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL(k_dequant_nvfp4, dim3(1024), dim3(kThreads), 0, stream, p, out);
+        if (p.mxfp4)
+            hipLaunchKernelGGL(k_dequant_nvfp4<true>, dim3(1024), dim3(kThreads), 0, stream, p, out);
+        else
+            hipLaunchKernelGGL(k_dequant_nvfp4<false>, dim3(1024), dim3(kThreads), 0, stream, p, out);
         return hipGetLastError();
     }
     if (p.fp8) {

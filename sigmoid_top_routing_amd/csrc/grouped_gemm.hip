@@ -943,7 +943,7 @@ bool grouped_supported(const GemmProblem &p) {
     const bool e2_ok = p.E2 == 0 ||
                        (p.E2 > 0 && !p.fp8 && p.offsets != nullptr && p.B2 != nullptr &&
                         b2_rows * p.b2_ld * 2 < (long long)kPastA && p.b2_ld >= p.K);
-    return !p.affine4 && !p.nvfp4 && fp8_ok && e2_ok && p.scatter == nullptr && p.K % kBK == 0 &&
+    return !p.affine4 && !p.nvfp4 && !p.mxfp4 && fp8_ok && e2_ok && p.scatter == nullptr && p.K % kBK == 0 &&
            p.K / kBK >= kStagesSmall && (p.offsets == nullptr || p.E + p.E2 <= kMaxE) &&
            a_rows * p.lda * 2 < (long long)kPastA &&
            (long long)p.N * p.K * (p.fp8 ? 1 : 2) < (long long)kPastA;

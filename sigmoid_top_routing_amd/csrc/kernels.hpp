@@ -55,6 +55,9 @@ struct GemmProblem {
     int nvfp4;                // B is NVFP4: e2m1 codes [E][N][K/2] (low nibble first), an
                               // e4m3 scale byte per 16 inputs [E][N][K/16]: the stream or
                               // launch_dequant reads it
+    int mxfp4;                // B is MXFP4: the same codes, an E8M0 scale byte per 32
+                              // inputs [E][N][K/32] (2^(b-127), 0xFF NaN): the stream or
+                              // launch_dequant reads it
     const uint16_t *A;        // bf16 rows, lda elements apart
     int lda;
     const int32_t *gather;    // A row of position p = gather[p] / gather_div (NULL: row p)
@@ -113,6 +116,7 @@ hipError_t launch_grouped_f8(const GemmProblem &p, hipStream_t stream);
 constexpr int kStreamMaxKAffine4 = 8192;
 constexpr int kStreamMaxKFp8 = 4096;
 constexpr int kStreamMaxKNvfp4 = 8192;
+constexpr int kStreamMaxKMxfp4 = 8192;
 bool stream_supported(const GemmProblem &p);
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream);
 

@@ -232,10 +232,13 @@ __global__ __launch_bounds__(kThreads) void k_stream(GemmProblem p) {
 //           converted exactly (v_cvt_scalef32_pk_bf16_fp4, two per
 //           instruction); the expert's global scale G multiplies the
 //           reduced sum.
+//   MXFP4:  the same 32 codes per lane and step, one E8M0 scale 2^(b-127)
+//           for all of them: w = s v, the lane partial times s.
 // The lane partials are then reduced across the wave as in k_stream.
 constexpr int kFmtAffine4 = 1;
 constexpr int kFmtFp8 = 2;
 constexpr int kFmtNvfp4 = 3;
+constexpr int kFmtMxfp4 = 4;
 
 template <int FMT>
 struct QFmt {
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
                 const bool in = u < units && kk < K;
                 sc[i][s][j] = 0.0f;
                 bi[i][s][j] = 0.0f;
-                if (FMT == kFmtAffine4 || FMT == kFmtNvfp4) {
+                if (FMT == kFmtAffine4 || FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
                     const uint8_t *row = (const uint8_t *)p.B + (erow + n) * (size_t)(K / 2);
                     w[i][s][j] = in ? __builtin_bit_cast(uint4, __builtin_nontemporal_load(
                                           reinterpret_cast<const u32x4 *>(row + kk / 2)))
@@ -339,6 +342,10 @@ __global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
                         const size_t g = (erow + n) * (size_t)(K / 64) + kk / 64;
                         sc[i][s][j] = bf16_to_f32(p.Bscale[g]);
                         bi[i][s][j] = bf16_to_f32(p.Bbias[g]);
+                    } else if (in && FMT == kFmtMxfp4) {
+                        // the one E8M0 scale of the lane's 32 codes
+                        sc[i][s][j] = e8m0_to_f32(
+                            ((const uint8_t *)p.Bscale)[(erow + n) * (size_t)(K / 32) + kk / 32]);
                     } else if (in) {
                         // the E4M3 scales of the lane's two 16-wide groups
                         // (sc: group 0, bi: group 1)
@@ -402,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void k_stream_q(GemmProblem p) {
 #pragma unroll
                             for (int b = 0; b < 4; ++b)
                                 pr[i][s][4 * q + b] = four[b];
-                        } else if constexpr (FMT == kFmtNvfp4) {
+                        } else if constexpr (FMT == kFmtNvfp4 || FMT == kFmtMxfp4) {
                             // byte b: codes 2b (low nibble) and 2b + 1
                             uint32_t four[4];
                             fp4_pairs(cw[q], four);
@@ -553,6 +560,8 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 bool stream_supported(const GemmProblem &p) {
     if (p.b_compact || p.scatter != nullptr || p.E2 > 0 || (p.Bglobal != nullptr && !p.nvfp4))
         return false;
+    if (p.mxfp4)        // 4 code words per lane and step: one 32-wide block
+        return p.K % 32 == 0 && p.K <= kStreamMaxKMxfp4;
     if (p.nvfp4)        // 4 code words per lane and step; groups of 16
         return p.K % 32 == 0 && p.K <= kStreamMaxKNvfp4;
     static_assert(kStreamMaxKAffine4 == 4 * QFmt<kFmtAffine4>::EPJ, "4-bit steps");
@@ -571,6 +580,8 @@ hipError_t launch_stream(const GemmProblem &p, hipStream_t stream) {
         return launch_q_fmt<kFmtFp8>(p, stream);
     if (p.nvfp4)
         return launch_q_fmt<kFmtNvfp4>(p, stream);
+    if (p.mxfp4)
+        return launch_q_fmt<kFmtMxfp4>(p, stream);
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp>(p, stream);
     case kGateUpLimit: return launch_mode<kGateUpLimit>(p, stream);

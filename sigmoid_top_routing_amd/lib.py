@@ -20,7 +20,7 @@ MOE_OK = 0
 STATUS = {0: "MOE_OK", -1: "MOE_E_NULL", -2: "MOE_E_SHAPE", -3: "MOE_E_ALIGN",
           -4: "MOE_E_UNSUPPORTED", -5: "MOE_E_WORKSPACE", -6: "MOE_E_HIP"}
 ACT = {"swiglu": 0, "relu2": 1}
-WFMT = {"bf16": 0, "affine4": 1, "fp8": 2, "nvfp4": 3}
+WFMT = {"bf16": 0, "affine4": 1, "fp8": 2, "nvfp4": 3, "mxfp4": 4}
 OUT = {torch.bfloat16: 0, torch.float32: 1}
 SCORE = {"sigmoid": 0, "softmax": 1}
 
@@ -310,7 +310,7 @@ def block_from_arrays(wl, inp: dict, device="cuda") -> MoEBlock:
     aff = wl.wfmt == "affine4"
     fp8 = wl.wfmt == "fp8"
     nv4 = wl.wfmt == "nvfp4"
-    quant = aff or fp8 or nv4
+    quant = aff or fp8 or nv4 or wl.wfmt == "mxfp4"
     return MoEBlock(H=wl.H, I=wl.I, E=wl.E, k=wl.k, router_w=dev("router_w"), bias=dev("bias"),
                     w_up=dev("w_up", not quant), w_down=dev("w_down", not quant),
                     w_up_scales=dev("w_up_scales", aff),

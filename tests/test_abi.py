@@ -134,6 +134,13 @@ def test_unsupported_options_are_refused():
     rc, nq = ws_bytes(dims(wfmt="nvfp4", T=64, H=256, I=256, E=8, k=2))
     rc16, n16 = ws_bytes(dims(T=64, H=256, I=256, E=8, k=2))
     assert rc == rc16 == 0 and nq >= n16 + 8 * 512 * 256 * 2
+    # MXFP4 the same way
+    rc, nq = ws_bytes(dims(wfmt="mxfp4", T=8, H=256, I=256, E=8, k=2))
+    rc16, n16 = ws_bytes(dims(T=8, H=256, I=256, E=8, k=2))
+    assert rc == rc16 == 0 and nq == n16
+    rc, nq = ws_bytes(dims(wfmt="mxfp4", T=64, H=256, I=256, E=8, k=2))
+    rc16, n16 = ws_bytes(dims(T=64, H=256, I=256, E=8, k=2))
+    assert rc == rc16 == 0 and nq >= n16 + 8 * 512 * 256 * 2
     assert ws_bytes(dims(score="softmax"))[0] == 0
     assert ws_bytes(dims(wfmt="fp8", H=192))[0] == -2
     assert "multiples of 128" in lib.load().moe_last_error().decode()
@@ -202,6 +209,11 @@ def test_forward_refuses_null_misaligned_and_short_workspace():
     rc = L.moe_forward(C.byref(dn), C.byref(wn), _fake(0x1000), _fake(0x1000), _fake(0x1000),
                        1 << 30, None, None, None, None)
     assert rc == -1 and "w_up_global" in L.moe_last_error().decode()
+    # MXFP4 weights without their E8M0 scales
+    dm = dims(wfmt="mxfp4")
+    rc = L.moe_forward(C.byref(dm), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       1 << 30, None, None, None, None)
+    assert rc == -1 and "w_up_scales" in L.moe_last_error().decode()
     # a shared expert without its weights
     ds = dims(I_shared=64)
     rc = L.moe_forward(C.byref(ds), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),

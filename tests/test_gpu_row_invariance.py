@@ -23,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 CASES = ["lfm2_prefill_t4096", "mid_relu2_shared", "mid_affine4", "mid_fp8", "mid_swiglu_limit",
-         "mid_relu2_nonfinite", "mid_relu2_shared_seg", "mid_nvfp4"]
+         "mid_relu2_nonfinite", "mid_relu2_shared_seg", "mid_nvfp4", "mid_mxfp4"]
 
 
 def _run(wl, inp, T, row_invariant):
