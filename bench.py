@@ -22,9 +22,9 @@ Besides the whole-block throughput the line carries:
                 bytes and flops and their fractions of the HBM and bf16 MFMA
                 peaks: the tiny block, the relu^2 block with a shared expert,
                 the 4-bit block, the 4-bit decode step (T = 8) without
-                and with the four boosted experts, the block-FP8 prefill and
-                decode steps, and the bf16 decode step with row_invariant
-                (every batch on the MFMA tiles).
+                and with the four boosted experts, the block-FP8, NVFP4 and
+                MXFP4 prefill and decode steps, and the bf16 decode step with
+                row_invariant (every batch on the MFMA tiles).
 """
 from __future__ import annotations
 
@@ -66,6 +66,12 @@ def expert_bytes(wl):
     elif wl.wfmt == "fp8":
         up = wl.n_up * wl.H + 4 * (wl.n_up // 128) * (wl.H // 128)
         down = wl.H * wl.I + 4 * (wl.H // 128) * (wl.I // 128)
+    elif wl.wfmt == "nvfp4":        # codes, an e4m3 scale per 16, the global scale
+        up = wl.n_up * wl.H // 2 + wl.n_up * wl.H // 16 + 4
+        down = wl.H * wl.I // 2 + wl.H * wl.I // 16 + 4
+    elif wl.wfmt == "mxfp4":        # codes, an e8m0 scale per 32
+        up = wl.n_up * wl.H // 2 + wl.n_up * wl.H // 32
+        down = wl.H * wl.I // 2 + wl.H * wl.I // 32
     else:
         up = 2 * wl.n_up * wl.H
         down = 2 * wl.H * wl.I
@@ -278,7 +284,11 @@ def main():
                                  ("affine4_decode", "affine4_flat_decode_t8", True),
                                  ("affine4_decode_boosted", "affine4_decode_t8", True),
                                  ("fp8", "lfm2_fp8_prefill_t4096", False),
-                                 ("fp8_decode", "lfm2_fp8_decode_t8", True)):
+                                 ("fp8_decode", "lfm2_fp8_decode_t8", True),
+                                 ("nvfp4", "lfm2_nvfp4_prefill_t4096", False),
+                                 ("nvfp4_decode", "lfm2_nvfp4_decode_t8", True),
+                                 ("mxfp4", "lfm2_mxfp4_prefill_t4096", False),
+                                 ("mxfp4_decode", "lfm2_mxfp4_decode_t8", True)):
             result["configs"][tag] = bench_step(W.by_name(name), W, lib, torch, flush=flush)
             print(f"bench: {tag} done", file=sys.stderr, flush=True)
         result["configs"]["decode_row_invariant"] = bench_step(W.DECODE, W, lib, torch, block=block,

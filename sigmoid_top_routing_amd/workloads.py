@@ -212,8 +212,10 @@ EXTRA = {
                                          E=32, k=4, wfmt="nvfp4", seed=121),
     "lfm2_nvfp4_decode_t8": Workload("lfm2_nvfp4_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
                                      wfmt="nvfp4", seed=122, weight_seed=121),
+    "lfm2_mxfp4_prefill_t4096": Workload("lfm2_mxfp4_prefill_t4096", T=4096, H=2048, I=1792,
+                                         E=32, k=4, wfmt="mxfp4", seed=125),
     "lfm2_mxfp4_decode_t8": Workload("lfm2_mxfp4_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
-                                     wfmt="mxfp4", seed=125),
+                                     wfmt="mxfp4", seed=126, weight_seed=125),
     "lfm2_fp8_decode_t8": Workload("lfm2_fp8_decode_t8", T=8, H=2048, I=1792, E=32, k=4,
                                    wfmt="fp8", scale_lo=1e-4, scale_hi=3e-4, seed=112,
                                    weight_seed=111),
