@@ -712,8 +712,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
             for (int i = 0; i < TM; ++i) {
 #pragma unroll
                 for (int j = 0; j < TN; ++j) {
-                    // F8: the finished sum in units of the last block's scale
-                    f32x16 v = F8 ? acc[i][j] * rho_gate : acc[i][j];
+                    // the tile's accumulators into VGPRs one read each (F8:
+                    // the finished sum in units of the last block's scale);
+                    // a whole-vector copy lets the compiler move every
+                    // accumulator of the tile list at once, which spills
+                    f32x16 v;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        if constexpr (F8)
+                            v[r] = acc[i][j][r] * rho_gate;
+                        else
+                            __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]));
+                    }
                     if (gscaled)
                         v = v * gsc;
                     // 32 rows x 32 fp32: row r at r * 128 bytes, 8 chunks of 4
