@@ -72,6 +72,14 @@ constexpr int kXcds = 8;
 constexpr int kMaxE = 256;
 constexpr uint32_t kPastA = 0x80000000u;   // an A offset past every A matrix: reads zeros
 
+// Weight formats of the tiles: bf16 (or bf16 decoded by a pass before),
+// block-FP8 codes, and 4-bit E2M1 codes with NVFP4 (E4M3 per 16) or MXFP4
+// (E8M0 per 32) scales.
+constexpr int kWBf16 = 0;
+constexpr int kWF8 = 1;
+constexpr int kWNv4 = 2;
+constexpr int kWMx4 = 3;
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) volatile u32x4 lds_u32x4;
@@ -99,11 +107,13 @@ __device__ __forceinline__ u32x4 park_get16(char *__restrict__ base, int off) {
 
 // F8: block-FP8 weights, one byte each in the stages (32-byte rows per
 // K-slice instead of 64).
-template <int BM, bool F8 = false>
+template <int BM, int WF = kWBf16>
 struct Geo {
+    static constexpr bool F8 = WF == kWF8;
+    static constexpr bool F4 = WF == kWNv4 || WF == kWMx4;
     static constexpr int TM = BM / 64;            // 32-token MFMA tiles per wave
     static constexpr int TN = kBN / 64;           // 32-weight-row MFMA tiles per wave
-    static constexpr int BROW = F8 ? 2 : 4;       // 16-byte slots per weight row of a stage
+    static constexpr int BROW = F8 ? 2 : F4 ? 1 : 4;  // 16-byte slots per weight row of a stage
     static constexpr int AI = BM * 4 / kThreads;  // A requests per thread per stage
     static constexpr int BI = kBN * BROW / kThreads; // B requests per thread per stage
     static constexpr int PER = AI + BI;
@@ -188,11 +198,12 @@ __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)
 }
 
 // Request state of the tile whose slices are being fetched.
-template <int BM, bool F8>
+template <int BM, int WF>
 struct Req {
+    static constexpr bool F8 = WF == kWF8;
     const char *b_base;               // uniform: the expert's weight rows
     uint32_t a_off[Geo<BM>::AI];      // per thread, bytes at K-slice 0
-    uint32_t b_off[Geo<BM, F8>::BI];
+    uint32_t b_off[Geo<BM, WF>::BI];
     float scale[F8 ? 2 : 1];          // F8: lane b holds the scale of K-block b of each
                                       // weight-row block of the wave (gate, up)
 };
@@ -207,9 +218,10 @@ struct Req {
 // loads the tile's block scales: for each weight-row block of the wave
 // (SwiGLU: the gate rows and the up rows; otherwise the wave's 128 rows),
 // lane b takes the scale of K-block b.
-template <int BM, int MODE, bool F8>
-__device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, Req<BM, F8> &q) {
-    using G = Geo<BM, F8>;
+template <int BM, int MODE, int WF>
+__device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, Req<BM, WF> &q) {
+    using G = Geo<BM, WF>;
+    constexpr bool F8 = G::F8;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     // segments past the experts: the shared expert's slices (bf16 only)
@@ -257,10 +269,11 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
 }
 
 // Piece m (A pieces first, then B pieces) of K-slice ks into one stage.
-template <int BM, int MODE, bool F8>
+template <int BM, int MODE, int WF>
 __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmProblem &p,
-                                        const Req<BM, F8> &q, int ks, int m) {
-    using G = Geo<BM, F8>;
+                                        const Req<BM, WF> &q, int ks, int m) {
+    using G = Geo<BM, WF>;
+    constexpr bool F8 = G::F8;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (m < G::AI) {
         // pieces of padding rows (offset kPastA) read as zeros
@@ -275,11 +288,11 @@ __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmPro
 // Fragment registers: slot 0 and 1 of a double buffer over sub-steps. F8
 // also holds the raw bytes of each weight fragment: 16 bytes per lane, both
 // sub-steps of a step (bytes 0-7 sub-step 0, 8-15 sub-step 1).
-template <int BM, bool F8 = false>
+template <int BM, int WF = kWBf16>
 struct Frags {
     bf16x8 a[2][Geo<BM>::TM];
     bf16x8 b[2][Geo<BM>::TN];
-    u32x4 braw[F8 ? Geo<BM>::TN : 1];
+    u32x4 braw[WF == kWF8 ? Geo<BM>::TN : 1];
 };
 
 // One 16-byte fragment read of a stage, through a __restrict__ pointer of
@@ -293,7 +306,7 @@ __device__ __forceinline__ u32x4 lds_frag(const uint4 *__restrict__ S, int slot)
 // exact (every e4m3 value, NaN included, is a bf16 value); the block scale
 // is applied to the fp32 sums, not here.
 template <int BM>
-__device__ __forceinline__ void cvt_b(Frags<BM, true> &f, int slot, int j) {
+__device__ __forceinline__ void cvt_b(Frags<BM, kWF8> &f, int slot, int j) {
     uint32_t o[4];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -327,7 +340,7 @@ __device__ __forceinline__ void read_frag(const uint4 *__restrict__ S, Frags<BM>
 template <int BM, int MODE, int NS>
 __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uint4 *__restrict__ Snext,
                                           uint4 *__restrict__ Sfill, const GemmProblem &p,
-                                          const Req<BM, false> &q, int ks, Frags<BM> &f,
+                                          const Req<BM, kWBf16> &q, int ks, Frags<BM> &f,
                                           f32x16 (&acc)[Geo<BM>::TM][Geo<BM>::TN],
                                           const int (&a_slot)[2], const int (&b_slot)[2],
                                           const int *b_toff) {
@@ -361,7 +374,7 @@ __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uin
             if (m < G::NF)
                 read_frag<BM>(Snext, f, 0, m, a_slot[0], b_slot[0], b_toff);
             else
-                request<BM, MODE, false>(Sfill, p, q, ks, m - G::NF);
+                request<BM, MODE, kWBf16>(Sfill, p, q, ks, m - G::NF);
         }
         fence();
     }
@@ -383,11 +396,11 @@ __device__ __forceinline__ void ring_step(const uint4 *__restrict__ S, const uin
 template <int BM, int MODE, int NS>
 __device__ __forceinline__ void ring_step_f8(const uint4 *__restrict__ S, const uint4 *__restrict__ Snext,
                                              uint4 *__restrict__ Sfill, const GemmProblem &p,
-                                             const Req<BM, true> &q, int ks, Frags<BM, true> &f,
+                                             const Req<BM, kWF8> &q, int ks, Frags<BM, kWF8> &f,
                                              f32x16 (&acc)[Geo<BM>::TM][Geo<BM>::TN],
                                              const int (&a_slot)[2], int b_slot, const int *b_toff,
                                              bool rescale, float r_gate, float r_up) {
-    using G = Geo<BM, true>;
+    using G = Geo<BM, kWF8>;
     constexpr int TM = G::TM, TN = G::TN;
     fence();
     // sub-step 0: MFMAs on slot 0, each weight fragment converted just
@@ -430,7 +443,7 @@ __device__ __forceinline__ void ring_step_f8(const uint4 *__restrict__ S, const 
             else if (m < TM + TN)
                 f.braw[m - TM] = lds_frag(Snext, b_slot + b_toff[m - TM]);
             else
-                request<BM, MODE, true>(Sfill, p, q, ks, m - TM - TN);
+                request<BM, MODE, kWF8>(Sfill, p, q, ks, m - TM - TN);
         }
         fence();
     }
@@ -438,20 +451,21 @@ __device__ __forceinline__ void ring_step_f8(const uint4 *__restrict__ S, const 
 
 // Prologue: the first NS - 1 slices of the first tile into stages 0 ..
 // NS - 2.
-template <int BM, int MODE, int NS, bool F8>
+template <int BM, int MODE, int NS, int WF>
 __device__ __forceinline__ void prime(uint4 *__restrict__ ring, const GemmProblem &p,
-                                      const Req<BM, F8> &q) {
-    using G = Geo<BM, F8>;
+                                      const Req<BM, WF> &q) {
+    using G = Geo<BM, WF>;
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
 #pragma unroll
         for (int m = 0; m < G::PER; ++m)
-            request<BM, MODE, F8>(ring + st * G::STAGE, p, q, st, m);
+            request<BM, MODE, WF>(ring + st * G::STAGE, p, q, st, m);
 }
 
-template <int BM, int MODE, int NS, bool F8>
+template <int BM, int MODE, int NS, int WF>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_tiles) {
-    using G = Geo<BM, F8>;
+    using G = Geo<BM, WF>;
+    constexpr bool F8 = G::F8;
     constexpr int TM = G::TM, TN = G::TN;
     constexpr int kAhead = NS - 1;           // stages requested ahead of the one multiplied
     __shared__ uint4 ring[NS * G::STAGE];
@@ -527,12 +541,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     int e, row0, row_end, nt;                // the tile being multiplied
     if (!place<BM>(tl, 0, e, row0, row_end, nt))
         return;                              // uniform
-    Req<BM, F8> req;                         // the tile being fetched
+    Req<BM, WF> req;                         // the tile being fetched
     {
         int raw[G::AI];
         const int valid = gathered_rows<BM>(p, row0, row_end, raw);
         a_offsets<BM>(p, raw, valid, req.a_off);
-        b_offsets<BM, MODE, F8>(p, p.b_compact && e < p.E ? s_rank[e] : e, nt, req);
+        b_offsets<BM, MODE, WF>(p, p.b_compact && e < p.E ? s_rank[e] : e, nt, req);
     }
     int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
     bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
@@ -570,10 +584,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     }
 
     const int KT = p.K / kBK;
-    prime<BM, MODE, NS, F8>(ring, p, req);
+    prime<BM, MODE, NS, WF>(ring, p, req);
     wait_vmcnt<(NS - 2) * G::PER>();
     __builtin_amdgcn_s_barrier();
-    Frags<BM, F8> f;
+    Frags<BM, WF> f;
     if constexpr (F8) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -665,7 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                     for (int i = 0; i < G::AI; ++i)
                         __asm__ volatile("" : "+v"(nraw[i]));
                     a_offsets<BM>(p, nraw, nvalid, req.a_off);
-                    b_offsets<BM, MODE, F8>(p, p.b_compact && ne < p.E ? s_rank[ne] : ne, nnt, req);
+                    b_offsets<BM, MODE, WF>(p, p.b_compact && ne < p.E ? s_rank[ne] : ne, nnt, req);
                 }
             }
         }
@@ -875,7 +889,7 @@ long long tiles_bound(const GemmProblem &p, int &n_tiles) {
     return (long long)mt_max * n_tiles;
 }
 
-template <int BM, int MODE, bool F8 = false>
+template <int BM, int MODE, int WF = kWBf16>
 hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
     int n_tiles = 0;
     const long long work = tiles_bound<BM, MODE>(p, n_tiles);
@@ -892,12 +906,12 @@ hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
     // the deep ring for 128-row tiles where K has the slices to fill it
     if constexpr (BM == 128) {
         if (p.K / kBK >= kStagesDeep) {
-            hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesDeep, F8>), dim3(blocks), dim3(kThreads), 0,
+            hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesDeep, WF>), dim3(blocks), dim3(kThreads), 0,
                                stream, p, n_tiles);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesSmall, F8>), dim3(blocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((k_grouped<BM, MODE, kStagesSmall, WF>), dim3(blocks), dim3(kThreads), 0, stream,
                        p, n_tiles);
     return hipGetLastError();
 }
@@ -929,10 +943,10 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 // them.
 hipError_t launch_grouped_f8(const GemmProblem &p, hipStream_t stream) {
     switch (p.mode) {
-    case kGateUp: return launch_bm<128, kGateUp, true>(p, stream);
-    case kGateUpLimit: return launch_bm<128, kGateUpLimit, true>(p, stream);
-    case kUpRelu2: return launch_bm<128, kUpRelu2, true>(p, stream);
-    default: return launch_bm<128, kDown, true>(p, stream);
+    case kGateUp: return launch_bm<128, kGateUp, kWF8>(p, stream);
+    case kGateUpLimit: return launch_bm<128, kGateUpLimit, kWF8>(p, stream);
+    case kUpRelu2: return launch_bm<128, kUpRelu2, kWF8>(p, stream);
+    default: return launch_bm<128, kDown, kWF8>(p, stream);
     }
 }
 #else

@@ -381,17 +381,40 @@ def run_forward(wl, inp, out_dtype=torch.bfloat16, x_bits=None, block=None):
     return to_np(out), ids.cpu().numpy(), w.cpu().numpy(), offs.cpu().numpy()
 
 
-@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("name", SMALL)
-def test_forward_matches_oracle_every_token(name, out_dtype):
+def test_forward_matches_oracle_every_token(name):
+    # fp32 and bf16 outputs of the same inputs: each against the oracle, and
+    # the bf16 output exactly the rounding of the fp32 one (which ties the
+    # bf16 leg's allowance for its own rounding to the fp32 result)
     wl, inp = small_inputs(name)
-    out, ids, w, offs = run_forward(wl, inp, out_dtype)
     refs, ids_ref, w_ref = refs_for(wl, inp, np.arange(wl.T), want_routing=True)
-    check_routing(ids, w, ids_ref, w_ref)
     _, o_ref, _, _ = oracle.plan(ids_ref, wl.E)
+    outs = {}
+    for out_dtype in (torch.float32, torch.bfloat16):
+        out, ids, w, offs = run_forward(wl, inp, out_dtype)
+        check_routing(ids, w, ids_ref, w_ref)
+        assert (offs == o_ref).all()
+        for ref, tol in refs:
+            check_out(out, ref, tol, rounded_to_bf16=out_dtype == torch.bfloat16)
+        outs[out_dtype] = out
+    assert (W.f32_to_bf16_bits(outs[torch.float32]) ==
+            W.f32_to_bf16_bits(outs[torch.bfloat16])).all()
+
+
+def test_forward_headline_every_token():
+    # the LFM2-shaped prefill (T = 4096) on all of its tokens, fp32 and bf16
+    wl = W.by_name("lfm2_prefill_t4096")
+    inp = W.generate(wl)
+    refs, ids_ref, w_ref = refs_for(wl, inp, np.arange(wl.T), want_routing=True)
+    _, o_ref, _, _ = oracle.plan(ids_ref, wl.E)
+    out32, ids, w, offs = run_forward(wl, inp, torch.float32)
+    check_routing(ids, w, ids_ref, w_ref)
     assert (offs == o_ref).all()
+    out16, _, _, _ = run_forward(wl, inp)
     for ref, tol in refs:
-        check_out(out, ref, tol, rounded_to_bf16=out_dtype == torch.bfloat16)
+        check_out(out32, ref, tol)
+        check_out(out16, ref, tol, rounded_to_bf16=True)
+    assert (W.f32_to_bf16_bits(out32) == W.f32_to_bf16_bits(out16)).all()
 
 
 @pytest.mark.parametrize("name", FULL)
