@@ -160,9 +160,11 @@ typedef struct {
  *  expert matrix (the fused gate_up matrix has one); the weight is
  *  e2m1 * scale * global, and w_*_biases are unused. Every e2m1 * scale
  *  product is exact in bf16: decode-sized batches stream the codes and
- *  scale each 16-input partial in fp32, larger ones decode the experts with
- *  rows to bf16 (exactly) in the workspace; the global scale multiplies
- *  the fp32 sums of each row.
+ *  scale each 16-input partial in fp32; larger ones (and every batch with
+ *  row_invariant) read the codes on the MFMA tiles, each code times its
+ *  scale converted exactly to bf16 in registers, which needs H and I of at
+ *  least 128 and T*k*max(H, I)*2 below 2^31 (MOE_E_UNSUPPORTED otherwise).
+ *  The global scale multiplies the fp32 sums of each row.
  *  For MOE_W_MXFP4 (the OCP microscaling sibling of NVFP4: the same E2M1
  *  codes with a power-of-two scale per 32 instead of an E4M3 one per 16) the
  *  codes are packed as for NVFP4, w_*_scales are E8M0 bytes [E, N, K/32],
@@ -170,7 +172,7 @@ typedef struct {
  *  e2m1 * scale, exact in bf16 (for scale bytes below 253), and
  *  w_*_biases and the global scales are unused. Decode-sized batches
  *  stream the codes and scale each lane's 32-input partial in fp32; larger
- *  ones decode the experts with rows to bf16 first.
+ *  ones take the MFMA tiles as NVFP4 does, under the same conditions.
  *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
  *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared]. */
 typedef struct {
@@ -189,10 +191,9 @@ typedef struct {
 } moe_weights;
 
 /* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
- * 4-bit, NVFP4 or MXFP4 experts and more than 2 E assignments (T * k > 2 E) or
- * row_invariant,
- * and with block-FP8 experts whose max(H, I) exceeds 8192 (and, at decode
- * sizes, 4096), this includes room for the bf16-decoded weights of every
+ * 4-bit experts and more than 2 E assignments (T * k > 2 E) or
+ * row_invariant, and with block-FP8 experts whose max(H, I) exceeds 8192
+ * (and, at decode sizes, 4096), this includes room for the bf16-decoded weights of every
  * expert that can have rows: min(E, T * k) * max(n_up * H, H * I) * 2 bytes,
  * n_up = 2 I (SwiGLU) or I. Otherwise the codes are read as stored. With a
  * shared expert whose I_shared is a whole number m of I, prompt-sized

@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["route.hip", "plan.hip", "gemm.hip", "grouped_gemm.hip", "grouped_gemm_f8.hip",
-           "stream.hip", "combine.hip", "norm.hip", "api.cpp"]
+           "grouped_gemm_f4.hip", "stream.hip", "combine.hip", "norm.hip", "api.cpp"]
 # Per-source flags: the FP8 grouped GEMM keeps its MFMA accumulators in VGPRs.
 SOURCE_FLAGS = {"grouped_gemm_f8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 FLAGS = [

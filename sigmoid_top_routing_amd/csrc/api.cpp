@@ -71,15 +71,25 @@ bool fp8_tiles(const moe_dims &d) {
     return d.wfmt == MOE_W_FP8 && d.H <= 64 * 128 && d.I <= 64 * 128;
 }
 
+// NVFP4 and MXFP4 experts the persistent MFMA kernel reads at their stored
+// width (half a byte per weight, each code times its scale converted
+// exactly to bf16 in registers): every batch the decode form does not take,
+// within the kernel's 32-bit row offsets.
+bool f4_tiles(const moe_dims &d) {
+    return (d.wfmt == MOE_W_NVFP4 || d.wfmt == MOE_W_MXFP4) && !quant_streams(d) &&
+           d.H >= 128 && d.I >= 128 &&
+           (int64_t)d.T * d.k * std::max(d.H, d.I) * 2 < ((int64_t)1 << 31);
+}
+
 // 4-bit experts of prompt-sized batches, and block-FP8 experts that neither
 // the decode form nor the FP8 tiles take, are decoded to bf16 (the weights
 // of the experts with rows, once per call) before the bf16 MFMA kernel
 // runs. Decode-sized 4-bit batches the stream does not take keep the decode
-// in the staged kernel's loads.
+// in the staged kernel's loads. (NVFP4 and MXFP4 batches take the stream or
+// their tiles; check_dims refuses the shapes neither takes.)
 bool dequant_first(const moe_dims &d) {
     return (d.wfmt == MOE_W_AFFINE4 && !decode_sized(d)) ||
-           (d.wfmt == MOE_W_FP8 && !quant_streams(d) && !fp8_tiles(d)) ||
-           ((d.wfmt == MOE_W_NVFP4 || d.wfmt == MOE_W_MXFP4) && !quant_streams(d));
+           (d.wfmt == MOE_W_FP8 && !quant_streams(d) && !fp8_tiles(d));
 }
 
 // The shared expert as m plan segments of the routed experts' width
@@ -90,7 +100,8 @@ bool dequant_first(const moe_dims &d) {
 // tiles with bf16 or decoded 4-bit experts; 0 otherwise (the shared expert
 // then runs as its own dense projections).
 int shared_segments(const moe_dims &d) {
-    if (d.I_shared <= 0 || d.I_shared % d.I != 0 || decode_sized(d) || d.wfmt == MOE_W_FP8)
+    if (d.I_shared <= 0 || d.I_shared % d.I != 0 || decode_sized(d) || d.wfmt == MOE_W_FP8 ||
+        f4_tiles(d))
         return 0;
     const int m = d.I_shared / d.I;
     const int64_t rows = (int64_t)d.T * d.k + (int64_t)m * d.T;   // plan positions
@@ -194,6 +205,12 @@ int check_dims(const char *what, const moe_dims *d, bool experts) {
     if (d->wfmt == MOE_W_AFFINE4)
         REQUIRE(d->group == 64, MOE_E_UNSUPPORTED, "%s: group = %d, the 4-bit format needs 64",
                 what, d->group);
+    if (d->wfmt == MOE_W_NVFP4 || d->wfmt == MOE_W_MXFP4)
+        REQUIRE(quant_streams(*d) || f4_tiles(*d), MOE_E_UNSUPPORTED,
+                "%s: NVFP4 / MXFP4 experts: a batch the weight-streaming form does not take "
+                "(T*k = %lld > 2E, row_invariant, or H or I past 8192) needs H, I >= 128 and "
+                "T*k*max(H, I)*2 < 2^31 for the MFMA tiles (H = %d, I = %d)",
+                what, (long long)d->T * d->k, d->H, d->I);
     REQUIRE(d->out_dtype == MOE_OUT_BF16 || d->out_dtype == MOE_OUT_F32, MOE_E_UNSUPPORTED,
             "%s: out_dtype = %d, need MOE_OUT_BF16 (0) or MOE_OUT_F32 (1)", what, d->out_dtype);
     REQUIRE(std::isfinite(d->routed_scale), MOE_E_SHAPE, "%s: routed_scale = %g is not finite",

@@ -614,67 +614,6 @@ __global__ __launch_bounds__(kThreads) void k_dequant_fp8(GemmProblem p,
     }
 }
 
-// NVFP4 weights of the experts with rows, decoded to bf16 in expert order
-// (b_compact), like k_dequant: each e2m1 code (v_cvt_scalef32_pk_bf16_fp4
-// with scale 1 gives its value exactly) times the e4m3 scale of its 16
-// inputs, in fp32. The product has at most 6 significant bits, so the
-// rounding to bf16 is exact; the matrix's global scale is applied to the
-// GEMM's fp32 sums (Bglobal). A thread decodes one 16-input group (8 code
-// bytes, one scale byte) per item.
-// MX: MXFP4, an E8M0 scale per 32 inputs (the group's scale is that of
-// its 32-wide block), no global scale.
-template <bool MX>
-__global__ __launch_bounds__(kThreads) void k_dequant_nvfp4(GemmProblem p,
-                                                            uint16_t *__restrict__ out) {
-    __shared__ int s_list[256];
-    __shared__ int s_cnt[kThreads / kWave];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const bool busy = tid < p.E && p.offsets[tid + 1] > p.offsets[tid];
-    const uint64_t m = __ballot(busy);
-    if (lane == 0)
-        s_cnt[wave] = __popcll(m);
-    __syncthreads();
-    int rank = __popcll(m & ((1ull << lane) - 1ull)), nb = 0;
-    for (int w = 0; w < kThreads / kWave; ++w) {
-        rank += w < wave ? s_cnt[w] : 0;
-        nb += s_cnt[w];
-    }
-    if (busy)
-        s_list[rank] = tid;
-    __syncthreads();
-    const int K16 = p.K / 16;
-    const size_t pieces = (size_t)p.N * K16;               // 16-input groups per expert
-    const size_t chunks = (pieces + kThreads - 1) / kThreads;
-    const uint8_t *codes = (const uint8_t *)p.B;
-    const uint8_t *scales = (const uint8_t *)p.Bscale;
-    for (size_t item = blockIdx.x; item < (size_t)nb * chunks; item += gridDim.x) {
-        const int y = (int)(item / chunks);
-        const size_t q = (item % chunks) * kThreads + tid;
-        if (q >= pieces)
-            continue;
-        const int e = s_list[y];
-        const size_t g = (size_t)e * pieces + q;           // the group's index in the expert array
-        const uint2 v = *reinterpret_cast<const uint2 *>(codes + g * 8);
-        const float sc = MX ? e8m0_to_f32(scales[g / 2]) : e4m3_to_f32(scales[g]);
-        const uint32_t w[2] = {v.x, v.y};
-        uint32_t packed[8];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            uint32_t pr[4];
-            fp4_pairs(w[i], pr);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                packed[4 * i + b] = pack_bf16x2(bf16_to_f32(pr[b] & 0xffffu) * sc,
-                                                bf16_to_f32(pr[b] >> 16) * sc);
-        }
-        uint4 *o = reinterpret_cast<uint4 *>(out + ((size_t)y * p.N) * p.K + q * 16);
-        o[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-        o[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    }
-}
-
 }  // namespace
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
@@ -702,15 +641,6 @@ hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream) {
 }
 
 hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream) {
-    if (p.nvfp4 || p.mxfp4) {
-        if (p.offsets == nullptr || p.E > 256 || p.K % (p.mxfp4 ? 32 : 16) != 0)
-            return hipErrorInvalidValue;
-        if (p.mxfp4)
-            hipLaunchKernelGGL(k_dequant_nvfp4<true>, dim3(1024), dim3(kThreads), 0, stream, p, out);
-        else
-            hipLaunchKernelGGL(k_dequant_nvfp4<false>, dim3(1024), dim3(kThreads), 0, stream, p, out);
-        return hipGetLastError();
-    }
     if (p.fp8) {
         if (p.offsets == nullptr || p.E > 256 || p.K % 128 != 0 || p.N % 128 != 0)
             return hipErrorInvalidValue;

@@ -201,11 +201,21 @@ __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)
 template <int BM, int WF>
 struct Req {
     static constexpr bool F8 = WF == kWF8;
+    static constexpr bool F4 = Geo<BM, WF>::F4;
     const char *b_base;               // uniform: the expert's weight rows
     uint32_t a_off[Geo<BM>::AI];      // per thread, bytes at K-slice 0
     uint32_t b_off[Geo<BM, WF>::BI];
     float scale[F8 ? 2 : 1];          // F8: lane b holds the scale of K-block b of each
                                       // weight-row block of the wave (gate, up)
+};
+
+// F4: where the scales of this lane's weight rows are (one row per weight
+// tile j of the wave): the expert's scale bytes (uniform) and, per j, the
+// row's first scale byte.
+template <int BM>
+struct Scales {
+    const uint8_t *base;
+    uint32_t off[Geo<BM>::TN];
 };
 
 // The weight side of a tile's requests: the expert's base and, per B piece
@@ -226,8 +236,10 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
     const int wave = threadIdx.x / kWave;
     // segments past the experts: the shared expert's slices (bf16 only)
     const bool sh = !F8 && e >= p.E;
+    // weights as stored: 2 bytes (bf16), 1 (FP8) or a half (E2M1) each
+    constexpr int kHalfBytes = F8 ? 2 : G::F4 ? 1 : 4;
     q.b_base = sh ? (const char *)(p.B2 + (size_t)(e - p.E) * p.b2_vstride)
-                  : (const char *)p.B + (size_t)e * p.N * p.K * (F8 ? 1 : 2);
+                  : (const char *)p.B + (size_t)e * p.N * p.K * kHalfBytes / 2;
     const uint32_t ld = sh ? (uint32_t)p.b2_ld : (uint32_t)p.K;
     const int up_rows = sh ? p.b2_up : p.I;
     if constexpr (F8) {
@@ -251,8 +263,9 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
 #pragma unroll
     for (int i = 0; i < G::BI; ++i) {
         const int s = (wave * G::BI + i) * kWave + lane;
-        const int r = F8 ? s >> 1 : s >> 2;
-        const int c = F8 ? (s & 1) ^ ((r >> 3) & 1) : (s & 3) ^ ((r >> 2) & 3);
+        // F4 rows are one 16-byte chunk per K-slice (32 codes)
+        const int r = G::F4 ? s : F8 ? s >> 1 : s >> 2;
+        const int c = G::F4 ? 0 : F8 ? (s & 1) ^ ((r >> 3) & 1) : (s & 3) ^ ((r >> 2) & 3);
         int wr;
         if (gated(MODE)) {
             int n = nt * (kBN / 2) + (r & (kBN / 2 - 1));
@@ -264,8 +277,54 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
             if (wr >= p.N)
                 wr = p.N - 1;
         }
-        q.b_off[i] = F8 ? (uint32_t)wr * ld + c * 16 : ((uint32_t)wr * ld + c * 8) * 2u;
+        q.b_off[i] = G::F4 ? (uint32_t)wr * (ld / 2)
+                     : F8 ? (uint32_t)wr * ld + c * 16 : ((uint32_t)wr * ld + c * 8) * 2u;
     }
+}
+
+// F4: the weight rows of this lane's fragments (row lane % 32 of each of the
+// wave's weight tiles j, mapped as the requests map stage rows) and the
+// offsets of their scale bytes: NVFP4 one E4M3 byte per 16 inputs, MXFP4 one
+// E8M0 byte per 32, rows of K / 16 or K / 32 bytes.
+template <int BM, int MODE, int WF>
+__device__ __forceinline__ void scale_rows(const GemmProblem &p, int e, int nt, Scales<BM> &sc) {
+    constexpr int TN = Geo<BM>::TN;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wn = (threadIdx.x / kWave) & 1;
+    const uint32_t row_bytes = (uint32_t)p.K / (WF == kWNv4 ? 16 : 32);
+    sc.base = (const uint8_t *)p.Bscale + (size_t)e * p.N * row_bytes;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        int wr;
+        if (gated(MODE)) {
+            // gate rows for j < TN / 2, the matching up rows after them
+            const int jj = j < TN / 2 ? j : j - TN / 2;
+            int n = nt * (kBN / 2) + wn * (kBN / 4) + jj * 32 + (lane & 31);
+            if (n >= p.I)
+                n = p.I - 1;
+            wr = j < TN / 2 ? n : p.I + n;
+        } else {
+            wr = nt * kBN + wn * (kBN / 2) + j * 32 + (lane & 31);
+            if (wr >= p.N)
+                wr = p.N - 1;
+        }
+        sc.off[j] = (uint32_t)wr * row_bytes;
+    }
+}
+
+// F4: the 16 scale bytes of block blk of each of this lane's rows (NVFP4:
+// 8 K-slices, two bytes each; MXFP4: 16 K-slices, one byte each). Bytes past
+// the expert's scales read as zeros (a partial last block).
+template <int BM, int WF>
+__device__ __forceinline__ void load_scales(const GemmProblem &p, const Scales<BM> &sc, int blk,
+                                            u32x4 (&dst)[Geo<BM>::TN]) {
+    const uint32_t row_bytes = (uint32_t)p.K / (WF == kWNv4 ? 16 : 32);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(sc.base), (short)0, (int)((uint32_t)p.N * row_bytes), kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < Geo<BM>::TN; ++j)
+        dst[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, sc.off[j] + 16u * (uint32_t)blk, 0, 0));
 }
 
 // Piece m (A pieces first, then B pieces) of K-slice ks into one stage.
@@ -281,7 +340,7 @@ __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmPro
     } else {
         const int i = m - G::AI;
         buffer_to_lds16(q.b_base, stage + BM * 4 + (wave * G::BI + i) * kWave,
-                        q.b_off[i] + (uint32_t)ks * (kBK * (F8 ? 1 : 2)));
+                        q.b_off[i] + (uint32_t)ks * (G::F4 ? kBK / 2 : kBK * (F8 ? 1 : 2)));
     }
 }
 
@@ -293,6 +352,8 @@ struct Frags {
     bf16x8 a[2][Geo<BM>::TM];
     bf16x8 b[2][Geo<BM>::TN];
     u32x4 braw[WF == kWF8 ? Geo<BM>::TN : 1];
+    // F4: 16 codes per lane, 8 for each sub-step (bytes 0-3, then 4-7)
+    u32x2 b4[Geo<BM, WF>::F4 ? Geo<BM>::TN : 1];
 };
 
 // One 16-byte fragment read of a stage, through a __restrict__ pointer of
@@ -300,6 +361,11 @@ struct Frags {
 // the compiler tell it from the requests still in flight into other stages.
 __device__ __forceinline__ u32x4 lds_frag(const uint4 *__restrict__ S, int slot) {
     return __builtin_bit_cast(u32x4, S[slot]);
+}
+
+// Half h (8 bytes) of a 16-byte slot, the same way.
+__device__ __forceinline__ u32x2 lds_frag8(const uint4 *__restrict__ S, int slot, int h) {
+    return reinterpret_cast<const u32x2 *__restrict__>(S + slot)[h];
 }
 
 // Slot `slot`'s weight fragment j from the raw FP8 bytes: e4m3 to bf16 is
@@ -315,6 +381,53 @@ __device__ __forceinline__ void cvt_b(Frags<BM, kWF8> &f, int slot, int j) {
         o[2 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     }
     f.b[slot][j] = __builtin_bit_cast(bf16x8, (u32x4){o[0], o[1], o[2], o[3]});
+}
+
+// Slot `slot`'s weight fragment j from the raw E2M1 codes (8 per lane, low
+// nibble first) times this lane's scale of them, exactly: an E2M1 value
+// times an E4M3 or a power-of-two scale has at most six significant bits.
+// MXFP4's power-of-two scale (E8M0, NaN included) is the conversion's own
+// scale operand, which multiplies by a power of two exactly; NVFP4's E4M3
+// scale is not a power of two, so those codes go to fp32 first, are
+// multiplied there and rounded to bf16 (exactly).
+template <int BM, int WF>
+__device__ __forceinline__ void cvt_b4(Frags<BM, WF> &f, int slot, int j, float scale) {
+    const uint32_t w = slot == 0 ? f.b4[j].x : f.b4[j].y;
+    uint32_t o[4];
+    if constexpr (WF == kWMx4) {
+        o[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+        o[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+        o[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+        o[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+    } else {
+        const f32x2_hw v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+        const f32x2_hw v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        const f32x2_hw v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        const f32x2_hw v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        o[0] = pack_bf16x2(v0.x * scale, v0.y * scale);
+        o[1] = pack_bf16x2(v1.x * scale, v1.y * scale);
+        o[2] = pack_bf16x2(v2.x * scale, v2.y * scale);
+        o[3] = pack_bf16x2(v3.x * scale, v3.y * scale);
+    }
+    f.b[slot][j] = __builtin_bit_cast(bf16x8, (u32x4){o[0], o[1], o[2], o[3]});
+}
+
+// F4: this lane's scale of the current K-slice from the front of its scale
+// block, which then moves on by one slice (MXFP4: one byte; NVFP4: two, of
+// which lane half h takes byte h, the 16-input group its K range is in).
+template <int WF>
+__device__ __forceinline__ float next_scale(u32x4 &blk, int h) {
+    constexpr int S = WF == kWNv4 ? 16 : 8;
+    const uint32_t b = (WF == kWNv4 ? blk.x >> (8 * h) : blk.x) & 0xffu;
+    blk.x = __builtin_amdgcn_alignbit(blk.y, blk.x, S);
+    blk.y = __builtin_amdgcn_alignbit(blk.z, blk.y, S);
+    blk.z = __builtin_amdgcn_alignbit(blk.w, blk.z, S);
+    blk.w = blk.w >> S;
+    if constexpr (WF == kWMx4)
+        return e8m0_to_f32(b);
+    // E4M3 -> bf16 exactly (scale 1), then fp32
+    const uint32_t pr = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(b, 1.0f, false));
+    return bf16_to_f32(pr & 0xffffu);
 }
 
 // Fragment m from a stage into a slot, in the order the MFMAs of a sub-step
@@ -449,6 +562,64 @@ __device__ __forceinline__ void ring_step_f8(const uint4 *__restrict__ S, const 
     }
 }
 
+// The same step on 4-bit E2M1 weights. The codes of both sub-steps come in
+// one 8-byte read per lane and weight tile (in the previous step's sub-step
+// 1); lane half h of sub-step kk covers K = 16 h + 8 kk .. + 7 of the slice,
+// as for FP8, and sc[j] is this lane's scale of its row of tile j in the
+// slice. `late`: scale loads were issued after the requests of the stage
+// waited for here, so TN more loads may still be in flight.
+template <int BM, int MODE, int NS, int WF>
+__device__ __forceinline__ void ring_step_f4(const uint4 *__restrict__ S, const uint4 *__restrict__ Snext,
+                                             uint4 *__restrict__ Sfill, const GemmProblem &p,
+                                             const Req<BM, WF> &q, int ks, Frags<BM, WF> &f,
+                                             f32x16 (&acc)[Geo<BM>::TM][Geo<BM>::TN],
+                                             const int (&a_slot)[2], int b_slot, const int *b_toff,
+                                             const float (&sc)[Geo<BM>::TN], bool late) {
+    using G = Geo<BM, WF>;
+    constexpr int TM = G::TM, TN = G::TN;
+    const int h = (threadIdx.x & (kWave - 1)) >> 5;
+    fence();
+    // sub-step 0: MFMAs on slot 0, each weight fragment converted just
+    // before its first MFMA; token fragments of sub-step 1 into slot 1 and
+    // its weight fragments converted
+#pragma unroll
+    for (int n = 0; n < G::NQ; ++n) {
+        const int i = n / TN, j = n % TN;
+        if (n < TN)
+            cvt_b4<BM, WF>(f, 0, j, sc[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[0][j], f.a[0][i], acc[i][j], 0, 0, 0);
+        if (n < TM)
+            f.a[1][n] = __builtin_bit_cast(bf16x8, lds_frag(S, a_slot[1] + n * 128));
+        else if (n - TM < TN)
+            cvt_b4<BM, WF>(f, 1, n - TM, sc[n - TM]);
+        fence();
+    }
+    if (late)
+        wait_vmcnt<(NS - 3) * G::PER + TN>();
+    else
+        wait_vmcnt<(NS - 3) * G::PER>();
+    __builtin_amdgcn_s_barrier();
+    fence();
+    // sub-step 1: MFMAs on slot 1; the next step's token fragments and
+    // codes, and the refill of the stage read in the previous step
+    constexpr int NM = TM + TN + G::PER;
+#pragma unroll
+    for (int n = 0; n < G::NQ; ++n) {
+        const int i = n / TN, j = n % TN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[1][j], f.a[1][i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int m = n * NM / G::NQ; m < (n + 1) * NM / G::NQ; ++m) {
+            if (m < TM)
+                f.a[0][m] = __builtin_bit_cast(bf16x8, lds_frag(Snext, a_slot[0] + m * 128));
+            else if (m < TM + TN)
+                f.b4[m - TM] = lds_frag8(Snext, b_slot + b_toff[m - TM], h);
+            else
+                request<BM, MODE, WF>(Sfill, p, q, ks, m - TM - TN);
+        }
+        fence();
+    }
+}
+
 // Prologue: the first NS - 1 slices of the first tile into stages 0 ..
 // NS - 2.
 template <int BM, int MODE, int NS, int WF>
@@ -466,6 +637,9 @@ template <int BM, int MODE, int NS, int WF>
 __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_tiles) {
     using G = Geo<BM, WF>;
     constexpr bool F8 = G::F8;
+    constexpr bool F4 = G::F4;
+    // F4: K-slices per scale block (16 bytes of a row's scales)
+    constexpr int SBS = WF == kWNv4 ? 8 : 16;
     constexpr int TM = G::TM, TN = G::TN;
     constexpr int kAhead = NS - 1;           // stages requested ahead of the one multiplied
     __shared__ uint4 ring[NS * G::STAGE];
@@ -550,6 +724,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     }
     int ne, nrow0, nrow_end, nnt;            // the next tile (if any)
     bool has_next = place<BM>(tl, 1, ne, nrow0, nrow_end, nnt);
+    // F4: the scale rows of this tile and the next, and this lane's scale
+    // blocks: the one being used (shifted on by a K-slice each step) and the
+    // one after it, loaded a block ahead (the first one here, before the
+    // first requests, so the first wait for it is a short one)
+    Scales<BM> scs, nscs;
+    u32x4 scur[F4 ? TN : 1], snext[F4 ? TN : 1];
+    if constexpr (F4) {
+        scale_rows<BM, MODE, WF>(p, e, nt, scs);
+        load_scales<BM, WF>(p, scs, 0, scur);
+    }
     int nraw[G::AI];
     int nvalid = gathered_rows<BM>(p, has_next ? nrow0 : row0, has_next ? nrow_end : row_end, nraw);
 
@@ -568,8 +752,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
     int a_slot[2], b_slot[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        // F8: lane half h of sub-step kk covers chunk 2 h + kk of the slice
-        const int ch = F8 ? 2 * (lane >> 5) + kk : kk * 2 + (lane >> 5);
+        // F8, F4: lane half h of sub-step kk covers chunk 2 h + kk of the slice
+        const int ch = F8 || F4 ? 2 * (lane >> 5) + kk : kk * 2 + (lane >> 5);
         a_slot[kk] = slot_of(a_tile_row + (lane & 31), ch);
         b_slot[kk] = BM * 4 + slot_of(b_row0 + (lane & 31), ch);
     }
@@ -581,6 +765,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             b_toff[j] /= 2;
+    }
+    if constexpr (F4) {
+        // the lane's row, one 16-byte slot of 32 codes (lane half h reads
+        // its 8 bytes 8 h ..)
+        b_slot[0] = BM * 4 + b_row0 + (lane & 31);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            b_toff[j] /= 4;
     }
 
     const int KT = p.K / kBK;
@@ -595,6 +787,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 #pragma unroll
         for (int j = 0; j < TN; ++j)
             f.braw[j] = __builtin_bit_cast(u32x4, ring[b_slot[0] + b_toff[j]]);
+    } else if constexpr (F4) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            f.a[0][i] = __builtin_bit_cast(bf16x8, ring[a_slot[0] + i * 128]);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            f.b4[j] = lds_frag8(ring, b_slot[0] + b_toff[j], lane >> 5);
     } else {
 #pragma unroll
         for (int m = 0; m < G::NF; ++m)
@@ -611,6 +810,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 
     f32x16 acc[TM][TN];
     int sl = 0;                              // ring slot of the next step (steps done % NS)
+    int late = 0;                            // F4: steps whose wait allows the scale loads
     for (int ti = 1;; ++ti) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -620,6 +820,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         // F8: this tile's block scales (lane b: K-block b) and the units the
         // sums are kept in (the scale of the K-block being multiplied)
         float sc_gate = 0.0f, sc_up = 0.0f, rho_gate = 0.0f, rho_up = 0.0f;
+        if constexpr (F4) {
+            if (has_next)
+                scale_rows<BM, MODE, WF>(p, ne, nnt, nscs);
+            else
+                nscs = scs;                  // loaded again, never used
+        }
         if constexpr (F8) {
             sc_gate = req.scale[0];
             sc_up = req.scale[1];
@@ -666,6 +872,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                 }
                 ring_step_f8<BM, MODE, NS>(S, Sn, Sf, p, req, ks, f, acc, a_slot, b_slot[0], b_toff,
                                            rescale, r_gate, r_up);
+            } else if constexpr (F4) {
+                // at the start of each scale block the next block's loads
+                // (this tile's, or the next tile's first): issued after the
+                // requests of the next two stages waited for, so those two
+                // waits allow TN more loads in flight
+                if (kt % SBS == 0) {
+                    const int nb = kt / SBS + 1;
+                    if (nb * SBS < KT)
+                        load_scales<BM, WF>(p, scs, nb, snext);
+                    else
+                        load_scales<BM, WF>(p, nscs, 0, snext);
+                    late = 2;
+                }
+                float sc[TN];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+                    sc[j] = next_scale<WF>(scur[j], lane >> 5);
+                ring_step_f4<BM, MODE, NS, WF>(S, Sn, Sf, p, req, ks, f, acc, a_slot, b_slot[0], b_toff,
+                                               sc, late > 0);
+                late = late > 0 ? late - 1 : 0;
+                if (kt % SBS == SBS - 1 || kt == KT - 1) {
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+                        scur[j] = snext[j];
+                }
             } else {
                 ring_step<BM, MODE, NS>(S, Sn, Sf, p, req, ks, f, acc, a_slot, b_slot, b_toff);
             }
@@ -846,6 +1077,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
 
         if (!has_next)
             break;
+        if constexpr (F4)
+            scs = nscs;
         e = ne;
         row0 = nrow0;
         row_end = nrow_end;
@@ -916,7 +1149,7 @@ hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
     return hipGetLastError();
 }
 
-#ifndef MOE_GROUPED_F8_UNIT
+#if !defined(MOE_GROUPED_F8_UNIT) && !defined(MOE_GROUPED_F4_UNIT)
 template <int MODE>
 hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
     int segs = 1;
@@ -936,7 +1169,27 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
 
 }  // namespace
 
-#ifdef MOE_GROUPED_F8_UNIT
+#if defined(MOE_GROUPED_F4_UNIT)
+// NVFP4 and MXFP4 weights: 256-row tiles (the scales are applied as the
+// codes are converted, so the accumulators need no rescaling and stay in
+// AGPRs, as for bf16)
+hipError_t launch_grouped_f4(const GemmProblem &p, hipStream_t stream) {
+    if (p.nvfp4) {
+        switch (p.mode) {
+        case kGateUp: return launch_bm<256, kGateUp, kWNv4>(p, stream);
+        case kGateUpLimit: return launch_bm<256, kGateUpLimit, kWNv4>(p, stream);
+        case kUpRelu2: return launch_bm<256, kUpRelu2, kWNv4>(p, stream);
+        default: return launch_bm<256, kDown, kWNv4>(p, stream);
+        }
+    }
+    switch (p.mode) {
+    case kGateUp: return launch_bm<256, kGateUp, kWMx4>(p, stream);
+    case kGateUpLimit: return launch_bm<256, kGateUpLimit, kWMx4>(p, stream);
+    case kUpRelu2: return launch_bm<256, kUpRelu2, kWMx4>(p, stream);
+    default: return launch_bm<256, kDown, kWMx4>(p, stream);
+    }
+}
+#elif defined(MOE_GROUPED_F8_UNIT)
 // FP8 weights: 128-row tiles, whose 128 accumulators per lane stay in VGPRs
 // (this unit is compiled with the MFMAs' VGPR form) so the per-K-block
 // rescale is one multiply per accumulator; the raw weight bytes fit beside
@@ -964,18 +1217,25 @@ bool grouped_supported(const GemmProblem &p) {
     // shared segments: bf16 weights beside bf16 (or decoded) experts, every
     // weight offset of a slice below kPastA
     const long long b2_rows = gated(p.mode) ? (long long)p.b2_up + p.I : p.N;
+    // NVFP4, MXFP4: the caller's codes and scales as stored, no shared
+    // segments (the shared expert's weights are bf16)
+    const bool f4 = p.nvfp4 || p.mxfp4;
+    const bool f4_ok = !f4 || (p.E2 == 0 && !p.b_compact && p.Bscale != nullptr);
     const bool e2_ok = p.E2 == 0 ||
-                       (p.E2 > 0 && !p.fp8 && p.offsets != nullptr && p.B2 != nullptr &&
+                       (p.E2 > 0 && !p.fp8 && !f4 && p.offsets != nullptr && p.B2 != nullptr &&
                         b2_rows * p.b2_ld * 2 < (long long)kPastA && p.b2_ld >= p.K);
-    return !p.affine4 && !p.nvfp4 && !p.mxfp4 && fp8_ok && e2_ok && p.scatter == nullptr && p.K % kBK == 0 &&
+    const long long b_bytes = p.fp8 ? (long long)p.N * p.K : f4 ? (long long)p.N * p.K / 2
+                                                                : (long long)p.N * p.K * 2;
+    return !p.affine4 && fp8_ok && f4_ok && e2_ok && p.scatter == nullptr && p.K % kBK == 0 &&
            p.K / kBK >= kStagesSmall && (p.offsets == nullptr || p.E + p.E2 <= kMaxE) &&
-           a_rows * p.lda * 2 < (long long)kPastA &&
-           (long long)p.N * p.K * (p.fp8 ? 1 : 2) < (long long)kPastA;
+           a_rows * p.lda * 2 < (long long)kPastA && b_bytes < (long long)kPastA;
 }
 
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream) {
     if (p.fp8)
         return launch_grouped_f8(p, stream);
+    if (p.nvfp4 || p.mxfp4)
+        return launch_grouped_f4(p, stream);
     switch (p.mode) {
     case kGateUp: return launch_mode<kGateUp>(p, stream);
     case kGateUpLimit: return launch_mode<kGateUpLimit>(p, stream);

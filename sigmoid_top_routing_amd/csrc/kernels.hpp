@@ -94,12 +94,10 @@ struct GemmProblem {
 
 hipError_t launch_gemm(const GemmProblem &p, hipStream_t stream);
 
-// The 4-bit (p.affine4), block-FP8 (p.fp8) or NVFP4 (p.nvfp4) weights of
-// p's experts that have rows (offsets set), decoded once to bf16 (scale * q
-// + bias, scale * e4m3 value, or e4m3 scale * e2m1 value, in fp32, rounded
-// to nearest even; the NVFP4 product is exact in bf16 and its global scale
-// is left to Bglobal) into out: [experts with rows][N][K], in expert order
-// (b_compact).
+// The 4-bit (p.affine4) or block-FP8 (p.fp8) weights of p's experts that
+// have rows (offsets set), decoded once to bf16 (scale * q + bias or scale
+// * e4m3 value, in fp32, rounded to nearest even) into out: [experts with
+// rows][N][K], in expert order (b_compact).
 hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t stream);
 
 // The persistent direct-to-LDS kernel (bf16 weights, K a multiple of 32 and
@@ -108,6 +106,8 @@ bool grouped_supported(const GemmProblem &p);
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream);
 // Its block-FP8 form (grouped_gemm_f8.hip); launch_grouped calls it.
 hipError_t launch_grouped_f8(const GemmProblem &p, hipStream_t stream);
+// NVFP4 / MXFP4 weights on the MFMA tiles (grouped_gemm_f4.hip)
+hipError_t launch_grouped_f4(const GemmProblem &p, hipStream_t stream);
 
 // The same problem in the weight-streaming (decode) form: few A rows per
 // expert, every touched weight row read once, v_dot2 accumulation.
