@@ -588,10 +588,15 @@ __device__ __forceinline__ void ring_step_f4(const uint4 *__restrict__ S, const 
         if (n < TN)
             cvt_b4<BM, WF>(f, 0, j, sc[j]);
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[0][j], f.a[0][i], acc[i][j], 0, 0, 0);
-        if (n < TM)
+        if (n < TM) {
             f.a[1][n] = __builtin_bit_cast(bf16x8, lds_frag(S, a_slot[1] + n * 128));
-        else if (n - TM < TN)
+        } else if (n - TM < TN) {
             cvt_b4<BM, WF>(f, 1, n - TM, sc[n - TM]);
+            // here, between these MFMAs: left alone, the compiler sinks the
+            // conversions to their first use, all of them after the last
+            // MFMA of the sub-step, where the next MFMAs wait for them
+            __asm__ volatile("" : "+v"(f.b[1][n - TM]));
+        }
         fence();
     }
     if (late)
