@@ -115,7 +115,9 @@ typedef struct {
     int32_t row_invariant; /* 0: decode-sized batches (T * k <= 2 E) take the
                              weight-streaming form, whose fp32 sums differ from the
                              MFMA tiles' in the last bits; 1: every batch takes the
-                             MFMA tiles (4-bit experts decoded to bf16 first), so a
+                             MFMA tiles (4-bit experts decoded to bf16 first;
+                             block-FP8, NVFP4 and MXFP4 codes on their own
+                             tiles), so a
                              token's output bits do not depend on how many tokens
                              share the call (TensorFold issue #548, the kernel
                              registry's family rule), at the tiles' cost for decode
