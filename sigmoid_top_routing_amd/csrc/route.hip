@@ -21,12 +21,13 @@
 // also adds the slices, k_route_fold).
 //
 // The logits are T*E*(H/64) independent fma chains of length 64, each in h
-// order, and each (t, e)'s slices are added in order. k_logits_ring (H a
-// multiple of 128) and k_logits (other H) run a lane per token; there the
-// broadcast LDS reads of the router rows are what bound them. Batches of at
-// most 8 tokens and 32 experts take k_logits_part (the slices spread over
-// the chip) and k_route_fold; at most 8 tokens with more experts,
-// k_logits_few.
+// order, and each (t, e)'s slices are added in order. k_logits_bc runs a
+// lane per token, the router weights brought to the fmas by DPP from
+// registers that hold 16 of them each; k_logits (the same lanes, the router
+// rows read from LDS by every lane at once) takes batches whose byte
+// offsets reach 2^31. Batches of at most 8 tokens and 32 experts take
+// k_logits_part (the slices spread over the chip) and k_route_fold; at most
+// 8 tokens with more experts, k_logits_few.
 //
 // k_topk reads z, applies the sigmoid (or softmax) and the bias, and picks the top k of
 // each token by the 64-bit (order key, ~index) candidates: with one expert
@@ -44,327 +45,248 @@ namespace {
 
 constexpr int kMaxThreads = 256;
 
-// k_logits: one lane per token, C experts per wave (C chains per lane).
-// A workgroup of 4 waves owns 64 tokens and 4*C experts and walks H in
-// chunks of kHC. Per chunk it stages the 64 token rows, converted once to
-// fp32 for the four waves that share them (a lane reads 4 of its own h per
-// 16-byte LDS read; rows are padded by 16 bytes so the 16 lanes of a pass
-// hit distinct banks), and the experts' router rows (every lane of a wave
-// reads the same address: one broadcast per 4 h and expert). The next
-// chunk's global loads are issued before the current chunk's fmas and
-// written to the other LDS buffer after them; within a chunk the LDS reads
-// of the next 16 h are issued before the fmas of the current 16. Each slice
-// of 64 h is one chain in h order, added to z when it ends.
 constexpr int kTok = 64;                 // tokens per workgroup (one per lane)
-constexpr int kHC = 256;                 // h per LDS chunk
-constexpr int kXRow = kHC / 4 + 1;       // float4 per staged token row (+ pad)
-constexpr int kWRow = kHC / 4 + 1;       // float4 per staged router row (+ pad)
-constexpr int kXLoads = kTok * (kHC / 8) / kMaxThreads;   // uint4 x loads per thread
 
-template <int C>
-__global__ __launch_bounds__(kMaxThreads) void k_logits(const uint16_t *__restrict__ x,
-                                                        const float *__restrict__ Wr, int T,
-                                                        int H, int E, float *__restrict__ z) {
-    constexpr int EB = 4 * C;                                  // experts per workgroup
-    constexpr int WLOADS = (EB * (kHC / 4) + kMaxThreads - 1) / kMaxThreads;
-    __shared__ float4 xs[2][kTok * kXRow];
-    __shared__ float4 ws[2][EB * kWRow];
+// k_logits_bc: a lane per token (64 tokens per workgroup) and CE experts
+// (8 or 16) per workgroup; the eight waves share those tokens and experts and
+// take alternate slices: in round m, wave w runs the CE chains of slice
+// 8m + w.
+// Eight waves (two per SIMD) because one wave alone cannot issue its fmas
+// back to back. Each wave moves its own 64 token rows' 64 h for the next
+// round (bf16) into its own two LDS stages by range-checked buffer loads,
+// so it only ever waits on its own requests; a token row's 16-byte pieces
+// (8 h) sit at piece c ^ (t / 2 mod 8) of its 128-byte LDS row, so 16 lanes
+// reading their piece c hit 16 distinct 16-byte bank groups.
+//
+// The router weights go to registers, not LDS: lane l loads h 4(l mod 16) ..
+// +3 of each of the CE router rows (the four 16-lane rows of the wave load
+// the same 256 bytes), a round ahead, and the fma of h takes its weight from
+// lane h / 4 of the lane's own 16-lane row through DPP (row_newbcast), so
+// one register carries 16 weights of a slice. The chains themselves are
+// unchanged: one v_fmac per term, h ascending from +0.
+//
+// After a round the eight slice partials go through LDS and wave w adds
+// them, in slice order, to the running logits of experts e0 + w CE/8 ..
+// +CE/8-1, which it writes at the end. A slice past the last one reads zeros, so its partial
+// is +0, and adding +0 leaves a running sum that started at +0 unchanged (it
+// is never -0): the fold has no branches.
+constexpr int kBcWaves = 8;                           // waves per workgroup
+constexpr int kBcThreads = kBcWaves * kWave;
+constexpr int kBcStage = kTok * 8;                    // 16-byte x pieces per stage
+constexpr uint32_t kBcPast = 0x80000000u;             // an offset that reads zeros
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int t0 = blockIdx.x * kTok;
-    const int e0 = blockIdx.y * EB;
+// acc = fma(w of lane N of this lane's 16-lane row, x, acc). A DPP
+// instruction must not read a VGPR that a VALU instruction wrote in the two
+// instructions before it; the callers keep every write of w, x and acc
+// further away than that (w comes from global loads, x is converted a piece
+// ahead, acc is written by the fma of the same chain CE instructions earlier
+// or by the zeroing at the round's start).
+template <int N>
+__device__ __forceinline__ void fmac_bcast(float &acc, float w, float x) {
+    asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc)
+                 : "v"(w), "v"(x), "n"(N));
+}
 
-    uint4 xreg[kXLoads];
-    float4 wreg[WLOADS];
-    // chunk h0 .. h0 + hc - 1 (hc a multiple of 64) into registers
-    auto load = [&](int h0, int hc) {
-        const int q = hc / 8;                                  // uint4 per token row
+// the 8 h of a 16-byte piece of a bf16 row, as fp32
+__device__ __forceinline__ void bc_convert(const uint4 v, float (&xs)[8]) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            const int idx = tid + i * kMaxThreads;
-            const int r = idx / (kHC / 8), c = idx % (kHC / 8);
-            const int t = t0 + r;
-            xreg[i] = (t < T && c < q) ? *reinterpret_cast<const uint4 *>(x + (size_t)t * H + h0 + 8 * c)
-                                       : make_uint4(0, 0, 0, 0);
-        }
-        const int qw = hc / 4;
-#pragma unroll
-        for (int i = 0; i < WLOADS; ++i) {
-            const int idx = tid + i * kMaxThreads;
-            const int r = idx / (kHC / 4), c = idx % (kHC / 4);
-            const int e = e0 + r;
-            wreg[i] = (r < EB && e < E && c < qw)
-                          ? *reinterpret_cast<const float4 *>(Wr + (size_t)e * H + h0 + 4 * c)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    auto store = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < kXLoads; ++i) {
-            const int idx = tid + i * kMaxThreads;
-            float4 *row = xs[buf] + (idx / (kHC / 8)) * kXRow + 2 * (idx % (kHC / 8));
-            const uint4 v = xreg[i];
-            row[0] = make_float4(bf16_to_f32(v.x & 0xffffu), bf16_to_f32(v.x >> 16),
-                                 bf16_to_f32(v.y & 0xffffu), bf16_to_f32(v.y >> 16));
-            row[1] = make_float4(bf16_to_f32(v.z & 0xffffu), bf16_to_f32(v.z >> 16),
-                                 bf16_to_f32(v.w & 0xffffu), bf16_to_f32(v.w >> 16));
-        }
-#pragma unroll
-        for (int i = 0; i < WLOADS; ++i) {
-            const int idx = tid + i * kMaxThreads;
-            if (idx / (kHC / 4) < EB)
-                ws[buf][(idx / (kHC / 4)) * kWRow + idx % (kHC / 4)] = wreg[i];
-        }
-    };
-
-    float acc[C], zc[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        acc[c] = 0.0f;
-        zc[c] = 0.0f;
-    }
-    // the slice just finished goes into z, and the next one starts at +0
-    auto fold = [&]() {
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            zc[c] = zc[c] + acc[c];
-            acc[c] = 0.0f;
-        }
-    };
-    // 16 h: x[i] holds h 4i..4i+3 of this lane's token, w[c][i] the same h
-    // of expert c
-    // (the chains alternate instruction by instruction: in-order issue then
-    // never waits on the previous fma of the same chain)
-    auto fma16 = [&](const float4 (&xv)[4], const float4 (&wv)[C][4]) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-                acc[c] = __builtin_fmaf(xv[i].x, wv[c][i].x, acc[c]);
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-                acc[c] = __builtin_fmaf(xv[i].y, wv[c][i].y, acc[c]);
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-                acc[c] = __builtin_fmaf(xv[i].z, wv[c][i].z, acc[c]);
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-                acc[c] = __builtin_fmaf(xv[i].w, wv[c][i].w, acc[c]);
-        }
-    };
-
-    int hc = H < kHC ? H : kHC;
-    load(0, hc);
-    int buf = 0;
-    for (int h0 = 0; h0 < H; h0 += kHC) {
-        store(buf);
-        __syncthreads();
-        const int hn = h0 + kHC;
-        const int hc_next = H - hn < kHC ? H - hn : kHC;
-        if (hn < H)
-            load(hn, hc_next);
-        const float4 *xr = xs[buf] + lane * kXRow;
-        const float4 *wr = ws[buf] + (wave * C) * kWRow;
-        float4 xa[4], xb[4];
-        float4 wa[C][4], wb[C][4];
-        auto read16 = [&](int g, float4 (&xv)[4], float4 (&wv)[C][4]) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xv[i] = xr[4 * g + i];
-#pragma unroll
-            for (int c = 0; c < C; ++c)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    wv[c][i] = wr[c * kWRow + 4 * g + i];
-        };
-        const int groups = hc / 16;          // hc is a multiple of 64: 4 groups a slice
-        read16(0, xa, wa);
-        for (int g = 0; g < groups; g += 2) {
-            read16(g + 1, xb, wb);
-            __builtin_amdgcn_sched_barrier(0);
-            fma16(xa, wa);
-            __builtin_amdgcn_sched_barrier(0);
-            read16(g + 2 < groups ? g + 2 : g + 1, xa, wa);   // no branch: no copies
-            __builtin_amdgcn_sched_barrier(0);
-            fma16(xb, wb);
-            if ((g & 3) == 2)
-                fold();
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        hc = hc_next;
-        buf ^= 1;
-        __syncthreads();                    // the buffer refilled next is no longer read
-    }
-    const int t = t0 + lane;
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int e = e0 + wave * C + c;
-        if (t < T && e < E)
-            z[(size_t)t * E + e] = zc[c];
+    for (int i = 0; i < 4; ++i) {
+        xs[2 * i] = __uint_as_float(u[i] << 16);
+        xs[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
     }
 }
 
-// k_logits_ring: the same lanes as k_logits<2> (a lane per token,
-// two experts per wave: 64 tokens and 8 experts per workgroup), for H a
-// multiple of 128. The operands come in by range-checked buffer loads
-// straight into a ring of 4 LDS stages of 128 h (x as bf16, the router rows
-// as fp32), requested three stages ahead, so the chains do not wait on
-// memory once the ring is full; no registers hold staged data. A token row's
-// 16-byte pieces (8 h) sit at piece c ^ (t % 16) of its LDS row, so the 16
-// lanes of a 16-byte read hit distinct banks; the router rows are read by
-// every lane at once (broadcast). A stage holds two slices.
-constexpr int kRingH = 128;
-constexpr int kRingStages = 4;
-constexpr int kRingX = kTok * (kRingH / 8);             // 16-byte x pieces per stage
-constexpr int kRingW = 8 * (kRingH / 4);                // 16-byte router pieces per stage
-constexpr int kRingStage = kRingX + kRingW;             // 20 KB
-constexpr int kRingPer = kRingStage / kMaxThreads;      // requests per thread per stage
-constexpr uint32_t kRingPast = 0x80000000u;             // an offset that reads zeros
+// the 8 CE fmas of piece P (h 8P .. 8P+7 of the slice), h ascending
+template <int CE, int P>
+__device__ __forceinline__ void bc_piece(float (&acc)[CE], const uint4 (&w)[CE],
+                                         const float (&xs)[8]) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int e = 0; e < CE; ++e) {
+                const uint32_t wj = j == 0 ? w[e].x : j == 1 ? w[e].y : j == 2 ? w[e].z : w[e].w;
+                if (half == 0)
+                    fmac_bcast<2 * P>(acc[e], __uint_as_float(wj), xs[j]);
+                else
+                    fmac_bcast<2 * P + 1>(acc[e], __uint_as_float(wj), xs[4 + j]);
+            }
+        }
+    }
+}
 
-// One stage: the chains over stage S (128 h); the refill of stage F with h
-// block sf (none when sf < 0). One call site, so the LDS reads of S and the
-// loads into F share one alias scope and the compiler does not order the
-// reads behind loads still in flight; the caller's waits do that.
-__device__ __forceinline__ void ring_stage(const uint4 *__restrict__ S, uint4 *__restrict__ F,
-                                           const uint16_t *x, const float *Wr,
-                                           const uint32_t (&xoff)[kRingPer - 1], uint32_t woff,
-                                           int sf, float &acc0, float &acc1) {
+// One round of a wave. Request its next stage F (slice sn, zeros when fill
+// is false) and that slice's router weights into wn; wait for this round's
+// stage R + s_at and weights w; run the CE chains; exchange the partials
+// through R + p_at and add the round's eight, in slice order, to z. Every
+// LDS access but the requests goes through R: one alias scope for them and
+// one for F, so the compiler neither orders the reads behind requests still
+// in flight nor waits for those requests itself; the explicit wait does that.
+template <int CE>
+__device__ __forceinline__ void bc_round(uint4 *__restrict__ R, int s_at, int p_at,
+                                         uint4 *__restrict__ F, const uint16_t *x,
+                                         __amdgpu_buffer_rsrc_t wrsrc, const uint32_t (&xoff)[8],
+                                         const uint32_t (&woff)[CE], int sn, bool fill,
+                                         const uint4 (&w)[CE], uint4 (&wn)[CE],
+                                         float (&z)[CE / kBcWaves]) {
+    constexpr int Q = CE / kBcWaves;                    // experts this wave adds up
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (sf >= 0) {
 #pragma unroll
-        for (int q = 0; q < kRingPer - 1; ++q)
-            buffer_to_lds16(x, F + (q * 4 + wave) * kWave, xoff[q] + sf * (kRingH * 2));
-        buffer_to_lds16(Wr, F + kRingX + wave * kWave, woff + sf * (kRingH * 4));
-    }
-    const int t = lane;
-    const uint4 *xrow = S + t * (kRingH / 8);
-    const float4 *wa = reinterpret_cast<const float4 *>(S + kRingX) + (2 * wave) * (kRingH / 4);
-    const float4 *wb = wa + kRingH / 4;
-    // The stage's two slices (h 0..63 and 64..127) run side by side: four
-    // chains per lane (2 experts x 2 slices). 8 h per group and slice: one
-    // 16-byte x piece, two float4 of each router row.
-    auto read = [&](int g, uint4 (&xv)[2], float4 (&av)[2][2], float4 (&bv)[2][2]) {
+    for (int q = 0; q < 8; ++q)
+        buffer_to_lds16(x, F + q * kWave, fill ? xoff[q] + (uint32_t)sn * 128u : kBcPast);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int q = g + 8 * j;
-            xv[j] = xrow[q ^ (t & 15)];
-            av[j][0] = wa[2 * q];
-            av[j][1] = wa[2 * q + 1];
-            bv[j][0] = wb[2 * q];
-            bv[j][1] = wb[2 * q + 1];
-        }
-    };
-    float pa[2] = {0.0f, 0.0f}, pb[2] = {0.0f, 0.0f};
-    auto fma8 = [&](const uint4 (&xv)[2], const float4 (&av)[2][2], const float4 (&bv)[2][2]) {
-        float xs[2][8], as[2][8], bs[2][8];
+    for (int e = 0; e < CE; ++e)
+        wn[e] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       wrsrc, fill ? woff[e] + (uint32_t)sn * 256u : kBcPast, 0, 0));
+    // this round's stage and weights are in once only the 16 requests just
+    // made may still be in flight
+    wait_vmcnt<8 + CE>();
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 *S = R + s_at;
+    uint4 xp[8];
+    const int key = (lane >> 1) & 7;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint4 v = xv[j];
-            const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    for (int c = 0; c < 8; ++c)
+        xp[c] = S[lane * 8 + (c ^ key)];
+    // the chains start from +0 (a write the compiler cannot move next to
+    // the first fma)
+    float acc[CE];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                xs[j][2 * i] = bf16_to_f32(u[i] & 0xffffu);
-                xs[j][2 * i + 1] = bf16_to_f32(u[i] >> 16);
-            }
-            const float4 a0 = av[j][0], a1 = av[j][1], b0 = bv[j][0], b1 = bv[j][1];
-            const float al[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-            const float bl[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    for (int e = 0; e < CE; ++e)
+        asm volatile("v_mov_b32 %0, 0" : "=v"(acc[e]));
+    // each piece is converted while the fmas of the one before run
+    float xa[8], xb[8];
+    bc_convert(xp[0], xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_convert(xp[1], xb);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 0>(acc, w, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_convert(xp[2], xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 1>(acc, w, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_convert(xp[3], xb);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 2>(acc, w, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_convert(xp[4], xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 3>(acc, w, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_convert(xp[5], xb);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 4>(acc, w, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_convert(xp[6], xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 5>(acc, w, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_convert(xp[7], xb);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 6>(acc, w, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    bc_piece<CE, 7>(acc, w, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    // the exchange, [wave][expert][token] floats: every wave is done with
+    // the last round's before any writes this round's
+    float *P = reinterpret_cast<float *>(R + p_at);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                as[j][i] = al[i];
-                bs[j][i] = bl[i];
-            }
-        }
+    for (int e = 0; e < CE; ++e)
+        P[(wave * CE + e) * kTok + lane] = acc[e];
+    __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    float p[kBcWaves][Q];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+    for (int v = 0; v < kBcWaves; ++v)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                pa[j] = __builtin_fmaf(xs[j][i], as[j][i], pa[j]);
-                pb[j] = __builtin_fmaf(xs[j][i], bs[j][i], pb[j]);
-            }
-        }
-    };
-    uint4 xa[2], xb[2];
-    float4 aa[2][2], ba[2][2], ab[2][2], bb[2][2];
-    constexpr int G = kRingH / 16;                          // 8 groups per slice, even
-    read(0, xa, aa, ba);
+        for (int i = 0; i < Q; ++i)
+            p[v][i] = P[(v * CE + wave * Q + i) * kTok + lane];
 #pragma unroll
-    for (int g = 0; g < G; g += 2) {
-        read(g + 1, xb, ab, bb);
-        __builtin_amdgcn_sched_barrier(0);
-        fma8(xa, aa, ba);
-        __builtin_amdgcn_sched_barrier(0);
-        read(g + 2 < G ? g + 2 : G - 1, xa, aa, ba);       // no branch: no copies
-        __builtin_amdgcn_sched_barrier(0);
-        fma8(xb, ab, bb);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    acc0 = acc0 + pa[0];
-    acc0 = acc0 + pa[1];
-    acc1 = acc1 + pb[0];
-    acc1 = acc1 + pb[1];
+    for (int v = 0; v < kBcWaves; ++v)
+#pragma unroll
+        for (int i = 0; i < Q; ++i)
+            z[i] = z[i] + p[v][i];
 }
 
-__global__ __launch_bounds__(kMaxThreads) void k_logits_ring(const uint16_t *__restrict__ x,
-                                                             const float *__restrict__ Wr, int T,
-                                                             int H, int E, float *__restrict__ z) {
-    __shared__ uint4 ring[kRingStages * kRingStage];    // 80 KB
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+template <int CE>
+__global__ __launch_bounds__(kBcThreads) void k_logits_bc(const uint16_t *__restrict__ x,
+                                                          const float *__restrict__ Wr, int T,
+                                                          int H, int E, float *__restrict__ zout) {
+    constexpr int RING = kBcWaves * 2 * kBcStage;       // two stages per wave
+    constexpr int XCH = kBcWaves * CE * kTok / 4;        // the exchange, in 16-byte pieces
+    constexpr int Q = CE / kBcWaves;                    // experts each wave adds up
+    __shared__ uint4 lds[RING + XCH];                   // 144 KB (CE = 8) or 160 KB (16)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int t0 = blockIdx.x * kTok;
-    const int e0 = blockIdx.y * 8;
-    const int S = H / kRingH;
-    // byte offsets of this thread's pieces in h block 0; rows past T or E
-    // read zeros
-    uint32_t xoff[kRingPer - 1];
+    const int e0 = blockIdx.y * CE;
+    const int S = H / 64;
+    const int M = (S + kBcWaves - 1) / kBcWaves;
+    // byte offsets in slice 0 of this lane's requests, from the workgroup's
+    // first token row and first router row (below 2^31 for H <= 65536, so
+    // any T and E); rows past T or E read zeros
+    const uint16_t *xw = x + (size_t)t0 * H;
+    const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float *>(Wr + (size_t)e0 * H), (short)0, 0x7fffffff, kBufferWord3);
+    uint32_t xoff[8];
 #pragma unroll
-    for (int q = 0; q < kRingPer - 1; ++q) {
-        const int pos = (q * 4 + wave) * kWave + lane;     // LDS piece
-        const int r = pos / (kRingH / 8), c = (pos % (kRingH / 8)) ^ (r & 15);
-        xoff[q] = t0 + r < T ? ((uint32_t)(t0 + r) * (uint32_t)H + 8u * c) * 2u : kRingPast;
+    for (int q = 0; q < 8; ++q) {
+        const int r = 8 * q + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        xoff[q] = t0 + r < T ? ((uint32_t)r * (uint32_t)H + 8u * c) * 2u : kBcPast;
     }
-    uint32_t woff;
+    uint32_t woff[CE];
+#pragma unroll
+    for (int e = 0; e < CE; ++e)
+        woff[e] = e0 + e < E ? ((uint32_t)e * (uint32_t)H + 4u * (lane & 15)) * 4u : kBcPast;
+    const int mine = wave * (2 * kBcStage);
+    // round 0's operands
+    uint4 wa[CE], wb[CE];
     {
-        const int pos = wave * kWave + lane;
-        const int j = pos / (kRingH / 4), c = pos % (kRingH / 4);
-        woff = e0 + j < E ? ((uint32_t)(e0 + j) * (uint32_t)H + 4u * c) * 4u : kRingPast;
-    }
-    // the first three stages
+        const bool ok = wave < S;
 #pragma unroll
-    for (int s = 0; s < kRingStages - 1; ++s) {
-        if (s < S) {
-            uint4 *F = ring + s * kRingStage;
+        for (int q = 0; q < 8; ++q)
+            buffer_to_lds16(xw, lds + mine + q * kWave, ok ? xoff[q] + (uint32_t)wave * 128u : kBcPast);
 #pragma unroll
-            for (int q = 0; q < kRingPer - 1; ++q)
-                buffer_to_lds16(x, F + (q * 4 + wave) * kWave, xoff[q] + s * (kRingH * 2));
-            buffer_to_lds16(Wr, F + kRingX + wave * kWave, woff + s * (kRingH * 4));
-        }
+        for (int e = 0; e < CE; ++e)
+            wa[e] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                           wrsrc, ok ? woff[e] + (uint32_t)wave * 256u : kBcPast, 0, 0));
     }
-    float acc0 = 0.0f, acc1 = 0.0f;
-    for (int s = 0; s < S; ++s) {
-        // stage s is in once at most the requests of the two stages after
-        // it are still in flight (fewer near the end)
-        if (s + 2 < S)
-            wait_vmcnt<2 * kRingPer>();
-        else if (s + 1 < S)
-            wait_vmcnt<kRingPer>();
-        else
-            wait_vmcnt<0>();
-        __builtin_amdgcn_s_barrier();       // every wave's pieces are in; stage s - 1 is read
-        ring_stage(ring + (s & 3) * kRingStage, ring + ((s + 3) & 3) * kRingStage, x, Wr, xoff,
-                   woff, s + 3 < S ? s + 3 : -1, acc0, acc1);
+    float z[Q];
+#pragma unroll
+    for (int i = 0; i < Q; ++i)
+        z[i] = 0.0f;
+    // two rounds per pass, so the weights alternate between wa and wb
+    // without copies; both run (an odd last round reads zeros and adds +0),
+    // as a load whose registers only a branch reads would be moved into it
+    for (int m = 0; m < M; m += 2) {
+        const int s1 = kBcWaves * (m + 1) + wave;
+        bc_round<CE>(lds, mine, RING, lds + mine + kBcStage, xw, wrsrc, xoff, woff, s1, s1 < S, wa, wb,
+                 z);
+        const int s2 = kBcWaves * (m + 2) + wave;
+        bc_round<CE>(lds, mine + kBcStage, RING, lds + mine, xw, wrsrc, xoff, woff, s2, s2 < S, wb, wa,
+                 z);
     }
+    // the requests of the round past the last (zeros) land before the
+    // workgroup's LDS is given up
+    wait_vmcnt<0>();
     const int t = t0 + lane;
-    const int e = e0 + 2 * wave;
-    if (t < T) {
-        if (e < E)
-            z[(size_t)t * E + e] = acc0;
-        if (e + 1 < E)
-            z[(size_t)t * E + e + 1] = acc1;
+#pragma unroll
+    for (int i = 0; i < Q; ++i) {
+        const int e = e0 + wave * Q + i;
+        if (t < T && e < E)
+            zout[(size_t)t * E + e] = z[i];
     }
 }
 
@@ -857,15 +779,6 @@ k_route_fold(
                          eps, ids, weights, plan, lds + kDecT * kDecE + kDecE);
 }
 
-// Two chains per lane when that still leaves a few hundred workgroups,
-// else one (decode-sized batches are latency-bound: more workgroups).
-template <int C>
-void launch_logits(hipStream_t stream, const uint16_t *x, const float *Wr, int T, int H, int E,
-                   float *z) {
-    const dim3 grid((T + kTok - 1) / kTok, (E + 4 * C - 1) / (4 * C));
-    hipLaunchKernelGGL(k_logits<C>, grid, dim3(kMaxThreads), 0, stream, x, Wr, T, H, E, z);
-}
-
 }  // namespace
 
 // Batches of at most 8 tokens and 32 experts take the two-launch decode
@@ -917,16 +830,14 @@ hipError_t launch_route(const uint16_t *x, const float *Wr, const float *bias, i
     if (T <= kFewT && H <= kFewMaxH && H % 128 == 0)
         hipLaunchKernelGGL(k_logits_few, dim3((E + kFewE - 1) / kFewE), dim3(kMaxThreads), 0,
                            stream, x, Wr, T, H, E, z_scratch);
-    else if ((int64_t)tblocks * ((E + 7) / 8) >= 128 && H % kRingH == 0 &&
-             (int64_t)T * H * 2 < ((int64_t)1 << 31) && (int64_t)E * H * 4 < ((int64_t)1 << 31))
-        // (the ring's requests form 32-bit byte offsets; an offset of 2^31
-        // or more reads zeros)
-        hipLaunchKernelGGL(k_logits_ring, dim3(tblocks, (E + 7) / 8), dim3(kMaxThreads), 0, stream,
-                           x, Wr, T, H, E, z_scratch);
-    else if ((int64_t)tblocks * ((E + 7) / 8) >= 128)
-        launch_logits<2>(stream, x, Wr, T, H, E, z_scratch);
+    else if (E >= 128)
+        // 16 experts per workgroup: each token row is read by half as many
+        // workgroups
+        hipLaunchKernelGGL(k_logits_bc<16>, dim3(tblocks, (E + 15) / 16), dim3(kBcThreads), 0,
+                           stream, x, Wr, T, H, E, z_scratch);
     else
-        launch_logits<1>(stream, x, Wr, T, H, E, z_scratch);
+        hipLaunchKernelGGL(k_logits_bc<8>, dim3(tblocks, (E + 7) / 8), dim3(kBcThreads), 0,
+                           stream, x, Wr, T, H, E, z_scratch);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess)
         return err;

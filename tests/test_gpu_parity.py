@@ -137,7 +137,7 @@ def test_route_matches_oracle(name):
 # Batches of at most 8 tokens and 32 experts take the two-launch decode
 # router (one workgroup per 64-h slice, then the fold, top-k and plan in one
 # workgroup) at any H; with more experts, the 8-experts-per-workgroup decode
-# logits (H a multiple of 128, H <= 2048) or the tiled logits. Every shape
+# logits (H a multiple of 128, H <= 2048) or the DPP logits. Every shape
 # here is one of those paths at an edge: one slice, an odd number of
 # slices, a single expert, E just past 32, H past 2048.
 ROUTE_DECODE = {
@@ -163,15 +163,17 @@ ROUTE_DECODE = {
 # a wrong slice width, one chain over all h, or the slices added in another
 # order moves some expert's logit by 1 or 2 and changes the picks. One shape
 # per router path: the one-workgroup decode router, the 8-experts decode
-# logits, the LDS-ring logits and the register-staged logits (C = 1 and 2).
+# logits, and the DPP logits with 8 and 16 experts per workgroup (full and
+# partial rounds of eight slices).
 SLICE_ORDER = {
     "decode_t8_h2048_e32": (8, 2048, 32),
     "decode_t1_h256_e32": (1, 256, 32),
+    "decode_t8_h2176_e32": (8, 2176, 32),
     "few_t8_h2048_e64": (8, 2048, 64),
-    "ring_t4096_h2048_e32": (4096, 2048, 32),
-    "logits1_t100_h2048_e32": (100, 2048, 32),
-    "logits1_t8_h2176_e32": (8, 2176, 32),
-    "logits2_t3000_h576_e32": (3000, 576, 32),
+    "bc8_t4096_h2048_e32": (4096, 2048, 32),
+    "bc8_t100_h2048_e32": (100, 2048, 32),
+    "bc8_t3000_h576_e32": (3000, 576, 32),
+    "bc16_t300_h2688_e136": (300, 2688, 136),
 }
 
 
@@ -212,18 +214,50 @@ def test_route_decode_sized(case):
     assert (offsets.cpu().numpy() == o_ref).all() and (srt.cpu().numpy() == s_ref).all()
 
 
+# The DPP logits (more than 8 tokens) at their edges: one slice (seven of
+# the eight waves on zeros), an odd number of rounds of eight slices, a
+# workgroup of 8 or 16 experts holding only some real ones, a token block
+# holding only some real tokens, NaN rows and ties, and the first batch past
+# the decode router.
+BC_EDGES = {
+    "t70_h64_e136_k6": dict(T=70, H=64, E=136, k=6),
+    "t65_h960_e9_k2": dict(T=65, H=960, E=9, k=2),
+    "t129_h2688_e128_k6": dict(T=129, H=2688, E=128, k=6, nan_rows=(3, 128), zero_tie_row=7,
+                               onehot_tie_row=64),
+    "t300_h4160_e32_k4": dict(T=300, H=4160, E=32, k=4),
+    "t9_h2048_e32_k4": dict(T=9, H=2048, E=32, k=4),
+    "t2000_h128_e256_k8": dict(T=2000, H=128, E=256, k=8),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BC_EDGES))
+def test_route_bc_edges(case):
+    wl = W.Workload("route_" + case, I=64, seed=480 + sorted(BC_EDGES).index(case),
+                    **BC_EDGES[case])
+    inp = W.generate(wl, experts=False)
+    x = lib.x_to_device(inp["x"])
+    wr = torch.from_numpy(inp["router_w"]).to(DEV)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    ids, w = lib.route(x, wr, b, wl.k, wl.norm_topk, wl.norm_eps)
+    torch.cuda.synchronize()
+    ids_ref, w_ref = oracle.route(inp["x"], inp["router_w"], inp["bias"], wl.k, wl.norm_topk,
+                                  wl.norm_eps)
+    check_routing(ids.cpu().numpy(), w.cpu().numpy(), ids_ref, w_ref)
+
+
 # The softmax router (TensorFold issue #548, the consolidation proposal) on
 # every router path and every top-k width: the decode fold (E <= 32, T <= 8),
-# the 8-experts decode logits, the LDS ring, the register-staged logits, and
-# one, two and four experts per top-k lane (E up to 64, 128, 256). Rows of
+# the 8-experts decode logits, the DPP logits with 8 and 16 experts per
+# workgroup, and one, two and four experts per top-k lane (E up to 64, 128,
+# 256). Rows of
 # NaN (every score NaN), zeros (an E-way tie) and a one-hot tie included.
 SOFTMAX_ROUTE = {
     "decode_t8_h2048_e32_k4": dict(T=8, H=2048, E=32, k=4),
     "decode_t3_h256_e7_k2": dict(T=3, H=256, E=7, k=2),
     "few_t8_h1024_e64_k6": dict(T=8, H=1024, E=64, k=6),
-    "ring_t2048_h2048_e32_k4": dict(T=2048, H=2048, E=32, k=4),
-    "logits1_t100_h576_e32_k4": dict(T=100, H=576, E=32, k=4),
-    "logits2_t3000_h576_e16_k2": dict(T=3000, H=576, E=16, k=2),
+    "bc8_t2048_h2048_e32_k4": dict(T=2048, H=2048, E=32, k=4),
+    "bc8_t100_h576_e32_k4": dict(T=100, H=576, E=32, k=4),
+    "bc8_t3000_h576_e16_k2": dict(T=3000, H=576, E=16, k=2),
     "re2_t500_h256_e128_k8": dict(T=500, H=256, E=128, k=8),
     "re4_t300_h256_e256_k8": dict(T=300, H=256, E=256, k=8),
     "re4_t40_h128_e200_k5": dict(T=40, H=128, E=200, k=5),
@@ -277,8 +311,8 @@ def test_route_eps_1e20(T, H, E):
 def test_route_rows_do_not_depend_on_the_row_count(score):
     # A token's ids and weights are the same bits whichever router path its
     # batch takes (TensorFold issue #548: a row's bits the same at every row
-    # count): the decode fold (T <= 8), the register-staged logits (T = 100)
-    # and the LDS ring (T = 4096) all add the same slices in the same order.
+    # count): the decode fold (T <= 8) and the DPP logits (T = 100 and 4096)
+    # add the same slices in the same order.
     wl = W.PREFILL.with_(score=score)
     inp = W.generate(wl, experts=False)
     wr = torch.from_numpy(inp["router_w"]).to(DEV)
