@@ -534,13 +534,6 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         return g;
     };
     const bool dq = dequant_first(*d) && moe::grouped_supported(dequantized(up));
-    if (dq) {
-        LAUNCH(moe::launch_dequant(up, wdq, stream));
-        LAUNCH(run(dequantized(up)));
-    } else {
-        LAUNCH(run(up));
-    }
-    LAUNCH(mark(3));
 
     moe::GemmProblem down{};
     down.mode = moe::kDown;
@@ -569,22 +562,15 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     down.I = I;
     down.C = y;                        // rows in segment order: the combine gathers them
     down.ldc = H;
-    if (dq && moe::grouped_supported(dequantized(down))) {
-        // (the up projection has read wdq by now: same stream)
-        LAUNCH(moe::launch_dequant(down, wdq, stream));
-        LAUNCH(run(dequantized(down)));
-    } else {
-        LAUNCH(run(down));
-    }
-    LAUNCH(mark(4));
 
+    // The bf16 decode form runs the down projection and the combine in one
+    // launch (launch_down_combine); the shared expert, which reads only x,
+    // then runs first.
+    const bool fused = decode_form && !dq && moe::stream_supported(up) &&
+                       moe::down_combine_supported(down, T, k);
     const float *shared = nullptr;
     int shared_terms = 1;
-    if (m > 0) {
-        // the segments' rows follow the routed ones: m partial outputs per token
-        shared = y + (size_t)A * H;
-        shared_terms = m;
-    } else if (d->I_shared > 0) {
+    auto run_shared = [&]() -> hipError_t {
         const int Is = d->I_shared;
         uint16_t *hs = (uint16_t *)(ws + L.hs);
         float *ys = (float *)(ws + L.ys);
@@ -602,7 +588,9 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         su.C = hs;
         su.ldc = Is;
         su.limit = up.limit;
-        LAUNCH(run(su));
+        hipError_t err = run(su);
+        if (err != hipSuccess)
+            return err;
         moe::GemmProblem sd{};
         sd.mode = moe::kDown;
         sd.A = hs;
@@ -616,13 +604,46 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         sd.I = Is;
         sd.C = ys;
         sd.ldc = H;
-        LAUNCH(run(sd));
         shared = ys;
+        return run(sd);
+    };
+    if (m > 0) {
+        // the segments' rows follow the routed ones: m partial outputs per token
+        shared = y + (size_t)A * H;
+        shared_terms = m;
+    } else if (d->I_shared > 0 && fused) {
+        LAUNCH(run_shared());
     }
+
+    if (dq) {
+        LAUNCH(moe::launch_dequant(up, wdq, stream));
+        LAUNCH(run(dequantized(up)));
+    } else {
+        LAUNCH(run(up));
+    }
+    LAUNCH(mark(3));
+
+    if (fused) {
+        const moe::CombineArgs comb{slot, wts, shared, shared_terms, T, k, d->routed_scale,
+                                    d->fold_routed_scale != 0, out,
+                                    d->out_dtype == MOE_OUT_F32};
+        LAUNCH(moe::launch_down_combine(down, comb, stream));
+    } else if (dq && moe::grouped_supported(dequantized(down))) {
+        // (the up projection has read wdq by now: same stream)
+        LAUNCH(moe::launch_dequant(down, wdq, stream));
+        LAUNCH(run(dequantized(down)));
+    } else {
+        LAUNCH(run(down));
+    }
+    LAUNCH(mark(4));
+
+    if (m == 0 && d->I_shared > 0 && !fused)
+        LAUNCH(run_shared());
     LAUNCH(mark(5));
-    LAUNCH(moe::launch_combine(y, slot, wts, shared, shared_terms, T, H, k, d->routed_scale,
-                               d->fold_routed_scale != 0, out,
-                               d->out_dtype == MOE_OUT_F32, stream));
+    if (!fused)
+        LAUNCH(moe::launch_combine(y, slot, wts, shared, shared_terms, T, H, k, d->routed_scale,
+                                   d->fold_routed_scale != 0, out,
+                                   d->out_dtype == MOE_OUT_F32, stream));
     LAUNCH(mark(6));
     return ok();
 }

@@ -46,6 +46,20 @@ hipError_t launch_plan(const int32_t *ids, int A, int E, int32_t *counts, int32_
 enum GemmMode { kGateUp = 0, kUpRelu2 = 1, kDown = 2, kGateUpLimit = 3 };
 constexpr bool gated(int mode) { return mode == kGateUp || mode == kGateUpLimit; }
 
+// The weighted combine of launch_combine, as launch_down_combine takes it.
+struct CombineArgs {
+    const int32_t *slot;      // slot_of [T*k]: the plan position of assignment t*k + j
+    const float *w;           // weights [T*k]
+    const float *shared;      // NULL or shared_terms rows of [T][H], T*H apart
+    int shared_terms;
+    int T;
+    int k;
+    float rsf;                // routed scale
+    int fold;                 // the routed scale folded into each weight
+    void *out;                // [T][H], bf16 or fp32
+    int out_f32;
+};
+
 struct GemmProblem {
     int mode;                 // GemmMode
     int affine4;              // B is 4-bit affine (codes + bf16 scale / bias, group 64)
@@ -119,6 +133,11 @@ constexpr int kStreamMaxKNvfp4 = 8192;
 constexpr int kStreamMaxKMxfp4 = 8192;
 bool stream_supported(const GemmProblem &p);
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream);
+// The decode form's bf16 down projection (kDown, offsets set, at most 32
+// plan positions, K <= 2048) with the weighted combine of launch_combine in
+// the same launch: out is written, y (p.C) is not.
+bool down_combine_supported(const GemmProblem &p, int T, int k);
+hipError_t launch_down_combine(const GemmProblem &p, const CombineArgs &c, hipStream_t stream);
 
 // Fused residual add + RMSNorm of T rows of H (a multiple of 64, at most
 // kNormMaxH): residual_out = bf16(h + residual), x = bf16(r gamma / rms).

@@ -534,6 +534,169 @@ hipError_t launch_q_fmt(const GemmProblem &p, hipStream_t stream) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// The decode form's down projection and the weighted combine in one launch.
+// A workgroup owns 8 output columns for every expert with rows: it stages
+// all the plan's rows (at most kDcRows of them, bf16) in LDS once; wave w
+// takes column w % 8 and every second expert (from w / 8), streams that
+// column's weight row of each of its experts in turn, kDcAhead ahead, and
+// forms the expert's y values exactly as k_stream does (the same lane
+// partials and butterfly); the y values stay in LDS. Then the workgroup
+// writes out[t, its columns] for every token exactly as k_combine does: acc =
+// fma(w[t,j], y, acc) over j ascending from +0, times the routed scale (or
+// the scale folded into each weight), plus the shared rows added in order,
+// one rounding. No y leaves the workgroup and no second launch follows.
+constexpr int kDcThreads = 1024;
+constexpr int kDcCols = 8;          // output columns per workgroup
+constexpr int kDcGroups = kDcThreads / kWave / kDcCols;   // waves per column
+constexpr int kDcRows = 32;         // plan positions one launch takes
+constexpr int kDcAhead = 4;         // experts whose weight rows a wave has in flight
+constexpr int kDcMaxE = 256;
+
+template <int NJ>
+__global__ __launch_bounds__(kDcThreads) void k_down_combine(GemmProblem p, CombineArgs c) {
+    __shared__ uint4 xs[kDcRows][NJ * kWave];       // the plan's rows, bf16
+    __shared__ float ys[kDcRows][kDcCols];          // y[position][column]
+    __shared__ int s_e[kDcMaxE], s_lo[kDcMaxE], s_hi[kDcMaxE];
+    __shared__ int s_nb;
+    __shared__ int s_slot[kDcRows];                 // the combine's inputs, loaded first
+    __shared__ float s_w[kDcRows];
+    __shared__ float s_sh[kDcRows][kDcCols];        // the shared rows' sum, per token
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int col = wave % kDcCols, grp = wave / kDcCols;
+    // the combine's inputs (wave 1; wave 0 lists the experts): the slots, the
+    // weights (the routed scale folded in with fold) and the shared rows
+    // added in order, for this workgroup's columns
+    if (wave == 1) {
+        const int A = c.T * c.k;
+        if (lane < A) {
+            s_slot[lane] = c.slot[lane];
+            s_w[lane] = c.fold ? c.rsf * c.w[lane] : c.w[lane];
+        }
+        for (int idx = lane; idx < c.T * kDcCols; idx += kWave) {
+            const int t = idx / kDcCols, h = blockIdx.x * kDcCols + idx % kDcCols;
+            float sh = 0.0f;
+            if (c.shared != nullptr && h < p.N) {
+                for (int v = 0; v < c.shared_terms; ++v) {
+                    const float e = c.shared[((size_t)v * c.T + t) * p.N + h];
+                    sh = v == 0 ? e : sh + e;
+                }
+            }
+            s_sh[t][idx % kDcCols] = sh;
+        }
+    }
+    const int K = p.K, N = p.N;
+    const int u = blockIdx.x * kDcCols + col;       // this wave's output column
+    // the experts with rows, in expert order
+    if (wave == 0) {
+        int nb = 0;
+        for (int base = 0; base < p.E; base += kWave) {
+            const int x = base + lane;
+            const int lo = x < p.E ? p.offsets[x] : 0;
+            const int hi = x < p.E ? p.offsets[x + 1] : 0;
+            const bool busy = hi > lo;
+            const uint64_t m = __ballot(busy);
+            if (busy) {
+                const int i = nb + __popcll(m & ((1ull << lane) - 1ull));
+                s_e[i] = x;
+                s_lo[i] = lo;
+                s_hi[i] = hi;
+            }
+            nb += __popcll(m);
+        }
+        if (lane == 0)
+            s_nb = nb;
+    }
+    __syncthreads();
+    const int nb = s_nb;
+    // this wave's weight row of its ii-th expert, busy expert grp + ii
+    // kDcGroups (zeros past the list)
+    auto load_row = [&](int ii, uint4 (&w)[NJ]) {
+        const int i = grp + ii * kDcGroups;
+        const bool ok = i < nb && u < N;
+        const int e = ok ? s_e[i] : 0;
+        const uint16_t *wp = (const uint16_t *)p.B + ((size_t)e * N + u) * K;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int kk = j * 512 + lane * 8;
+            w[j] = (ok && kk < K) ? stream_load(wp + kk) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    uint4 wb[kDcAhead][NJ];
+#pragma unroll
+    for (int q = 0; q < kDcAhead; ++q)
+        load_row(q, wb[q]);
+    // the plan's rows, while the first weight rows are in flight: every load
+    // of a thread issued before its first LDS write
+    const int A = p.offsets[p.E];
+    constexpr int SL = kDcRows * NJ * kWave / kDcThreads;   // 16-byte pieces per thread
+    uint4 sv[SL];
+#pragma unroll
+    for (int q = 0; q < SL; ++q) {
+        const int idx = q * kDcThreads + threadIdx.x;
+        const int r = idx / (NJ * kWave), cc = idx % (NJ * kWave);
+        sv[q] = (r < A && cc * 8 < K)
+                    ? *reinterpret_cast<const uint4 *>(p.A + (size_t)r * p.lda + cc * 8)
+                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < SL; ++q) {
+        const int idx = q * kDcThreads + threadIdx.x;
+        xs[idx / (NJ * kWave)][idx % (NJ * kWave)] = sv[q];
+    }
+    __syncthreads();
+    const int mine = nb > grp ? (nb - grp + kDcGroups - 1) / kDcGroups : 0;
+    for (int i0 = 0; i0 < mine; i0 += kDcAhead) {
+#pragma unroll
+        for (int q = 0; q < kDcAhead; ++q) {
+            const int ii = i0 + q;
+            if (ii < mine) {                            // uniform
+                const int i = grp + ii * kDcGroups;
+                const int lo = s_lo[i], hi = s_hi[i];
+                for (int g0 = lo; g0 < hi; g0 += kTG) {
+                    const int nr = min(kTG, hi - g0);
+                    float v[kTG];
+#pragma unroll
+                    for (int r = 0; r < kTG; ++r) {
+                        float acc = 0.0f;
+                        if (r < nr) {                   // uniform
+#pragma unroll
+                            for (int j = 0; j < NJ; ++j)
+                                acc = dot8(wb[q][j], xs[g0 + r][j * kWave + lane], acc);
+                        }
+                        v[r] = acc;
+                    }
+                    transpose_reduce<kTG, 1>(v, lane);
+                    // lane bits 5, 4 name the row r whose sum this lane now holds
+                    const int r = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+                    if ((lane & 15) == 0 && r < nr)
+                        ys[g0 + r][col] = v[0];
+                }
+            }
+            load_row(ii + kDcAhead, wb[q]);
+        }
+    }
+    __syncthreads();
+    const int H = N;
+    for (int idx = threadIdx.x; idx < c.T * kDcCols; idx += kDcThreads) {
+        const int t = idx / kDcCols, cc = idx % kDcCols, h = blockIdx.x * kDcCols + cc;
+        if (h >= H)
+            continue;
+        float acc = 0.0f;
+        for (int j = 0; j < c.k; ++j)
+            acc = __builtin_fmaf(s_w[t * c.k + j], ys[s_slot[t * c.k + j]][cc], acc);
+        if (!c.fold)
+            acc = acc * c.rsf;
+        if (c.shared != nullptr)
+            acc = acc + s_sh[t][cc];
+        if (c.out_f32)
+            ((float *)c.out)[(size_t)t * H + h] = acc;
+        else
+            ((uint16_t *)c.out)[(size_t)t * H + h] = (uint16_t)f32_to_bf16(acc);
+    }
+}
+
 template <int MODE, int NJ>
 hipError_t launch_nj(const GemmProblem &p, hipStream_t stream) {
     const int units = gated(MODE) ? p.I : p.N;
@@ -571,6 +734,27 @@ bool stream_supported(const GemmProblem &p) {
     if (p.fp8)          // 128 x 128 scale blocks
         return p.K % 128 == 0 && p.N % 128 == 0 && p.K <= kStreamMaxKFp8;
     return p.K <= 4096;
+}
+
+bool down_combine_supported(const GemmProblem &p, int T, int k) {
+    return p.mode == kDown && !p.affine4 && !p.fp8 && !p.nvfp4 && !p.mxfp4 &&
+           p.offsets != nullptr && p.E2 == 0 && p.scatter == nullptr && !p.b_compact &&
+           p.Bglobal == nullptr && p.E <= kDcMaxE && p.K <= 2048 && p.N % 8 == 0 &&
+           (int64_t)T * k <= kDcRows;
+}
+
+hipError_t launch_down_combine(const GemmProblem &p, const CombineArgs &c, hipStream_t stream) {
+    if (!down_combine_supported(p, c.T, c.k))
+        return hipErrorInvalidValue;
+    const dim3 grid((p.N + kDcCols - 1) / kDcCols);
+    const int nj = (p.K + 511) / 512;
+    if (nj <= 1)
+        hipLaunchKernelGGL(k_down_combine<1>, grid, dim3(kDcThreads), 0, stream, p, c);
+    else if (nj <= 2)
+        hipLaunchKernelGGL(k_down_combine<2>, grid, dim3(kDcThreads), 0, stream, p, c);
+    else
+        hipLaunchKernelGGL(k_down_combine<4>, grid, dim3(kDcThreads), 0, stream, p, c);
+    return hipGetLastError();
 }
 
 hipError_t launch_stream(const GemmProblem &p, hipStream_t stream) {

@@ -469,7 +469,7 @@ def test_forward_full_size_sampled(name):
 
 DECODE_CASES = [("tiny_t64_e8_k2", 8), ("tiny_t64_e8_k2", 1), ("mid_swiglu", 8),
                 ("mid_swiglu", 3), ("mid_relu2_shared", 8), ("mid_relu2_shared", 1),
-                ("mid_e256_k8", 64), ("mid_e256_k8", 7), ("mid_nan_ties", 4),
+                ("mid_e256_k8", 64), ("mid_e256_k8", 7), ("mid_e256_k8", 4), ("mid_nan_ties", 4),
                 ("mid_swiglu_bigseg", 2), ("mid_softmax", 8), ("mid_softmax", 2),
                 ("mid_swiglu_limit", 8), ("mid_swiglu_limit", 1), ("mid_fp8", 4), ("mid_fp8", 1),
                 ("mid_fp8_relu2", 8), ("mid_fp8_wide", 8), ("mid_fp8_wide", 2),
