@@ -259,7 +259,10 @@ int moe_forward(const moe_dims *d, const moe_weights *w, const uint16_t *x, void
  * [3] after the routed up-projection GEMM (gate_up + SwiGLU, or up +
  * relu^2), [4] after the routed down GEMM, [5] after the shared expert
  * (same as [4] without one), [6] after the combine. Each entry is a
- * hipEvent_t created by the caller, or NULL to skip it. */
+ * hipEvent_t created by the caller, or NULL to skip it. The bf16 decode form
+ * (T*k <= 32, I <= 2048) runs the shared expert before the routed up
+ * projection and the combine inside the down GEMM's launch: there [4], [5]
+ * and [6] follow that launch back to back. */
 #define MOE_PROFILE_EVENTS 7
 int moe_forward_profiled(const moe_dims *d, const moe_weights *w, const uint16_t *x, void *out,
                          void *workspace, size_t workspace_bytes, hipStream_t stream,
