@@ -539,9 +539,12 @@ hipError_t launch_q_fmt(const GemmProblem &p, hipStream_t stream) {
 // A workgroup owns 8 output columns for every expert with rows: it stages
 // all the plan's rows (at most kDcRows of them, bf16) in LDS once; wave w
 // takes column w % 8 and every second expert (from w / 8), streams that
-// column's weight row of each of its experts in turn, kDcAhead ahead, and
-// forms the expert's y values exactly as k_stream does (the same lane
-// partials and butterfly); the y values stay in LDS. Then the workgroup
+// column's weight row of each of its experts in turn, and forms the expert's
+// y values exactly as k_stream does (the same lane partials and butterfly);
+// the y values stay in LDS. A wave has one weight row in flight at a time:
+// the rows in flight then come from few experts at once, and with more of
+// them ahead (two, four, six) the step took 0.6, 2.8 and 24 us longer, the
+// reads spread over more experts' weights. Then the workgroup
 // writes out[t, its columns] for every token exactly as k_combine does: acc =
 // fma(w[t,j], y, acc) over j ascending from +0, times the routed scale (or
 // the scale folded into each weight), plus the shared rows added in order,
@@ -550,7 +553,7 @@ constexpr int kDcThreads = 1024;
 constexpr int kDcCols = 8;          // output columns per workgroup
 constexpr int kDcGroups = kDcThreads / kWave / kDcCols;   // waves per column
 constexpr int kDcRows = 32;         // plan positions one launch takes
-constexpr int kDcAhead = 4;         // experts whose weight rows a wave has in flight
+constexpr int kDcAhead = 1;         // experts whose weight rows a wave has in flight
 constexpr int kDcMaxE = 256;
 
 template <int NJ>
