@@ -254,6 +254,11 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS}
     roof["traffic"] = load_traffic("gemm_up", wl.name, GEMM_SOURCES)
     roof["avg_launch_us"] = 1e3 * stages["up"]
+    # which calls the launch time comes from (not the throughput region's,
+    # which records no events; the kernel trace of the same command gives the
+    # same calls' dispatch times, a few microseconds below these)
+    roof["timing"] = ("HIP events on the call's stream around the up stage, mean of the %d calls "
+                      "with stage events that follow the timed region" % args.steps)
 
     result = {
         "metric": METRIC,
