@@ -23,9 +23,9 @@
 // The logits are T*E*(H/64) independent fma chains of length 64, each in h
 // order, and each (t, e)'s slices are added in order. k_logits_bc runs a
 // lane per token, the router weights brought to the fmas by DPP from
-// registers that hold 16 of them each; k_logits (the same lanes, the router
-// rows read from LDS by every lane at once) takes batches whose byte
-// offsets reach 2^31. Batches of at most 8 tokens and 32 experts take
+// registers that hold 16 of them each; its byte offsets are formed from
+// each workgroup's first token and router rows, so it takes any T and E
+// (H <= 65536). Batches of at most 8 tokens and 32 experts take
 // k_logits_part (the slices spread over the chip) and k_route_fold; at most
 // 8 tokens with more experts, k_logits_few.
 //
