@@ -310,6 +310,26 @@ int check_device(const char *what, const char *name, const void *p) {
             return fail(MOE_E_HIP, "%s: launch failed: %s", what, hipGetErrorString(e_)); \
     } while (0)
 
+// The tensor moe_pack_tiles packs: rows N, row length K and whether it is a
+// fused gate/up tensor.
+struct PackShape {
+    int N, K, I;
+    bool gate_up;
+};
+int pack_shape(const char *what, const moe_dims *d, int32_t which, PackShape *ps) {
+    TRY(check_dims(what, d, true));
+    REQUIRE(d->wfmt == MOE_W_BF16, MOE_E_UNSUPPORTED,
+            "%s: wfmt = %d, the tile-packed copy is for bf16 experts", what, d->wfmt);
+    REQUIRE(which == MOE_TILES_UP || which == MOE_TILES_DOWN, MOE_E_UNSUPPORTED,
+            "%s: which = %d, need MOE_TILES_UP (0) or MOE_TILES_DOWN (1)", what, which);
+    const bool swiglu = d->act == MOE_ACT_SWIGLU;
+    if (which == MOE_TILES_UP)
+        *ps = PackShape{swiglu ? 2 * d->I : d->I, d->H, d->I, swiglu};
+    else
+        *ps = PackShape{d->H, d->I, d->I, false};
+    return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,6 +339,31 @@ int moe_workspace_bytes(const moe_dims *d, size_t *bytes) {
     TRY(check_dims(what, d, true));
     REQUIRE(bytes != nullptr, MOE_E_NULL, "%s: bytes is NULL", what);
     *bytes = layout(*d).total;
+    return ok();
+}
+
+int moe_tiles_bytes(const moe_dims *d, int32_t which, size_t *bytes) {
+    const char *what = "moe_tiles_bytes";
+    PackShape ps{};
+    TRY(pack_shape(what, d, which, &ps));
+    REQUIRE(bytes != nullptr, MOE_E_NULL, "%s: bytes is NULL", what);
+    *bytes = moe::pack_tiles_bytes(d->E, ps.N, ps.K, ps.I, ps.gate_up);
+    return ok();
+}
+
+int moe_pack_tiles(const moe_dims *d, int32_t which, const uint16_t *w, uint16_t *tiles,
+                   size_t tiles_bytes, hipStream_t stream) {
+    const char *what = "moe_pack_tiles";
+    PackShape ps{};
+    TRY(pack_shape(what, d, which, &ps));
+    const size_t need = moe::pack_tiles_bytes(d->E, ps.N, ps.K, ps.I, ps.gate_up);
+    REQUIRE(tiles_bytes >= need, MOE_E_WORKSPACE, "%s: tiles_bytes = %zu, need >= %zu", what,
+            tiles_bytes, need);
+    TRY(check_ptr(what, "w", w));
+    TRY(check_ptr(what, "tiles", tiles));
+    TRY(check_device(what, "w", w));
+    TRY(check_device(what, "tiles", tiles));
+    LAUNCH(moe::launch_pack_tiles(w, tiles, d->E, ps.N, ps.K, ps.I, ps.gate_up, stream));
     return ok();
 }
 
@@ -419,6 +464,11 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         TRY(check_ptr(what, "w->shared_up", w->shared_up));
         TRY(check_ptr(what, "w->shared_down", w->shared_down));
     }
+    REQUIRE((w->w_up_tiles == nullptr && w->w_down_tiles == nullptr) || d->wfmt == MOE_W_BF16,
+            MOE_E_UNSUPPORTED, "%s: w->w_up_tiles / w->w_down_tiles are for bf16 experts (wfmt = %d)",
+            what, d->wfmt);
+    TRY(check_opt_ptr(what, "w->w_up_tiles", w->w_up_tiles));
+    TRY(check_opt_ptr(what, "w->w_down_tiles", w->w_down_tiles));
     TRY(check_opt_ptr(what, "ids_out", ids_out));
     TRY(check_opt_ptr(what, "weights_out", weights_out));
     TRY(check_opt_ptr(what, "offsets_out", offsets_out));
@@ -440,12 +490,13 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
                          d->I_shared ? w->shared_up : nullptr,
                          d->I_shared ? w->shared_down : nullptr, ids_out, weights_out,
                          offsets_out, nv4 ? w->w_up_global : nullptr,
-                         nv4 ? w->w_down_global : nullptr};
+                         nv4 ? w->w_down_global : nullptr, w->w_up_tiles, w->w_down_tiles};
     const char *dev_names[] = {"x", "out", "workspace", "w->router_w", "w->expert_bias",
                                "w->w_up", "w->w_down", "w->w_up_scales", "w->w_up_biases",
                                "w->w_down_scales", "w->w_down_biases", "w->shared_up",
                                "w->shared_down", "ids_out", "weights_out", "offsets_out",
-                               "w->w_up_global", "w->w_down_global"};
+                               "w->w_up_global", "w->w_down_global", "w->w_up_tiles",
+                               "w->w_down_tiles"};
     for (size_t i = 0; i < sizeof dev / sizeof dev[0]; ++i)
         TRY(check_device(what, dev_names[i], dev[i]));
 
@@ -511,6 +562,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         up.b2_vstride = (long long)I * H;
     }
     up.B = w->w_up;
+    up.Btiles = w->w_up_tiles;
     up.Bscale = (const uint16_t *)w->w_up_scales;
     up.Bbias = (const uint16_t *)w->w_up_biases;
     up.N = d->act == MOE_ACT_SWIGLU ? 2 * I : I;
@@ -528,6 +580,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         g.nvfp4 = 0;                 // (an NVFP4 global scale stays in Bglobal)
         g.mxfp4 = 0;
         g.B = wdq;
+        g.Btiles = nullptr;
         g.Bscale = nullptr;
         g.Bbias = nullptr;
         g.b_compact = 1;
@@ -555,6 +608,7 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         down.b2_vstride = I;
     }
     down.B = w->w_down;
+    down.Btiles = w->w_down_tiles;
     down.Bscale = (const uint16_t *)w->w_down_scales;
     down.Bbias = (const uint16_t *)w->w_down_biases;
     down.N = H;

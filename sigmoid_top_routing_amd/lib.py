@@ -25,8 +25,10 @@ OUT = {torch.bfloat16: 0, torch.float32: 1}
 SCORE = {"sigmoid": 0, "softmax": 1}
 
 # every entry point include/moe.h declares
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_plan", "moe_forward", "moe_forward_profiled",
-           "moe_forward_noalloc", "moe_add_rmsnorm", "moe_last_error")
+EXPORTS = ("moe_workspace_bytes", "moe_tiles_bytes", "moe_pack_tiles", "moe_route", "moe_plan",
+           "moe_forward", "moe_forward_profiled", "moe_forward_noalloc", "moe_add_rmsnorm",
+           "moe_last_error")
+TILES = {"up": 0, "down": 1}
 NOALLOC_SCRATCH_BYTES = 64 << 20
 PROFILE_EVENTS = 7
 STAGES = ("route", "plan", "up", "down", "shared", "combine")
@@ -51,7 +53,7 @@ class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in (
         "router_w", "expert_bias", "w_up", "w_up_scales", "w_up_biases", "w_down",
         "w_down_scales", "w_down_biases", "shared_up", "shared_down", "w_up_global",
-        "w_down_global")]
+        "w_down_global", "w_up_tiles", "w_down_tiles")]
 
 
 _lib = None
@@ -67,6 +69,10 @@ def load():
         p, i = C.c_void_p, C.c_int
         L.moe_workspace_bytes.argtypes = [C.POINTER(Dims), C.POINTER(C.c_size_t)]
         L.moe_workspace_bytes.restype = i
+        L.moe_tiles_bytes.argtypes = [C.POINTER(Dims), C.c_int32, C.POINTER(C.c_size_t)]
+        L.moe_tiles_bytes.restype = i
+        L.moe_pack_tiles.argtypes = [C.POINTER(Dims), C.c_int32, p, p, C.c_size_t, p]
+        L.moe_pack_tiles.restype = i
         L.moe_route.argtypes = [C.POINTER(Dims), p, p, p, p, p, p, C.c_size_t, p]
         L.moe_route.restype = i
         L.moe_plan.argtypes = [C.POINTER(Dims), p, p, p, p, p, p, p, C.c_size_t, p]
@@ -116,6 +122,23 @@ def workspace_bytes(d: Dims) -> int:
     n = C.c_size_t()
     _check(load().moe_workspace_bytes(C.byref(d), C.byref(n)))
     return n.value
+
+
+def tiles_bytes(d: Dims, which: str) -> int:
+    """Bytes of the tile-packed copy of w_up ("up") or w_down ("down") (moe_tiles_bytes)."""
+    n = C.c_size_t()
+    _check(load().moe_tiles_bytes(C.byref(d), TILES[which], C.byref(n)))
+    return n.value
+
+
+def pack_tiles(d: Dims, which: str, w, stream=None) -> torch.Tensor:
+    """The tile-packed copy of a bf16 weight tensor (moe_pack_tiles), as a
+    flat bf16 tensor on w's device."""
+    n = tiles_bytes(d, which)
+    tiles = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    _check(load().moe_pack_tiles(C.byref(d), TILES[which], _ptr(w), _ptr(tiles), n,
+                                 _stream(stream)))
+    return tiles
 
 
 def route(x, router_w, bias, k, norm_topk=True, norm_eps=1e-6, stream=None, score="sigmoid"):
@@ -186,6 +209,8 @@ class MoEBlock:
     w_down_global: torch.Tensor | None = None
     shared_up: torch.Tensor | None = None
     shared_down: torch.Tensor | None = None
+    w_up_tiles: torch.Tensor | None = None       # tile-packed copies (pack_tiles)
+    w_down_tiles: torch.Tensor | None = None
     act: str = "swiglu"
     wfmt: str = "bf16"
     rsf: float = 1.0
@@ -215,13 +240,23 @@ class MoEBlock:
         return (_ptr(self.router_w), _ptr(self.bias), _ptr(self.w_up), _ptr(self.w_up_scales),
                 _ptr(self.w_up_biases), _ptr(self.w_down), _ptr(self.w_down_scales),
                 _ptr(self.w_down_biases), _ptr(self.shared_up), _ptr(self.shared_down),
-                _ptr(self.w_up_global), _ptr(self.w_down_global))
+                _ptr(self.w_up_global), _ptr(self.w_down_global), _ptr(self.w_up_tiles),
+                _ptr(self.w_down_tiles))
 
     def weights(self) -> Weights:
-        (rw, b, wu, wus, wub, wd, wds, wdb, su, sd, ug, dg) = self._weight_ptrs()
+        (rw, b, wu, wus, wub, wd, wds, wdb, su, sd, ug, dg, ut, dt) = self._weight_ptrs()
         return Weights(router_w=rw, expert_bias=b, w_up=wu, w_up_scales=wus, w_up_biases=wub,
                        w_down=wd, w_down_scales=wds, w_down_biases=wdb, shared_up=su,
-                       shared_down=sd, w_up_global=ug, w_down_global=dg)
+                       shared_down=sd, w_up_global=ug, w_down_global=dg, w_up_tiles=ut,
+                       w_down_tiles=dt)
+
+    def pack_tiles(self, stream=None):
+        """Give the block tile-packed copies of its bf16 expert weights
+        (moe_pack_tiles), which the prompt-sized MFMA tiles then read."""
+        d = self.dims(0)
+        self.w_up_tiles = pack_tiles(d, "up", self.w_up, stream)
+        self.w_down_tiles = pack_tiles(d, "down", self.w_down, stream)
+        return self
 
     def _marshalled(self, T, out_dtype):
         """(dims, weights, workspace bytes) of a call: built once per shape,

@@ -277,3 +277,46 @@ def test_binding_fails_loudly_without_the_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lib, "LIBPATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         lib.load()
+
+
+def test_tiles_bytes_and_pack_refusals():
+    # the tile-packed copy: E * n_tiles * K * 512 bytes, n_tiles over 128
+    # gate columns (SwiGLU up) or 256 rows (relu^2 up, down)
+    L = lib.load()
+    lfm2 = dims(T=0, H=2048, I=1792, E=32, k=4)
+    assert lib.tiles_bytes(lfm2, "up") == 32 * 14 * 2048 * 512 == 32 * 2 * 1792 * 2048 * 2
+    assert lib.tiles_bytes(lfm2, "down") == 32 * 8 * 1792 * 512 == 32 * 2048 * 1792 * 2
+    relu2 = dims(T=0, H=2688, I=1856, E=128, k=6, act="relu2")
+    assert lib.tiles_bytes(relu2, "up") == 128 * 8 * 2688 * 512       # 1856 rows -> 2048
+    assert lib.tiles_bytes(relu2, "down") == 128 * 11 * 1856 * 512    # 2688 rows -> 2816
+    ragged = dims(T=0, H=128, I=192, E=3, k=2)
+    assert lib.tiles_bytes(ragged, "up") == 3 * 2 * 128 * 512         # 192 gate columns -> 256
+    n = C.c_size_t()
+    # bf16 experts only; which is 0 or 1
+    assert L.moe_tiles_bytes(C.byref(dims(wfmt="fp8", H=256, I=256)), 0, C.byref(n)) == -4
+    assert "bf16" in L.moe_last_error().decode()
+    assert L.moe_tiles_bytes(C.byref(lfm2), 2, C.byref(n)) == -4
+    assert "which = 2" in L.moe_last_error().decode()
+    assert L.moe_tiles_bytes(C.byref(lfm2), 0, None) == -1
+    # pack: a short destination, NULL and misaligned pointers, before any launch
+    need = lib.tiles_bytes(ragged, "up")
+    f = L.moe_pack_tiles
+    assert f(C.byref(ragged), 0, _fake(0x1000), _fake(0x2000), need - 1, None) == -5
+    assert str(need) in L.moe_last_error().decode()
+    assert f(C.byref(ragged), 0, None, _fake(0x2000), need, None) == -1
+    assert f(C.byref(ragged), 1, _fake(0x1000), _fake(0x2008), need, None) == -3
+    assert "tiles" in L.moe_last_error().decode()
+
+
+def test_forward_refuses_tiles_of_quantized_experts():
+    L = lib.load()
+    w = lib.Weights(router_w=0x1000, w_up=0x2000, w_down=0x3000, w_up_scales=0x4000,
+                    w_down_scales=0x5000, w_up_tiles=0x6000)
+    d = dims(wfmt="fp8", H=256, I=256)
+    rc = L.moe_forward(C.byref(d), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
+                       1 << 30, None, None, None, None)
+    assert rc == -4 and "w_up_tiles" in L.moe_last_error().decode()
+    w = lib.Weights(router_w=0x1000, w_up=0x2000, w_down=0x3000, w_down_tiles=0x6008)
+    rc = L.moe_forward(C.byref(dims()), C.byref(w), _fake(0x1000), _fake(0x1000),
+                       _fake(0x1000), 1 << 30, None, None, None, None)
+    assert rc == -3 and "w_down_tiles" in L.moe_last_error().decode()
