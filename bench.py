@@ -12,6 +12,13 @@ because the part's clock ramps up over about 50 ms of load after idle; each
 other configuration gets 50 ms of untimed calls for the same reason. Prints
 one JSON line.
 
+bf16 and block-FP8 expert weights get their tile-packed copy (moe_pack_tiles)
+once, before any timed call, as a caller does when it loads the weights: the
+prompt-sized MFMA tiles read it (the same output bits, each K-slice of a tile
+one contiguous 16 KB, 8 KB for FP8); the time of that one-off copy is
+reported as pack_tiles_ms. With --no-tiles the tiles read the weights as
+stored.
+
 Besides the whole-block throughput the line carries:
   roofline      the dominant kernel (the routed up-projection GEMM) against
                 the bf16 MFMA peak (or HBM for a decode-sized batch), timed
@@ -110,6 +117,8 @@ def profile_run(args):
     wl = W.by_name(args.workload)
     inp = W.generate(wl)
     block = lib.block_from_arrays(wl, inp)
+    if wl.wfmt in ("bf16", "fp8") and not args.no_tiles:
+        block.pack_tiles()
     x = lib.x_to_device(inp["x"])
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     for _ in range(args.steps):
@@ -193,6 +202,8 @@ def main():
                     help="router scores in place of the workload's own")
     ap.add_argument("--swiglu-limit", type=float, default=None,
                     help="SwiGLU input limit in place of the workload's own")
+    ap.add_argument("--no-tiles", action="store_true",
+                    help="no tile-packed copy of the bf16 expert weights")
     ap.add_argument("--profile-run", action="store_true",
                     help="untimed calls plus a calibration copy, for rocprofv3 to wrap")
     args = ap.parse_args()
@@ -211,6 +222,8 @@ def main():
     wl = variant(W.by_name(args.workload), args)
     inp = W.generate(wl)
     block = lib.block_from_arrays(wl, inp)
+    tiles = wl.wfmt in ("bf16", "fp8") and not args.no_tiles
+    pack_ms = pack(block, torch) if tiles else None
     x = lib.x_to_device(inp["x"])
     out = torch.empty((wl.T, wl.H), dtype=torch.bfloat16, device="cuda")
     ids = torch.empty((wl.T, wl.k), dtype=torch.int32, device="cuda")
@@ -276,7 +289,8 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "I": wl.I, "E": wl.E, "k": wl.k,
                    "act": wl.act, "weights": wl.wfmt, "rsf": wl.rsf, "I_shared": wl.I_shared,
                    "score": wl.score, "swiglu_limit": wl.swiglu_limit,
-                   "parallelism": "single GPU"},
+                   "tile_packed_weights": tiles, "parallelism": "single GPU"},
+        "pack_tiles_ms": pack_ms,
         "roofline": roof,
         "block": {"tflops": total_f / (ms_per_step * 1e-3) / 1e12,
                   "frac_bf16_peak": total_f / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
@@ -300,7 +314,8 @@ def main():
                                  ("nvfp4_decode", "lfm2_nvfp4_decode_t8", True),
                                  ("mxfp4", "lfm2_mxfp4_prefill_t4096", False),
                                  ("mxfp4_decode", "lfm2_mxfp4_decode_t8", True)):
-            result["configs"][tag] = bench_step(W.by_name(name), W, lib, torch, flush=flush)
+            result["configs"][tag] = bench_step(W.by_name(name), W, lib, torch, flush=flush,
+                                                tiles=not args.no_tiles)
             print(f"bench: {tag} done", file=sys.stderr, flush=True)
         result["configs"]["decode_row_invariant"] = bench_step(W.DECODE, W, lib, torch, block=block,
                                                                flush=True, row_invariant=True)
@@ -339,6 +354,19 @@ def bench_norm(T, H, W, lib, torch, steps=20):
             "frac_hbm": gbs / PEAK_HBM_GBS, "timing": "median of %d calls, cache evicted" % steps}
 
 
+def pack(block, torch):
+    """The block's tile-packed weight copies (moe_pack_tiles), made once;
+    returns the milliseconds the copy took on the GPU."""
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    block.pack_tiles()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
 def warm(torch, fn, ms=50.0):
     """Untimed calls of fn until `ms` milliseconds of them have run (at least
     three): the clock ramps up over about 50 ms of load after idle, and the
@@ -359,7 +387,8 @@ def shared_bytes(wl):
     return 2 * (n_sup + wl.I_shared) * wl.H
 
 
-def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20, row_invariant=False):
+def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20, row_invariant=False,
+               tiles=True):
     """One workload's step, each call between its own event pair on the
     current stream (the median call is reported), then the stage breakdown
     from calls with the stage events inside (each record adds a few
@@ -369,12 +398,15 @@ def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20, row_invaria
     than written so no dirty lines are written back during the timed call.
     block: the weights already on the device (the workload's x is drawn on
     its own seed). row_invariant: the call with that option (the block's
-    own setting is restored afterwards). Algorithmic work: the MFMA flops of the routed and shared
+    own setting is restored afterwards). tiles: a new block of bf16 experts gets
+    its tile-packed copy first. Algorithmic work: the MFMA flops of the routed and shared
     projections, and the bytes of the D distinct experts touched (as stored),
     the shared expert, the router weight, x and the bf16 output."""
     inp = W.generate(wl, experts=block is None)
     if block is None:
         block = lib.block_from_arrays(wl, inp)
+        if tiles and wl.wfmt in ("bf16", "fp8"):
+            block.pack_tiles()
     saved = block.row_invariant
     block.row_invariant = row_invariant
     x = lib.x_to_device(inp["x"])
@@ -416,6 +448,7 @@ def bench_step(wl, W, lib, torch, block=None, flush=False, steps=20, row_invaria
             "algorithmic_bytes": algo, "GBps": gbs, "frac_hbm": gbs / PEAK_HBM_GBS,
             "flops": flops, "tflops": tfs, "frac_bf16_peak": tfs / PEAK_BF16_TFLOPS,
             "cache_evicted": bool(flush), "row_invariant": bool(row_invariant),
+            "tile_packed_weights": block.w_up_tiles is not None,
             "timing": "median of %d calls, one event pair each" % steps,
             "stages_us_with_events": {k: 1e3 * float(np.median([u[k] for u in ups]))
                                       for k in lib.STAGES}}

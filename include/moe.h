@@ -177,13 +177,14 @@ typedef struct {
  *  ones take the MFMA tiles as NVFP4 does, under the same conditions.
  *  shared_up   bf16 [2*I_shared, H] (SwiGLU, gate rows first) or
  *              [I_shared, H] (relu^2); shared_down bf16 [H, I_shared].
- *  w_up_tiles, w_down_tiles  optional (NULL: none), bf16 experts only: the
- *              tile-packed copies of w_up and w_down that moe_pack_tiles
- *              writes. Given, prompt-sized batches' MFMA tiles read their
- *              expert weights there (each K-slice of a tile is one
- *              contiguous 16 KB) and give the same bits as without them;
- *              w_up and w_down are still required and still read by the
- *              decode form, the shared expert and every other path. */
+ *  w_up_tiles, w_down_tiles  optional (NULL: none), bf16 and block-FP8
+ *              experts only: the tile-packed copies of w_up and w_down that
+ *              moe_pack_tiles writes. Given, prompt-sized batches' MFMA
+ *              tiles read their expert weights there (each K-slice of a
+ *              tile is one contiguous 16 KB, 8 KB for FP8) and give the same
+ *              bits as without them; w_up and w_down (and the FP8 scales)
+ *              are still required and still read by the decode form, the
+ *              shared expert and every other path. */
 typedef struct {
     const float *router_w;
     const float *expert_bias;
@@ -197,8 +198,8 @@ typedef struct {
     const uint16_t *shared_down;
     const float *w_up_global;      /* MOE_W_NVFP4: fp32 [E]; otherwise unused */
     const float *w_down_global;
-    const uint16_t *w_up_tiles;    /* moe_pack_tiles(MOE_TILES_UP) of w_up, or NULL */
-    const uint16_t *w_down_tiles;  /* moe_pack_tiles(MOE_TILES_DOWN) of w_down, or NULL */
+    const void *w_up_tiles;        /* moe_pack_tiles(MOE_TILES_UP) of w_up, or NULL */
+    const void *w_down_tiles;      /* moe_pack_tiles(MOE_TILES_DOWN) of w_down, or NULL */
 } moe_weights;
 
 /* Bytes of workspace moe_forward() and moe_plan() need for these dims. With
@@ -211,33 +212,36 @@ typedef struct {
  * batches also hold its m segments' rows: m*T more rows of h and y. */
 int moe_workspace_bytes(const moe_dims *d, size_t *bytes);
 
-/* Tile-packed expert weights (bf16), written once when the weights are
- * loaded, for the grouped GEMMs of the gate_up and down projections
- * (TileGym PR #187, "Weight layout and routing": w_up and w_down as the
- * caller stores them; the packed order is this library's). The MFMA tiles
- * take 256 weight rows at a time (SwiGLU: 128 gate rows, then the 128 up
- * rows of the same columns) and 32 weights of each row per K-slice; in the
- * caller's layout those 16 KB lie in 256 pieces of 64 bytes, 2K bytes
- * apart. The packed copy stores them in the order a stage holds them:
- *   tiles[e][nt][ks][s], 16 bytes per s = 0 .. 1023:
+/* Tile-packed expert weights (bf16 or block-FP8 codes), written once when
+ * the weights are loaded, for the grouped GEMMs of the gate_up and down
+ * projections (TileGym PR #187, "Weight layout and routing": w_up and w_down
+ * as the caller stores them; the packed order is this library's). The MFMA
+ * tiles take 256 weight rows at a time (SwiGLU: 128 gate rows, then the 128
+ * up rows of the same columns) and 32 weights of each row per K-slice; in
+ * the caller's layout those 16 KB (bf16) lie in 256 pieces of 64 bytes, 2K
+ * bytes apart. The packed copy stores them in the order a stage holds them:
+ *   bf16: tiles[e][nt][ks][s], 16 bytes per s = 0 .. 1023:
  *     row r = s / 4 of n-tile nt, chunk c = (s % 4) xor ((r / 4) % 4),
  *     that is weights 32 ks + 8 c .. + 7 of expert row
  *       SwiGLU up:  n = 128 nt + r % 128 (clamped to I - 1), row n for
  *                   r < 128, else row I + n
  *       otherwise:  256 nt + r, clamped to N - 1
  *   nt < ceil(I / 128) (SwiGLU up) or ceil(N / 256), ks < K / 32.
+ *   FP8: the same with 16 codes per slot and two slots per row and slice,
+ *     s = 0 .. 511: row r = s / 2, chunk c = (s % 2) xor ((r / 8) % 2),
+ *     codes 32 ks + 16 c .. + 15.
  * which: MOE_TILES_UP packs w_up (N = 2I or I rows of H), MOE_TILES_DOWN
  * w_down (N = H rows of I). moe_tiles_bytes gives the size:
- * E * n_tiles * K * 512 bytes (rows past N are stored as copies of the
- * last row, so a ragged N costs up to 255 rows per expert). moe_pack_tiles
- * enqueues the copy on stream (w and tiles device memory, 16-byte aligned,
- * not overlapping). d is checked as for moe_forward, and H, I, E and act
- * shape the copy; wfmt must be MOE_W_BF16 (MOE_E_UNSUPPORTED otherwise);
- * MOE_E_WORKSPACE if tiles_bytes is short. The copy is valid while w is
- * unchanged. */
+ * E * n_tiles * K * 512 bytes for bf16, half that for FP8 (rows past N are
+ * stored as copies of the last row, so a ragged N costs up to 255 rows per
+ * expert). moe_pack_tiles enqueues the copy on stream (w and tiles device
+ * memory, 16-byte aligned, not overlapping). d is checked as for
+ * moe_forward, and H, I, E, act and wfmt shape the copy; wfmt must be
+ * MOE_W_BF16 or MOE_W_FP8 (MOE_E_UNSUPPORTED otherwise); MOE_E_WORKSPACE if
+ * tiles_bytes is short. The copy is valid while w is unchanged. */
 typedef enum { MOE_TILES_UP = 0, MOE_TILES_DOWN = 1 } moe_tiles_which;
 int moe_tiles_bytes(const moe_dims *d, int32_t which, size_t *bytes);
-int moe_pack_tiles(const moe_dims *d, int32_t which, const uint16_t *w, uint16_t *tiles,
+int moe_pack_tiles(const moe_dims *d, int32_t which, const void *w, void *tiles,
                    size_t tiles_bytes, hipStream_t stream);
 
 /* Router and top-k (TileGym PR #187 "Weight layout and routing"; TensorFold

@@ -315,18 +315,21 @@ int check_device(const char *what, const char *name, const void *p) {
 struct PackShape {
     int N, K, I;
     bool gate_up;
+    int esz;                       // bytes per weight: 2 (bf16) or 1 (FP8 codes)
 };
 int pack_shape(const char *what, const moe_dims *d, int32_t which, PackShape *ps) {
     TRY(check_dims(what, d, true));
-    REQUIRE(d->wfmt == MOE_W_BF16, MOE_E_UNSUPPORTED,
-            "%s: wfmt = %d, the tile-packed copy is for bf16 experts", what, d->wfmt);
+    REQUIRE(d->wfmt == MOE_W_BF16 || d->wfmt == MOE_W_FP8, MOE_E_UNSUPPORTED,
+            "%s: wfmt = %d, the tile-packed copy is for bf16 and block-FP8 experts", what,
+            d->wfmt);
     REQUIRE(which == MOE_TILES_UP || which == MOE_TILES_DOWN, MOE_E_UNSUPPORTED,
             "%s: which = %d, need MOE_TILES_UP (0) or MOE_TILES_DOWN (1)", what, which);
     const bool swiglu = d->act == MOE_ACT_SWIGLU;
+    const int esz = d->wfmt == MOE_W_FP8 ? 1 : 2;
     if (which == MOE_TILES_UP)
-        *ps = PackShape{swiglu ? 2 * d->I : d->I, d->H, d->I, swiglu};
+        *ps = PackShape{swiglu ? 2 * d->I : d->I, d->H, d->I, swiglu, esz};
     else
-        *ps = PackShape{d->H, d->I, d->I, false};
+        *ps = PackShape{d->H, d->I, d->I, false, esz};
     return MOE_OK;
 }
 
@@ -347,23 +350,23 @@ int moe_tiles_bytes(const moe_dims *d, int32_t which, size_t *bytes) {
     PackShape ps{};
     TRY(pack_shape(what, d, which, &ps));
     REQUIRE(bytes != nullptr, MOE_E_NULL, "%s: bytes is NULL", what);
-    *bytes = moe::pack_tiles_bytes(d->E, ps.N, ps.K, ps.I, ps.gate_up);
+    *bytes = moe::pack_tiles_bytes(d->E, ps.N, ps.K, ps.I, ps.gate_up, ps.esz);
     return ok();
 }
 
-int moe_pack_tiles(const moe_dims *d, int32_t which, const uint16_t *w, uint16_t *tiles,
+int moe_pack_tiles(const moe_dims *d, int32_t which, const void *w, void *tiles,
                    size_t tiles_bytes, hipStream_t stream) {
     const char *what = "moe_pack_tiles";
     PackShape ps{};
     TRY(pack_shape(what, d, which, &ps));
-    const size_t need = moe::pack_tiles_bytes(d->E, ps.N, ps.K, ps.I, ps.gate_up);
+    const size_t need = moe::pack_tiles_bytes(d->E, ps.N, ps.K, ps.I, ps.gate_up, ps.esz);
     REQUIRE(tiles_bytes >= need, MOE_E_WORKSPACE, "%s: tiles_bytes = %zu, need >= %zu", what,
             tiles_bytes, need);
     TRY(check_ptr(what, "w", w));
     TRY(check_ptr(what, "tiles", tiles));
     TRY(check_device(what, "w", w));
     TRY(check_device(what, "tiles", tiles));
-    LAUNCH(moe::launch_pack_tiles(w, tiles, d->E, ps.N, ps.K, ps.I, ps.gate_up, stream));
+    LAUNCH(moe::launch_pack_tiles(w, tiles, d->E, ps.N, ps.K, ps.I, ps.gate_up, ps.esz, stream));
     return ok();
 }
 
@@ -464,8 +467,10 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
         TRY(check_ptr(what, "w->shared_up", w->shared_up));
         TRY(check_ptr(what, "w->shared_down", w->shared_down));
     }
-    REQUIRE((w->w_up_tiles == nullptr && w->w_down_tiles == nullptr) || d->wfmt == MOE_W_BF16,
-            MOE_E_UNSUPPORTED, "%s: w->w_up_tiles / w->w_down_tiles are for bf16 experts (wfmt = %d)",
+    REQUIRE((w->w_up_tiles == nullptr && w->w_down_tiles == nullptr) || d->wfmt == MOE_W_BF16 ||
+                d->wfmt == MOE_W_FP8,
+            MOE_E_UNSUPPORTED,
+            "%s: w->w_up_tiles / w->w_down_tiles are for bf16 and block-FP8 experts (wfmt = %d)",
             what, d->wfmt);
     TRY(check_opt_ptr(what, "w->w_up_tiles", w->w_up_tiles));
     TRY(check_opt_ptr(what, "w->w_down_tiles", w->w_down_tiles));

@@ -205,7 +205,7 @@ struct Req {
     const char *b_base;               // uniform: the expert's weight rows
     uint32_t a_off[Geo<BM>::AI];      // per thread, bytes at K-slice 0
     uint32_t b_off[Geo<BM, WF>::BI];
-    uint32_t b_kstep;                 // uniform: bytes from one K-slice to the next (bf16)
+    uint32_t b_kstep;                 // uniform: bytes from one K-slice to the next (bf16, F8)
     float scale[F8 ? 2 : 1];          // F8: lane b holds the scale of K-block b of each
                                       // weight-row block of the wave (gate, up)
 };
@@ -239,10 +239,16 @@ __device__ __forceinline__ int tile_weight_row(int r, int nt, bool gate_up, int 
 // bf16 stages hold 64 bytes (32 weights along K) of each weight row, four
 // 16-byte slots: chunk c of row r sits at slot 4 r + (c xor bits 2..3 of r),
 // so a fragment read (16 lanes on 16 consecutive rows, one chunk each)
-// covers the 64 banks once. The row and chunk of slot s:
+// covers the 64 banks once. F8 stages hold 32 bytes of each row, two slots:
+// chunk c of row r at slot 2 r + (c xor bit 3 of r). The row and chunk of
+// slot s:
 __device__ __forceinline__ void bf16_slot(int s, int &r, int &c) {
     r = s >> 2;
     c = (s & 3) ^ ((r >> 2) & 3);
+}
+__device__ __forceinline__ void f8_slot(int s, int &r, int &c) {
+    r = s >> 1;
+    c = (s & 1) ^ ((r >> 3) & 1);
 }
 
 // n-tiles of one expert's weight matrix
@@ -254,10 +260,10 @@ __device__ __host__ __forceinline__ int weight_tiles(bool gate_up, int N, int I)
 // of this thread, the byte offset of its row and chunk at K-slice 0 (rows
 // past N are clamped to a valid row).
 //
-// With the tile-packed copy (bf16 experts, p.Btiles) the 16 KB of each
-// K-slice of a tile lie in stage order, so piece s of every slice is at
-// 16 s bytes from the slice's start and one request reads 1 KB in one
-// piece.
+// With the tile-packed copy (bf16 or FP8 experts, p.Btiles) the 16 KB (8
+// KB) of each K-slice of a tile lie in stage order, so piece s of every
+// slice is at 16 s bytes from the slice's start and one request reads 1 KB
+// in one piece.
 //
 // F8 stage rows are 32 bytes, two 16-byte chunks: chunk c of row r sits at
 // slot 2 r + (c ^ bit 3 of r). A fragment read (16 lanes, 16 consecutive
@@ -277,11 +283,11 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
     constexpr int kHalfBytes = F8 ? 2 : G::F4 ? 1 : 4;
     q.b_base = sh ? (const char *)(p.B2 + (size_t)(e - p.E) * p.b2_vstride)
                   : (const char *)p.B + (size_t)e * p.N * p.K * kHalfBytes / 2;
-    const bool tiles = !F8 && !G::F4 && !sh && p.Btiles != nullptr && !p.b_compact;
+    const bool tiles = !G::F4 && !sh && p.Btiles != nullptr && !p.b_compact;
     if (tiles)
-        q.b_base = (const char *)p.Btiles +
-                   ((size_t)e * weight_tiles(gated(MODE), p.N, p.I) + nt) * (size_t)p.K * (kBN * 2);
-    q.b_kstep = tiles ? kBN * 64 : kBK * 2;
+        q.b_base = (const char *)p.Btiles + ((size_t)e * weight_tiles(gated(MODE), p.N, p.I) + nt) *
+                                                (size_t)p.K * (kBN * kHalfBytes / 2);
+    q.b_kstep = (tiles ? kBN : 1) * kBK * kHalfBytes / 2;
     const uint32_t ld = sh ? (uint32_t)p.b2_ld : (uint32_t)p.K;
     const int up_rows = sh ? p.b2_up : p.I;
     if constexpr (F8) {
@@ -311,8 +317,7 @@ __device__ __forceinline__ void b_offsets(const GemmProblem &p, int e, int nt, R
             r = s;
             c = 0;
         } else if (F8) {
-            r = s >> 1;
-            c = (s & 1) ^ ((r >> 3) & 1);
+            f8_slot(s, r, c);
         } else {
             bf16_slot(s, r, c);
         }
@@ -381,8 +386,8 @@ __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmPro
     } else {
         const int i = m - G::AI;
         uint32_t kstep;
-        if constexpr (G::F4 || F8)
-            kstep = G::F4 ? kBK / 2 : kBK;
+        if constexpr (G::F4)
+            kstep = kBK / 2;
         else
             kstep = q.b_kstep;
         buffer_to_lds16(q.b_base, stage + BM * 4 + (wave * G::BI + i) * kWave,
@@ -1201,29 +1206,33 @@ hipError_t launch_bm(const GemmProblem &p, hipStream_t stream) {
 }
 
 #if !defined(MOE_GROUPED_F8_UNIT) && !defined(MOE_GROUPED_F4_UNIT)
-// The tile-packed copy of a bf16 weight tensor W [E][N][K]: tiles[e][nt][ks]
-// is the 16 KB that K-slice ks of n-tile nt puts into a stage, slot s (16
-// bytes) at 16 s. One thread per slot, read from W as the requests of the
-// standard layout read it.
-__global__ __launch_bounds__(kThreads) void k_pack_tiles(const uint4 *__restrict__ W,
+// The tile-packed copy of a weight tensor W [E][N][K] of bf16 (esz 2) or
+// FP8 codes (esz 1): tiles[e][nt][ks] is what K-slice ks of n-tile nt puts
+// into a stage (16 or 8 KB), slot s (16 bytes) at 16 s. One thread per
+// slot, read from W as the requests of the standard layout read it.
+__global__ __launch_bounds__(kThreads) void k_pack_tiles(const char *__restrict__ W,
                                                          uint4 *__restrict__ tiles, int E, int N,
-                                                         int K, int I, int gate_up) {
+                                                         int K, int I, int gate_up, int esz) {
     const int nts = weight_tiles(gate_up != 0, N, I);
     const int KS = K / kBK;
-    constexpr int kSlots = kBN * 4;
-    const size_t total = (size_t)E * nts * KS * kSlots;
+    const int slots = kBN * 2 * esz;
+    const size_t total = (size_t)E * nts * KS * slots;
     for (size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
          idx += (size_t)gridDim.x * kThreads) {
-        const int s = (int)(idx % kSlots);
-        size_t rest = idx / kSlots;
+        const int s = (int)(idx % slots);
+        size_t rest = idx / slots;
         const int ks = (int)(rest % KS);
         rest /= KS;
         const int nt = (int)(rest % nts);
         const int e = (int)(rest / nts);
         int r, c;
-        bf16_slot(s, r, c);
+        if (esz == 2)
+            bf16_slot(s, r, c);
+        else
+            f8_slot(s, r, c);
         const int wr = tile_weight_row(r, nt, gate_up != 0, N, I, I);
-        tiles[idx] = W[(((size_t)e * N + wr) * K + (size_t)ks * kBK + (size_t)c * 8) / 8];
+        const size_t src = (((size_t)e * N + wr) * K + (size_t)ks * kBK) * esz + (size_t)c * 16;
+        tiles[idx] = *(const uint4 *)(W + src);
     }
 }
 
@@ -1308,21 +1317,21 @@ bool grouped_supported(const GemmProblem &p) {
            a_rows * p.lda * 2 < (long long)kPastA && b_bytes < (long long)kPastA;
 }
 
-size_t pack_tiles_bytes(int E, int N, int K, int I, bool gate_up) {
-    return (size_t)E * weight_tiles(gate_up, N, I) * (size_t)K * (kBN * 2);
+size_t pack_tiles_bytes(int E, int N, int K, int I, bool gate_up, int esz) {
+    return (size_t)E * weight_tiles(gate_up, N, I) * (size_t)K * kBN * esz;
 }
 
-hipError_t launch_pack_tiles(const uint16_t *w, uint16_t *tiles, int E, int N, int K, int I,
-                             bool gate_up, hipStream_t stream) {
+hipError_t launch_pack_tiles(const void *w, void *tiles, int E, int N, int K, int I, bool gate_up,
+                             int esz, hipStream_t stream) {
     if (E == 0)
         return hipSuccess;
-    if (K % kBK != 0 || (gate_up && N != 2 * I))
+    if (K % kBK != 0 || (gate_up && N != 2 * I) || (esz != 1 && esz != 2))
         return hipErrorInvalidValue;
-    const size_t slots = pack_tiles_bytes(E, N, K, I, gate_up) / 16;
+    const size_t slots = pack_tiles_bytes(E, N, K, I, gate_up, esz) / 16;
     const size_t want = (slots + kThreads - 1) / kThreads;
     const int blocks = (int)(want < 65536 ? want : 65536);
-    hipLaunchKernelGGL(k_pack_tiles, dim3(blocks), dim3(kThreads), 0, stream, (const uint4 *)w,
-                       (uint4 *)tiles, E, N, K, I, gate_up ? 1 : 0);
+    hipLaunchKernelGGL(k_pack_tiles, dim3(blocks), dim3(kThreads), 0, stream, (const char *)w,
+                       (uint4 *)tiles, E, N, K, I, gate_up ? 1 : 0, esz);
     return hipGetLastError();
 }
 

@@ -81,8 +81,8 @@ struct GemmProblem {
     int E;
     int max_rows;             // bound on offsets[E] (sizes the grid)
     const void *B;            // [E][N][K] bf16, or uint32 codes [E][N][K/8]
-    const void *Btiles;       // bf16 B's tile-packed copy (launch_pack_tiles) or NULL; the
-                              // persistent kernel's expert tiles read it instead of B
+    const void *Btiles;       // bf16 or FP8 B's tile-packed copy (launch_pack_tiles) or
+                              // NULL; the persistent kernel's expert tiles read it instead of B
     const uint16_t *Bscale;   // [E][N][K/64] (affine-4); fp32 [E][N/128][K/128] (fp8)
     const uint16_t *Bbias;
     int N;                    // rows of B per expert
@@ -120,14 +120,14 @@ hipError_t launch_dequant(const GemmProblem &p, uint16_t *out, hipStream_t strea
 // at least 128); launch_gemm routes the problems it supports there.
 bool grouped_supported(const GemmProblem &p);
 hipError_t launch_grouped(const GemmProblem &p, hipStream_t stream);
-// The tile-packed copy of a bf16 weight tensor w [E][N][K] (K a multiple of
-// 32; gate_up: N = 2 I, gate rows first) and its size in bytes: for each
-// expert and n-tile (256 weight rows; SwiGLU: 128 gate rows and their 128 up
-// rows), K / 32 slices of 16 KB in the order the persistent kernel's stages
-// hold them.
-size_t pack_tiles_bytes(int E, int N, int K, int I, bool gate_up);
-hipError_t launch_pack_tiles(const uint16_t *w, uint16_t *tiles, int E, int N, int K, int I,
-                             bool gate_up, hipStream_t stream);
+// The tile-packed copy of a weight tensor w [E][N][K] of bf16 (esz 2) or FP8
+// codes (esz 1) (K a multiple of 32; gate_up: N = 2 I, gate rows first) and
+// its size in bytes: for each expert and n-tile (256 weight rows; SwiGLU:
+// 128 gate rows and their 128 up rows), K / 32 slices of 16 or 8 KB in the
+// order the persistent kernel's stages hold them.
+size_t pack_tiles_bytes(int E, int N, int K, int I, bool gate_up, int esz);
+hipError_t launch_pack_tiles(const void *w, void *tiles, int E, int N, int K, int I, bool gate_up,
+                             int esz, hipStream_t stream);
 // Its block-FP8 form (grouped_gemm_f8.hip); launch_grouped calls it.
 hipError_t launch_grouped_f8(const GemmProblem &p, hipStream_t stream);
 // NVFP4 / MXFP4 weights on the MFMA tiles (grouped_gemm_f4.hip)

@@ -132,10 +132,10 @@ def tiles_bytes(d: Dims, which: str) -> int:
 
 
 def pack_tiles(d: Dims, which: str, w, stream=None) -> torch.Tensor:
-    """The tile-packed copy of a bf16 weight tensor (moe_pack_tiles), as a
-    flat bf16 tensor on w's device."""
+    """The tile-packed copy of a bf16 or FP8 weight tensor (moe_pack_tiles),
+    as a flat uint8 tensor on w's device."""
     n = tiles_bytes(d, which)
-    tiles = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    tiles = torch.empty(n, dtype=torch.uint8, device=w.device)
     _check(load().moe_pack_tiles(C.byref(d), TILES[which], _ptr(w), _ptr(tiles), n,
                                  _stream(stream)))
     return tiles
@@ -251,8 +251,8 @@ class MoEBlock:
                        w_down_tiles=dt)
 
     def pack_tiles(self, stream=None):
-        """Give the block tile-packed copies of its bf16 expert weights
-        (moe_pack_tiles), which the prompt-sized MFMA tiles then read."""
+        """Give the block tile-packed copies of its bf16 or block-FP8 expert
+        weights (moe_pack_tiles), which the prompt-sized MFMA tiles then read."""
         d = self.dims(0)
         self.w_up_tiles = pack_tiles(d, "up", self.w_up, stream)
         self.w_down_tiles = pack_tiles(d, "down", self.w_down, stream)

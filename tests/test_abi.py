@@ -291,10 +291,14 @@ def test_tiles_bytes_and_pack_refusals():
     assert lib.tiles_bytes(relu2, "down") == 128 * 11 * 1856 * 512    # 2688 rows -> 2816
     ragged = dims(T=0, H=128, I=192, E=3, k=2)
     assert lib.tiles_bytes(ragged, "up") == 3 * 2 * 128 * 512         # 192 gate columns -> 256
+    # block-FP8 codes: one byte per weight
+    fp8 = dims(T=0, H=2048, I=1792, E=32, k=4, wfmt="fp8")
+    assert lib.tiles_bytes(fp8, "up") == lib.tiles_bytes(lfm2, "up") // 2
     n = C.c_size_t()
-    # bf16 experts only; which is 0 or 1
-    assert L.moe_tiles_bytes(C.byref(dims(wfmt="fp8", H=256, I=256)), 0, C.byref(n)) == -4
-    assert "bf16" in L.moe_last_error().decode()
+    # bf16 and block-FP8 experts only; which is 0 or 1
+    for fmt in ("affine4", "nvfp4", "mxfp4"):
+        assert L.moe_tiles_bytes(C.byref(dims(wfmt=fmt, H=256, I=256)), 0, C.byref(n)) == -4
+        assert "bf16 and block-FP8" in L.moe_last_error().decode()
     assert L.moe_tiles_bytes(C.byref(lfm2), 2, C.byref(n)) == -4
     assert "which = 2" in L.moe_last_error().decode()
     assert L.moe_tiles_bytes(C.byref(lfm2), 0, None) == -1
@@ -312,7 +316,7 @@ def test_forward_refuses_tiles_of_quantized_experts():
     L = lib.load()
     w = lib.Weights(router_w=0x1000, w_up=0x2000, w_down=0x3000, w_up_scales=0x4000,
                     w_down_scales=0x5000, w_up_tiles=0x6000)
-    d = dims(wfmt="fp8", H=256, I=256)
+    d = dims(wfmt="mxfp4", H=256, I=256)
     rc = L.moe_forward(C.byref(d), C.byref(w), _fake(0x1000), _fake(0x1000), _fake(0x1000),
                        1 << 30, None, None, None, None)
     assert rc == -4 and "w_up_tiles" in L.moe_last_error().decode()
