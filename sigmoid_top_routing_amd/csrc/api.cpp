@@ -133,7 +133,7 @@ Layout layout(const moe_dims &d) {
     L.sorted = take(R * 4);
     L.slot = take(A * 4);
     L.chunk_counts = take((size_t)moe::plan_chunks((int)A) * d.E * 4);
-    L.h = take(R * d.I * 2);
+    L.h = take(((R + 15) & ~(size_t)15) * d.I * 2);   // whole row blocks of 16
     L.y = take(R * d.H * 4);
     if (d.I_shared > 0 && m == 0) {
         L.hs = take((size_t)d.T * d.I_shared * 2);
@@ -627,6 +627,21 @@ int forward_impl(const char *what, const moe_dims *d, const moe_weights *w, cons
     // then runs first.
     const bool fused = decode_form && !dq && moe::stream_supported(up) &&
                        moe::down_combine_supported(down, T, k);
+    // h in row blocks of 16 (each K-slice of a block 1 KB in one piece) when
+    // the persistent kernel both writes it (up) and reads it back (down)
+    {
+        const moe::GemmProblem up_run = dq ? dequantized(up) : up;
+        const moe::GemmProblem down_run =
+            dq && moe::grouped_supported(dequantized(down)) ? dequantized(down) : down;
+        const bool up_tiles = !(decode_form && moe::stream_supported(up_run)) &&
+                              moe::grouped_supported(up_run);
+        const bool down_tiles = !fused && !(decode_form && moe::stream_supported(down_run)) &&
+                                moe::grouped_supported(down_run);
+        const bool blocked = up_tiles && down_tiles && I % 32 == 0 &&
+                             ((int64_t)R + 16) * I * 2 < ((int64_t)1 << 31);
+        up.c_blocked = blocked;
+        down.a_blocked = blocked;
+    }
     const float *shared = nullptr;
     int shared_terms = 1;
     auto run_shared = [&]() -> hipError_t {

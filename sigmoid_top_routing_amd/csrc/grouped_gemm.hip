@@ -183,6 +183,16 @@ __device__ __forceinline__ int gathered_rows(const GemmProblem &p, int row0, int
     return valid;
 }
 
+// Row blocks (p.a_blocked, and p.c_blocked for the bf16 output of the up
+// projections): rows in groups of 16, and within a group the 32 columns of
+// each K-slice of every row together, so group g's slice ks is 1 KB at
+// (g * ld / 32 + ks) * 1 KB, row r of the group at 64 r in it. A request's
+// 16 consecutive rows are then one or two 1 KB pieces. The byte offset of
+// row r, column c (c within the row of ld elements):
+__device__ __forceinline__ uint32_t blocked_offset(uint32_t r, uint32_t c, uint32_t ld) {
+    return (r >> 4) * ld * 32u + (c >> 5) * 1024u + (r & 15u) * 64u + (c & 31u) * 2u;
+}
+
 template <int BM>
 __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)[Geo<BM>::AI],
                                           int valid, uint32_t (&off)[Geo<BM>::AI]) {
@@ -193,7 +203,9 @@ __device__ __forceinline__ void a_offsets(const GemmProblem &p, const int (&raw)
         const int s = (wave * Geo<BM>::AI + i) * kWave + lane;
         const int c = (s & 3) ^ ((s >> 4) & 3);
         const int arow = p.gather ? raw[i] / p.gather_div : raw[i];
-        off[i] = (valid >> i) & 1 ? ((uint32_t)arow * (uint32_t)p.lda + c * 8) * 2u : kPastA;
+        const uint32_t o = p.a_blocked ? blocked_offset((uint32_t)arow, c * 8u, (uint32_t)p.lda)
+                                       : ((uint32_t)arow * (uint32_t)p.lda + c * 8) * 2u;
+        off[i] = (valid >> i) & 1 ? o : kPastA;
     }
 }
 
@@ -382,7 +394,8 @@ __device__ __forceinline__ void request(uint4 *__restrict__ stage, const GemmPro
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (m < G::AI) {
         // pieces of padding rows (offset kPastA) read as zeros
-        buffer_to_lds16(p.A, stage + (wave * G::AI + m) * kWave, q.a_off[m] + (uint32_t)ks * (kBK * 2));
+        const uint32_t kstep = p.a_blocked ? 1024u : kBK * 2;
+        buffer_to_lds16(p.A, stage + (wave * G::AI + m) * kWave, q.a_off[m] + (uint32_t)ks * kstep);
     } else {
         const int i = m - G::AI;
         uint32_t kstep;
@@ -1004,9 +1017,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
         const bool gscaled = !F8 && p.Bglobal != nullptr && e < p.E;
         const float gsc = gscaled ? p.Bglobal[e] : 1.0f;
         const int span_rows = min(row_end - row0, BM);
+        // row blocks: based at the block of row0, spanning the blocks of the
+        // tile's rows (rows past row_end are dropped by their offset)
+        const bool cb = MODE != kDown && p.c_blocked;
+        const int row_base = cb ? row0 & ~15 : row0;
+        const uint32_t span_bytes =
+            cb ? (uint32_t)(((row0 + span_rows + 15) & ~15) - row_base) * (uint32_t)p.ldc * 2u
+               : (uint32_t)span_rows * (uint32_t)p.ldc * kElt;
         const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (char *)p.C + (size_t)row0 * (size_t)p.ldc * kElt, (short)0,
-            (int)((uint32_t)span_rows * (uint32_t)p.ldc * kElt), kBufferWord3);
+            (char *)p.C + (size_t)row_base * (size_t)p.ldc * kElt, (short)0, (int)span_bytes,
+            kBufferWord3);
         if (MODE == kDown) {
             const int n0 = nt * kBN + wn * (kBN / 2);
 #pragma unroll
@@ -1121,9 +1141,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_grouped(GemmProblem p, int n_ti
                         const u32x4 w4 = park_get16(park, r * 128 + chunk * 16);
                         const int prel = a_tile_row + i * 32 + r;   // row within the tile
                         const int col = n0 + jp * 32 + 8 * c;
-                        const uint32_t off = (row0 + prel < row_end && col < ncols)
-                                                 ? ((uint32_t)prel * (uint32_t)p.ldc + col) * 2u
-                                                 : kDropped;
+                        const uint32_t at =
+                            cb ? blocked_offset((uint32_t)(row0 - row_base + prel), (uint32_t)col,
+                                                (uint32_t)p.ldc)
+                               : ((uint32_t)prel * (uint32_t)p.ldc + col) * 2u;
+                        const uint32_t off = (row0 + prel < row_end && col < ncols) ? at : kDropped;
                         __builtin_amdgcn_raw_buffer_store_b128(w4, out_rsrc, off, 0, 0);
                     }
                     fence();

@@ -74,6 +74,11 @@ struct GemmProblem {
                               // launch_dequant reads it
     const uint16_t *A;        // bf16 rows, lda elements apart
     int lda;
+    int a_blocked;            // A in row blocks (the persistent kernel's output with
+                              // c_blocked): rows in groups of 16, each group's K-slices of
+                              // 32 columns 1 KB apiece; not gathered
+    int c_blocked;            // kGateUp / kUpRelu2 on the persistent kernel: C (bf16) in those
+                              // row blocks, for a down projection with a_blocked
     const int32_t *gather;    // A row of position p = gather[p] / gather_div (NULL: row p)
     int gather_div;
     const int32_t *offsets;   // [E+1] segment bounds (NULL: one segment [0, rows))
