@@ -1270,6 +1270,16 @@ hipError_t launch_mode(const GemmProblem &p, hipStream_t stream) {
     int n_tiles = 0;
     if (avg >= 192 && (p.offsets != nullptr || tiles_bound<256, MODE>(p, n_tiles) >= cu_count()))
         return launch_bm<256, MODE>(p, stream);
+    // The down projection of a routed batch takes them from 64 rows per
+    // segment on when they still fill two rounds of CUs: at 96 rows over 130
+    // segments (the relu^2 block, T = 2048, E = 128, k = 6, its shared expert
+    // as two segments) 256-row tiles ran 363 us against 401 us for 128-row
+    // tiles, where the up projection went the other way (408 against 392 us);
+    // at 128 rows over 32 segments, four of them long (the 4-bit block at
+    // T = 1024), they left CUs idle: 55 against 50 us
+    if (MODE == kDown && p.offsets != nullptr && avg >= 64 &&
+        tiles_bound<256, MODE>(p, n_tiles) >= 2LL * cu_count())
+        return launch_bm<256, MODE>(p, stream);
     return launch_bm<128, MODE>(p, stream);
 }
 
